@@ -1,0 +1,235 @@
+/* spb.h -- C ABI of libspb: the packed forward of one token-budget scoring pass
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [PyPI]    "spinf-serve 0.1.1", project page on pypi.org;
+ *   [man]     "spinf-serve", man page on linuxcommandlibrary.com;
+ *   [article] "Bulk classification and decision inference on one GPU"
+ *             (English original on aitujian.cn).
+ *
+ * The pass: many inputs are packed into one forward pass of at most a token
+ * budget (16,384 by default) [PyPI "What it does": Throughput; man PARAMETERS
+ * --token-budget].  Each input is a content read once, followed by its
+ * questions as branches of that read [PyPI "What it does": Many questions, one
+ * read].  A question is a template ending where the answer goes; multi-token
+ * options hang under it as a token trie [PyPI "What it does": Scoring; PyPI
+ * "Layout": compiler.py].  Every token attends to its own content and the
+ * causal prefix of its own branch only.  At the answer slot each option gets a
+ * vocab-wide log-probability, p renormalised over the options, the residual
+ * mass outside them, and the floor p of the same question on empty content
+ * [article, the response example and the paragraph after it].
+ *
+ * Conventions for every call:
+ *   - The caller owns every buffer (host arrays and device memory).  The library
+ *     owns only the opaque plan.  No call allocates device memory or
+ *     synchronises a stream; work is enqueued on the caller's stream
+ *     (a hipStream_t passed as void*, NULL = the null stream).
+ *   - All argument and limit checks run on the host before any HIP call, so a
+ *     call that returns an error has enqueued nothing.  Kernel faults surface
+ *     at the caller's next synchronisation as HIP errors.
+ *   - Errors: a negative spb_status; spb_last_error() gives a message
+ *     (thread-local, valid until the next spb_* call on that thread).
+ *   - Plans are immutable after spb_pack_pass: concurrent readers are safe.
+ *   - Results are a function of the logical problem alone: an input's scores
+ *     are bit-identical whatever it is packed with, in any order, at any budget
+ *     ("batch invariance", [PyPI "What it does"]).
+ */
+#ifndef SPB_H
+#define SPB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t spb_status;
+enum {
+  SPB_OK = 0,
+  SPB_ERR_ARG = -1,   /* null pointer, malformed CSR, token id >= vocab, duplicate option */
+  SPB_ERR_LIMIT = -2, /* a request limit or the token budget is exceeded                  */
+  SPB_ERR_DTYPE = -3, /* unsupported dtype, head_dim, GQA ratio or hidden size            */
+  SPB_ERR_SIZE = -4,  /* caller buffer, metadata or workspace too small                   */
+  SPB_ERR_HIP = -5    /* HIP runtime or launch error (no device, bad launch)               */
+};
+
+typedef enum { SPB_F32 = 0, SPB_BF16 = 1, SPB_FP8_E4M3 = 2 /* OCP e4m3fn */ } spb_dtype;
+
+const char *spb_last_error(void);
+/* Build id, tile constants and numerics-contract version.  Two results are
+ * bit-comparable when their fingerprints are equal (PyPI "What it does":
+ * system_fingerprint). */
+const char *spb_fingerprint(void);
+
+/* ------------------------------------------------------------------ problem
+ * The logical problem, in token ids.  Host memory, owned by the caller, read
+ * only during spb_pack_pass.
+ *   input i: content of content_len[i] tokens; asks the questions
+ *            branch_q[branch_off[i] .. branch_off[i+1]).
+ *   question q: template of q_len[q] tokens (the last one is the row in front
+ *            of the answer slot, whose next-token distribution scores the
+ *            options' first tokens); options opt_off[q] .. opt_off[q+1).
+ *   option o: tokens tok[tok_off[o] .. tok_off[o+1]).
+ * Options of one question must be distinct (SPB_ERR_ARG).  An option that is
+ * a prefix of another is accepted; then the residual can be negative.
+ *
+ * Logical rows (the numbering activations are addressed by): inputs in order,
+ * then, with floors, one floor input per distinct asked question in ascending
+ * id; inside an input its content rows, then per branch the template rows
+ * followed by the option-trie nodes of its question.  Trie nodes are the
+ * distinct proper prefixes of the options in first-appearance order (options
+ * in order, each option's prefixes by increasing length). */
+typedef struct {
+  int32_t n_inputs;
+  const int32_t *content_len; /* [n_inputs], >= 0                  */
+  const int32_t *branch_off;  /* [n_inputs + 1]                    */
+  const int32_t *branch_q;    /* [branch_off[n_inputs]]            */
+  int32_t n_questions;
+  const int32_t *q_len;       /* [n_questions], >= 1               */
+  const int32_t *opt_off;     /* [n_questions + 1]                 */
+  const int32_t *tok_off;     /* [opt_off[n_questions] + 1]        */
+  const int32_t *tok;         /* [tok_off[n_options]], < vocab     */
+  int32_t vocab;
+} spb_problem;
+
+/* Packing options; request limits default to the man page's [man PARAMETERS]. */
+typedef struct {
+  int32_t token_budget;          /* packed tokens per pass, default 16384                    */
+  int32_t floors;                /* 1: add one empty-content floor branch per asked question */
+  int32_t max_content_tokens;    /* default 4096                                             */
+  int32_t max_query_tokens;      /* default 256 (template length)                           */
+  int32_t max_options;           /* default 1000 (per question)                             */
+  int32_t max_option_tokens;     /* default 5                                                */
+  int32_t max_prompts_per_input; /* default 10000 (branches per input)                      */
+  int64_t max_processed_tokens;  /* default 2000000 (all passes, re-staged content, floors) */
+} spb_pack_opts;
+
+void spb_pack_opts_default(spb_pack_opts *opts);
+
+typedef struct spb_plan spb_plan; /* opaque, library-owned */
+
+typedef struct {
+  int32_t n_tokens;       /* packed rows of the pass                          */
+  int32_t n_segments;     /* placed contents (a re-staged content counts again) */
+  int32_t n_branches;     /* branches placed (content + floor)                */
+  int32_t n_options;      /* option slots (lp / p outputs)                    */
+  int32_t n_scored_rows;  /* rows fed to the lm head                          */
+  int32_t n_targets;      /* distinct (scored row, next token) logits captured */
+  int32_t n_tiles;        /* attention tiles (at most 128 rows of one segment) */
+  int32_t n_passes;       /* totals only (pass = -1)                          */
+  int64_t unmasked_pairs; /* (query row, key row) pairs attended, per head    */
+  size_t meta_bytes;      /* device metadata size for spb_plan_upload         */
+  int32_t n_content_branches, n_content_options; /* totals only: finalize sizes */
+  int32_t n_logical_inputs; /* totals only: inputs, then floor inputs           */
+} spb_pass_info;
+
+/* Packs every input (and the floors) into passes of at most token_budget rows.
+ * Rule: inputs in order, then floors; an input goes whole into the current
+ * pass if it fits, else whole into a new pass; an input larger than the
+ * budget spills at branch boundaries, its content re-staged in each pass it
+ * continues in.  SPB_ERR_LIMIT when content + one branch exceeds the budget.
+ * Cites [PyPI "What it does": Throughput; man PARAMETERS --token-budget,
+ * --max-tokens and the request limits; man CAVEATS]. */
+spb_status spb_pack_pass(const spb_problem *problem, const spb_pack_opts *opts, spb_plan **out);
+void spb_plan_free(spb_plan *plan);
+spb_status spb_plan_num_passes(const spb_plan *plan, int32_t *n);
+spb_status spb_plan_info(const spb_plan *plan, int32_t pass, spb_pass_info *out); /* pass -1: totals */
+/* logical_row[n_tokens]: the logical row placed at each pass row.
+ * scored_row[n_scored_rows]: pass rows read by the lm head, in scoring order.
+ * Either pointer may be NULL.  Host buffers, caller-owned. */
+spb_status spb_plan_rows(const spb_plan *plan, int32_t pass, int64_t *logical_row, int32_t *scored_row);
+/* Per placed branch of the pass: its logical branch (content branches numbered
+ * in input / CSR order, then floor branches in ascending question id) and its
+ * first option slot.  Either pointer may be NULL. */
+spb_status spb_plan_branches(const spb_plan *plan, int32_t pass, int32_t *logical_branch, int32_t *opt_first);
+/* Logical inputs in row-numbering order (inputs, then floor inputs):
+ * row_off[n_logical_inputs + 1] is the first logical row of each;
+ * floor_question[n_logical_inputs] is the question of a floor input, -1 for
+ * a content input.  Either pointer may be NULL. */
+spb_status spb_plan_inputs(const spb_plan *plan, int64_t *row_off, int32_t *floor_question);
+/* Host debugging aid: the pass rows that pass row `row` attends to, read from
+ * the same metadata and visibility rule the kernel uses. */
+spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int32_t *keys, int32_t cap,
+                            int32_t *n_keys);
+/* Copies the pass's device metadata (meta_bytes) from host to d_meta on the
+ * stream.  d_meta: device memory, 256-byte aligned, caller-owned. */
+spb_status spb_plan_upload(const spb_plan *plan, int32_t pass, void *d_meta, size_t bytes, void *stream);
+
+/* ------------------------------------------------------------------ attention
+ * For every packed row x and query head h:
+ *   O[x,h] = sum_{y in path(x)} softmax_y(scale * q[x,h] . k[y,g]) v[y,g],
+ *   g = h / (hq / hkv),
+ * path(x) = own content (causal for content rows, all of it for branch rows),
+ * own template prefix, own option-trie ancestors.  Equals plain causal
+ * attention over each content + branch sequence run alone [PyPI "Speed and
+ * scale": the same answers as per-question prompts].
+ * Layout: q [rows, hq, d], k and v [rows, hkv, d], o [rows, hq, d], token-major,
+ * contiguous, device memory, rows >= n_tokens of the pass.  All inputs finite.
+ * in_dtype: SPB_F32 (rounded to bf16 on load), SPB_BF16, or SPB_FP8_E4M3 with
+ * per-tensor dequantisation scales s_q, s_k, s_v (static "fp8s"-style
+ * calibration [man DESCRIPTION: calibrate]; QK^T on fp8 MFMA, P.V on bf16).
+ * out_dtype: SPB_F32 or SPB_BF16.  head_dim 64 or 128; hq % hkv == 0 and
+ * hq / hkv in {1, 2, 4}.  softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * d_meta: the upload of (plan, pass). */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  int32_t in_dtype, out_dtype;
+  int32_t hq, hkv, head_dim;
+  float softmax_scale;
+  float s_q, s_k, s_v;
+  int64_t rows; /* rows of q/k/v/o buffers, >= n_tokens */
+} spb_attn_args;
+
+spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_attn_args *args,
+                                void *stream);
+
+/* ------------------------------------------------------------------ scoring
+ * For every scored row r (each template's last row and each trie node):
+ *   z_r = W h_r over the whole vocabulary, f32 (the "f32out" lm head [man
+ *   PARAMETERS --lm-head]); LSE_r = log sum exp z_r.
+ * For option o of a branch with tokens t_1..t_n:
+ *   lp_o = sum_k z_{r_{k-1}}[t_k] - LSE_{r_{k-1}}  (r_0 = template's last row,
+ *          r_k = trie node of t_1..t_k);
+ *   p_o  = exp(lp_o) / sum_{o'} exp(lp_o')        (probability among the options);
+ *   residual = 1 - sum_o exp(lp_o)                (mass outside the options)
+ * [article, the response example and the paragraph after it].
+ * hidden [rows, hidden_dim] (SPB_BF16, or SPB_F32 rounded to bf16 on load),
+ * only scored rows are read; lm_head [vocab, hidden_dim] bf16 row-major;
+ * hidden_dim % 64 == 0.  Outputs (device, f32): lp and p [n_options],
+ * residual [n_branches], in the pass's slot order.  workspace: device memory
+ * of spb_score_workspace_bytes, 256-byte aligned; no state is kept in it
+ * between calls. */
+typedef struct {
+  const void *hidden;
+  int32_t h_dtype;
+  int32_t hidden_dim;
+  int64_t rows; /* rows of the hidden buffer, >= n_tokens */
+  const void *lm_head;
+  int32_t vocab;
+  void *workspace;
+  size_t workspace_bytes;
+  float *lp, *p, *residual;
+} spb_score_args;
+
+spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, size_t *out);
+spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *args,
+                             void *stream);
+
+/* Host, after all passes: gathers each content branch's results into logical
+ * order and joins the floors.  *_per_pass[k] are host copies of pass k's lp,
+ * p and residual outputs.  Outputs (host, caller-owned): lp, p, floor_p, lift
+ * [n_content_options] and residual [n_content_branches] in logical order
+ * (content branches in input / CSR order, options in question order).
+ * floor_p = p of the same question's floor branch, lift = p - floor_p
+ * [PyPI "What it does": Scoring; article, after the response example]; NaN
+ * when the plan has no floors.  Any output pointer may be NULL. */
+spb_status spb_score_finalize(const spb_plan *plan, const float *const *lp_per_pass, const float *const *p_per_pass,
+                              const float *const *residual_per_pass, float *lp, float *p, float *residual,
+                              float *floor_p, float *lift);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPB_H */

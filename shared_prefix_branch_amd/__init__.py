@@ -1,0 +1,310 @@
+"""Python binding of libspb (ctypes; argument marshalling only).
+
+Every step of the path runs in libspb: the host packer and metadata builder
+(C++) and the gfx950 kernels.  torch tensors are used only as device memory
+and for the current HIP stream.  The functions mirror the C ABI in
+include/spb.h; errors raise ``SpbError(code, message)``.  If the library is
+not built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "SpbError", "lib", "library_path", "fingerprint", "Plan", "pack_pass", "branch_attention",
+    "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
+    "EXPORTED_SYMBOLS",
+]
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libspb.so")
+
+EXPORTED_SYMBOLS = [
+    "spb_last_error", "spb_fingerprint", "spb_pack_opts_default", "spb_pack_pass", "spb_plan_free",
+    "spb_plan_num_passes", "spb_plan_info", "spb_plan_rows", "spb_plan_branches", "spb_plan_inputs",
+    "spb_plan_visible",
+    "spb_plan_upload", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
+    "spb_score_finalize",
+]
+
+
+class SpbError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"spb error {code}: {message}")
+        self.code = code
+
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f32p = ctypes.POINTER(ctypes.c_float)
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("n_inputs", ctypes.c_int32), ("content_len", _i32p), ("branch_off", _i32p),
+                ("branch_q", _i32p), ("n_questions", ctypes.c_int32), ("q_len", _i32p),
+                ("opt_off", _i32p), ("tok_off", _i32p), ("tok", _i32p), ("vocab", ctypes.c_int32)]
+
+
+class _PackOpts(ctypes.Structure):
+    _fields_ = [("token_budget", ctypes.c_int32), ("floors", ctypes.c_int32),
+                ("max_content_tokens", ctypes.c_int32), ("max_query_tokens", ctypes.c_int32),
+                ("max_options", ctypes.c_int32), ("max_option_tokens", ctypes.c_int32),
+                ("max_prompts_per_input", ctypes.c_int32), ("max_processed_tokens", ctypes.c_int64)]
+
+
+class _PassInfo(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("n_segments", ctypes.c_int32), ("n_branches", ctypes.c_int32),
+                ("n_options", ctypes.c_int32), ("n_scored_rows", ctypes.c_int32), ("n_targets", ctypes.c_int32),
+                ("n_tiles", ctypes.c_int32), ("n_passes", ctypes.c_int32), ("unmasked_pairs", ctypes.c_int64),
+                ("meta_bytes", ctypes.c_size_t), ("n_content_branches", ctypes.c_int32),
+                ("n_content_options", ctypes.c_int32), ("n_logical_inputs", ctypes.c_int32)]
+
+
+class _AttnArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("hq", ctypes.c_int32),
+                ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("s_q", ctypes.c_float), ("s_k", ctypes.c_float), ("s_v", ctypes.c_float),
+                ("rows", ctypes.c_int64)]
+
+
+class _ScoreArgs(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_void_p), ("h_dtype", ctypes.c_int32), ("hidden_dim", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("lm_head", ctypes.c_void_p), ("vocab", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("lp", _f32p), ("p", _f32p), ("residual", _f32p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspb (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise SpbError(-5, f"{library_path} is not built: run `python -m shared_prefix_branch_amd.build`")
+        L = ctypes.CDLL(library_path)
+        L.spb_last_error.restype = ctypes.c_char_p
+        L.spb_fingerprint.restype = ctypes.c_char_p
+        L.spb_pack_opts_default.argtypes = [ctypes.POINTER(_PackOpts)]
+        L.spb_pack_opts_default.restype = None
+        L.spb_pack_pass.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_PackOpts), ctypes.POINTER(ctypes.c_void_p)]
+        L.spb_plan_free.argtypes = [ctypes.c_void_p]
+        L.spb_plan_free.restype = None
+        L.spb_plan_num_passes.argtypes = [ctypes.c_void_p, _i32p]
+        L.spb_plan_info.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(_PassInfo)]
+        L.spb_plan_rows.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i64p, _i32p]
+        L.spb_plan_branches.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
+        L.spb_plan_inputs.argtypes = [ctypes.c_void_p, _i64p, _i32p]
+        L.spb_plan_visible.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p]
+        L.spb_plan_upload.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.spb_branch_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.POINTER(_AttnArgs), ctypes.c_void_p]
+        L.spb_score_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+        L.spb_score_options.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.POINTER(_ScoreArgs), ctypes.c_void_p]
+        fpp = ctypes.POINTER(_f32p)
+        L.spb_score_finalize.argtypes = [ctypes.c_void_p, fpp, fpp, fpp, _f32p, _f32p, _f32p, _f32p, _f32p]
+        for name in EXPORTED_SYMBOLS:
+            if name not in ("spb_last_error", "spb_fingerprint", "spb_pack_opts_default", "spb_plan_free"):
+                getattr(L, name).restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SpbError(int(status), lib().spb_last_error().decode())
+
+
+def fingerprint() -> str:
+    return lib().spb_fingerprint().decode()
+
+
+def _ptr(a: np.ndarray, typ):
+    return a.ctypes.data_as(typ)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """An opaque packing plan (owned here, freed with the object)."""
+
+    def __init__(self, handle: int, keep):
+        self._h = ctypes.c_void_p(handle)
+        self._keep = keep
+        n = ctypes.c_int32()
+        _check(lib().spb_plan_num_passes(self._h, ctypes.byref(n)))
+        self.n_passes = int(n.value)
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and self._h.value and _lib is not None:
+            _lib.spb_plan_free(self._h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self, pass_: int = -1) -> dict:
+        s = _PassInfo()
+        _check(lib().spb_plan_info(self._h, pass_, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in _PassInfo._fields_}
+
+    def rows(self, pass_: int):
+        inf = self.info(pass_)
+        lr = np.empty(inf["n_tokens"], np.int64)
+        sr = np.empty(inf["n_scored_rows"], np.int32)
+        _check(lib().spb_plan_rows(self._h, pass_, _ptr(lr, _i64p), _ptr(sr, _i32p)))
+        return lr, sr
+
+    def branches(self, pass_: int):
+        inf = self.info(pass_)
+        lb = np.empty(inf["n_branches"], np.int32)
+        of = np.empty(inf["n_branches"], np.int32)
+        _check(lib().spb_plan_branches(self._h, pass_, _ptr(lb, _i32p), _ptr(of, _i32p)))
+        return lb, of
+
+    def inputs(self):
+        """(row_off [n_logical_inputs + 1] int64, floor_question [n_logical_inputs] int32)."""
+        n = self.info()["n_logical_inputs"]
+        off = np.empty(n + 1, np.int64)
+        fq = np.empty(n, np.int32)
+        _check(lib().spb_plan_inputs(self._h, _ptr(off, _i64p), _ptr(fq, _i32p)))
+        return off, fq
+
+    def visible(self, pass_: int, row: int, cap: int = 1 << 16) -> List[int]:
+        keys = np.empty(cap, np.int32)
+        n = ctypes.c_int32()
+        _check(lib().spb_plan_visible(self._h, pass_, row, _ptr(keys, _i32p), cap, ctypes.byref(n)))
+        return keys[:n.value].tolist()
+
+    def upload(self, pass_: int, d_meta, stream=None):
+        _check(lib().spb_plan_upload(self._h, pass_, ctypes.c_void_p(d_meta.data_ptr()),
+                                     d_meta.numel() * d_meta.element_size(), ctypes.c_void_p(_stream_handle(stream))))
+
+
+def pack_pass(problem, token_budget: int = 16384, floors: bool = True, **limits) -> Plan:
+    """Packs a logical problem (any object with the CSR fields of spb_problem)."""
+    arrs = {f: np.ascontiguousarray(getattr(problem, f), dtype=np.int32)
+            for f in ("content_len", "branch_off", "branch_q", "q_len", "opt_off", "tok_off", "tok")}
+    P = _Problem()
+    P.n_inputs = int(arrs["content_len"].shape[0])
+    P.n_questions = int(arrs["q_len"].shape[0])
+    for f, a in arrs.items():
+        setattr(P, f, _ptr(a, _i32p))
+    P.vocab = int(problem.vocab)
+    O = _PackOpts()
+    lib().spb_pack_opts_default(ctypes.byref(O))
+    O.token_budget = int(token_budget)
+    O.floors = 1 if floors else 0
+    for k, v in limits.items():
+        setattr(O, k, int(v))
+    h = ctypes.c_void_p()
+    _check(lib().spb_pack_pass(ctypes.byref(P), ctypes.byref(O), ctypes.byref(h)))
+    return Plan(h.value, None)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise SpbError(-3, f"unsupported tensor dtype {t.dtype}")
+
+
+def branch_attention(plan: Plan, pass_: int, d_meta, q, k, v, o, softmax_scale: float = 0.0,
+                     scales: Sequence[float] = (1.0, 1.0, 1.0), stream=None):
+    """q [rows, hq, d], k/v [rows, hkv, d], o [rows, hq, d]: contiguous device tensors."""
+    for t in (q, k, v, o):
+        if not t.is_contiguous():
+            raise SpbError(-1, "tensors must be contiguous")
+    A = _AttnArgs()
+    A.q, A.k, A.v, A.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    A.in_dtype = _dtype_code(q)
+    if _dtype_code(k) != A.in_dtype or _dtype_code(v) != A.in_dtype:
+        raise SpbError(-3, "q, k and v must share one dtype")
+    A.out_dtype = _dtype_code(o)
+    A.hq, A.hkv, A.head_dim = int(q.shape[1]), int(k.shape[1]), int(q.shape[2])
+    if k.shape[2] != A.head_dim or o.shape[1] != A.hq or o.shape[2] != A.head_dim or v.shape != k.shape:
+        raise SpbError(-1, "q/k/v/o shapes disagree")
+    A.softmax_scale = float(softmax_scale)
+    A.s_q, A.s_k, A.s_v = (float(s) for s in scales)
+    A.rows = int(min(q.shape[0], k.shape[0], v.shape[0], o.shape[0]))
+    _check(lib().spb_branch_attention(plan.handle, pass_, ctypes.c_void_p(d_meta.data_ptr()), ctypes.byref(A),
+                                      ctypes.c_void_p(_stream_handle(stream))))
+
+
+def score_workspace_bytes(plan: Plan, pass_: int, vocab: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().spb_score_workspace_bytes(plan.handle, pass_, int(vocab), ctypes.byref(n)))
+    return int(n.value)
+
+
+def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual, stream=None):
+    """hidden [rows, H] (bf16/f32), lm_head [V, H] bf16, workspace uint8 device buffer,
+    lp/p [n_options] and residual [n_branches] float32 device tensors."""
+    import torch
+    if lm_head.dtype != torch.bfloat16:
+        raise SpbError(-3, "lm_head must be bfloat16")
+    for t in (lp, p, residual):
+        if t.dtype != torch.float32:
+            raise SpbError(-3, "outputs must be float32")
+    S = _ScoreArgs()
+    S.hidden = hidden.data_ptr()
+    S.h_dtype = _dtype_code(hidden)
+    S.hidden_dim = int(hidden.shape[1])
+    S.rows = int(hidden.shape[0])
+    if int(lm_head.shape[1]) != S.hidden_dim:
+        raise SpbError(-1, "lm_head and hidden disagree on the hidden size")
+    S.lm_head = lm_head.data_ptr()
+    S.vocab = int(lm_head.shape[0])
+    S.workspace = workspace.data_ptr()
+    S.workspace_bytes = workspace.numel() * workspace.element_size()
+    S.lp = ctypes.cast(ctypes.c_void_p(lp.data_ptr()), _f32p)
+    S.p = ctypes.cast(ctypes.c_void_p(p.data_ptr()), _f32p)
+    S.residual = ctypes.cast(ctypes.c_void_p(residual.data_ptr()), _f32p)
+    _check(lib().spb_score_options(plan.handle, pass_, ctypes.c_void_p(d_meta.data_ptr()), ctypes.byref(S),
+                                   ctypes.c_void_p(_stream_handle(stream))))
+
+
+def score_finalize(plan: Plan, lp_per_pass, p_per_pass, res_per_pass) -> dict:
+    """Host floor join.  Inputs: per-pass float32 numpy arrays.  Returns numpy
+    arrays lp, p, floor_p, lift [n_content_options], residual [n_content_branches]."""
+    inf = plan.info(-1)
+    n = plan.n_passes
+    keep = []
+
+    def table(arrs):
+        t = (_f32p * n)()
+        for i, a in enumerate(arrs):
+            a = np.ascontiguousarray(a, dtype=np.float32)
+            keep.append(a)
+            t[i] = _ptr(a, _f32p)
+        return t
+
+    tl, tp, tr = table(lp_per_pass), table(p_per_pass), table(res_per_pass)
+    no, nb = inf["n_content_options"], inf["n_content_branches"]
+    out = {k: np.empty(no, np.float32) for k in ("lp", "p", "floor_p", "lift")}
+    out["residual"] = np.empty(nb, np.float32)
+    _check(lib().spb_score_finalize(plan.handle, tl, tp, tr, _ptr(out["lp"], _f32p), _ptr(out["p"], _f32p),
+                                    _ptr(out["residual"], _f32p), _ptr(out["floor_p"], _f32p),
+                                    _ptr(out["lift"], _f32p)))
+    return out

@@ -1,0 +1,51 @@
+"""Builds libspb.so in-tree for gfx950 with hipcc.
+
+    python -m shared_prefix_branch_amd.build
+
+One shared library: the host planner and C ABI (spb_host.cpp) and the two
+kernel sources.  Packed-FP32 instruction selection is switched off for the GPU
+code (-packed-fp32-ops).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libspb.so")
+SOURCES = ["spb_host.cpp", "spb_attention.hip", "spb_score.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles the library (always) and returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", "-I", os.path.join(HERE, "..", "include")]
+    cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
+    if verbose and errs:
+        print(errs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,819 @@
+// spb_host.cpp -- the host half of libspb: request validation, the pass packer
+// and metadata builder, metadata upload, kernel-argument checks and the
+// floor join.  Pure C++17 plus the HIP runtime's copy call; no kernels here.
+//
+// Packing follows the pages: inputs are packed into token-budget passes, the
+// content read once and every question a branch of the same pass [PyPI
+// "spinf-serve 0.1.1", "What it does": Many questions, one read; Throughput].
+// Option strings become token tries [PyPI, "Layout": compiler.py]; request
+// limits default to the man page's [man page "spinf-serve", PARAMETERS].
+#define SPB_HD
+#include "spb_meta.h"
+#include "spb_launch.h"
+#include "../../include/spb.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <new>
+#include <set>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+using namespace spb;
+
+namespace {
+
+thread_local std::string g_err;
+
+spb_status fail(spb_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+spb_status ok() {
+  g_err.clear();
+  return SPB_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ----------------------------------------------------------------- questions
+
+// One question compiled: its template length and the trie of its options.
+struct Question {
+  int L = 0;
+  int n_nodes = 0;
+  int n_opt = 0;
+  std::vector<int> node_depth;                  // [n_nodes]
+  std::vector<std::vector<int>> node_anc;       // [n_nodes][depth]: extended indices, self last
+  // scored rows of one branch: 0 = template's last row, 1 + i = node i
+  std::vector<std::vector<int>> targets;        // [1 + n_nodes]: distinct next tokens
+  // per option: (local scored row, index into that row's targets) per token
+  std::vector<std::vector<std::pair<int, int>>> steps;
+  int n_targets = 0;
+  int n_steps = 0;
+  int E() const { return L + n_nodes; }
+};
+
+spb_status compile_question(const spb_problem &P, int q, const spb_pack_opts &o, Question &Q) {
+  Q.L = P.q_len[q];
+  if (Q.L < 1) return fail(SPB_ERR_ARG, "question %d: template length %d < 1", q, Q.L);
+  if (Q.L > o.max_query_tokens)
+    return fail(SPB_ERR_LIMIT, "question %d: template of %d tokens exceeds max_query_tokens %d", q, Q.L,
+                o.max_query_tokens);
+  int o0 = P.opt_off[q], o1 = P.opt_off[q + 1];
+  if (o1 < o0) return fail(SPB_ERR_ARG, "opt_off not monotone at question %d", q);
+  Q.n_opt = o1 - o0;
+  if (Q.n_opt < 1) return fail(SPB_ERR_ARG, "question %d has no options", q);
+  if (Q.n_opt > o.max_options)
+    return fail(SPB_ERR_LIMIT, "question %d: %d options exceed max_options %d", q, Q.n_opt, o.max_options);
+  std::vector<std::vector<int>> opts(Q.n_opt);
+  std::set<std::vector<int>> seen;
+  for (int k = 0; k < Q.n_opt; ++k) {
+    int t0 = P.tok_off[o0 + k], t1 = P.tok_off[o0 + k + 1];
+    if (t1 < t0) return fail(SPB_ERR_ARG, "tok_off not monotone at option %d", o0 + k);
+    int n = t1 - t0;
+    if (n < 1) return fail(SPB_ERR_ARG, "question %d option %d is empty", q, k);
+    if (n > o.max_option_tokens)
+      return fail(SPB_ERR_LIMIT, "question %d option %d: %d tokens exceed max_option_tokens %d", q, k, n,
+                  o.max_option_tokens);
+    if (n - 1 > kMaxDepth) return fail(SPB_ERR_LIMIT, "option of %d tokens exceeds the trie depth %d", n, kMaxDepth);
+    for (int t = t0; t < t1; ++t) {
+      if (P.tok[t] < 0 || P.tok[t] >= P.vocab)
+        return fail(SPB_ERR_ARG, "question %d option %d: token id %d outside [0, %d)", q, k, P.tok[t], P.vocab);
+      opts[k].push_back(P.tok[t]);
+    }
+    if (!seen.insert(opts[k]).second) return fail(SPB_ERR_ARG, "question %d: option %d is a duplicate", q, k);
+  }
+  // trie nodes: distinct proper prefixes in first-appearance order
+  std::map<std::vector<int>, int> node_of;
+  std::vector<std::vector<int>> prefixes;
+  for (auto &op : opts)
+    for (size_t k = 1; k < op.size(); ++k) {
+      std::vector<int> pre(op.begin(), op.begin() + k);
+      if (!node_of.count(pre)) {
+        node_of[pre] = (int)prefixes.size();
+        prefixes.push_back(pre);
+      }
+    }
+  Q.n_nodes = (int)prefixes.size();
+  if (Q.E() > 32767) return fail(SPB_ERR_LIMIT, "question %d: template + trie of %d rows exceeds 32767", q, Q.E());
+  Q.node_depth.resize(Q.n_nodes);
+  Q.node_anc.resize(Q.n_nodes);
+  for (int i = 0; i < Q.n_nodes; ++i) {
+    const auto &pre = prefixes[i];
+    Q.node_depth[i] = (int)pre.size();
+    for (size_t k = 1; k <= pre.size(); ++k) {
+      std::vector<int> a(pre.begin(), pre.begin() + k);
+      Q.node_anc[i].push_back(Q.L + node_of[a]);
+    }
+  }
+  Q.targets.assign(1 + Q.n_nodes, {});
+  Q.steps.assign(Q.n_opt, {});
+  for (int k = 0; k < Q.n_opt; ++k) {
+    const auto &op = opts[k];
+    for (size_t t = 0; t < op.size(); ++t) {
+      int src = t == 0 ? 0 : 1 + node_of[std::vector<int>(op.begin(), op.begin() + t)];
+      auto &tg = Q.targets[src];
+      int idx = -1;
+      for (size_t j = 0; j < tg.size(); ++j)
+        if (tg[j] == op[t]) idx = (int)j;
+      if (idx < 0) {
+        idx = (int)tg.size();
+        tg.push_back(op[t]);
+      }
+      Q.steps[k].push_back({src, idx});
+    }
+    Q.n_steps += (int)op.size();
+  }
+  for (auto &tg : Q.targets) Q.n_targets += (int)tg.size();
+  return SPB_OK;
+}
+
+// ----------------------------------------------------------------- plan
+
+struct PassPlan {
+  int n_tokens = 0;
+  int n_segments = 0;
+  int64_t pairs = 0;
+  std::vector<int64_t> logical_row;
+  std::vector<SpbRow> rows;
+  std::vector<SpbTile> tiles;
+  std::vector<SpbBranch> branches;
+  std::vector<int32_t> logical_branch;
+  std::vector<int32_t> scored, tgt_off, tgt_tok, opt_step_off, step_slot, step_row;
+  std::vector<unsigned char> blob;
+};
+
+}  // namespace
+
+struct spb_plan {
+  std::vector<PassPlan> passes;
+  bool floors = false;
+  int n_content_branches = 0, n_content_options = 0;
+  std::vector<int> lb_question, lb_pass, lb_slot;  // per logical branch (content, then floors)
+  std::vector<int> content_opt_off;                // [n_content_branches + 1]
+  std::vector<int> floor_lb_of_q;                  // question -> logical branch of its floor, -1
+  std::vector<int> q_nopt;
+  std::vector<int64_t> input_row_off;   // [n_logical_inputs + 1]
+  std::vector<int32_t> input_floor_q;   // [n_logical_inputs]
+};
+
+namespace {
+
+struct Unit {  // one logical input to place
+  int C;
+  int64_t first_row;                 // logical row of its first token
+  std::vector<int> qs;               // questions (branches) in order
+  std::vector<int> lbs;              // logical branch id of each branch
+  std::vector<int64_t> br_first_row; // logical row of each branch's template token 0
+};
+
+struct Packer {
+  const std::vector<Question> &Q;
+  int B;
+  std::vector<PassPlan> passes;
+  int group_start = 0;      // first row of the current tiling group in the current pass
+  bool group_empty_content = false;
+  std::vector<std::pair<int, int>> groups;  // per current pass: [g0, g1) tiling groups
+  std::vector<std::vector<std::pair<int, int>>> pass_groups;
+  std::vector<int> group_seg;               // content start of each group
+  std::vector<std::vector<int>> pass_group_seg;
+
+  explicit Packer(const std::vector<Question> &q, int budget) : Q(q), B(budget) { open(); }
+
+  PassPlan &cur() { return passes.back(); }
+  int fill() { return (int)cur().rows.size(); }
+
+  void open() {
+    passes.emplace_back();
+    pass_groups.emplace_back();
+    pass_group_seg.emplace_back();
+  }
+  void close_if_nonempty() {
+    if (!cur().rows.empty()) open();
+  }
+
+  // starts a tiling group for a content segment, or joins the running run of
+  // empty-content units
+  void begin_group(int C) {
+    auto &G = pass_groups.back();
+    auto &S = pass_group_seg.back();
+    int f = fill();
+    if (C == 0 && !G.empty() && S.back() < 0 && G.back().second == f) return;  // extend the C=0 run
+    G.push_back({f, f});
+    S.push_back(C > 0 ? f : -1);
+  }
+  void end_rows() { pass_groups.back().back().second = fill(); }
+
+  void place_content(const Unit &u, int &seg) {
+    begin_group(u.C);
+    PassPlan &P = cur();
+    seg = fill();
+    for (int t = 0; t < u.C; ++t) {
+      SpbRow r{};
+      r.cvis = t + 1;
+      r.seg = seg;
+      r.br = -1;
+      r.e = t;
+      P.rows.push_back(r);
+      P.logical_row.push_back(u.first_row + t);
+      P.pairs += t + 1;
+    }
+    if (u.C > 0) P.n_segments++;
+    end_rows();
+  }
+
+  void place_branch(const Unit &u, int bi, int seg, std::vector<int> &lb_pass, std::vector<int> &lb_slot) {
+    PassPlan &P = cur();
+    const Question &q = Q[u.qs[bi]];
+    int start = fill();
+    SpbBranch b{};
+    b.start = start;
+    b.L = q.L;
+    b.E = q.E();
+    b.n_opt = q.n_opt;
+    b.question = u.qs[bi];
+    lb_pass[u.lbs[bi]] = (int)passes.size() - 1;
+    lb_slot[u.lbs[bi]] = (int)P.branches.size();
+    P.branches.push_back(b);
+    P.logical_branch.push_back(u.lbs[bi]);
+    for (int j = 0; j < q.L; ++j) {
+      SpbRow r{};
+      r.cvis = u.C;
+      r.seg = u.C > 0 ? seg : start;
+      r.br = start;
+      r.e = j;
+      r.L = q.L;
+      P.rows.push_back(r);
+      P.logical_row.push_back(u.br_first_row[bi] + j);
+      P.pairs += u.C + j + 1;
+    }
+    for (int i = 0; i < q.n_nodes; ++i) {
+      SpbRow r{};
+      r.cvis = u.C;
+      r.seg = u.C > 0 ? seg : start;
+      r.br = start;
+      r.e = q.L + i;
+      r.L = q.L;
+      r.depth = q.node_depth[i];
+      int a[4] = {0, 0, 0, 0};
+      for (int k = 0; k < r.depth; ++k) a[k] = q.node_anc[i][k];
+      r.anc01 = (int32_t)((uint32_t)a[0] | ((uint32_t)a[1] << 16));
+      r.anc23 = (int32_t)((uint32_t)a[2] | ((uint32_t)a[3] << 16));
+      P.rows.push_back(r);
+      P.logical_row.push_back(u.br_first_row[bi] + q.L + i);
+      P.pairs += u.C + q.L + r.depth;
+    }
+    end_rows();
+  }
+
+  void place(const Unit &u, std::vector<int> &lb_pass, std::vector<int> &lb_slot) {
+    int64_t size = u.C;
+    for (int q : u.qs) size += Q[q].E();
+    int seg = 0;
+    if (size <= B - fill()) {
+      place_content(u, seg);
+      for (size_t bi = 0; bi < u.qs.size(); ++bi) place_branch(u, (int)bi, seg, lb_pass, lb_slot);
+      return;
+    }
+    if (size <= B) {
+      close_if_nonempty();
+      place_content(u, seg);
+      for (size_t bi = 0; bi < u.qs.size(); ++bi) place_branch(u, (int)bi, seg, lb_pass, lb_slot);
+      return;
+    }
+    // larger than a pass: spill at branch boundaries, content re-staged
+    if (u.C + (u.qs.empty() ? 0 : Q[u.qs[0]].E()) > B - fill()) close_if_nonempty();
+    place_content(u, seg);
+    for (size_t bi = 0; bi < u.qs.size(); ++bi) {
+      if (Q[u.qs[bi]].E() > B - fill()) {
+        open();
+        place_content(u, seg);
+      }
+      place_branch(u, (int)bi, seg, lb_pass, lb_slot);
+    }
+  }
+};
+
+void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, const std::vector<int> &gseg) {
+  for (size_t g = 0; g < groups.size(); ++g) {
+    int g0 = groups[g].first, g1 = groups[g].second;
+    for (int r0 = g0; r0 < g1; r0 += kTileRows) {
+      SpbTile t{};
+      t.row0 = r0;
+      t.nrows = std::min(kTileRows, g1 - r0);
+      t.seg = gseg[g] >= 0 ? gseg[g] : r0;
+      int maxc = 0;
+      for (int r = r0; r < r0 + t.nrows; ++r) maxc = std::max(maxc, P.rows[r].cvis);
+      t.ncc = (maxc + kChunk - 1) / kChunk;
+      t.b_lo = t.b_hi = 0;
+      // branches intersecting [r0, r0 + nrows): the branch table is in row order
+      int lo = -1, hi = -1;
+      for (int r = r0; r < r0 + t.nrows; ++r) {
+        if (P.rows[r].br < 0) continue;
+        // locate by binary search on start
+        int s = P.rows[r].br;
+        auto it = std::lower_bound(P.branches.begin(), P.branches.end(), s,
+                                   [](const SpbBranch &b, int v) { return b.start < v; });
+        int bi = (int)(it - P.branches.begin());
+        if (lo < 0) lo = bi;
+        hi = bi;
+      }
+      int bchunks = 0;
+      if (lo >= 0) {
+        t.b_lo = lo;
+        t.b_hi = hi + 1;
+        for (int b = lo; b <= hi; ++b) {
+          const SpbBranch &B = P.branches[b];
+          int last = std::min(B.start + B.E, r0 + t.nrows) - 1 - B.start;
+          bchunks += last / kChunk + 1;
+        }
+      }
+      t.cost = t.ncc + bchunks;
+      P.tiles.push_back(t);
+    }
+  }
+  // longest work first, so the tail of the grid holds the short items
+  std::stable_sort(P.tiles.begin(), P.tiles.end(), [](const SpbTile &a, const SpbTile &b) { return a.cost > b.cost; });
+}
+
+void build_scoring(PassPlan &P, const std::vector<Question> &Q) {
+  int opt = 0;
+  P.tgt_off.push_back(0);
+  P.opt_step_off.push_back(0);
+  for (auto &b : P.branches) {
+    const Question &q = Q[b.question];
+    b.opt0 = opt;
+    b.scored0 = (int)P.scored.size();
+    b.n_scored = 1 + q.n_nodes;
+    P.scored.push_back(b.start + q.L - 1);
+    for (int i = 0; i < q.n_nodes; ++i) P.scored.push_back(b.start + q.L + i);
+    for (int s = 0; s <= q.n_nodes; ++s) {
+      for (int t : q.targets[s]) P.tgt_tok.push_back(t);
+      P.tgt_off.push_back((int)P.tgt_tok.size());
+    }
+    for (int k = 0; k < q.n_opt; ++k) {
+      for (auto st : q.steps[k]) {
+        int row = b.scored0 + st.first;
+        P.step_row.push_back(row);
+        P.step_slot.push_back(P.tgt_off[row] + st.second);
+      }
+      P.opt_step_off.push_back((int)P.step_slot.size());
+    }
+    opt += q.n_opt;
+  }
+}
+
+template <class T>
+void put(std::vector<unsigned char> &blob, size_t off, const std::vector<T> &v) {
+  if (!v.empty()) memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
+}
+
+void build_blob(PassPlan &P, int pass) {
+  SpbMetaHeader h{};
+  h.magic = kMetaMagic;
+  h.version = kMetaVersion;
+  h.pass = pass;
+  h.n_tokens = (int)P.rows.size();
+  h.n_tiles = (int)P.tiles.size();
+  h.n_branches = (int)P.branches.size();
+  h.n_options = (int)P.opt_step_off.size() - 1;
+  h.n_scored = (int)P.scored.size();
+  h.n_targets = (int)P.tgt_tok.size();
+  h.n_steps = (int)P.step_slot.size();
+  size_t off = align256(sizeof(SpbMetaHeader));
+  auto place = [&](int64_t &field, size_t bytes) {
+    field = (int64_t)off;
+    off = align256(off + bytes);
+  };
+  place(h.off_rows, P.rows.size() * sizeof(SpbRow));
+  place(h.off_tiles, P.tiles.size() * sizeof(SpbTile));
+  place(h.off_branches, P.branches.size() * sizeof(SpbBranch));
+  place(h.off_scored, P.scored.size() * 4);
+  place(h.off_tgt_off, P.tgt_off.size() * 4);
+  place(h.off_tgt_tok, P.tgt_tok.size() * 4);
+  place(h.off_opt_step_off, P.opt_step_off.size() * 4);
+  place(h.off_step_slot, P.step_slot.size() * 4);
+  place(h.off_step_row, P.step_row.size() * 4);
+  h.total_bytes = (int64_t)off;
+  P.blob.assign(off, 0);
+  memcpy(P.blob.data(), &h, sizeof h);
+  put(P.blob, h.off_rows, P.rows);
+  put(P.blob, h.off_tiles, P.tiles);
+  put(P.blob, h.off_branches, P.branches);
+  put(P.blob, h.off_scored, P.scored);
+  put(P.blob, h.off_tgt_off, P.tgt_off);
+  put(P.blob, h.off_tgt_tok, P.tgt_tok);
+  put(P.blob, h.off_opt_step_off, P.opt_step_off);
+  put(P.blob, h.off_step_slot, P.step_slot);
+  put(P.blob, h.off_step_row, P.step_row);
+  P.n_tokens = h.n_tokens;
+}
+
+const SpbMetaHeader &header(const PassPlan &P) { return *reinterpret_cast<const SpbMetaHeader *>(P.blob.data()); }
+
+spb_status check_pass(const spb_plan *plan, int32_t pass) {
+  if (!plan) return fail(SPB_ERR_ARG, "plan is NULL");
+  if (pass < 0 || pass >= (int32_t)plan->passes.size())
+    return fail(SPB_ERR_ARG, "pass %d outside [0, %zu)", pass, plan->passes.size());
+  return SPB_OK;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+
+extern "C" {
+
+const char *spb_last_error(void) { return g_err.c_str(); }
+
+const char *spb_fingerprint(void) {
+  static char fp[160];
+  snprintf(fp, sizeof fp, "spb-0.1 gfx950 meta%d attn:rows%d,chunk%d,mfma32x32 head:vslice%d,k64 numerics:1",
+           kMetaVersion, kTileRows, kChunk, kVocabTile);
+  return fp;
+}
+
+void spb_pack_opts_default(spb_pack_opts *o) {
+  if (!o) return;
+  o->token_budget = 16384;
+  o->floors = 1;
+  o->max_content_tokens = 4096;
+  o->max_query_tokens = 256;
+  o->max_options = 1000;
+  o->max_option_tokens = 5;
+  o->max_prompts_per_input = 10000;
+  o->max_processed_tokens = 2000000;
+}
+
+spb_status spb_pack_pass(const spb_problem *P, const spb_pack_opts *opts, spb_plan **out) {
+  if (!P || !out) return fail(SPB_ERR_ARG, "problem and out must not be NULL");
+  *out = nullptr;
+  spb_pack_opts o;
+  spb_pack_opts_default(&o);
+  if (opts) o = *opts;
+  if (o.token_budget < 1) return fail(SPB_ERR_ARG, "token_budget %d < 1", o.token_budget);
+  if (P->n_inputs < 0 || P->n_questions < 0) return fail(SPB_ERR_ARG, "negative input or question count");
+  if (P->vocab < 1) return fail(SPB_ERR_ARG, "vocab %d < 1", P->vocab);
+  if ((P->n_inputs > 0 && (!P->content_len || !P->branch_off)) || (P->n_questions > 0 && (!P->q_len || !P->opt_off)))
+    return fail(SPB_ERR_ARG, "NULL problem array");
+  if (P->n_inputs > 0 && P->branch_off[0] != 0) return fail(SPB_ERR_ARG, "branch_off[0] must be 0");
+  if (P->n_questions > 0 && P->opt_off[0] != 0) return fail(SPB_ERR_ARG, "opt_off[0] must be 0");
+  int n_opt_total = P->n_questions > 0 ? P->opt_off[P->n_questions] : 0;
+  if (n_opt_total < 0) return fail(SPB_ERR_ARG, "opt_off not monotone");
+  if (n_opt_total > 0 && (!P->tok_off || !P->tok)) return fail(SPB_ERR_ARG, "NULL option arrays");
+  if (n_opt_total > 0 && P->tok_off[0] != 0) return fail(SPB_ERR_ARG, "tok_off[0] must be 0");
+  for (int q = 0; q < P->n_questions; ++q)
+    if (P->opt_off[q + 1] < P->opt_off[q]) return fail(SPB_ERR_ARG, "opt_off not monotone at question %d", q);
+
+  std::vector<Question> Q(P->n_questions);
+  for (int q = 0; q < P->n_questions; ++q) {
+    spb_status s = compile_question(*P, q, o, Q[q]);
+    if (s != SPB_OK) return s;
+  }
+  std::unique_ptr<spb_plan> plan(new (std::nothrow) spb_plan());
+  if (!plan) return fail(SPB_ERR_ARG, "out of host memory");
+  plan->floors = o.floors != 0;
+  plan->q_nopt.resize(P->n_questions);
+  for (int q = 0; q < P->n_questions; ++q) plan->q_nopt[q] = Q[q].n_opt;
+
+  // logical units: inputs, then floors
+  std::vector<Unit> units;
+  int64_t row = 0;
+  int lb = 0;
+  int64_t processed = 0;
+  for (int i = 0; i < P->n_inputs; ++i) {
+    Unit u;
+    u.C = P->content_len[i];
+    if (u.C < 0) return fail(SPB_ERR_ARG, "input %d: content_len %d < 0", i, u.C);
+    if (u.C > o.max_content_tokens)
+      return fail(SPB_ERR_LIMIT, "input %d: content of %d tokens exceeds max_content_tokens %d", i, u.C,
+                  o.max_content_tokens);
+    if (u.C > o.token_budget)
+      return fail(SPB_ERR_LIMIT, "input %d: content of %d tokens exceeds the token budget %d", i, u.C, o.token_budget);
+    int b0 = P->branch_off[i], b1 = P->branch_off[i + 1];
+    if (b1 < b0) return fail(SPB_ERR_ARG, "branch_off not monotone at input %d", i);
+    if (b1 - b0 > o.max_prompts_per_input)
+      return fail(SPB_ERR_LIMIT, "input %d: %d questions exceed max_prompts_per_input %d", i, b1 - b0,
+                  o.max_prompts_per_input);
+    if (b1 > b0 && !P->branch_q) return fail(SPB_ERR_ARG, "branch_q is NULL");
+    u.first_row = row;
+    row += u.C;
+    for (int b = b0; b < b1; ++b) {
+      int q = P->branch_q[b];
+      if (q < 0 || q >= P->n_questions) return fail(SPB_ERR_ARG, "input %d asks question %d outside [0, %d)", i, q,
+                                                    P->n_questions);
+      if ((int64_t)u.C + Q[q].E() > o.token_budget)
+        return fail(SPB_ERR_LIMIT, "input %d: content %d + question %d (%d rows) exceeds the token budget %d", i, u.C,
+                    q, Q[q].E(), o.token_budget);
+      u.qs.push_back(q);
+      u.lbs.push_back(lb++);
+      u.br_first_row.push_back(row);
+      row += Q[q].E();
+      plan->lb_question.push_back(q);
+    }
+    units.push_back(std::move(u));
+  }
+  plan->n_content_branches = lb;
+  plan->content_opt_off.push_back(0);
+  for (int b = 0; b < lb; ++b) plan->content_opt_off.push_back(plan->content_opt_off.back() + Q[plan->lb_question[b]].n_opt);
+  plan->n_content_options = plan->content_opt_off.back();
+  plan->floor_lb_of_q.assign(P->n_questions, -1);
+  if (plan->floors) {
+    std::vector<char> asked(P->n_questions, 0);
+    for (int b = 0; b < lb; ++b) asked[plan->lb_question[b]] = 1;
+    for (int q = 0; q < P->n_questions; ++q) {
+      if (!asked[q]) continue;
+      Unit u;
+      u.C = 0;
+      u.first_row = row;
+      u.qs.push_back(q);
+      u.lbs.push_back(lb);
+      u.br_first_row.push_back(row);
+      plan->floor_lb_of_q[q] = lb++;
+      plan->lb_question.push_back(q);
+      row += Q[q].E();
+      units.push_back(std::move(u));
+    }
+  }
+  for (auto &u : units) {
+    plan->input_row_off.push_back(u.first_row);
+    plan->input_floor_q.push_back(-1);
+  }
+  plan->input_row_off.push_back(row);
+  for (size_t n = (size_t)P->n_inputs; n < units.size(); ++n) plan->input_floor_q[n] = units[n].qs[0];
+  plan->lb_pass.assign(lb, -1);
+  plan->lb_slot.assign(lb, -1);
+
+  Packer pk(Q, o.token_budget);
+  for (auto &u : units) {
+    pk.place(u, plan->lb_pass, plan->lb_slot);
+  }
+  if (pk.cur().rows.empty() && pk.passes.size() > 1) {
+    pk.passes.pop_back();
+    pk.pass_groups.pop_back();
+    pk.pass_group_seg.pop_back();
+  }
+  for (auto &p : pk.passes) processed += (int64_t)p.rows.size();
+  if (processed > o.max_processed_tokens)
+    return fail(SPB_ERR_LIMIT, "%lld processed tokens exceed max_processed_tokens %lld", (long long)processed,
+                (long long)o.max_processed_tokens);
+  for (size_t k = 0; k < pk.passes.size(); ++k) {
+    PassPlan &pp = pk.passes[k];
+    build_tiles(pp, pk.pass_groups[k], pk.pass_group_seg[k]);
+    build_scoring(pp, Q);
+    build_blob(pp, (int)k);
+  }
+  plan->passes = std::move(pk.passes);
+  *out = plan.release();
+  return ok();
+}
+
+void spb_plan_free(spb_plan *plan) { delete plan; }
+
+spb_status spb_plan_num_passes(const spb_plan *plan, int32_t *n) {
+  if (!plan || !n) return fail(SPB_ERR_ARG, "NULL argument");
+  *n = (int32_t)plan->passes.size();
+  return ok();
+}
+
+spb_status spb_plan_info(const spb_plan *plan, int32_t pass, spb_pass_info *out) {
+  if (!plan || !out) return fail(SPB_ERR_ARG, "NULL argument");
+  spb_pass_info s{};
+  auto add = [&](const PassPlan &P) {
+    const SpbMetaHeader &h = header(P);
+    s.n_tokens += h.n_tokens;
+    s.n_segments += P.n_segments;
+    s.n_branches += h.n_branches;
+    s.n_options += h.n_options;
+    s.n_scored_rows += h.n_scored;
+    s.n_targets += h.n_targets;
+    s.n_tiles += h.n_tiles;
+    s.unmasked_pairs += P.pairs;
+    s.meta_bytes = std::max(s.meta_bytes, P.blob.size());
+  };
+  if (pass == -1) {
+    for (auto &P : plan->passes) add(P);
+  } else {
+    spb_status st = check_pass(plan, pass);
+    if (st != SPB_OK) return st;
+    add(plan->passes[pass]);
+  }
+  s.n_passes = (int32_t)plan->passes.size();
+  s.n_content_branches = plan->n_content_branches;
+  s.n_content_options = plan->n_content_options;
+  s.n_logical_inputs = (int32_t)plan->input_floor_q.size();
+  *out = s;
+  return ok();
+}
+
+spb_status spb_plan_rows(const spb_plan *plan, int32_t pass, int64_t *logical_row, int32_t *scored_row) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  const PassPlan &P = plan->passes[pass];
+  if (logical_row) memcpy(logical_row, P.logical_row.data(), P.logical_row.size() * sizeof(int64_t));
+  if (scored_row) memcpy(scored_row, P.scored.data(), P.scored.size() * sizeof(int32_t));
+  return ok();
+}
+
+spb_status spb_plan_branches(const spb_plan *plan, int32_t pass, int32_t *logical_branch, int32_t *opt_first) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  const PassPlan &P = plan->passes[pass];
+  for (size_t b = 0; b < P.branches.size(); ++b) {
+    if (logical_branch) logical_branch[b] = P.logical_branch[b];
+    if (opt_first) opt_first[b] = P.branches[b].opt0;
+  }
+  return ok();
+}
+
+spb_status spb_plan_inputs(const spb_plan *plan, int64_t *row_off, int32_t *floor_question) {
+  if (!plan) return fail(SPB_ERR_ARG, "plan is NULL");
+  if (row_off) memcpy(row_off, plan->input_row_off.data(), plan->input_row_off.size() * sizeof(int64_t));
+  if (floor_question)
+    memcpy(floor_question, plan->input_floor_q.data(), plan->input_floor_q.size() * sizeof(int32_t));
+  return ok();
+}
+
+spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int32_t *keys, int32_t cap,
+                            int32_t *n_keys) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  const PassPlan &P = plan->passes[pass];
+  if (row < 0 || row >= (int32_t)P.rows.size()) return fail(SPB_ERR_ARG, "row %d outside the pass", row);
+  if (!n_keys || (cap > 0 && !keys)) return fail(SPB_ERR_ARG, "NULL argument");
+  const SpbRow &r = P.rows[row];
+  int n = 0;
+  auto emit = [&](int y) {
+    if (n < cap) keys[n] = y;
+    ++n;
+  };
+  for (int j = 0; j < r.cvis; ++j) emit(r.seg + j);
+  if (r.br >= 0) {
+    int E = r.L;
+    for (auto &b : P.branches)
+      if (b.start == r.br) E = b.E;
+    for (int ep = 0; ep < E; ++ep)
+      if (branch_visible(r, ep)) emit(r.br + ep);
+  }
+  *n_keys = n;
+  if (n > cap) return fail(SPB_ERR_SIZE, "%d keys exceed cap %d", n, cap);
+  return ok();
+}
+
+spb_status spb_plan_upload(const spb_plan *plan, int32_t pass, void *d_meta, size_t bytes, void *stream) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  const PassPlan &P = plan->passes[pass];
+  if (!d_meta) return fail(SPB_ERR_ARG, "d_meta is NULL");
+  if ((uintptr_t)d_meta % 256) return fail(SPB_ERR_ARG, "d_meta must be 256-byte aligned");
+  if (bytes < P.blob.size()) return fail(SPB_ERR_SIZE, "metadata needs %zu bytes, buffer has %zu", P.blob.size(), bytes);
+  hipError_t e = hipMemcpyAsync(d_meta, P.blob.data(), P.blob.size(), hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SPB_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  return ok();
+}
+
+spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_attn_args *a,
+                                void *stream) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  if (!a || !d_meta) return fail(SPB_ERR_ARG, "NULL argument");
+  const PassPlan &P = plan->passes[pass];
+  const SpbMetaHeader &h = header(P);
+  if (a->head_dim != 64 && a->head_dim != 128) return fail(SPB_ERR_DTYPE, "head_dim %d not in {64, 128}", a->head_dim);
+  if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv) return fail(SPB_ERR_DTYPE, "hq %d not a multiple of hkv %d", a->hq, a->hkv);
+  int g = a->hq / a->hkv;
+  if (g != 1 && g != 2 && g != 4) return fail(SPB_ERR_DTYPE, "hq / hkv = %d not in {1, 2, 4}", g);
+  if (a->in_dtype != SPB_F32 && a->in_dtype != SPB_BF16 && a->in_dtype != SPB_FP8_E4M3)
+    return fail(SPB_ERR_DTYPE, "in_dtype %d unsupported", a->in_dtype);
+  if (a->out_dtype != SPB_F32 && a->out_dtype != SPB_BF16) return fail(SPB_ERR_DTYPE, "out_dtype %d unsupported", a->out_dtype);
+  if (a->in_dtype == SPB_FP8_E4M3 && a->head_dim != 128) return fail(SPB_ERR_DTYPE, "fp8 inputs need head_dim 128");
+  if (a->rows < h.n_tokens) return fail(SPB_ERR_SIZE, "buffers hold %lld rows, the pass has %d", (long long)a->rows, h.n_tokens);
+  if (h.n_tokens > 0 && (!a->q || !a->k || !a->v || !a->o)) return fail(SPB_ERR_ARG, "NULL tensor");
+  float sq = a->in_dtype == SPB_FP8_E4M3 ? a->s_q : 1.f;
+  float sk = a->in_dtype == SPB_FP8_E4M3 ? a->s_k : 1.f;
+  float sv = a->in_dtype == SPB_FP8_E4M3 ? a->s_v : 1.f;
+  if (!(sq > 0.f) || !(sk > 0.f) || !(sv > 0.f) || !std::isfinite(sq * sk * sv))
+    return fail(SPB_ERR_ARG, "fp8 scales must be finite and > 0");
+  if ((uintptr_t)d_meta % 256) return fail(SPB_ERR_ARG, "d_meta must be 256-byte aligned");
+  if (h.n_tiles == 0) return ok();
+  AttnLaunch L{};
+  L.q = a->q; L.k = a->k; L.v = a->v; L.o = a->o;
+  L.in_dtype = a->in_dtype; L.out_dtype = a->out_dtype;
+  L.hq = a->hq; L.hkv = a->hkv; L.head_dim = a->head_dim;
+  L.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)a->head_dim);
+  L.s_q = sq; L.s_k = sk; L.s_v = sv;
+  L.n_tokens = h.n_tokens;
+  L.n_tiles = h.n_tiles;
+  const char *base = (const char *)d_meta;
+  L.rows = base + h.off_rows;
+  L.tiles = base + h.off_tiles;
+  L.branches = base + h.off_branches;
+  int e = launch_attention(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "branch attention launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, size_t *out) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  if (!out || vocab < 1) return fail(SPB_ERR_ARG, "bad argument");
+  const SpbMetaHeader &h = header(plan->passes[pass]);
+  *out = align256((size_t)h.n_scored * n_vocab_slices(vocab) * 2 * sizeof(float)) +
+         align256((size_t)h.n_targets * sizeof(float)) + align256((size_t)h.n_scored * sizeof(float));
+  return ok();
+}
+
+spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *a,
+                             void *stream) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  if (!a || !d_meta) return fail(SPB_ERR_ARG, "NULL argument");
+  const PassPlan &P = plan->passes[pass];
+  const SpbMetaHeader &h = header(P);
+  if (a->h_dtype != SPB_BF16 && a->h_dtype != SPB_F32) return fail(SPB_ERR_DTYPE, "h_dtype %d unsupported", a->h_dtype);
+  if (a->hidden_dim < 64 || a->hidden_dim % 64) return fail(SPB_ERR_DTYPE, "hidden_dim %d not a positive multiple of 64", a->hidden_dim);
+  if (a->vocab < 1) return fail(SPB_ERR_ARG, "vocab %d < 1", a->vocab);
+  for (int t : P.tgt_tok)
+    if (t >= a->vocab) return fail(SPB_ERR_ARG, "option token %d >= vocab %d", t, a->vocab);
+  if (a->rows < h.n_tokens) return fail(SPB_ERR_SIZE, "hidden holds %lld rows, the pass has %d", (long long)a->rows, h.n_tokens);
+  size_t need = 0;
+  spb_score_workspace_bytes(plan, pass, a->vocab, &need);
+  if (a->workspace_bytes < need) return fail(SPB_ERR_SIZE, "workspace needs %zu bytes, got %zu", need, a->workspace_bytes);
+  if (h.n_scored > 0 && (!a->hidden || !a->lm_head || !a->workspace || !a->lp || !a->p || !a->residual))
+    return fail(SPB_ERR_ARG, "NULL tensor");
+  if ((uintptr_t)d_meta % 256 || (uintptr_t)a->workspace % 256) return fail(SPB_ERR_ARG, "d_meta and workspace must be 256-byte aligned");
+  if (h.n_scored == 0) return ok();
+  ScoreLaunch L{};
+  L.hidden = a->hidden; L.h_dtype = a->h_dtype; L.hidden_dim = a->hidden_dim;
+  L.lm_head = a->lm_head; L.vocab = a->vocab;
+  L.n_scored = h.n_scored; L.n_targets = h.n_targets; L.n_branches = h.n_branches; L.n_options = h.n_options;
+  const char *base = (const char *)d_meta;
+  L.scored = base + h.off_scored;
+  L.tgt_off = base + h.off_tgt_off;
+  L.tgt_tok = base + h.off_tgt_tok;
+  L.branches = base + h.off_branches;
+  L.opt_step_off = base + h.off_opt_step_off;
+  L.step_slot = base + h.off_step_slot;
+  L.step_row = base + h.off_step_row;
+  char *ws = (char *)a->workspace;
+  L.part = (float *)ws;
+  ws += align256((size_t)h.n_scored * n_vocab_slices(a->vocab) * 2 * sizeof(float));
+  L.tz = (float *)ws;
+  ws += align256((size_t)h.n_targets * sizeof(float));
+  L.lse = (float *)ws;
+  L.lp = a->lp; L.p = a->p; L.residual = a->residual;
+  int e = launch_score(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "score launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_score_finalize(const spb_plan *plan, const float *const *lp_pp, const float *const *p_pp,
+                              const float *const *res_pp, float *lp, float *p, float *residual, float *floor_p,
+                              float *lift) {
+  if (!plan) return fail(SPB_ERR_ARG, "plan is NULL");
+  if ((lp && !lp_pp) || ((p || floor_p || lift) && !p_pp) || (residual && !res_pp))
+    return fail(SPB_ERR_ARG, "per-pass input arrays missing");
+  for (size_t k = 0; k < plan->passes.size(); ++k)
+    if ((lp && !lp_pp[k]) || ((p || floor_p || lift) && !p_pp[k]) || (residual && !res_pp[k]))
+      return fail(SPB_ERR_ARG, "per-pass array %zu is NULL", k);
+  const float nan = std::nanf("");
+  for (int b = 0; b < plan->n_content_branches; ++b) {
+    int q = plan->lb_question[b];
+    int ps = plan->lb_pass[b], sl = plan->lb_slot[b];
+    const SpbBranch &B = plan->passes[ps].branches[sl];
+    int fb = plan->floor_lb_of_q[q];
+    const SpbBranch *F = nullptr;
+    int fps = -1;
+    if (fb >= 0) {
+      fps = plan->lb_pass[fb];
+      F = &plan->passes[fps].branches[plan->lb_slot[fb]];
+    }
+    if (residual) residual[b] = res_pp[ps][sl];
+    for (int o = 0; o < B.n_opt; ++o) {
+      int dst = plan->content_opt_off[b] + o;
+      if (lp) lp[dst] = lp_pp[ps][B.opt0 + o];
+      float pv = (p || lift) ? p_pp[ps][B.opt0 + o] : 0.f;
+      if (p) p[dst] = pv;
+      float fv = F ? p_pp[fps][F->opt0 + o] : nan;
+      if (floor_p) floor_p[dst] = fv;
+      if (lift) lift[dst] = F ? pv - fv : nan;
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

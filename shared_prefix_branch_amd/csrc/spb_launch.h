@@ -1,0 +1,41 @@
+// spb_launch.h -- host-side launchers of the gfx950 kernels (internal to libspb).
+// Implemented in spb_attention.hip and spb_score.hip; called by spb_host.cpp
+// after every argument has been validated.  Each returns 0 or a hipError_t
+// value and never allocates.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spb {
+
+struct AttnLaunch {
+  const void *q, *k, *v;
+  void *o;
+  int in_dtype, out_dtype;   // spb_dtype values
+  int hq, hkv, head_dim;
+  float scale;               // softmax scale (already resolved)
+  float s_q, s_k, s_v;       // fp8 dequantisation scales (1 otherwise)
+  int n_tokens, n_tiles;
+  const void *rows, *tiles, *branches;  // device pointers into the metadata blob
+};
+
+struct ScoreLaunch {
+  const void *hidden;
+  int h_dtype, hidden_dim;
+  const void *lm_head;
+  int vocab;
+  int n_scored, n_targets, n_branches, n_options;
+  const void *scored, *tgt_off, *tgt_tok, *branches, *opt_step_off, *step_slot, *step_row;
+  float *part;   // workspace: [n_scored][n_slices][2] (max, sum of exp) per vocabulary slice
+  float *tz;     // workspace: [n_targets] captured logits
+  float *lse;    // workspace: [n_scored]
+  float *lp, *p, *residual;
+};
+
+inline int n_vocab_slices(int vocab) { return (vocab + 255) / 256; }
+
+int launch_attention(const AttnLaunch &a, void *stream);
+int launch_score(const ScoreLaunch &a, void *stream);
+const char *hip_error_string(int err);
+
+}  // namespace spb

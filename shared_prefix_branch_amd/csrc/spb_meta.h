@@ -1,0 +1,85 @@
+// spb_meta.h -- the device metadata of one packed pass (internal to libspb).
+//
+// One contiguous blob, built by the host planner and copied to device memory
+// once per pass: a header, then arrays each starting on a 256-byte boundary.
+// Every kernel reads only this blob plus the caller's tensors.
+//
+// Including translation units define SPB_HD first: `__host__ __device__` in
+// HIP sources, empty in host-only C++.
+#pragma once
+#include <stdint.h>
+
+#ifndef SPB_HD
+#error "define SPB_HD before including spb_meta.h"
+#endif
+
+namespace spb {
+
+constexpr int32_t kMetaMagic = 0x53504231;  // "SPB1"
+constexpr int32_t kMetaVersion = 1;
+constexpr int kTileRows = 128;  // rows per attention tile (one to two work groups)
+constexpr int kChunk = 64;      // keys per chunk; content chunks start at the
+                                // content start, branch chunks at the branch start
+constexpr int kMaxDepth = 4;    // option-trie depth (options of at most 5 tokens)
+constexpr int kVocabTile = 256; // vocabulary rows per lm-head slice (LSE partial)
+
+// One per pass row.  Visibility of key row y from query row x:
+//   content key: y in [x.seg, x.seg + x.cvis)
+//   branch key:  x.br >= 0 and y in [x.br, x.br + E) with e' = y - x.br:
+//     e' <  x.L : visible iff e' <= x.e  (template rows causal; nodes see all)
+//     e' >= x.L : visible iff e' is one of the node's ancestors anc[0..depth)
+struct SpbRow {
+  int32_t cvis;   // content keys visible (content row t: t+1; branch rows: C)
+  int32_t seg;    // pass row of the segment's first content token
+  int32_t br;     // pass row of the branch's template token 0; -1 for content rows
+  int32_t e;      // extended index in the branch (template j or L + node index); content: t
+  int32_t L;      // template length of the branch (0 for content rows)
+  int32_t depth;  // option-trie depth (0 for content and template rows)
+  int32_t anc01;  // extended indices of ancestors at depth 1 and 2 (low / high 16 bits)
+  int32_t anc23;  // depth 3 and 4; anc[depth-1] is the node itself
+};
+
+// One attention work item: at most kTileRows consecutive rows of one segment
+// (or of a run of empty-content floor branches).
+struct SpbTile {
+  int32_t row0, nrows;
+  int32_t seg;    // content start (pass row) shared by the tile's rows
+  int32_t ncc;    // content chunks to visit: ceil(max cvis / kChunk)
+  int32_t b_lo, b_hi;  // branch-table range intersecting the tile
+  int32_t cost, pad;
+};
+
+struct SpbBranch {
+  int32_t start;   // pass row of template token 0
+  int32_t L, E;    // template length; template + trie nodes
+  int32_t n_opt;   // options of the question
+  int32_t opt0;    // first option slot of the pass
+  int32_t scored0; // scored-row index of the template's last row (nodes follow)
+  int32_t n_scored;
+  int32_t question;
+};
+
+struct SpbMetaHeader {
+  int32_t magic, version;
+  int32_t pass, n_tokens;
+  int32_t n_tiles, n_branches, n_options, n_scored;
+  int32_t n_targets, n_steps, pad0, pad1;
+  int64_t off_rows, off_tiles, off_branches, off_scored;
+  int64_t off_tgt_off, off_tgt_tok, off_opt_step_off, off_step_slot;
+  int64_t off_step_row, total_bytes, pad2, pad3;
+};
+
+SPB_HD inline int anc_of(const SpbRow &r, int i) {
+  int32_t w = i < 2 ? r.anc01 : r.anc23;
+  return (i & 1) ? (int)((uint32_t)w >> 16) : (int)(w & 0xFFFF);
+}
+
+// Is branch key with extended index ep visible from row r (r in that branch)?
+SPB_HD inline bool branch_visible(const SpbRow &r, int ep) {
+  if (ep < r.L) return ep <= r.e;
+  bool v = false;
+  for (int i = 0; i < kMaxDepth; ++i) v = v || (i < r.depth && anc_of(r, i) == ep);
+  return v;
+}
+
+}  // namespace spb

@@ -1,0 +1,248 @@
+"""CPU tests of libspb's host side: exports, the packer's plan, error paths,
+the floor join.  No kernel runs here."""
+import collections
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import shared_prefix_branch_amd as spb
+import synth
+from oracle import tree as OT
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "spb.h")).read()
+    declared = set(re.findall(r"\b(spb_[a-z_]+)\s*\(", hdr))
+    assert declared == set(spb.EXPORTED_SYMBOLS)
+    L = spb.lib()
+    for name in sorted(declared):
+        assert hasattr(L, name), name
+    assert spb.fingerprint().startswith("spb-")
+
+
+def _placements(plan):
+    out = []
+    for k in range(plan.n_passes):
+        lr, sr = plan.rows(k)
+        out.append((lr, sr))
+    return out
+
+
+def _check_plan(prob, plan, budget, floors=True):
+    lay = OT.build_layout(prob, floors=floors)
+    seen = collections.Counter()
+    content_rows = set(np.nonzero(lay.row_kind == 0)[0].tolist())
+    for k in range(plan.n_passes):
+        lr, sr = plan.rows(k)
+        assert len(lr) <= budget
+        assert len(set(lr.tolist())) == len(lr)          # no row twice in one pass
+        seen.update(lr.tolist())
+        # scored rows: the template's last row and every trie node
+        want = sorted(x for x in range(len(lr)) if lay.row_kind[lr[x]] == 2 or
+                      (lay.row_kind[lr[x]] == 1 and
+                       lay.row_pos[lr[x]] == lay.inputs[lay.row_input[lr[x]]].branches[lay.row_branch[lr[x]]].L - 1))
+        assert sorted(sr.tolist()) == want
+    # every branch row exactly once; content rows at least once, and in every
+    # pass that holds one of the input's branches
+    for r in range(lay.n_rows):
+        if r in content_rows:
+            assert seen[r] >= 1
+        else:
+            assert seen[r] == 1, r
+    return lay
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("budget", [40, 64, 200, 16384])
+def test_plan_places_every_row_and_visibility_equals_root_paths(seed, budget):
+    prob = synth.make_problem("random", 200 + seed, vocab=32, n_inputs=4, n_questions=5, max_content=24,
+                              max_len=6, max_options=4, max_option_tokens=5)
+    try:
+        plan = spb.pack_pass(prob, token_budget=budget)
+    except spb.SpbError as e:
+        assert e.code == -2  # content + one branch larger than the budget
+        return
+    lay = _check_plan(prob, plan, budget)
+    for k in range(plan.n_passes):
+        lr, _ = plan.rows(k)
+        for x in range(len(lr)):
+            keys = plan.visible(k, x)
+            assert len(set(keys)) == len(keys)
+            assert sorted(lr[keys].tolist()) == sorted(OT.root_path(lay, int(lr[x])))
+
+
+def test_plan_counts_and_pairs():
+    prob = synth.make_problem("random", 9, vocab=16, n_inputs=3, n_questions=4, max_content=12,
+                              max_len=5, max_options=3, max_option_tokens=4)
+    plan = spb.pack_pass(prob, token_budget=16384)
+    lay = OT.build_layout(prob, floors=True)
+    inf = plan.info()
+    assert inf["n_tokens"] == lay.n_rows
+    assert inf["unmasked_pairs"] == sum(len(OT.root_path(lay, x)) for x in range(lay.n_rows))
+    assert inf["n_branches"] == sum(len(li.branches) for li in lay.inputs)
+    assert inf["n_content_branches"] == len(prob.branch_q)
+    assert inf["n_scored_rows"] == len(OT.scored_rows(lay))
+
+
+def test_spill_restages_content():
+    # extreme shape, scaled down: inputs larger than a pass spill at branch
+    # boundaries with the content re-staged
+    wl = synth.make_workload("extreme", n_questions=60, content=100)
+    prob = wl.problem
+    budget = 512
+    plan = spb.pack_pass(prob, token_budget=budget)
+    lay = _check_plan(prob, plan, budget)
+    for k in range(plan.n_passes):
+        lr, _ = plan.rows(k)
+        ins = set(int(lay.row_input[r]) for r in lr if lay.row_kind[r] != 0)
+        for i in ins:
+            li = lay.inputs[i]
+            c = set(range(li.first_row, li.first_row + li.C))
+            assert c <= set(lr.tolist())      # the content is in every pass of the input
+    assert plan.n_passes > 1
+
+
+def test_news_two_pass_and_21x_token_saving():
+    # the pages: 24 articles of ~470 tokens x 56 two-option questions pack into
+    # two 16k passes, and the shared read saves ~21x the tokens of asking each
+    # question with its own copy of the article
+    wl = synth.make_workload("news2")
+    prob = wl.problem
+    plan = spb.pack_pass(prob, token_budget=16384)
+    assert plan.n_passes == 2
+    lay = OT.build_layout(prob, floors=False)
+    shared = lay.n_rows
+    separate = sum(int(prob.content_len[i]) + int(prob.q_len[q])
+                   for i in range(prob.n_inputs) for q in prob.questions_of(i))
+    assert 19.0 < separate / shared < 23.0
+    # the configured news shape (templates 14-26 tokens) needs a third pass
+    assert spb.pack_pass(synth.make_workload("news").problem).n_passes == 3
+
+
+def test_floors_deduplicated_per_question():
+    wl = synth.make_workload("fp8", n_inputs=30)
+    plan = spb.pack_pass(wl.problem, token_budget=8192)
+    asked = set(int(q) for q in wl.problem.branch_q)
+    inf = plan.info()
+    assert inf["n_branches"] == len(wl.problem.branch_q) + len(asked)
+
+
+def _prob(**kw):
+    base = dict(content_len=[3], branch_off=[0, 1], branch_q=[0], q_len=[2], opt_off=[0, 2],
+                tok_off=[0, 1, 2], tok=[1, 2], vocab=8)
+    base.update(kw)
+    return synth.Problem(*(np.asarray(base[f], np.int32) for f in
+                           ("content_len", "branch_off", "branch_q", "q_len", "opt_off", "tok_off", "tok")),
+                         base["vocab"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tok=[1, 1]), -1),                                   # duplicate option
+    (dict(tok=[1, 9]), -1),                                   # token id >= vocab
+    (dict(branch_q=[3]), -1),                                 # question out of range
+    (dict(branch_off=[0, 2]), -1),                            # CSR past the end of branch_q
+    (dict(q_len=[0]), -1),                                    # empty template
+    (dict(content_len=[-1]), -1),
+    (dict(content_len=[5000]), -2),                           # max_content_tokens 4096
+    (dict(q_len=[300]), -2),                                  # max_query_tokens 256
+    (dict(tok_off=[0, 1, 8], tok=[1, 2, 3, 4, 5, 6, 7, 0]), -2),  # 6-token option > 5
+])
+def test_error_paths(kw, code):
+    p = _prob(**kw)
+    if kw.get("branch_off") == [0, 2]:
+        p.branch_q = np.asarray([0, 7], np.int32)
+    with pytest.raises(spb.SpbError) as e:
+        spb.pack_pass(p)
+    assert e.value.code == code
+    assert spb.lib().spb_last_error().decode() != ""
+
+
+def test_budget_too_small_and_processed_limit():
+    with pytest.raises(spb.SpbError) as e:
+        spb.pack_pass(_prob(), token_budget=4)   # content 3 + branch 2 > 4
+    assert e.value.code == -2
+    with pytest.raises(spb.SpbError) as e:
+        spb.pack_pass(_prob(), max_processed_tokens=4)
+    assert e.value.code == -2
+    with pytest.raises(spb.SpbError) as e:
+        spb.pack_pass(_prob(), max_options=1)
+    assert e.value.code == -2
+
+
+def test_kernel_entry_points_validate_before_any_hip_call():
+    plan = spb.pack_pass(_prob())
+    L = spb.lib()
+    A = spb._AttnArgs()
+    A.q = A.k = A.v = A.o = 256
+    A.in_dtype, A.out_dtype, A.hq, A.hkv, A.head_dim, A.rows = spb.BF16, spb.BF16, 4, 2, 96, 1 << 20
+    meta = ctypes.c_void_p(4096)
+    assert L.spb_branch_attention(plan.handle, 0, meta, ctypes.byref(A), None) == -3   # head_dim
+    A.head_dim = 128
+    A.hq = 24; A.hkv = 3
+    assert L.spb_branch_attention(plan.handle, 0, meta, ctypes.byref(A), None) == -3   # GQA 8
+    A.hq, A.hkv = 4, 2
+    A.rows = 2
+    assert L.spb_branch_attention(plan.handle, 0, meta, ctypes.byref(A), None) == -4   # rows < n_tokens
+    assert L.spb_branch_attention(plan.handle, 5, meta, ctypes.byref(A), None) == -1   # no such pass
+    S = spb._ScoreArgs()
+    S.hidden = S.lm_head = S.workspace = 256
+    S.h_dtype, S.hidden_dim, S.rows, S.vocab, S.workspace_bytes = spb.BF16, 100, 1 << 20, 8, 1 << 20
+    assert L.spb_score_options(plan.handle, 0, meta, ctypes.byref(S), None) == -3      # hidden % 64
+    S.hidden_dim = 128
+    S.vocab = 2
+    assert L.spb_score_options(plan.handle, 0, meta, ctypes.byref(S), None) == -1      # token >= vocab
+    S.vocab = 8
+    S.workspace_bytes = 16
+    assert L.spb_score_options(plan.handle, 0, meta, ctypes.byref(S), None) == -4      # workspace
+
+
+def test_upload_rejects_small_or_misaligned_buffers():
+    plan = spb.pack_pass(_prob())
+    L = spb.lib()
+    need = plan.info(0)["meta_bytes"]
+    assert L.spb_plan_upload(plan.handle, 0, ctypes.c_void_p(4096), need - 1, None) == -4
+    assert L.spb_plan_upload(plan.handle, 0, ctypes.c_void_p(4097), need, None) == -1
+
+
+def test_score_finalize_joins_floors_in_logical_order():
+    prob = synth.make_problem("random", 41, vocab=16, n_inputs=5, n_questions=3, max_content=10,
+                              max_len=4, max_options=3, max_option_tokens=2)
+    plan = spb.pack_pass(prob, token_budget=30)
+    lay = OT.build_layout(prob, floors=True)
+    # per-pass outputs encode (logical branch, option) so the join can be read back
+    lps, ps, rs = [], [], []
+    for k in range(plan.n_passes):
+        lb, of = plan.branches(k)
+        inf = plan.info(k)
+        lp = np.zeros(inf["n_options"], np.float32)
+        p = np.zeros(inf["n_options"], np.float32)
+        r = np.zeros(inf["n_branches"], np.float32)
+        for b in range(len(lb)):
+            r[b] = lb[b]
+            q = list(lay.branches())[lb[b]].question
+            n_opt = prob.opt_off[q + 1] - prob.opt_off[q]
+            for o in range(n_opt):
+                lp[of[b] + o] = -(lb[b] * 10 + o)
+                p[of[b] + o] = lb[b] * 10 + o
+        lps.append(lp); ps.append(p); rs.append(r)
+    out = spb.score_finalize(plan, lps, ps, rs)
+    branches = list(lay.branches())
+    nb = len(prob.branch_q)
+    floor_of = {b.question: i for i, b in enumerate(branches) if b.is_floor}
+    pos = 0
+    for b in range(nb):
+        q = branches[b].question
+        assert out["residual"][b] == b
+        n_opt = prob.opt_off[q + 1] - prob.opt_off[q]
+        for o in range(n_opt):
+            assert out["p"][pos] == b * 10 + o
+            assert out["lp"][pos] == -(b * 10 + o)
+            assert out["floor_p"][pos] == floor_of[q] * 10 + o
+            assert out["lift"][pos] == np.float32(b * 10 + o) - np.float32(floor_of[q] * 10 + o)
+            pos += 1
+    assert pos == len(out["p"])
