@@ -213,7 +213,9 @@ typedef struct {
   float *lp, *p, *residual;
 } spb_score_args;
 
-spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, size_t *out);
+/* Workspace bytes spb_score_options needs for this pass, vocabulary and hidden size. */
+spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, int32_t hidden_dim,
+                                     size_t *out);
 spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *args,
                              void *stream);
 

@@ -106,7 +106,7 @@ def lib() -> ctypes.CDLL:
         L.spb_plan_upload.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.spb_branch_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.POINTER(_AttnArgs), ctypes.c_void_p]
-        L.spb_score_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        L.spb_score_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_options.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.POINTER(_ScoreArgs), ctypes.c_void_p]
@@ -252,9 +252,9 @@ def branch_attention(plan: Plan, pass_: int, d_meta, q, k, v, o, softmax_scale: 
                                       ctypes.c_void_p(_stream_handle(stream))))
 
 
-def score_workspace_bytes(plan: Plan, pass_: int, vocab: int) -> int:
+def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int) -> int:
     n = ctypes.c_size_t()
-    _check(lib().spb_score_workspace_bytes(plan.handle, pass_, int(vocab), ctypes.byref(n)))
+    _check(lib().spb_score_workspace_bytes(plan.handle, pass_, int(vocab), int(hidden_dim), ctypes.byref(n)))
     return int(n.value)
 
 

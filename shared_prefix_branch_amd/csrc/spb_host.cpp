@@ -423,6 +423,21 @@ void build_blob(PassPlan &P, int pass) {
   P.n_tokens = h.n_tokens;
 }
 
+// Workspace of spb_score_options: slice partials, captured logits, LSE per
+// row, gathered hidden states.  Returns the total; off[] gets the offsets.
+size_t score_workspace_layout(int n_scored, int n_targets, int vocab, int hidden_dim, size_t *off) {
+  int n_chunks = 0, mw = 0;
+  head_m_layout(n_scored, &n_chunks, &mw);
+  size_t sizes[4] = {(size_t)n_scored * n_vocab_slices(vocab) * 2 * sizeof(float), (size_t)n_targets * sizeof(float),
+                     (size_t)n_scored * sizeof(float), (size_t)n_chunks * 64 * mw * (size_t)hidden_dim * 2};
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (off) off[i] = o;
+    o += align256(sizes[i]);
+  }
+  return o;
+}
+
 const SpbMetaHeader &header(const PassPlan &P) { return *reinterpret_cast<const SpbMetaHeader *>(P.blob.data()); }
 
 spb_status check_pass(const spb_plan *plan, int32_t pass) {
@@ -727,13 +742,13 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
   return ok();
 }
 
-spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, size_t *out) {
+spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, int32_t hidden_dim,
+                                     size_t *out) {
   spb_status st = check_pass(plan, pass);
   if (st != SPB_OK) return st;
-  if (!out || vocab < 1) return fail(SPB_ERR_ARG, "bad argument");
+  if (!out || vocab < 1 || hidden_dim < 1) return fail(SPB_ERR_ARG, "bad argument");
   const SpbMetaHeader &h = header(plan->passes[pass]);
-  *out = align256((size_t)h.n_scored * n_vocab_slices(vocab) * 2 * sizeof(float)) +
-         align256((size_t)h.n_targets * sizeof(float)) + align256((size_t)h.n_scored * sizeof(float));
+  *out = score_workspace_layout(h.n_scored, h.n_targets, vocab, hidden_dim, nullptr);
   return ok();
 }
 
@@ -747,11 +762,12 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   if (a->h_dtype != SPB_BF16 && a->h_dtype != SPB_F32) return fail(SPB_ERR_DTYPE, "h_dtype %d unsupported", a->h_dtype);
   if (a->hidden_dim < 64 || a->hidden_dim % 64) return fail(SPB_ERR_DTYPE, "hidden_dim %d not a positive multiple of 64", a->hidden_dim);
   if (a->vocab < 1) return fail(SPB_ERR_ARG, "vocab %d < 1", a->vocab);
+  if ((int64_t)a->vocab * a->hidden_dim > (int64_t)UINT32_MAX)
+    return fail(SPB_ERR_DTYPE, "vocab x hidden_dim = %lld elements exceeds 2^32 - 1", (long long)a->vocab * a->hidden_dim);
   for (int t : P.tgt_tok)
     if (t >= a->vocab) return fail(SPB_ERR_ARG, "option token %d >= vocab %d", t, a->vocab);
   if (a->rows < h.n_tokens) return fail(SPB_ERR_SIZE, "hidden holds %lld rows, the pass has %d", (long long)a->rows, h.n_tokens);
-  size_t need = 0;
-  spb_score_workspace_bytes(plan, pass, a->vocab, &need);
+  const size_t need = score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, nullptr);
   if (a->workspace_bytes < need) return fail(SPB_ERR_SIZE, "workspace needs %zu bytes, got %zu", need, a->workspace_bytes);
   if (h.n_scored > 0 && (!a->hidden || !a->lm_head || !a->workspace || !a->lp || !a->p || !a->residual))
     return fail(SPB_ERR_ARG, "NULL tensor");
@@ -769,12 +785,13 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   L.opt_step_off = base + h.off_opt_step_off;
   L.step_slot = base + h.off_step_slot;
   L.step_row = base + h.off_step_row;
+  size_t off[4];
+  score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, off);
   char *ws = (char *)a->workspace;
-  L.part = (float *)ws;
-  ws += align256((size_t)h.n_scored * n_vocab_slices(a->vocab) * 2 * sizeof(float));
-  L.tz = (float *)ws;
-  ws += align256((size_t)h.n_targets * sizeof(float));
-  L.lse = (float *)ws;
+  L.part = (float *)(ws + off[0]);
+  L.tz = (float *)(ws + off[1]);
+  L.lse = (float *)(ws + off[2]);
+  L.hg = ws + off[3];
   L.lp = a->lp; L.p = a->p; L.residual = a->residual;
   int e = launch_score(L, stream);
   if (e) return fail(SPB_ERR_HIP, "score launch: %s", hip_error_string(e));

@@ -29,10 +29,22 @@ struct ScoreLaunch {
   float *part;   // workspace: [n_scored][n_slices][2] (max, sum of exp) per vocabulary slice
   float *tz;     // workspace: [n_targets] captured logits
   float *lse;    // workspace: [n_scored]
+  void *hg;      // workspace: gathered hidden states, bf16 [m_pad][hidden_dim]
   float *lp, *p, *residual;
 };
 
 inline int n_vocab_slices(int vocab) { return (vocab + 255) / 256; }
+
+// Scored rows per lm-head work group: n_chunks chunks of 64*mw rows (mw in
+// 1..4), the fewest chunks of at most 256 rows, each as small as possible.
+inline void head_m_layout(int M, int *n_chunks, int *mw) {
+  int n = (M + 255) / 256;
+  if (n < 1) n = 1;
+  int per = (M + n - 1) / n;
+  int w = (per + 63) / 64;
+  *n_chunks = n;
+  *mw = w < 1 ? 1 : (w > 4 ? 4 : w);
+}
 
 int launch_attention(const AttnLaunch &a, void *stream);
 int launch_score(const ScoreLaunch &a, void *stream);

@@ -9,11 +9,15 @@
 // example and the paragraph after it].  Logits are f32, the pages' default
 // lm-head precision [man page "spinf-serve", PARAMETERS: --lm-head f32out].
 //
+// Kernel 0 (gather_hidden_kernel): packs the scored rows' hidden states as
+//   bf16 rows, zero-padded to the GEMM's row tiling.
 // Kernel 1 (head_lse_kernel): Z^T[v, m] = W[v, :] . h[m, :] on MFMA 32x32x16
 //   bf16 with f32 accumulation, one work group per (256-row vocabulary slice,
-//   128 scored rows).  Logits never leave registers: the epilogue writes, per
-//   (row, slice), the slice max and sum of exp(z - max), and stores the logits
-//   of the option tokens the row predicts.
+//   64..256 scored rows); W and h tiles of 32 hidden elements are staged
+//   through registers two stages ahead into a double-buffered, XOR-swizzled
+//   LDS ring.  Logits never leave registers: the epilogue writes, per (row,
+//   slice), the slice max and sum of exp(z - max), and stores the logits of
+//   the option tokens the row predicts.
 // Kernel 2 (finalize_kernel): one wave per branch merges a row's slices in
 //   slice order into LSE, sums each option's chain of log-probabilities in
 //   token order, and renormalises.
@@ -34,12 +38,11 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kMT = 128;      // scored rows per work group
-constexpr int kKT = 64;       // hidden elements per K stage
-constexpr int kHP = kKT + 8;  // LDS pitch of the hidden tile (bf16)
-constexpr int kThreads = 256; // 4 waves x 64 vocabulary rows
+constexpr int kKT = 32;        // hidden elements per K stage (64-byte LDS rows)
+constexpr int kThreads = 256;  // 2 x 2 waves: vocabulary halves x scored-row halves
 
 __device__ inline uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
@@ -47,39 +50,119 @@ __device__ inline uint32_t f2bf(float f) {
   return u >> 16;
 }
 
-struct HeadParams {
+// LDS position, in 16-byte units, of chunk c (0..3) of row r of a tile with
+// 64-byte rows.  The XOR spreads the 16 rows one quarter-wave reads across
+// all 64 banks.
+__device__ inline int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+struct GatherParams {
   const void *hidden;
+  const int32_t *scored;
+  uint16_t *hg;
+  int H, M, M_pad;
+};
+
+// hg[m] = bf16(hidden[scored[m]]) for m < M, zero rows up to M_pad.
+template <int HIN>
+__global__ __launch_bounds__(256) void gather_hidden_kernel(GatherParams g) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // one 8-element unit
+  const int per_row = g.H / 8;
+  if (i >= (long long)g.M_pad * per_row) return;
+  const int m = (int)(i / per_row), k = (int)(i % per_row) * 8;
+  uint4 v = {0u, 0u, 0u, 0u};
+  if (m < g.M) {
+    const long long row = g.scored[m];
+    if constexpr (HIN == SPB_BF16) {
+      v = *(const uint4 *)((const uint16_t *)g.hidden + row * g.H + k);
+    } else {
+      const float4 *s = (const float4 *)((const float *)g.hidden + row * g.H + k);
+      float4 a = s[0], b = s[1];
+      v.x = f2bf(a.x) | (f2bf(a.y) << 16);
+      v.y = f2bf(a.z) | (f2bf(a.w) << 16);
+      v.z = f2bf(b.x) | (f2bf(b.y) << 16);
+      v.w = f2bf(b.z) | (f2bf(b.w) << 16);
+    }
+  }
+  *(uint4 *)(g.hg + (long long)m * g.H + k) = v;
+}
+
+struct HeadParams {
+  const uint16_t *hg;  // gathered hidden states [M_pad][H] bf16
   const uint16_t *W;
   int H, V, M;
   int n_slices, n_mchunks;
-  const int32_t *scored, *tgt_off, *tgt_tok;
+  const int32_t *tgt_off, *tgt_tok;
   float *part, *tz;
 };
 
-template <int HIN>
-__device__ inline uint4 load_hidden8(const void *hidden, int row, int H, int k) {
-  if constexpr (HIN == SPB_BF16) {
-    return *(const uint4 *)((const uint16_t *)hidden + (size_t)row * H + k);
-  } else {
-    const float4 *s = (const float4 *)((const float *)hidden + (size_t)row * H + k);
-    float4 a = s[0], b = s[1];
-    uint4 u;
-    u.x = f2bf(a.x) | (f2bf(a.y) << 16);
-    u.y = f2bf(a.z) | (f2bf(a.w) << 16);
-    u.z = f2bf(b.x) | (f2bf(b.y) << 16);
-    u.w = f2bf(b.z) | (f2bf(b.w) << 16);
-    return u;
+// barrier for the LDS hand-off that leaves outstanding global loads in flight
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int MW>
+struct HeadTile {
+  static constexpr int TM = 64 * MW;   // scored rows per work group
+  static constexpr int HU = TM / 64;   // hidden-tile 16-byte units per thread per stage
+  static constexpr int WU = 4;         // W-tile 16-byte units per thread per stage
+};
+
+// Loads stage s (hidden elements s*32 .. +32) of the W and h tiles into registers.
+// Thread t moves chunk t%4 of rows t/4 + 64 i.
+template <int MW>
+__device__ __attribute__((always_inline)) inline void head_load(u32x4 (&wr)[4], u32x4 (&hr)[HeadTile<MW>::HU],
+                                                                const uint16_t *wbase, const uint32_t (&woff)[4],
+                                                                const uint16_t *hbase, uint32_t hstride, int s) {
+  const int k0 = s * kKT;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wr[i] = *(const u32x4 *)(wbase + woff[i] + k0);
+#pragma unroll
+  for (int i = 0; i < HeadTile<MW>::HU; ++i) hr[i] = *(const u32x4 *)(hbase + (size_t)i * hstride + k0);
+}
+
+template <int MW>
+__device__ __attribute__((always_inline)) inline void head_store(const u32x4 (&wr)[4], const u32x4 (&hr)[HeadTile<MW>::HU],
+                                                                 u32x4 *Wb, u32x4 *Hb, int sr, int sc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Wb[swz(i * 64 + sr, sc)] = wr[i];
+#pragma unroll
+  for (int i = 0; i < HeadTile<MW>::HU; ++i) Hb[swz(i * 64 + sr, sc)] = hr[i];
+}
+
+template <int MW>
+__device__ __attribute__((always_inline)) inline void head_compute(f32x16 (&acc)[4][MW], const u32x4 *Wb, const u32x4 *Hb,
+                                                                   int wv, int wm, int qi, int half) {
+#pragma unroll
+  for (int ks = 0; ks < kKT / 16; ++ks) {
+    bf16x8_t a[4];
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+      u32x4 u = Wb[swz(wv * 128 + vb * 32 + qi, ks * 2 + half)];
+      a[vb] = *(bf16x8_t *)&u;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+      u32x4 u = Hb[swz(wm * 32 * MW + mb * 32 + qi, ks * 2 + half)];
+      bf16x8_t bb = *(bf16x8_t *)&u;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+        acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vb], bb, acc[vb][mb], 0, 0, 0);
+    }
   }
 }
 
-template <int HIN>
-__global__ __launch_bounds__(kThreads) void head_lse_kernel(HeadParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[2][kMT * kHP];
-  __shared__ float red[4][kMT][2];
+// MW: 32-row m blocks per wave; a work group covers 256 vocabulary rows x
+// 64*MW scored rows.  Wave (wv, wm) owns vocabulary rows wv*128 .. +128 and
+// scored rows wm*32*MW .. +32*MW.
+template <int MW>
+__global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
+  using T = HeadTile<MW>;
+  constexpr int TM = T::TM;
+  __shared__ u32x4 Ws[2][kVocabTile * 4];
+  __shared__ u32x4 Hs[2][TM * 4];
+  __shared__ float red[2][TM][2];
 
   // XCD-aware order: work groups are dealt round-robin to the 8 XCDs, so the
-  // M chunks of one vocabulary slice are given consecutive slots of one XCD
-  // and stream the same W rows through its L2 together.
+  // M chunks of one vocabulary slice get consecutive slots of one XCD and
+  // stream the same W rows through its L2 together.
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int slice = (slot / p.n_mchunks) * 8 + xcd;
@@ -88,120 +171,91 @@ __global__ __launch_bounds__(kThreads) void head_lse_kernel(HeadParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int qi = lane & 31, half = lane >> 5;
-  const int v_w0 = slice * kVocabTile + wave * 64;  // this wave's 64 vocabulary rows
-  const int m0 = mchunk * kMT;
+  const int wv = wave & 1, wm = wave >> 1;
+  const int v0 = slice * kVocabTile;
+  const int m0 = mchunk * TM;
 
-  // W row pointers (rows past the vocabulary read row 0 and are masked later)
-  const uint16_t *wrow[2];
+  const int sc = tid & 3, sr = tid >> 2;
+  uint32_t woff[4];
 #pragma unroll
-  for (int vb = 0; vb < 2; ++vb) {
-    int v = v_w0 + vb * 32 + qi;
-    wrow[vb] = p.W + (size_t)(v < p.V ? v : 0) * p.H + half * 8;
+  for (int i = 0; i < 4; ++i) {
+    int v = v0 + i * 64 + sr;
+    woff[i] = (uint32_t)(v < p.V ? v : p.V - 1) * (uint32_t)p.H + sc * 8;
   }
-  // hidden tile: 128 rows x 64 k per stage, 16-byte units (4 per thread)
-  int hrow[4], hm[4], hk[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    int unit = tid + u * kThreads;
-    hm[u] = unit >> 3;
-    hk[u] = (unit & 7) * 8;
-    int m = m0 + hm[u];
-    hrow[u] = m < p.M ? p.scored[m] : -1;
-  }
+  const uint16_t *hbase = p.hg + (size_t)(m0 + sr) * p.H + sc * 8;
+  const uint32_t hstride = 64u * (uint32_t)p.H;
 
-  f32x16 acc[2][4];
+  u32x4 wrA[4], hrA[T::HU], wrB[4], hrB[T::HU];
+  f32x16 acc[4][MW];
 #pragma unroll
-  for (int vb = 0; vb < 2; ++vb)
+  for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[vb][mb] = f32x16{0.f};
+    for (int mb = 0; mb < MW; ++mb) acc[vb][mb] = f32x16{0.f};
 
+  // stage j's registers are set j%2; LDS buffer j%2 holds stage j while it is read
   const int S = p.H / kKT;
-  bf16x8_t wcur[2][4], wnext[2][4];
-  uint4 hreg[4];
-#pragma unroll
-  for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wcur[vb][ks] = *(const bf16x8_t *)(wrow[vb] + ks * 16);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    uint4 val = hrow[u] >= 0 ? load_hidden8<HIN>(p.hidden, hrow[u], p.H, hk[u]) : uint4{0u, 0u, 0u, 0u};
-    *(uint4 *)(&Hs[0][hm[u] * kHP + hk[u]]) = val;
+  head_load<MW>(wrA, hrA, p.W, woff, hbase, hstride, 0);
+  if (S > 1) head_load<MW>(wrB, hrB, p.W, woff, hbase, hstride, 1);
+  head_store<MW>(wrA, hrA, Ws[0], Hs[0], sr, sc);
+  lds_barrier();
+  int s = 0;
+  for (; s + 1 < S; s += 2) {  // two stages per trip; no early exit, so acc stays in one register set
+    if (s + 2 < S) head_load<MW>(wrA, hrA, p.W, woff, hbase, hstride, s + 2);
+    head_compute<MW>(acc, Ws[0], Hs[0], wv, wm, qi, half);
+    head_store<MW>(wrB, hrB, Ws[1], Hs[1], sr, sc);
+    lds_barrier();
+    if (s + 3 < S) head_load<MW>(wrB, hrB, p.W, woff, hbase, hstride, s + 3);
+    head_compute<MW>(acc, Ws[1], Hs[1], wv, wm, qi, half);
+    if (s + 2 < S) head_store<MW>(wrA, hrA, Ws[0], Hs[0], sr, sc);
+    lds_barrier();
   }
-  __syncthreads();
+  if (s < S) head_compute<MW>(acc, Ws[0], Hs[0], wv, wm, qi, half);  // odd stage count: last stage in buffer 0
 
-  for (int s = 0; s < S; ++s) {
-    const int k1 = (s + 1) * kKT;
-    const bool more = s + 1 < S;
-    if (more) {
+  // epilogue.  Lane holds column m = m0 + wm*32*MW + mb*32 + qi; register r
+  // of block vb holds vocabulary row v0 + wv*128 + vb*32 + (r/4)*8 + half*4 + r%4.
+  const int vw0 = v0 + wv * 128;
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) wnext[vb][ks] = *(const bf16x8_t *)(wrow[vb] + k1 + ks * 16);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        hreg[u] = hrow[u] >= 0 ? load_hidden8<HIN>(p.hidden, hrow[u], p.H, k1 + hk[u]) : uint4{0u, 0u, 0u, 0u};
-    }
-    const uint16_t *Hb = Hs[s & 1];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        bf16x8_t bfrag = *(const bf16x8_t *)(Hb + (mb * 32 + qi) * kHP + ks * 16 + half * 8);
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
-          acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wcur[vb][ks], bfrag, acc[vb][mb], 0, 0, 0);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) *(uint4 *)(&Hs[(s + 1) & 1][hm[u] * kHP + hk[u]]) = hreg[u];
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) wcur[vb][ks] = wnext[vb][ks];
-    }
-    __syncthreads();
-  }
-
-  // epilogue.  Lane holds column m = mb*32 + qi; register r of block vb holds
-  // vocabulary row v_w0 + vb*32 + (r/4)*8 + half*4 + r%4.
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MW; ++mb) {
+    // rows past the vocabulary (last slice only) are excluded
+    const int nvalid = p.V - vw0;
     float mx = kNegInf;
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
+    for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int v = v_w0 + vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        if (v >= p.V) acc[vb][mb][r] = kNegInf;
-        mx = fmaxf(mx, acc[vb][mb][r]);
+        const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+        mx = fmaxf(mx, vr < nvalid ? acc[vb][mb][r] : kNegInf);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     float se = 0.f;
     if (mx != kNegInf) {
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
+      for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) se += __expf(acc[vb][mb][r] - mx);
+        for (int r = 0; r < 16; ++r) {
+          const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          se += vr < nvalid ? __expf(acc[vb][mb][r] - mx) : 0.f;
+        }
     }
     se = se + __shfl_xor(se, 32);
+    const int ml = wm * 32 * MW + mb * 32 + qi;
     if (half == 0) {
-      red[wave][mb * 32 + qi][0] = mx;
-      red[wave][mb * 32 + qi][1] = se;
+      red[wv][ml][0] = mx;
+      red[wv][ml][1] = se;
     }
     // capture the logits of the tokens this row predicts
-    const int m = m0 + mb * 32 + qi;
+    const int m = m0 + ml;
     if (m < p.M) {
       const int t0 = p.tgt_off[m], t1 = p.tgt_off[m + 1];
       for (int t = t0; t < t1; ++t) {
-        const int rel = p.tgt_tok[t] - v_w0;
-        if (rel < 0 || rel >= 64) continue;
+        const int rel = p.tgt_tok[t] - vw0;
+        if (rel < 0 || rel >= 128) continue;
         const int rr = rel & 31;
         if (((rr >> 2) & 1) != half) continue;
         const int vbt = rel >> 5, rt = (rr >> 3) * 4 + (rr & 3);
         float val = 0.f;
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
+        for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) val = (vb == vbt && r == rt) ? acc[vb][mb][r] : val;
         p.tz[t] = val;
@@ -209,18 +263,13 @@ __global__ __launch_bounds__(kThreads) void head_lse_kernel(HeadParams p) {
     }
   }
   __syncthreads();
-  if (tid < kMT) {
-    const int m = m0 + tid;
+  for (int ml = tid; ml < TM; ml += kThreads) {
+    const int m = m0 + ml;
     if (m < p.M) {
-      float M = kNegInf;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w][tid][0]);
-      float Ssum = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float mw = red[w][tid][0];
-        Ssum += mw == kNegInf ? 0.f : red[w][tid][1] * __expf(mw - M);
-      }
+      const float a = red[0][ml][0], c = red[1][ml][0];
+      const float M = fmaxf(a, c);
+      const float Ssum = (a == kNegInf ? 0.f : red[0][ml][1] * __expf(a - M)) +
+                         (c == kNegInf ? 0.f : red[1][ml][1] * __expf(c - M));
       float *dst = p.part + ((size_t)m * p.n_slices + slice) * 2;
       dst[0] = M;
       dst[1] = Ssum;
@@ -288,26 +337,47 @@ __global__ __launch_bounds__(64) void finalize_kernel(FinParams f) {
 
 int launch_score(const ScoreLaunch &a, void *stream) {
   hipStream_t s = (hipStream_t)stream;
+  int n_chunks = 0, mw = 0;
+  head_m_layout(a.n_scored, &n_chunks, &mw);
+  const int m_pad = n_chunks * 64 * mw;
+  GatherParams g;
+  g.hidden = a.hidden;
+  g.scored = (const int32_t *)a.scored;
+  g.hg = (uint16_t *)a.hg;
+  g.H = a.hidden_dim;
+  g.M = a.n_scored;
+  g.M_pad = m_pad;
+  long long units = (long long)m_pad * (a.hidden_dim / 8);
+  unsigned gblocks = (unsigned)((units + 255) / 256);
+  if (a.h_dtype == SPB_BF16)
+    hipLaunchKernelGGL(gather_hidden_kernel<SPB_BF16>, dim3(gblocks), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL(gather_hidden_kernel<SPB_F32>, dim3(gblocks), dim3(256), 0, s, g);
+  int e = (int)hipGetLastError();
+  if (e) return e;
+
   HeadParams p;
-  p.hidden = a.hidden;
+  p.hg = (const uint16_t *)a.hg;
   p.W = (const uint16_t *)a.lm_head;
   p.H = a.hidden_dim;
   p.V = a.vocab;
   p.M = a.n_scored;
   p.n_slices = n_vocab_slices(a.vocab);
-  p.n_mchunks = (a.n_scored + kMT - 1) / kMT;
-  p.scored = (const int32_t *)a.scored;
+  p.n_mchunks = n_chunks;
   p.tgt_off = (const int32_t *)a.tgt_off;
   p.tgt_tok = (const int32_t *)a.tgt_tok;
   p.part = a.part;
   p.tz = a.tz;
   long long groups = (long long)((p.n_slices + 7) / 8) * 8 * p.n_mchunks;
   if (groups > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
-  if (a.h_dtype == SPB_BF16)
-    hipLaunchKernelGGL(head_lse_kernel<SPB_BF16>, dim3((unsigned)groups), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(head_lse_kernel<SPB_F32>, dim3((unsigned)groups), dim3(kThreads), 0, s, p);
-  int e = (int)hipGetLastError();
+  dim3 grid((unsigned)groups), block(kThreads);
+  switch (mw) {
+    case 1: hipLaunchKernelGGL(head_lse_kernel<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(head_lse_kernel<2>, grid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL(head_lse_kernel<3>, grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL(head_lse_kernel<4>, grid, block, 0, s, p); break;
+  }
+  e = (int)hipGetLastError();
   if (e) return e;
   FinParams f;
   f.n_slices = p.n_slices;

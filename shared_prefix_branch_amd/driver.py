@@ -56,7 +56,7 @@ class Job:
         n = max(1, inf["n_tokens"])
         dev = self.device
         meta = t.empty(inf["meta_bytes"], dtype=t.uint8, device=dev)
-        ws = t.empty(max(256, score_workspace_bytes(self.plan, k, self.V)), dtype=t.uint8, device=dev)
+        ws = t.empty(max(256, score_workspace_bytes(self.plan, k, self.V, self.H)), dtype=t.uint8, device=dev)
         return PassBuffers(
             inf["n_tokens"],
             t.empty((n, self.hq, self.d), dtype=self.qkv_dtype, device=dev),

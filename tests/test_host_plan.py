@@ -246,3 +246,18 @@ def test_score_finalize_joins_floors_in_logical_order():
             assert out["lift"][pos] == np.float32(b * 10 + o) - np.float32(floor_of[q] * 10 + o)
             pos += 1
     assert pos == len(out["p"])
+
+
+def test_score_workspace_covers_gathered_hidden_rows():
+    # the lm head packs the scored rows' hidden states into the workspace, so
+    # its size must grow with the hidden size by at least M rows of bf16
+    prob = synth.make_problem("random", 5, vocab=1000, n_inputs=4, n_questions=5, max_content=40,
+                              max_len=8, max_options=4, max_option_tokens=3)
+    plan = spb.pack_pass(prob)
+    M = plan.info(0)["n_scored_rows"]
+    small = spb.score_workspace_bytes(plan, 0, 1000, 64)
+    big = spb.score_workspace_bytes(plan, 0, 1000, 3840)
+    assert big - small >= M * (3840 - 64) * 2
+    assert small >= M * 64 * 2 + M * 4 * 2 * 4  # hidden rows + (max, sum) per 256-row vocabulary slice
+    with pytest.raises(spb.SpbError):
+        spb.score_workspace_bytes(plan, 0, 1000, 0)
