@@ -12,15 +12,21 @@
 // segment) and one KV head.  Wave w handles 32 query rows for query head
 // kvh*G + w%G; the G query heads of a KV group share every staged K/V chunk.
 //
-// Per chunk of 64 keys staged in LDS (K row-major, V transposed to d-major):
+// Keys are visited as a list of chunks built per work item: content chunks of
+// 64 keys aligned to the content start, then for each branch that meets the
+// work item's rows, chunks of 32 keys aligned to the branch start (template
+// rows, then option-trie nodes).  Each chunk is staged row-major in LDS (K and
+// V, rows padded against bank conflicts), double-buffered, loaded into
+// registers one chunk ahead:
 //   S^T = K Q^T      (MFMA 32x32x16 bf16, or 32x32x64 OCP e4m3 for fp8 Q/K)
 //   online softmax   (each lane owns one query; f32, base-2 exponent)
-//   O^T += V^T P^T   (MFMA 32x32x16 bf16, P rounded to bf16)
+//   O^T += V^T P^T   (MFMA 32x32x16 bf16 with P in bf16; the V^T operand is
+//                     read from row-major V with the LDS transpose read)
 //
-// Batch invariance: a row consumes its content keys in 64-key chunks aligned
-// to its content start, then its branch keys in 64-key chunks aligned to its
-// branch start.  Slot i of a chunk always holds chunk-relative key i, every
-// masked slot contributes an exact zero and leaves the running max unchanged
+// Batch invariance: a row sees its content keys in 64-key chunks aligned to
+// its content start and its branch keys in 32-key chunks aligned to its branch
+// start.  Slot i of a chunk always holds chunk-relative key i, every masked
+// slot contributes an exact zero and leaves the running max unchanged
 // (alpha = 1), and every per-row sum runs in a fixed slot order.  So a row's
 // bits depend on its own root path only, not on where its input was packed.
 #define SPB_HD __host__ __device__
@@ -36,18 +42,23 @@ namespace spb {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kMaxChunks = kMaxTileChunks;  // chunk-list capacity per work item (checked on the host)
 
-__device__ inline uint32_t f2bf(float f) {  // round to nearest even (inputs finite)
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+__device__ inline uint32_t pack_bf16(float a, float b) {  // round to nearest even
+  bf16x2_t v = __builtin_convertvector(f32x2{a, b}, bf16x2_t);
+  return *(uint32_t *)&v;
 }
-__device__ inline float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
 // OCP e4m3fn byte -> bf16 bits (exact: every e4m3 value is a bf16 value).
 __device__ inline uint32_t e4m3_to_bf(uint32_t b) {
@@ -72,100 +83,23 @@ struct AttnParams {
 
 template <int D, int G, int IN>
 struct Cfg {
-  static constexpr int RW = G == 4 ? 2 : 4;      // 32-row groups per work item
-  static constexpr int NW = RW * G;              // waves
+  static constexpr bool FP8 = IN == SPB_FP8_E4M3;
+  static constexpr int RW = G == 4 ? 2 : 4;   // 32-row groups per work item
+  static constexpr int NW = RW * G;           // waves
   static constexpr int NT = NW * 64;
   static constexpr int ROWS = 32 * RW;
-  static constexpr int SPLITS = 128 / ROWS;      // work items per 128-row tile
-  static constexpr int KPAD = IN == SPB_FP8_E4M3 ? D + 16 : D + 8;  // K row pitch (elements)
-  static constexpr int KBYTES = 64 * KPAD * (IN == SPB_FP8_E4M3 ? 1 : 2);
-  static constexpr int VPAD = 68;                // V^T row pitch (bf16): 64 keys + 4
-  static constexpr int VBYTES = D * VPAD * 2;
+  static constexpr int SPLITS = 128 / ROWS;   // work items per 128-row tile
+  static constexpr int KROWB = FP8 ? D : 2 * D;  // bytes per staged K row
+  static constexpr int KCH = KROWB / 16;         // 16-byte chunks per K row
+  static constexpr int VCH = 2 * D / 16;         // V is staged as bf16
+  static constexpr int KPT = (64 * KCH + NT - 1) / NT;  // K units per thread (64-key chunk)
+  static constexpr int VPT = (64 * VCH + NT - 1) / NT;
+  // LDS row pitches (bytes).  K: +16 so the 16 rows a quarter-wave reads at
+  // one column rotate through all banks.  V: +64 so the 4 rows of one
+  // transpose read fall in disjoint quarters of the banks.
+  static constexpr int KPITCH = KROWB + 16;
+  static constexpr int VPITCH = 2 * D + 64;
 };
-
-// ----------------------------------------------------------------- staging
-
-template <int D, int G, int IN>
-__device__ inline void stage_chunk(const AttnParams &p, int kvh, int key0, unsigned char *Ks, uint16_t *Vt) {
-  using C = Cfg<D, G, IN>;
-  const int tid = threadIdx.x;
-  const int n = p.n_tokens;
-  if constexpr (IN == SPB_FP8_E4M3) {
-    const unsigned char *kp = (const unsigned char *)p.k;
-    constexpr int KU = 64 * D / 16;
-    for (int u = tid; u < KU; u += C::NT) {
-      int key = u / (D / 16), dc = u % (D / 16);
-      int y = key0 + key;
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (y < n) val = *(const uint4 *)(kp + ((size_t)y * p.hkv + kvh) * D + dc * 16);
-      *(uint4 *)(Ks + key * C::KPAD + dc * 16) = val;
-    }
-  } else {
-    uint16_t *Kd = (uint16_t *)Ks;
-    constexpr int KU = 64 * D / 8;
-    for (int u = tid; u < KU; u += C::NT) {
-      int key = u / (D / 8), dc = u % (D / 8);
-      int y = key0 + key;
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (y < n) {
-        if constexpr (IN == SPB_BF16) {
-          val = *(const uint4 *)((const uint16_t *)p.k + ((size_t)y * p.hkv + kvh) * D + dc * 8);
-        } else {
-          const float4 *src = (const float4 *)((const float *)p.k + ((size_t)y * p.hkv + kvh) * D + dc * 8);
-          float4 a = src[0], b = src[1];
-          val.x = f2bf(a.x) | (f2bf(a.y) << 16);
-          val.y = f2bf(a.z) | (f2bf(a.w) << 16);
-          val.z = f2bf(b.x) | (f2bf(b.y) << 16);
-          val.w = f2bf(b.z) | (f2bf(b.w) << 16);
-        }
-      }
-      *(uint4 *)(Kd + key * C::KPAD + dc * 8) = val;
-    }
-  }
-  // V^T: each unit is 4 keys x 8 dims, written as 8 rows of 4 keys
-  constexpr int VU = 16 * (D / 8);
-  for (int u = tid; u < VU; u += C::NT) {
-    int kg = u / (D / 8), dc = u % (D / 8);
-    uint32_t e[4][8];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      int y = key0 + kg * 4 + kk;
-      bool in = y < n;
-      size_t base = ((size_t)(in ? y : 0) * p.hkv + kvh) * D + dc * 8;
-      if constexpr (IN == SPB_BF16) {
-        uint4 w = in ? *(const uint4 *)((const uint16_t *)p.v + base) : uint4{0u, 0u, 0u, 0u};
-        uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[kk][2 * i] = ww[i] & 0xFFFFu;
-          e[kk][2 * i + 1] = ww[i] >> 16;
-        }
-      } else if constexpr (IN == SPB_F32) {
-        const float4 *src = (const float4 *)((const float *)p.v + base);
-        float4 a = in ? src[0] : float4{0.f, 0.f, 0.f, 0.f};
-        float4 b = in ? src[1] : float4{0.f, 0.f, 0.f, 0.f};
-        e[kk][0] = f2bf(a.x); e[kk][1] = f2bf(a.y); e[kk][2] = f2bf(a.z); e[kk][3] = f2bf(a.w);
-        e[kk][4] = f2bf(b.x); e[kk][5] = f2bf(b.y); e[kk][6] = f2bf(b.z); e[kk][7] = f2bf(b.w);
-      } else {
-        uint2 w = in ? *(const uint2 *)((const unsigned char *)p.v + base) : uint2{0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[kk][i] = e4m3_to_bf((w.x >> (8 * i)) & 0xFFu);
-          e[kk][4 + i] = e4m3_to_bf((w.y >> (8 * i)) & 0xFFu);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint2 w;
-      w.x = e[0][i] | (e[1][i] << 16);
-      w.y = e[2][i] | (e[3][i] << 16);
-      *(uint2 *)(Vt + (dc * 8 + i) * C::VPAD + kg * 4) = w;
-    }
-  }
-}
-
-// ----------------------------------------------------------------- one chunk
 
 template <int D, int IN>
 struct QFrag {
@@ -173,98 +107,206 @@ struct QFrag {
   typename std::conditional<IN == SPB_FP8_E4M3, i32x8, bf16x8_t>::type f[STEPS];
 };
 
-struct RowState {
-  float m;   // running max (base-2 logits)
-  float l;   // this lane's partial row sum
+template <int D, int G, int IN>
+struct Stage {  // one chunk's K and V units held by this thread
+  u32x4 k[Cfg<D, G, IN>::KPT];
+  u32x4 v[Cfg<D, G, IN>::VPT];
 };
 
+// Global -> registers: rows key0 .. key0 + nrows of K and V for KV head kvh.
 template <int D, int G, int IN>
-__device__ inline void chunk_step(const unsigned char *Ks, const uint16_t *Vt, const QFrag<D, IN> &qf,
-                                  uint64_t mask, float sc, RowState &st, f32x16 (&o)[D / 32]) {
+__device__ inline void stage_load(Stage<D, G, IN> &st, const AttnParams &p, int kvh, int key0, int nrows) {
+  using C = Cfg<D, G, IN>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::KPT; ++i) {
+    const int u = tid + i * C::NT;
+    const int r = u / C::KCH, c = u % C::KCH;
+    const int y = key0 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (r < nrows && y < p.n_tokens) {
+      const size_t row = (size_t)y * p.hkv + kvh;
+      if constexpr (IN == SPB_FP8_E4M3) {
+        val = *(const u32x4 *)((const unsigned char *)p.k + row * D + c * 16);
+      } else if constexpr (IN == SPB_BF16) {
+        val = *(const u32x4 *)((const uint16_t *)p.k + row * D + c * 8);
+      } else {
+        const float *src = (const float *)p.k + row * D + c * 8;
+        u32x4 a = *(const u32x4 *)src, b = *(const u32x4 *)(src + 4);
+        val = u32x4{pack_bf16(__uint_as_float(a.x), __uint_as_float(a.y)),
+                    pack_bf16(__uint_as_float(a.z), __uint_as_float(a.w)),
+                    pack_bf16(__uint_as_float(b.x), __uint_as_float(b.y)),
+                    pack_bf16(__uint_as_float(b.z), __uint_as_float(b.w))};
+      }
+    }
+    st.k[i] = val;
+  }
+#pragma unroll
+  for (int i = 0; i < C::VPT; ++i) {
+    const int u = tid + i * C::NT;
+    const int r = u / C::VCH, c = u % C::VCH;
+    const int y = key0 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (r < nrows && y < p.n_tokens) {
+      const size_t row = (size_t)y * p.hkv + kvh;
+      if constexpr (IN == SPB_FP8_E4M3) {
+        u32x2 w = *(const u32x2 *)((const unsigned char *)p.v + row * D + c * 8);
+        val = u32x4{e4m3_to_bf(w.x & 0xFFu) | (e4m3_to_bf((w.x >> 8) & 0xFFu) << 16),
+                    e4m3_to_bf((w.x >> 16) & 0xFFu) | (e4m3_to_bf(w.x >> 24) << 16),
+                    e4m3_to_bf(w.y & 0xFFu) | (e4m3_to_bf((w.y >> 8) & 0xFFu) << 16),
+                    e4m3_to_bf((w.y >> 16) & 0xFFu) | (e4m3_to_bf(w.y >> 24) << 16)};
+      } else if constexpr (IN == SPB_BF16) {
+        val = *(const u32x4 *)((const uint16_t *)p.v + row * D + c * 8);
+      } else {
+        const float *src = (const float *)p.v + row * D + c * 8;
+        u32x4 a = *(const u32x4 *)src, b = *(const u32x4 *)(src + 4);
+        val = u32x4{pack_bf16(__uint_as_float(a.x), __uint_as_float(a.y)),
+                    pack_bf16(__uint_as_float(a.z), __uint_as_float(a.w)),
+                    pack_bf16(__uint_as_float(b.x), __uint_as_float(b.y)),
+                    pack_bf16(__uint_as_float(b.z), __uint_as_float(b.w))};
+      }
+    }
+    st.v[i] = val;
+  }
+}
+
+// registers -> LDS buffers (swizzled)
+template <int D, int G, int IN>
+__device__ inline void stage_store(const Stage<D, G, IN> &st, char *Ks, char *Vs, int nrows) {
+  using C = Cfg<D, G, IN>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::KPT; ++i) {
+    const int u = tid + i * C::NT;
+    const int r = u / C::KCH, c = u % C::KCH;
+    if (r < nrows) *(u32x4 *)(Ks + r * C::KPITCH + c * 16) = st.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < C::VPT; ++i) {
+    const int u = tid + i * C::NT;
+    const int r = u / C::VCH, c = u % C::VCH;
+    if (r < nrows) *(u32x4 *)(Vs + r * C::VPITCH + c * 16) = st.v[i];
+  }
+}
+
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct RowState {
+  float m;  // running max of the scaled (base-2) logits
+  float l;  // this lane's partial row sum
+};
+
+// Which keys of a chunk this lane's query sees.  Register r of block kb
+// holds chunk key kb*32 + (r/4)*8 + half*4 + r%4; with the lane's half folded
+// into the thresholds, every test compares a compile-time slot offset
+// kb*32 + (r/4)*8 + r%4 against per-lane values:
+//   visible = slot < thr  ||  slot is one of anc[0..3]  (ANC only)
+struct Vis {
+  int thr;        // keys [0, thr + 4*half) visible
+  int anc[kMaxDepth];  // option-trie ancestor keys minus 4*half, or -1000
+};
+
+// One chunk of NKB*32 keys.  MODE 0: every key visible to every lane;
+// 1: prefix test only; 2: prefix test and ancestor keys.
+template <int D, int G, int IN, int NKB, int MODE>
+__device__ inline void chunk_step(const char *Ks, const char *Vs, const QFrag<D, IN> &qf, const Vis &vis,
+                                  float sc, RowState &st, f32x16 (&o)[D / 32]) {
   using C = Cfg<D, G, IN>;
   const int lane = threadIdx.x & 63;
   const int qi = lane & 31, half = lane >> 5;
-  f32x16 s[2];
+  f32x16 s[NKB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
+    asm volatile("" ::: "memory");  // keeps each block's LDS reads next to its MFMAs
     s[kb] = f32x16{0.f};
-    if constexpr (IN == SPB_FP8_E4M3) {
+    const int r = kb * 32 + qi;
+    if constexpr (C::FP8) {
 #pragma unroll
       for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-        const unsigned char *src = Ks + (kb * 32 + qi) * C::KPAD + t * 64 + half * 32;
-        i32x8 a;
-        uint4 a0 = *(const uint4 *)src, a1 = *(const uint4 *)(src + 16);
-        a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
-        a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+        const char *src = Ks + r * C::KPITCH + t * 64 + half * 32;
+        u32x4 a0 = *(const u32x4 *)src, a1 = *(const u32x4 *)(src + 16);
+        i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf.f[t], s[kb], 0, 0, 0, 0, 0, 0);
       }
     } else {
-      const uint16_t *Kd = (const uint16_t *)Ks;
 #pragma unroll
       for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-        bf16x8_t a = *(const bf16x8_t *)(Kd + (kb * 32 + qi) * C::KPAD + t * 16 + half * 8);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.f[t], s[kb], 0, 0, 0);
+        u32x4 u = *(const u32x4 *)(Ks + r * C::KPITCH + t * 32 + half * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(bf16x8_t *)&u, qf.f[t], s[kb], 0, 0, 0);
       }
     }
   }
   // online softmax: lane owns query qi; register r of block kb holds key
   // kb*32 + (r/4)*8 + half*4 + r%4
+  if constexpr (MODE != 0) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int slot = kb * 32 + (r >> 2) * 8 + (r & 3);
+        bool v = slot < vis.thr;
+        if constexpr (MODE == 2) {
+#pragma unroll
+          for (int a = 0; a < kMaxDepth; ++a) v = v || slot == vis.anc[a];
+        }
+        s[kb][r] = v ? s[kb][r] : kNegInf;
+      }
+  }
   float mloc = kNegInf;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      int key = kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-      float t = ((mask >> key) & 1ull) ? s[kb][r] * sc : kNegInf;
-      s[kb][r] = t;
-      mloc = fmaxf(mloc, t);
-    }
+    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kb][r]);
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  float mnew = fmaxf(st.m, mloc);
-  float alpha = mnew == kNegInf ? 1.f : exp2f(st.m - mnew);
-  uint32_t pk[2][8];
+  const float mnew = fmaxf(st.m, mloc * sc);
+  const bool none = mnew == kNegInf;  // nothing visible yet: p = 0, alpha = 1
+  const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(st.m - mnew);
+  const float negm = none ? 0.f : -mnew;
+  uint32_t pk[NKB][8];
   float lsum = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float p0 = s[kb][r] == kNegInf ? 0.f : exp2f(s[kb][r] - mnew);
-      float p1 = s[kb][r + 1] == kNegInf ? 0.f : exp2f(s[kb][r + 1] - mnew);
-      uint32_t b0 = f2bf(p0), b1 = f2bf(p1);
-      lsum += bf2f(b0);
-      lsum += bf2f(b1);
-      pk[kb][r >> 1] = b0 | (b1 << 16);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sc, negm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], sc, negm));
+      lsum += p0;
+      lsum += p1;
+      pk[kb][r >> 1] = pack_bf16(p0, p1);
     }
   st.l = st.l * alpha + lsum;
   st.m = mnew;
+  if (__ballot(alpha != 1.f)) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-  // O^T += V^T P^T: k-step j covers keys 16j + half*4 + {0..3} and 16j + 8 + half*4 + {0..3}
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+  }
+  // O^T += V^T P^T.  k-step j covers keys 16j + half*4 + {0..3} and
+  // 16j + 8 + half*4 + {0..3}: the P^T operand is registers 8(j%2) .. +8 of
+  // block j/2, the V^T operand two transpose reads of 4 rows each.
+  const int g = qi >> 4, l16 = lane & 15;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2 * NKB; ++j) {
+    asm volatile("" ::: "memory");
     const int kb = j >> 1, rb = (j & 1) * 4;
     union {
       uint32_t u[4];
       bf16x8_t v;
     } b;
     b.u[0] = pk[kb][rb]; b.u[1] = pk[kb][rb + 1]; b.u[2] = pk[kb][rb + 2]; b.u[3] = pk[kb][rb + 3];
+    // lane reads 4 bf16 at row 16j + half*4 + l16/4 (and +8), column
+    // db*32 + g*16 + 4*(l16%4); the transpose hands it column db*32 + qi
+    const char *vrow = Vs + (16 * j + half * 4 + (l16 >> 2)) * C::VPITCH + (g * 16 + 4 * (l16 & 3)) * 2;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint16_t *row = Vt + (db * 32 + qi) * C::VPAD + 16 * j + half * 4;
       union {
-        uint2 u[2];
+        i16x4 h[2];
         bf16x8_t v;
       } a;
-      a.u[0] = *(const uint2 *)row;
-      a.u[1] = *(const uint2 *)(row + 8);
+      a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + db * 64));
+      a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 8 * C::VPITCH + db * 64));
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, o[db], 0, 0, 0);
     }
   }
-}
-
-__device__ inline uint64_t range_mask(int n) {  // bits [0, n), n clamped to [0, 64]
-  n = n < 0 ? 0 : (n > 64 ? 64 : n);
-  return n == 64 ? ~0ull : ((1ull << n) - 1ull);
 }
 
 // ----------------------------------------------------------------- kernel
@@ -272,8 +314,10 @@ __device__ inline uint64_t range_mask(int n) {  // bits [0, n), n clamped to [0,
 template <int D, int G, int IN, int OUT>
 __global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(AttnParams p) {
   using C = Cfg<D, G, IN>;
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[C::KBYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[C::VBYTES / 2];
+  __shared__ __attribute__((aligned(16))) char Ks[2][64 * C::KPITCH];
+  __shared__ __attribute__((aligned(16))) char Vs[2][64 * C::VPITCH];
+  __shared__ int2 chunks[kMaxChunks];  // (key0, info): info < 0 content chunk -1-c; else branch << 10 | c
+  __shared__ int n_chunks_s;
 
   const int w = blockIdx.x;
   const int kvh = w % p.hkv;
@@ -284,13 +328,43 @@ __global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(A
   const int sub_n = min(C::ROWS, tile.row0 + tile.nrows - sub0);
   if (sub_n <= 0) return;  // uniform over the work group
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rw = wave / G, gh = wave % G;
   const int h = kvh * G + gh;
   const int qi = lane & 31, half = lane >> 5;
   const int local = rw * 32 + qi;
   const bool active = local < sub_n;
   const int x = sub0 + local;
+
+  // chunk list (wave 0): content chunks, then the chunks of each branch that
+  // meets rows [sub0, sub0 + sub_n)
+  if (wave == 0) {
+    for (int c = lane; c < tile.ncc && c < kMaxChunks; c += 64) chunks[c] = int2{tile.seg + c * kChunk, -1 - c};
+    int n = tile.ncc;
+    for (int b0 = tile.b_lo; b0 < tile.b_hi; b0 += 64) {
+      const int b = b0 + lane;
+      int cnt = 0, start = 0;
+      if (b < tile.b_hi) {
+        const SpbBranch br = p.branches[b];
+        start = br.start;
+        if (br.start + br.E > sub0 && br.start < sub0 + sub_n) {
+          const int last = min(br.start + br.E, sub0 + sub_n) - 1 - br.start;
+          cnt = last / kBranchChunk + 1;
+        }
+      }
+      int incl = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      const int base = n + incl - cnt;
+      for (int c = 0; c < cnt; ++c)
+        if (base + c < kMaxChunks) chunks[base + c] = int2{start + c * kBranchChunk, (b << 10) | c};
+      n += __shfl(incl, 63);
+    }
+    if (lane == 0) n_chunks_s = n < kMaxChunks ? n : kMaxChunks;
+  }
 
   SpbRow row;
   if (active) {
@@ -300,39 +374,34 @@ __global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(A
   }
 
   QFrag<D, IN> qf;
-  if constexpr (IN == SPB_FP8_E4M3) {
+  if constexpr (C::FP8) {
     const unsigned char *qp = (const unsigned char *)p.q + ((size_t)x * p.hq + h) * D;
 #pragma unroll
     for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-      uint4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
       if (active) {
-        a0 = *(const uint4 *)(qp + t * 64 + half * 32);
-        a1 = *(const uint4 *)(qp + t * 64 + half * 32 + 16);
+        a0 = *(const u32x4 *)(qp + t * 64 + half * 32);
+        a1 = *(const u32x4 *)(qp + t * 64 + half * 32 + 16);
       }
-      qf.f[t][0] = a0.x; qf.f[t][1] = a0.y; qf.f[t][2] = a0.z; qf.f[t][3] = a0.w;
-      qf.f[t][4] = a1.x; qf.f[t][5] = a1.y; qf.f[t][6] = a1.z; qf.f[t][7] = a1.w;
+      qf.f[t] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     }
   } else {
 #pragma unroll
     for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-      union {
-        uint4 u;
-        bf16x8_t v;
-      } a;
-      a.u = uint4{0u, 0u, 0u, 0u};
+      u32x4 a = {0u, 0u, 0u, 0u};
       if (active) {
         if constexpr (IN == SPB_BF16) {
-          a.u = *(const uint4 *)((const uint16_t *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8);
+          a = *(const u32x4 *)((const uint16_t *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8);
         } else {
-          const float4 *src = (const float4 *)((const float *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8);
-          float4 b0 = src[0], b1 = src[1];
-          a.u.x = f2bf(b0.x) | (f2bf(b0.y) << 16);
-          a.u.y = f2bf(b0.z) | (f2bf(b0.w) << 16);
-          a.u.z = f2bf(b1.x) | (f2bf(b1.y) << 16);
-          a.u.w = f2bf(b1.z) | (f2bf(b1.w) << 16);
+          const float *src = (const float *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8;
+          u32x4 f0 = *(const u32x4 *)src, f1 = *(const u32x4 *)(src + 4);
+          a = u32x4{pack_bf16(__uint_as_float(f0.x), __uint_as_float(f0.y)),
+                    pack_bf16(__uint_as_float(f0.z), __uint_as_float(f0.w)),
+                    pack_bf16(__uint_as_float(f1.x), __uint_as_float(f1.y)),
+                    pack_bf16(__uint_as_float(f1.z), __uint_as_float(f1.w))};
         }
       }
-      qf.f[t] = a.v;
+      qf.f[t] = *(bf16x8_t *)&a;
     }
   }
 
@@ -341,61 +410,91 @@ __global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(A
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{0.f};
 
-  // content phase: chunks aligned to the content start
-  for (int c = 0; c < tile.ncc; ++c) {
-    __syncthreads();
-    stage_chunk<D, G, IN>(p, kvh, tile.seg + c * kChunk, Ks, Vt);
-    __syncthreads();
-    uint64_t mask = range_mask(row.cvis - c * kChunk);
-    if (__ballot(mask != 0ull)) chunk_step<D, G, IN>(Ks, Vt, qf, mask, p.sc, st, o);
+  __syncthreads();  // chunk list ready
+  const int nch = n_chunks_s;
+
+  // Prefetch loads are issued on every trip (past the end they reload the
+  // last chunk), so no branch changes the count of outstanding loads and each
+  // LDS store waits only for the chunk it writes.
+  auto nrows_of = [&](int i) { return chunks[i].y < 0 ? kChunk : kBranchChunk; };
+  Stage<D, G, IN> stg;
+  if (nch > 0) {
+    stage_load<D, G, IN>(stg, p, kvh, chunks[0].x, nrows_of(0));
+    stage_store<D, G, IN>(stg, Ks[0], Vs[0], nrows_of(0));
+    lds_barrier();
+    const int i1 = min(1, nch - 1);
+    stage_load<D, G, IN>(stg, p, kvh, chunks[i1].x, nrows_of(i1));
   }
-  // branch phase: chunks aligned to each branch start
-  for (int b = tile.b_lo; b < tile.b_hi; ++b) {
-    const SpbBranch br = p.branches[b];
-    if (br.start + br.E <= sub0 || br.start >= sub0 + sub_n) continue;
-    const int last = min(br.start + br.E, sub0 + sub_n) - 1 - br.start;
-    const bool mine = row.br == br.start;
-    for (int c = 0; c * kChunk <= last; ++c) {
-      __syncthreads();
-      stage_chunk<D, G, IN>(p, kvh, br.start + c * kChunk, Ks, Vt);
-      __syncthreads();
-      uint64_t mask = 0ull;
-      if (mine) {
-        const int lo = c * kChunk;
-        mask = range_mask(min(row.e + 1, row.L) - lo);
+
+  for (int i = 0; i < nch; ++i) {
+    const int buf = i & 1;
+    const int2 ch = chunks[i];
+    Vis vis;
 #pragma unroll
-        for (int i = 0; i < kMaxDepth; ++i) {
-          int a = anc_of(row, i) - lo;
-          if (i < row.depth && a >= 0 && a < kChunk) mask |= 1ull << a;
+    for (int a = 0; a < kMaxDepth; ++a) vis.anc[a] = -1000;
+    if (ch.y < 0) {  // content chunk c: keys [c*64, c*64 + 64) of the content
+      const int c = -1 - ch.y;
+      const int nvis = row.cvis - c * kChunk;
+      vis.thr = nvis - 4 * half;
+      if (__ballot(nvis > 0)) {
+        if (__ballot(nvis < kChunk))
+          chunk_step<D, G, IN, 2, 1>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
+        else
+          chunk_step<D, G, IN, 2, 0>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
+      }
+    } else {  // branch chunk c: extended keys [c*32, c*32 + 32) of the branch
+      const int c = ch.y & 1023;
+      const int lo = c * kBranchChunk;
+      const bool mine = row.br == ch.x - lo;
+      int nt = mine ? min(min(row.e + 1, row.L) - lo, kBranchChunk) : 0;
+      bool any = nt > 0;
+      const bool node = mine && row.depth > 0;
+      if (node) {
+#pragma unroll
+        for (int a = 0; a < kMaxDepth; ++a) {
+          const int e = anc_of(row, a) - lo;
+          if (a < row.depth && e >= 0 && e < kBranchChunk) {
+            vis.anc[a] = e - 4 * half;
+            any = true;
+          }
         }
       }
-      if (__ballot(mask != 0ull)) chunk_step<D, G, IN>(Ks, Vt, qf, mask, p.sc, st, o);
+      vis.thr = nt - 4 * half;
+      if (__ballot(any)) {
+        if (__ballot(node))
+          chunk_step<D, G, IN, 1, 2>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
+        else
+          chunk_step<D, G, IN, 1, 1>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
+      }
     }
+    const int i1 = min(i + 1, nch - 1), i2 = min(i + 2, nch - 1);
+    stage_store<D, G, IN>(stg, Ks[buf ^ 1], Vs[buf ^ 1], nrows_of(i1));
+    lds_barrier();
+    stage_load<D, G, IN>(stg, p, kvh, chunks[i2].x, nrows_of(i2));
   }
 
   // normalise and store: lane holds d = db*32 + (r/4)*8 + half*4 + r%4
-  float l = st.l + __shfl_xor(st.l, 32);
-  float inv = p.s_v / l;
+  const float l = st.l + __shfl_xor(st.l, 32);
+  const float inv = p.s_v / l;
   if (active) {
     if constexpr (OUT == SPB_F32) {
       float *op = (float *)p.o + ((size_t)x * p.hq + h) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float4 v = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
-          *(float4 *)(op + db * 32 + g * 8 + half * 4) = v;
+        for (int gg = 0; gg < 4; ++gg) {
+          float4 v = {o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv, o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv};
+          *(float4 *)(op + db * 32 + gg * 8 + half * 4) = v;
         }
     } else {
       uint16_t *op = (uint16_t *)p.o + ((size_t)x * p.hq + h) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 v;
-          v.x = f2bf(o[db][4 * g] * inv) | (f2bf(o[db][4 * g + 1] * inv) << 16);
-          v.y = f2bf(o[db][4 * g + 2] * inv) | (f2bf(o[db][4 * g + 3] * inv) << 16);
-          *(uint2 *)(op + db * 32 + g * 8 + half * 4) = v;
+        for (int gg = 0; gg < 4; ++gg) {
+          u32x2 v = {pack_bf16(o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv),
+                     pack_bf16(o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv)};
+          *(u32x2 *)(op + db * 32 + gg * 8 + half * 4) = v;
         }
     }
   }

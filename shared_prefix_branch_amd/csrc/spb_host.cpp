@@ -339,7 +339,7 @@ void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, co
         for (int b = lo; b <= hi; ++b) {
           const SpbBranch &B = P.branches[b];
           int last = std::min(B.start + B.E, r0 + t.nrows) - 1 - B.start;
-          bchunks += last / kChunk + 1;
+          bchunks += last / kBranchChunk + 1;
         }
       }
       t.cost = t.ncc + bchunks;
@@ -725,6 +725,9 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
     return fail(SPB_ERR_ARG, "fp8 scales must be finite and > 0");
   if ((uintptr_t)d_meta % 256) return fail(SPB_ERR_ARG, "d_meta must be 256-byte aligned");
   if (h.n_tiles == 0) return ok();
+  for (const SpbTile &t : P.tiles)
+    if (t.cost > kMaxTileChunks)
+      return fail(SPB_ERR_LIMIT, "an attention tile needs %d key chunks, more than %d", t.cost, kMaxTileChunks);
   AttnLaunch L{};
   L.q = a->q; L.k = a->k; L.v = a->v; L.o = a->o;
   L.in_dtype = a->in_dtype; L.out_dtype = a->out_dtype;
@@ -762,8 +765,8 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   if (a->h_dtype != SPB_BF16 && a->h_dtype != SPB_F32) return fail(SPB_ERR_DTYPE, "h_dtype %d unsupported", a->h_dtype);
   if (a->hidden_dim < 64 || a->hidden_dim % 64) return fail(SPB_ERR_DTYPE, "hidden_dim %d not a positive multiple of 64", a->hidden_dim);
   if (a->vocab < 1) return fail(SPB_ERR_ARG, "vocab %d < 1", a->vocab);
-  if ((int64_t)a->vocab * a->hidden_dim > (int64_t)UINT32_MAX)
-    return fail(SPB_ERR_DTYPE, "vocab x hidden_dim = %lld elements exceeds 2^32 - 1", (long long)a->vocab * a->hidden_dim);
+  if ((int64_t)a->vocab * a->hidden_dim * 2 > (int64_t)UINT32_MAX)
+    return fail(SPB_ERR_DTYPE, "the lm head (%lld bytes) exceeds 4 GiB", (long long)a->vocab * a->hidden_dim * 2);
   for (int t : P.tgt_tok)
     if (t >= a->vocab) return fail(SPB_ERR_ARG, "option token %d >= vocab %d", t, a->vocab);
   if (a->rows < h.n_tokens) return fail(SPB_ERR_SIZE, "hidden holds %lld rows, the pass has %d", (long long)a->rows, h.n_tokens);

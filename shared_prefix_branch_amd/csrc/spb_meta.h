@@ -18,8 +18,9 @@ namespace spb {
 constexpr int32_t kMetaMagic = 0x53504231;  // "SPB1"
 constexpr int32_t kMetaVersion = 1;
 constexpr int kTileRows = 128;  // rows per attention tile (one to two work groups)
-constexpr int kChunk = 64;      // keys per chunk; content chunks start at the
-                                // content start, branch chunks at the branch start
+constexpr int kChunk = 64;      // keys per content chunk, chunks start at the content start
+constexpr int kBranchChunk = 32;  // keys per branch chunk, chunks start at the branch start
+constexpr int kMaxTileChunks = 320;  // key chunks one attention tile may visit
 constexpr int kMaxDepth = 4;    // option-trie depth (options of at most 5 tokens)
 constexpr int kVocabTile = 256; // vocabulary rows per lm-head slice (LSE partial)
 
@@ -46,7 +47,8 @@ struct SpbTile {
   int32_t seg;    // content start (pass row) shared by the tile's rows
   int32_t ncc;    // content chunks to visit: ceil(max cvis / kChunk)
   int32_t b_lo, b_hi;  // branch-table range intersecting the tile
-  int32_t cost, pad;
+  int32_t cost;        // key chunks the tile visits (content + branch)
+  int32_t pad;
 };
 
 struct SpbBranch {

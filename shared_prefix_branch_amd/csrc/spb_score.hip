@@ -100,64 +100,84 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 
 template <int MW>
 struct HeadTile {
-  static constexpr int TM = 64 * MW;   // scored rows per work group
-  static constexpr int HU = TM / 64;   // hidden-tile 16-byte units per thread per stage
-  static constexpr int WU = 4;         // W-tile 16-byte units per thread per stage
+  static constexpr int TM = 64 * MW;             // scored rows per work group
+  static constexpr int WBYTES = kVocabTile * 64; // W stage: 256 rows x 32 bf16
+  static constexpr int HBYTES = TM * 64;         // h stage: TM rows x 32 bf16
+  static constexpr int SLOT = WBYTES + HBYTES;
+  static constexpr int NI = 4 + MW;              // DMA instructions per wave per stage
+  static constexpr int D = MW == 1 ? 6 : MW == 2 ? 5 : MW == 3 ? 4 : 3;  // stages in flight
+  static constexpr int R = D + 1;                // LDS ring slots (~140 KB)
 };
 
-// Loads stage s (hidden elements s*32 .. +32) of the W and h tiles into registers.
-// Thread t moves chunk t%4 of rows t/4 + 64 i.
-template <int MW>
-__device__ __attribute__((always_inline)) inline void head_load(u32x4 (&wr)[4], u32x4 (&hr)[HeadTile<MW>::HU],
-                                                                const uint16_t *wbase, const uint32_t (&woff)[4],
-                                                                const uint16_t *hbase, uint32_t hstride, int s) {
-  const int k0 = s * kKT;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wr[i] = *(const u32x4 *)(wbase + woff[i] + k0);
-#pragma unroll
-  for (int i = 0; i < HeadTile<MW>::HU; ++i) hr[i] = *(const u32x4 *)(hbase + (size_t)i * hstride + k0);
+// Asynchronous copy of 16 bytes per lane from global memory into LDS: lane i
+// writes lds + 16 i.  Issued from inline assembly so that the compiler does
+// not wait on it before unrelated LDS reads; the kernel orders it with
+// explicit vmcnt waits and barriers.  m0 (the LDS address operand) is saved
+// and restored around the copy.
+__device__ inline void dma16(const void *base, uint32_t voff, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory");
 }
 
-template <int MW>
-__device__ __attribute__((always_inline)) inline void head_store(const u32x4 (&wr)[4], const u32x4 (&hr)[HeadTile<MW>::HU],
-                                                                 u32x4 *Wb, u32x4 *Hb, int sr, int sc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) Wb[swz(i * 64 + sr, sc)] = wr[i];
-#pragma unroll
-  for (int i = 0; i < HeadTile<MW>::HU; ++i) Hb[swz(i * 64 + sr, sc)] = hr[i];
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Fragments of one 16-element K step: A = 4 vocabulary blocks, B = MW
+// scored-row blocks.
 template <int MW>
-__device__ __attribute__((always_inline)) inline void head_compute(f32x16 (&acc)[4][MW], const u32x4 *Wb, const u32x4 *Hb,
-                                                                   int wv, int wm, int qi, int half) {
+struct Frags {
+  bf16x8_t a[4];
+  bf16x8_t b[MW];
+};
+
+template <int MW>
+__device__ __attribute__((always_inline)) inline void head_frags(Frags<MW> &f, const u32x4 *Wb, const u32x4 *Hb,
+                                                                 int ks, int wv, int wm, int qi, int half) {
 #pragma unroll
-  for (int ks = 0; ks < kKT / 16; ++ks) {
-    bf16x8_t a[4];
-#pragma unroll
-    for (int vb = 0; vb < 4; ++vb) {
-      u32x4 u = Wb[swz(wv * 128 + vb * 32 + qi, ks * 2 + half)];
-      a[vb] = *(bf16x8_t *)&u;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MW; ++mb) {
-      u32x4 u = Hb[swz(wm * 32 * MW + mb * 32 + qi, ks * 2 + half)];
-      bf16x8_t bb = *(bf16x8_t *)&u;
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb)
-        acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vb], bb, acc[vb][mb], 0, 0, 0);
-    }
+  for (int vb = 0; vb < 4; ++vb) {
+    u32x4 u = Wb[swz(wv * 128 + vb * 32 + qi, ks * 2 + half)];
+    f.a[vb] = *(bf16x8_t *)&u;
   }
+#pragma unroll
+  for (int mb = 0; mb < MW; ++mb) {
+    u32x4 u = Hb[swz(wm * 32 * MW + mb * 32 + qi, ks * 2 + half)];
+    f.b[mb] = *(bf16x8_t *)&u;
+  }
+}
+
+template <int MW>
+__device__ __attribute__((always_inline)) inline void head_mfma(f32x16 (&acc)[4][MW], const Frags<MW> &f) {
+#pragma unroll
+  for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+      acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0);
 }
 
 // MW: 32-row m blocks per wave; a work group covers 256 vocabulary rows x
 // 64*MW scored rows.  Wave (wv, wm) owns vocabulary rows wv*128 .. +128 and
 // scored rows wm*32*MW .. +32*MW.
+//
+// Pipeline over stages of 32 hidden elements (two 16-element K steps): the W
+// and h tiles of stage j are copied straight into LDS ring slot j % R, D
+// stages ahead of use; in trip s the first K step of stage s+1 is read while
+// the second of stage s is multiplied, so every LDS read is covered by a block
+// of 4*MW MFMAs and every global load by D trips.
 template <int MW>
 __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   using T = HeadTile<MW>;
   constexpr int TM = T::TM;
-  __shared__ u32x4 Ws[2][kVocabTile * 4];
-  __shared__ u32x4 Hs[2][TM * 4];
+  __shared__ __attribute__((aligned(16))) char ring[T::R][T::SLOT];
   __shared__ float red[2][TM][2];
 
   // XCD-aware order: work groups are dealt round-robin to the 8 XCDs, so the
@@ -169,47 +189,76 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   const int mchunk = slot % p.n_mchunks;
   if (slice >= p.n_slices) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform within the wave
   const int qi = lane & 31, half = lane >> 5;
   const int wv = wave & 1, wm = wave >> 1;
   const int v0 = slice * kVocabTile;
   const int m0 = mchunk * TM;
 
-  const int sc = tid & 3, sr = tid >> 2;
-  uint32_t woff[4];
+  // DMA layout: one instruction moves 16 rows x 64 bytes; lane t fills LDS
+  // slot t of the instruction = row t/4, position t%4 of the swizzled row,
+  // so it fetches chunk (t%4) ^ ((row/4)%4) = (t%4) ^ (t/16).
+  const int dr = lane >> 2;
+  const uint32_t dc = (uint32_t)((lane & 3) ^ (lane >> 4));
+  uint32_t woff[4], hoff[MW];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int v = v0 + i * 64 + sr;
-    woff[i] = (uint32_t)(v < p.V ? v : p.V - 1) * (uint32_t)p.H + sc * 8;
+    const int v = v0 + wave * 64 + i * 16 + dr;
+    woff[i] = ((uint32_t)(v < p.V ? v : p.V - 1) * (uint32_t)p.H + dc * 8) * 2;
   }
-  const uint16_t *hbase = p.hg + (size_t)(m0 + sr) * p.H + sc * 8;
-  const uint32_t hstride = 64u * (uint32_t)p.H;
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    const int m = m0 + (wave * MW + i) * 16 + dr;
+    hoff[i] = ((uint32_t)m * (uint32_t)p.H + dc * 8) * 2;
+  }
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&ring[0][0]);
+  auto issue = [&](int stage, int sl) {
+    const uint32_t kb = (uint32_t)stage * kKT * 2;
+    const uint32_t s0 = ring0 + (uint32_t)sl * T::SLOT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma16(p.W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 16) * 64));
+#pragma unroll
+    for (int i = 0; i < MW; ++i)
+      dma16(p.hg, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + T::WBYTES + (wave * MW + i) * 16 * 64));
+  };
 
-  u32x4 wrA[4], hrA[T::HU], wrB[4], hrB[T::HU];
   f32x16 acc[4][MW];
 #pragma unroll
   for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
     for (int mb = 0; mb < MW; ++mb) acc[vb][mb] = f32x16{0.f};
 
-  // stage j's registers are set j%2; LDS buffer j%2 holds stage j while it is read
   const int S = p.H / kKT;
-  head_load<MW>(wrA, hrA, p.W, woff, hbase, hstride, 0);
-  if (S > 1) head_load<MW>(wrB, hrB, p.W, woff, hbase, hstride, 1);
-  head_store<MW>(wrA, hrA, Ws[0], Hs[0], sr, sc);
+  const int last = S - 1;
+  // stages past the last reload it into a slot nothing reads again, so the
+  // count of copies in flight is the same on every trip
+#pragma unroll
+  for (int j = 0; j < T::D; ++j) issue(min(j, last), j);
+  wait_vmcnt<(T::D - 2) * T::NI>();  // stages 0 and 1 landed (this wave's copies)
   lds_barrier();
-  int s = 0;
-  for (; s + 1 < S; s += 2) {  // two stages per trip; no early exit, so acc stays in one register set
-    if (s + 2 < S) head_load<MW>(wrA, hrA, p.W, woff, hbase, hstride, s + 2);
-    head_compute<MW>(acc, Ws[0], Hs[0], wv, wm, qi, half);
-    head_store<MW>(wrB, hrB, Ws[1], Hs[1], sr, sc);
+  Frags<MW> f0, f1;
+  head_frags<MW>(f0, (const u32x4 *)ring[0], (const u32x4 *)(ring[0] + T::WBYTES), 0, wv, wm, qi, half);
+
+  int sl = 0;  // ring slot of stage s
+  for (int s = 0; s < S; ++s) {
+    const int sn = sl + 1 == T::R ? 0 : sl + 1;
+    const int sd = sl == 0 ? T::R - 1 : sl - 1;  // slot of stage s + D (= s - 1 mod R)
+    issue(min(s + T::D, last), sd);
+    head_frags<MW>(f1, (const u32x4 *)ring[sl], (const u32x4 *)(ring[sl] + T::WBYTES), 1, wv, wm, qi, half);
+    __builtin_amdgcn_sched_barrier(0);
+    head_mfma<MW>(acc, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    head_frags<MW>(f0, (const u32x4 *)ring[sn], (const u32x4 *)(ring[sn] + T::WBYTES), 0, wv, wm, qi, half);
+    __builtin_amdgcn_sched_barrier(0);
+    head_mfma<MW>(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(T::D - 2) * T::NI>();  // stage s + 2 landed
     lds_barrier();
-    if (s + 3 < S) head_load<MW>(wrB, hrB, p.W, woff, hbase, hstride, s + 3);
-    head_compute<MW>(acc, Ws[1], Hs[1], wv, wm, qi, half);
-    if (s + 2 < S) head_store<MW>(wrA, hrA, Ws[0], Hs[0], sr, sc);
-    lds_barrier();
+    sl = sn;
   }
-  if (s < S) head_compute<MW>(acc, Ws[0], Hs[0], wv, wm, qi, half);  // odd stage count: last stage in buffer 0
+  wait_vmcnt<0>();  // no copy may land after the work group's LDS is released
 
   // epilogue.  Lane holds column m = m0 + wm*32*MW + mb*32 + qi; register r
   // of block vb holds vocabulary row v0 + wv*128 + vb*32 + (r/4)*8 + half*4 + r%4.
