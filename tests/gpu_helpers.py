@@ -29,7 +29,7 @@ class Case:
 
     def __init__(self, wl: synth.Workload, budget: int, inputs: Optional[Sequence[int]] = None,
                  floors: bool = True, peaked: bool = False, device: str = "cuda", gen_device: str = "cuda",
-                 chained: bool = False):
+                 chained: bool = False, cache: Optional[dict] = None):
         import torch
         self.torch = torch
         self.wl = wl
@@ -47,7 +47,7 @@ class Case:
         self.ids = ids
         self.dims = wl.dims
         self.scales = synth.fp8_scales(wl) if wl.dims.dtype == "fp8" else (1.0, 1.0, 1.0)
-        self._blocks: Dict[tuple, tuple] = {}
+        self._blocks: Dict[tuple, tuple] = {} if cache is None else cache  # activations by identity
 
     # -- inputs --------------------------------------------------------------
     def block(self, ident):
