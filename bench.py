@@ -10,15 +10,24 @@ step's batch while the GPU runs the current one.  Inputs (Q/K/V, hidden
 states, lm head) are resident in HBM before timing starts.
 
 Prints one JSON line: whole-job packed tokens/s as `value`, plus scored
-questions/s, per-kernel timings from HIP events on the launch stream, the
-roofline of the dominant kernel (the lm head) and the oracle timed on the
-host cores as `cpu_baseline`.
+questions/s, per-kernel timings from HIP events recorded on the launch stream
+inside the timed steps, the roofline of the dominant kernel (the lm-head GEMM)
+and the oracle timed on the host cores as `cpu_baseline`.  The roofline's
+`traffic` is the kernel's HBM bytes per launch from the committed counter
+summary in profiles/ (null when the kernel source has changed since).
+
+    python bench.py --copy-calibration
+
+runs only a plain 1 GiB device-to-device copy, three times, for scaling the
+FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,6 +35,9 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HERE = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCES = ("shared_prefix_branch_amd/csrc/spb_score.hip", "shared_prefix_branch_amd/csrc/spb_launch.h")
+TRAFFIC_SUMMARY = "profiles/head_lse_kernel_news_traffic.md"
 
 
 def parse():
@@ -35,8 +47,47 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="news")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-inputs", type=int, default=2)
+    ap.add_argument("--cpu-sample-inputs", type=int, default=0,
+                    help="contents in the oracle's sample (0: all of the workload's)")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per lm-head GEMM launch from the committed counter summary,
+    or None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(HERE, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    m_src = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_val):
+        return None, "counter summary unreadable"
+    if m_src.group(1) != gemm_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(m_val.group(1)), TRAFFIC_SUMMARY
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 3}}),
+          flush=True)
 
 
 def main():
@@ -45,6 +96,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the path has no multi-GPU leg; "
               "passes are independent and would shard as data parallelism across processes.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import synth
     import shared_prefix_branch_amd as spb
@@ -81,46 +135,43 @@ def main():
     questions = int(info["n_content_branches"])
     tokens = int(info["n_tokens"])
 
-    def step(next_plan_holder):
+    def step(next_plan_holder, marks=None):
         # enqueue every pass, pack the next batch on the host meanwhile,
         # then bring the scores back and join the floors
         p = next_plan_holder[0]
         job.plan = p
-        job.run(W, stream=stream)
+        job.run(W, stream=stream, marks=marks)
         next_plan_holder[0] = spb.pack_pass(prob, token_budget=budget)
         res = job.finalize()   # synchronises on the copies back
         return res
+
+    # HIP events on the launch stream, created up front (a torch event exists
+    # once recorded), recorded inside the timed steps
+    marks = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_pass)]
+             for _ in range(args.steps)]
+    for ms in marks:
+        for mk in ms:
+            for ev in mk:
+                ev.record(stream)
+    torch.cuda.synchronize()
 
     holder = [spb.pack_pass(prob, token_budget=budget)]
     for _ in range(args.warmup):
         step(holder)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        res = step(holder)
+    for i in range(args.steps):
+        res = step(holder, marks[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    # ---- per-kernel timing with HIP events on the launch stream
-    reps = max(3, min(10, args.steps))
     att_ms = np.zeros(n_pass)
     head_ms = np.zeros(n_pass)
-    for k in range(n_pass):
-        buf = job.passes[k]
-        plan.upload(k, buf.meta, stream)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        for r in range(reps + 1):
-            ev[0].record(stream)
-            spb.branch_attention(plan, k, buf.meta, buf.q, buf.k, buf.v, buf.o, scales=scales, stream=stream)
-            ev[1].record(stream)
-            spb.score_options(plan, k, buf.meta, buf.hidden, W, buf.workspace, buf.lp, buf.p, buf.residual,
-                              stream=stream)
-            ev[2].record(stream)
-            torch.cuda.synchronize()
-            if r > 0:
-                att_ms[k] += ev[0].elapsed_time(ev[1]) / reps
-                head_ms[k] += ev[1].elapsed_time(ev[2]) / reps
+    for ms in marks:
+        for k, mk in enumerate(ms):
+            att_ms[k] += mk[0].elapsed_time(mk[1]) / args.steps
+            head_ms[k] += mk[2].elapsed_time(mk[3]) / args.steps
     pair_flops = 4.0 * d.head_dim * d.hq
     att_flops = np.array([plan.info(k)["unmasked_pairs"] * pair_flops for k in range(n_pass)])
     M = np.array([plan.info(k)["n_scored_rows"] for k in range(n_pass)], dtype=np.float64)
@@ -131,15 +182,19 @@ def main():
     head_tflops = head_flops.sum() / (head_ms.sum() * 1e-3) / 1e12
     head_gbs = head_bytes.sum() / (head_ms.sum() * 1e-3) / 1e9
     head_bound = "mfma" if M.mean() > PEAK_BF16_TFLOPS / PEAK_HBM_GBS else "hbm"
+    traffic, traffic_src = measured_traffic() if args.workload == "news" else (None, "counters taken on news only")
     if head_bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(head_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(head_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(head_tflops / PEAK_BF16_TFLOPS, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(head_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(head_gbs / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["kernel"] = "head_lse_kernel (spb_score_options)"
+                "unit": "GB/s", "frac": round(head_gbs / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None if traffic is None else round(traffic)
+    roof["traffic_source"] = traffic_src
+    roof["kernel"] = "head_lse_kernel (lm-head GEMM with fused log-sum-exp, in spb_score_options)"
     roof["per_launch"] = {"ms": [round(x, 4) for x in head_ms], "scored_rows": M.astype(int).tolist(),
-                          "flops_per_scored_row": 2 * d.hidden * d.vocab, "w_bytes": int(w_bytes)}
+                          "flops_per_scored_row": 2 * d.hidden * d.vocab,
+                          "algorithmic_bytes": [int(x) for x in head_bytes]}
 
     line = {
         "metric": "packed tokens/s + scored questions/s per MI355X; attention MFMA util",
@@ -163,11 +218,12 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, W, scales, args.cpu_sample_inputs, provider_host=None)
+        n_cpu = args.cpu_sample_inputs if args.cpu_sample_inputs > 0 else prob.n_inputs
+        line["cpu_baseline"] = cpu_baseline(wl, W, scales, min(n_cpu, prob.n_inputs))
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, W, scales, n_inputs, provider_host=None):
+def cpu_baseline(wl, W, scales, n_inputs):
     """The float64 oracle, as it stands, on a bounded sample: the first
     ``n_inputs`` contents with all their questions, plus the floors."""
     import torch

@@ -211,6 +211,10 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
   float *lp, *p, *residual;
+  /* Optional timing hooks: hipEvent_t handles (created by the caller) recorded
+   * on the stream right before and right after the lm-head GEMM kernel, so a
+   * caller can time that kernel alone.  NULL: not recorded. */
+  void *gemm_event_begin, *gemm_event_end;
 } spb_score_args;
 
 /* Workspace bytes spb_score_options needs for this pass, vocabulary and hidden size. */

@@ -77,7 +77,8 @@ class _ScoreArgs(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_void_p), ("h_dtype", ctypes.c_int32), ("hidden_dim", ctypes.c_int32),
                 ("rows", ctypes.c_int64), ("lm_head", ctypes.c_void_p), ("vocab", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("lp", _f32p), ("p", _f32p), ("residual", _f32p)]
+                ("lp", _f32p), ("p", _f32p), ("residual", _f32p),
+                ("gemm_event_begin", ctypes.c_void_p), ("gemm_event_end", ctypes.c_void_p)]
 
 
 _lib = None
@@ -258,9 +259,12 @@ def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int) -
     return int(n.value)
 
 
-def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual, stream=None):
+def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual, stream=None,
+                  gemm_events=None):
     """hidden [rows, H] (bf16/f32), lm_head [V, H] bf16, workspace uint8 device buffer,
-    lp/p [n_options] and residual [n_branches] float32 device tensors."""
+    lp/p [n_options] and residual [n_branches] float32 device tensors.
+    gemm_events: optional pair of created ``torch.cuda.Event`` recorded on the
+    stream around the lm-head GEMM kernel."""
     import torch
     if lm_head.dtype != torch.bfloat16:
         raise SpbError(-3, "lm_head must be bfloat16")
@@ -281,6 +285,12 @@ def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp
     S.lp = ctypes.cast(ctypes.c_void_p(lp.data_ptr()), _f32p)
     S.p = ctypes.cast(ctypes.c_void_p(p.data_ptr()), _f32p)
     S.residual = ctypes.cast(ctypes.c_void_p(residual.data_ptr()), _f32p)
+    if gemm_events is not None:
+        for ev in gemm_events:
+            if not ev.cuda_event:
+                raise SpbError(-1, "timing events must be created (recorded once) before use")
+        S.gemm_event_begin = gemm_events[0].cuda_event
+        S.gemm_event_end = gemm_events[1].cuda_event
     _check(lib().spb_score_options(plan.handle, pass_, ctypes.c_void_p(d_meta.data_ptr()), ctypes.byref(S),
                                    ctypes.c_void_p(_stream_handle(stream))))
 

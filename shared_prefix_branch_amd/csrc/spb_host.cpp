@@ -796,6 +796,7 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   L.lse = (float *)(ws + off[2]);
   L.hg = ws + off[3];
   L.lp = a->lp; L.p = a->p; L.residual = a->residual;
+  L.ev_begin = a->gemm_event_begin; L.ev_end = a->gemm_event_end;
   int e = launch_score(L, stream);
   if (e) return fail(SPB_ERR_HIP, "score launch: %s", hip_error_string(e));
   return ok();

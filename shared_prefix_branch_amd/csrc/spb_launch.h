@@ -31,6 +31,7 @@ struct ScoreLaunch {
   float *lse;    // workspace: [n_scored]
   void *hg;      // workspace: gathered hidden states, bf16 [m_pad][hidden_dim]
   float *lp, *p, *residual;
+  void *ev_begin, *ev_end;  // optional hipEvent_t around the GEMM kernel
 };
 
 inline int n_vocab_slices(int vocab) { return (vocab + 255) / 256; }

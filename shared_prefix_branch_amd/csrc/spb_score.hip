@@ -41,7 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kKT = 32;        // hidden elements per K stage (64-byte LDS rows)
+constexpr int kKT = 64;        // hidden elements per K stage (128-byte LDS rows: one cache line)
 constexpr int kThreads = 256;  // 2 x 2 waves: vocabulary halves x scored-row halves
 
 __device__ inline uint32_t f2bf(float f) {
@@ -50,10 +50,11 @@ __device__ inline uint32_t f2bf(float f) {
   return u >> 16;
 }
 
-// LDS position, in 16-byte units, of chunk c (0..3) of row r of a tile with
-// 64-byte rows.  The XOR spreads the 16 rows one quarter-wave reads across
-// all 64 banks.
-__device__ inline int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+// LDS position, in 16-byte units, of chunk c (0..7) of row r of a tile with
+// 128-byte rows.  A fragment read has 16 lanes in flight on 16 consecutive
+// rows at one chunk; the XOR by (r/2)%8 puts them on 16 distinct 16-byte bank
+// groups of the 64 banks.
+__device__ inline int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 struct GatherParams {
   const void *hidden;
@@ -100,13 +101,14 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 
 template <int MW>
 struct HeadTile {
-  static constexpr int TM = 64 * MW;             // scored rows per work group
-  static constexpr int WBYTES = kVocabTile * 64; // W stage: 256 rows x 32 bf16
-  static constexpr int HBYTES = TM * 64;         // h stage: TM rows x 32 bf16
-  static constexpr int SLOT = WBYTES + HBYTES;
-  static constexpr int NI = 4 + MW;              // DMA instructions per wave per stage
-  static constexpr int D = MW == 1 ? 6 : MW == 2 ? 5 : MW == 3 ? 4 : 3;  // stages in flight
-  static constexpr int R = D + 1;                // LDS ring slots (~140 KB)
+  static constexpr int TM = 64 * MW;                // scored rows per work group
+  static constexpr int WBYTES = kVocabTile * 128;   // W stage: 256 rows x 64 bf16
+  static constexpr int HBYTES = TM * 128;           // h stage: TM rows x 64 bf16
+  static constexpr int RW = 3;                      // W ring: two stages in flight
+  static constexpr int RH = 2;                      // h ring: one stage in flight (L2-resident)
+  static constexpr int LDS = RW * WBYTES + RH * HBYTES;  // 112..160 KB
+  static constexpr int NW = 8;                      // W copies per wave per stage
+  static constexpr int NH = 2 * MW;                 // h copies per wave per stage
 };
 
 // Asynchronous copy of 16 bytes per lane from global memory into LDS: lane i
@@ -140,6 +142,8 @@ struct Frags {
   bf16x8_t b[MW];
 };
 
+// K step ks (0..3) of a 64-element stage: lane (qi, half) takes elements
+// 16 ks + 8 half .. +8 of its row, i.e. chunk 2 ks + half.
 template <int MW>
 __device__ __attribute__((always_inline)) inline void head_frags(Frags<MW> &f, const u32x4 *Wb, const u32x4 *Hb,
                                                                  int ks, int wv, int wm, int qi, int half) {
@@ -168,17 +172,19 @@ __device__ __attribute__((always_inline)) inline void head_mfma(f32x16 (&acc)[4]
 // 64*MW scored rows.  Wave (wv, wm) owns vocabulary rows wv*128 .. +128 and
 // scored rows wm*32*MW .. +32*MW.
 //
-// Pipeline over stages of 32 hidden elements (two 16-element K steps): the W
-// and h tiles of stage j are copied straight into LDS ring slot j % R, D
-// stages ahead of use; in trip s the first K step of stage s+1 is read while
-// the second of stage s is multiplied, so every LDS read is covered by a block
-// of 4*MW MFMAs and every global load by D trips.
+// Pipeline over stages of 64 hidden elements (four 16-element K steps), so
+// every row of a stage is one whole 128-byte line and each global request
+// carries a full line.  Stage j's W tile is copied straight into LDS slot
+// j % 3 two stages ahead of use; its h tile (small and shared by every work
+// group, so L2-resident) into slot j % 2 one stage ahead.  Within a stage the
+// fragments of K step t+1 are read while step t is multiplied.
 template <int MW>
 __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   using T = HeadTile<MW>;
   constexpr int TM = T::TM;
-  __shared__ __attribute__((aligned(16))) char ring[T::R][T::SLOT];
-  __shared__ float red[2][TM][2];
+  __shared__ __attribute__((aligned(16))) char lds[T::LDS];
+  char *const wring = lds;
+  char *const hring = lds + T::RW * T::WBYTES;
 
   // XCD-aware order: work groups are dealt round-robin to the 8 XCDs, so the
   // M chunks of one vocabulary slice get consecutive slots of one XCD and
@@ -196,32 +202,39 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   const int v0 = slice * kVocabTile;
   const int m0 = mchunk * TM;
 
-  // DMA layout: one instruction moves 16 rows x 64 bytes; lane t fills LDS
-  // slot t of the instruction = row t/4, position t%4 of the swizzled row,
-  // so it fetches chunk (t%4) ^ ((row/4)%4) = (t%4) ^ (t/16).
-  const int dr = lane >> 2;
-  const uint32_t dc = (uint32_t)((lane & 3) ^ (lane >> 4));
-  uint32_t woff[4], hoff[MW];
+  // DMA layout: one instruction moves 8 rows x 128 bytes; lane t fills LDS
+  // position t%8 of row r = r8 + t/8 (r8 a multiple of 8), which swz() maps
+  // to chunk (t%8) ^ ((r/2)%8) of the row.
+  const int dr = lane >> 3;
+  uint32_t woff[T::NW], hoff[T::NH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = v0 + wave * 64 + i * 16 + dr;
-    woff[i] = ((uint32_t)(v < p.V ? v : p.V - 1) * (uint32_t)p.H + dc * 8) * 2;
+  for (int i = 0; i < T::NW; ++i) {
+    const int r = wave * 64 + i * 8 + dr;  // tile row
+    const int v = v0 + r;
+    const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    woff[i] = ((uint32_t)(v < p.V ? v : p.V - 1) * (uint32_t)p.H + c * 8) * 2;
   }
 #pragma unroll
-  for (int i = 0; i < MW; ++i) {
-    const int m = m0 + (wave * MW + i) * 16 + dr;
-    hoff[i] = ((uint32_t)m * (uint32_t)p.H + dc * 8) * 2;
+  for (int i = 0; i < T::NH; ++i) {
+    const int r = (wave * T::NH + i) * 8 + dr;
+    const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    hoff[i] = ((uint32_t)(m0 + r) * (uint32_t)p.H + c * 8) * 2;
   }
-  const uint32_t ring0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&ring[0][0]);
-  auto issue = [&](int stage, int sl) {
+  const uint32_t lds0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&lds[0]);
+  auto issue_w = [&](int stage, int sl) {
     const uint32_t kb = (uint32_t)stage * kKT * 2;
-    const uint32_t s0 = ring0 + (uint32_t)sl * T::SLOT;
+    const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma16(p.W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 16) * 64));
+    for (int i = 0; i < T::NW; ++i)
+      dma16(p.W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 8) * 128));
+  };
+  auto issue_h = [&](int stage, int sl) {
+    const uint32_t kb = (uint32_t)stage * kKT * 2;
+    const uint32_t s0 = lds0 + T::RW * T::WBYTES + (uint32_t)sl * T::HBYTES;
 #pragma unroll
-    for (int i = 0; i < MW; ++i)
-      dma16(p.hg, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + T::WBYTES + (wave * MW + i) * 16 * 64));
+    for (int i = 0; i < T::NH; ++i)
+      dma16(p.hg, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
   };
 
   f32x16 acc[4][MW];
@@ -232,33 +245,47 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
 
   const int S = p.H / kKT;
   const int last = S - 1;
-  // stages past the last reload it into a slot nothing reads again, so the
-  // count of copies in flight is the same on every trip
-#pragma unroll
-  for (int j = 0; j < T::D; ++j) issue(min(j, last), j);
-  wait_vmcnt<(T::D - 2) * T::NI>();  // stages 0 and 1 landed (this wave's copies)
+  // Copies past the last stage reload it into a slot nothing reads again, so
+  // the count of copies in flight is the same on every trip.  Issue order
+  // per trip s: h(s+1), then W(s+2); at the trip's end only W(s+2) may still
+  // be in flight.
+  issue_h(0, 0);
+  issue_w(0, 0);
+  issue_w(min(1, last), 1);
+  wait_vmcnt<T::NW>();  // h(0), W(0) landed (this wave's copies)
   lds_barrier();
-  Frags<MW> f0, f1;
-  head_frags<MW>(f0, (const u32x4 *)ring[0], (const u32x4 *)(ring[0] + T::WBYTES), 0, wv, wm, qi, half);
 
-  int sl = 0;  // ring slot of stage s
+  int sw = 0, sh = 0;  // ring slots of stage s
   for (int s = 0; s < S; ++s) {
-    const int sn = sl + 1 == T::R ? 0 : sl + 1;
-    const int sd = sl == 0 ? T::R - 1 : sl - 1;  // slot of stage s + D (= s - 1 mod R)
-    issue(min(s + T::D, last), sd);
-    head_frags<MW>(f1, (const u32x4 *)ring[sl], (const u32x4 *)(ring[sl] + T::WBYTES), 1, wv, wm, qi, half);
+    const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
+    const u32x4 *Hb = (const u32x4 *)(hring + sh * T::HBYTES);
+    Frags<MW> f0, f1;
+    head_frags<MW>(f0, Wb, Hb, 0, wv, wm, qi, half);
+    const int sw2 = sw == 0 ? 2 : sw - 1;  // slot of stage s + 2 (= s - 1 mod 3)
+    issue_h(min(s + 1, last), sh ^ 1);
+    issue_w(min(s + 2, last), sw2);
+    head_frags<MW>(f1, Wb, Hb, 1, wv, wm, qi, half);
     __builtin_amdgcn_sched_barrier(0);
     head_mfma<MW>(acc, f0);
     __builtin_amdgcn_sched_barrier(0);
-    head_frags<MW>(f0, (const u32x4 *)ring[sn], (const u32x4 *)(ring[sn] + T::WBYTES), 0, wv, wm, qi, half);
+    head_frags<MW>(f0, Wb, Hb, 2, wv, wm, qi, half);
     __builtin_amdgcn_sched_barrier(0);
     head_mfma<MW>(acc, f1);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<(T::D - 2) * T::NI>();  // stage s + 2 landed
+    head_frags<MW>(f1, Wb, Hb, 3, wv, wm, qi, half);
+    __builtin_amdgcn_sched_barrier(0);
+    head_mfma<MW>(acc, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    head_mfma<MW>(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<T::NW>();  // h(s+1) and W(s+1) landed
     lds_barrier();
-    sl = sn;
+    sw = sw == 2 ? 0 : sw + 1;
+    sh ^= 1;
   }
-  wait_vmcnt<0>();  // no copy may land after the work group's LDS is released
+  wait_vmcnt<0>();  // no copy may land after the ring is reused or released
+  lds_barrier();
+  float (*red)[TM][2] = (float (*)[TM][2])lds;  // [2][TM][2], reusing the ring
 
   // epilogue.  Lane holds column m = m0 + wm*32*MW + mb*32 + qi; register r
   // of block vb holds vocabulary row v0 + wv*128 + vb*32 + (r/4)*8 + half*4 + r%4.
@@ -420,6 +447,10 @@ int launch_score(const ScoreLaunch &a, void *stream) {
   long long groups = (long long)((p.n_slices + 7) / 8) * 8 * p.n_mchunks;
   if (groups > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
   dim3 grid((unsigned)groups), block(kThreads);
+  if (a.ev_begin) {
+    e = (int)hipEventRecord((hipEvent_t)a.ev_begin, s);
+    if (e) return e;
+  }
   switch (mw) {
     case 1: hipLaunchKernelGGL(head_lse_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(head_lse_kernel<2>, grid, block, 0, s, p); break;
@@ -428,6 +459,10 @@ int launch_score(const ScoreLaunch &a, void *stream) {
   }
   e = (int)hipGetLastError();
   if (e) return e;
+  if (a.ev_end) {
+    e = (int)hipEventRecord((hipEvent_t)a.ev_end, s);
+    if (e) return e;
+  }
   FinParams f;
   f.n_slices = p.n_slices;
   f.branches = (const SpbBranch *)a.branches;

@@ -100,18 +100,25 @@ class Job:
             self.fill(k, buf, provider, cache)
             self.passes.append(buf)
 
-    def run_pass(self, k: int, lm_head, stream=None, attention=True, scoring=True):
+    def run_pass(self, k: int, lm_head, stream=None, attention=True, scoring=True, marks=None):
+        """Enqueues pass k.  ``marks``, if given, holds four created events:
+        recorded on ``stream`` around the attention kernel (0, 1) and, by the
+        library, around the lm-head GEMM kernel (2, 3)."""
         buf = self.passes[k]
         self.plan.upload(k, buf.meta, stream)
+        if marks is not None:
+            marks[0].record(stream)
         if attention:
             branch_attention(self.plan, k, buf.meta, buf.q, buf.k, buf.v, buf.o, scales=self.scales, stream=stream)
+        if marks is not None:
+            marks[1].record(stream)
         if scoring:
             score_options(self.plan, k, buf.meta, buf.hidden, lm_head, buf.workspace, buf.lp, buf.p, buf.residual,
-                          stream=stream)
+                          stream=stream, gemm_events=None if marks is None else (marks[2], marks[3]))
 
-    def run(self, lm_head, stream=None, attention=True, scoring=True):
+    def run(self, lm_head, stream=None, attention=True, scoring=True, marks=None):
         for k in range(self.plan.n_passes):
-            self.run_pass(k, lm_head, stream, attention, scoring)
+            self.run_pass(k, lm_head, stream, attention, scoring, None if marks is None else marks[k])
 
     def pass_outputs(self, k: int):
         """Host copies of pass k's lp, p, residual."""
