@@ -171,6 +171,7 @@ spb_status spb_plan_upload(const spb_plan *plan, int32_t pass, void *d_meta, siz
  * calibration [man DESCRIPTION: calibrate]; QK^T on fp8 MFMA, P.V on bf16).
  * out_dtype: SPB_F32 or SPB_BF16.  head_dim 64 or 128; hq % hkv == 0 and
  * hq / hkv in {1, 2, 4}.  softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * SPB_BF16 passes need n_tokens * hkv * head_dim * 2 < 4 GiB (SPB_ERR_LIMIT).
  * d_meta: the upload of (plan, pass). */
 typedef struct {
   const void *q, *k, *v;

@@ -8,30 +8,39 @@
 // equal to running each content + question as its own prompt [PyPI, "Speed
 // and scale"].
 //
-// Work item: up to 32*RW consecutive rows of one 128-row tile (rows of one
-// segment) and one KV head.  Wave w handles 32 query rows for query head
-// kvh*G + w%G; the G query heads of a KV group share every staged K/V chunk.
-//
-// Keys are visited as a list of chunks built per work item: content chunks of
-// 64 keys aligned to the content start, then for each branch that meets the
-// work item's rows, chunks of 32 keys aligned to the branch start (template
-// rows, then option-trie nodes).  Each chunk is staged row-major in LDS (K and
-// V, rows padded against bank conflicts), double-buffered, loaded into
-// registers one chunk ahead:
+// Work item: up to 128 consecutive rows of one 128-row tile (rows of one
+// segment) and one KV head.  Keys are visited as a list of chunks built per
+// work item: content chunks of 64 keys aligned to the content start, then for
+// each branch that meets the work item's rows, chunks of 32 keys aligned to
+// the branch start (template rows, then option-trie nodes).  Per chunk:
 //   S^T = K Q^T      (MFMA 32x32x16 bf16, or 32x32x64 OCP e4m3 for fp8 Q/K)
-//   online softmax   (each lane owns one query; f32, base-2 exponent)
+//   online softmax   (each lane owns one query; f32, base-2 exponent, the
+//                     exponent reference moved lazily)
 //   O^T += V^T P^T   (MFMA 32x32x16 bf16 with P in bf16; the V^T operand is
 //                     read from row-major V with the LDS transpose read)
+//
+// Two kernels share that chunk step:
+//  * bf16 inputs (dma kernel): K and V rows are copied straight from global
+//    memory into a 3-deep LDS ring (XOR-swizzled rows, no staging registers),
+//    two chunks ahead; a wave owns 32 query rows of one query head (two heads
+//    for d = 64, sharing every K/V fragment read and visibility test).
+//  * f32 / fp8 inputs (staged kernel): K and V pass through registers, where
+//    f32 is rounded to bf16 and e4m3 V is widened to bf16, into a
+//    double-buffered padded LDS layout; one head per wave.
+// Both run one chunk step per chunk (a single instance in the loop, so the
+// O accumulators keep their registers).
 //
 // Batch invariance: a row sees its content keys in 64-key chunks aligned to
 // its content start and its branch keys in 32-key chunks aligned to its branch
 // start.  Slot i of a chunk always holds chunk-relative key i, every masked
-// slot contributes an exact zero and leaves the running max unchanged
-// (alpha = 1), and every per-row sum runs in a fixed slot order.  So a row's
-// bits depend on its own root path only, not on where its input was packed.
+// slot contributes an exact zero, the exponent reference follows only the
+// row's own chunk maxima, and every per-row sum runs in a fixed slot order.
+// So a row's bits depend on its own root path only, not on where its input
+// was packed.
 #define SPB_HD __host__ __device__
 #include "spb_meta.h"
 #include "spb_launch.h"
+#include "spb_dev.h"
 #include "../../include/spb.h"
 
 #include <hip/hip_runtime.h>
@@ -81,11 +90,522 @@ struct AttnParams {
   const SpbBranch *branches;
 };
 
+template <int D, int IN>
+struct QFrag {
+  static constexpr int STEPS = IN == SPB_FP8_E4M3 ? D / 64 : D / 16;
+  typename std::conditional<IN == SPB_FP8_E4M3, i32x8, bf16x8_t>::type f[STEPS];
+};
+
+// Per-lane LDS byte offsets of the wave's fragment reads, relative to a K
+// block (32 key rows) and to a V k-step (16 key rows).  K: step t, piece pc
+// (bf16: one 16-byte piece; e4m3: two).  V: d-block db, first of the two
+// transpose reads (the second is 8 rows further).
+template <int D, int IN>
+struct FragOffsets {
+  static constexpr int STEPS = QFrag<D, IN>::STEPS;
+  static constexpr int NPC = IN == SPB_FP8_E4M3 ? 2 : 1;
+  uint32_t k[STEPS][NPC];
+  uint32_t v[D / 32];
+};
+
+struct RowState {
+  float m;  // exponent reference (scaled, base 2)
+  float l;  // this lane's partial row sum
+};
+
+// Which keys of a 32-key block this lane's query sees.  Register r of a block
+// holds block key (r/4)*8 + half*4 + r%4; with the lane's half folded into the
+// per-lane values, every test compares a compile-time slot (r/4)*8 + r%4:
+//   visible = slot < thr  ||  slot is one of anc[0..3]
+struct Vis {
+  int thr;             // block keys [0, thr + 4*half) visible
+  int anc[kMaxDepth];  // option-trie ancestor keys minus 4*half, or -1000
+};
+
+template <int ANC>
+__device__ __attribute__((always_inline)) inline void mask_block(f32x16 &s, const Vis &vis) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int slot = (r >> 2) * 8 + (r & 3);
+    bool v = slot < vis.thr;
+    if constexpr (ANC) {
+#pragma unroll
+      for (int a = 0; a < kMaxDepth; ++a) v = v || slot == vis.anc[a];
+    }
+    s[r] = v ? s[r] : kNegInf;
+  }
+}
+
+// Online softmax over one chunk -- one 32-key block, or two when `two`
+// (runtime, uniform over the wave) -- for one head, with a lazily moved
+// reference: the row's exponent reference m changes only when the chunk's max
+// exceeds it by more than kLazy (log2 units) -- always on the first visible
+// chunk, where O and l are still zero -- so p = 2^(s - m) stays at most
+// 2^kLazy and O is rescaled (by 2^(m_old - m_new)) only on those rare moves.
+// The quotient O / l is the same softmax for any reference.  Returns P as
+// bf16 pairs; the row sum runs over block 0 then block 1, registers in order.
+constexpr float kLazy = 8.f;
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void softmax_chunk(const f32x16 &s0, const f32x16 &s1, bool two,
+                                                                     float sc, RowState &st, f32x16 (&o)[D / 32],
+                                                                     uint32_t (&pk)[2][8]) {
+  float mloc = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s0[r]);
+  if (two) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s1[r]);
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sc;
+  const bool first = st.m == kNegInf;
+  const bool move = !first && mloc > st.m + kLazy;
+  const float mnew = (first || move) ? mloc : st.m;
+  const float negm = mnew == kNegInf ? 0.f : -mnew;
+  float lsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sc, negm));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], sc, negm));
+    lsum += p0;
+    lsum += p1;
+    pk[0][r >> 1] = pack_bf16(p0, p1);
+  }
+  if (two) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sc, negm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], sc, negm));
+      lsum += p0;
+      lsum += p1;
+      pk[1][r >> 1] = pack_bf16(p0, p1);
+    }
+  }
+  if (__ballot(move)) {
+    const float alpha = move ? __builtin_amdgcn_exp2f(st.m - mnew) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+  }
+  st.l += lsum;
+  st.m = mnew;
+}
+
+// S^T of one 32-key block for HPW heads: each K fragment read from LDS feeds
+// one MFMA per head.  Kblk: the block's first key row in LDS.
+template <int D, int IN, int HPW>
+__device__ __attribute__((always_inline)) inline void qk_block(const char *Kblk, const FragOffsets<D, IN> &fo,
+                                                               const QFrag<D, IN> (&qf)[HPW], f32x16 (&s)[HPW]) {
+  constexpr int STEPS = QFrag<D, IN>::STEPS;
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) s[j] = f32x16{0.f};
+  if constexpr (IN == SPB_FP8_E4M3) {
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      asm volatile("" ::: "memory");
+      u32x4 a0 = *(const u32x4 *)(Kblk + fo.k[t][0]), a1 = *(const u32x4 *)(Kblk + fo.k[t][1]);
+      i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+      for (int j = 0; j < HPW; ++j)
+        s[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[j].f[t], s[j], 0, 0, 0, 0, 0, 0);
+    }
+  } else {
+    constexpr int GRP = STEPS < 4 ? STEPS : 4;
+#pragma unroll
+    for (int t0 = 0; t0 < STEPS; t0 += GRP) {
+      asm volatile("" ::: "memory");  // keeps each group's LDS reads next to its MFMAs
+      u32x4 a[GRP];
+#pragma unroll
+      for (int t = 0; t < GRP; ++t) a[t] = *(const u32x4 *)(Kblk + fo.k[t0 + t][0]);
+#pragma unroll
+      for (int t = 0; t < GRP; ++t)
+#pragma unroll
+        for (int j = 0; j < HPW; ++j)
+          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)&a[t], qf[j].f[t0 + t], s[j], 0, 0, 0);
+    }
+  }
+}
+
+// O^T += V^T P^T over one 32-key block (two k-steps of 16 keys).
+// k-step j covers block keys 16(j%2) + half*4 + {0..3} and +8: the P^T
+// operand is registers 8(j%2) .. +8 of the block, the V^T operand two
+// transpose reads of 4 rows each, shared by the HPW heads.  VSTRIDE: bytes
+// per V row in LDS.
+template <int D, int IN, int HPW, int VSTRIDE>
+__device__ __attribute__((always_inline)) inline void pv_block(const char *Vblk, const FragOffsets<D, IN> &fo,
+                                                               const uint32_t (&pk)[HPW][8],
+                                                               f32x16 (&o)[HPW][D / 32]) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    asm volatile("" ::: "memory");  // keeps each k-step's transpose reads next to its MFMAs
+    const int rb = jj * 4;
+    const char *vstep = Vblk + 16 * jj * VSTRIDE;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      union {
+        i16x4 h[2];
+        bf16x8_t v;
+      } a;
+      a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vstep + fo.v[db]));
+      a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vstep + fo.v[db] + 8 * VSTRIDE));
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        union {
+          uint32_t u[4];
+          bf16x8_t v;
+        } b;
+        b.u[0] = pk[h][rb]; b.u[1] = pk[h][rb + 1]; b.u[2] = pk[h][rb + 2]; b.u[3] = pk[h][rb + 3];
+        o[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, o[h][db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Chunk list of the work item (built by wave 0): content chunks, then the
+// chunks of each branch that meets rows [sub0, sub0 + sub_n).
+__device__ inline void build_chunk_list(const AttnParams &p, const SpbTile &tile, int sub0, int sub_n, int lane,
+                                        int2 *chunks, int *n_chunks) {
+  for (int c = lane; c < tile.ncc && c < kMaxChunks; c += 64) chunks[c] = int2{tile.seg + c * kChunk, -1 - c};
+  int n = tile.ncc;
+  for (int b0 = tile.b_lo; b0 < tile.b_hi; b0 += 64) {
+    const int b = b0 + lane;
+    int cnt = 0, start = 0;
+    if (b < tile.b_hi) {
+      const SpbBranch br = p.branches[b];
+      start = br.start;
+      if (br.start + br.E > sub0 && br.start < sub0 + sub_n) {
+        const int last = min(br.start + br.E, sub0 + sub_n) - 1 - br.start;
+        cnt = last / kBranchChunk + 1;
+      }
+    }
+    int incl = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const int base = n + incl - cnt;
+    for (int c = 0; c < cnt; ++c)
+      if (base + c < kMaxChunks) chunks[base + c] = int2{start + c * kBranchChunk, (b << 10) | c};
+    n += __shfl(incl, 63);
+  }
+  if (lane == 0) *n_chunks = n < kMaxChunks ? n : kMaxChunks;
+}
+
+// Q fragments of row x, query head h (zeros for inactive lanes).
+template <int D, int IN>
+__device__ inline void load_q(QFrag<D, IN> &qf, const AttnParams &p, int x, int h, bool active, int half) {
+  if constexpr (IN == SPB_FP8_E4M3) {
+    const unsigned char *qp = (const unsigned char *)p.q + ((size_t)x * p.hq + h) * D;
+#pragma unroll
+    for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
+      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+      if (active) {
+        a0 = *(const u32x4 *)(qp + t * 64 + half * 32);
+        a1 = *(const u32x4 *)(qp + t * 64 + half * 32 + 16);
+      }
+      qf.f[t] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (active) {
+        if constexpr (IN == SPB_BF16) {
+          a = *(const u32x4 *)((const uint16_t *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8);
+        } else {
+          const float *src = (const float *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8;
+          u32x4 f0 = *(const u32x4 *)src, f1 = *(const u32x4 *)(src + 4);
+          a = u32x4{pack_bf16(__uint_as_float(f0.x), __uint_as_float(f0.y)),
+                    pack_bf16(__uint_as_float(f0.z), __uint_as_float(f0.w)),
+                    pack_bf16(__uint_as_float(f1.x), __uint_as_float(f1.y)),
+                    pack_bf16(__uint_as_float(f1.z), __uint_as_float(f1.w))};
+        }
+      }
+      qf.f[t] = *(bf16x8_t *)&a;
+    }
+  }
+}
+
+// normalise and store: lane holds d = db*32 + (r/4)*8 + half*4 + r%4
+template <int D, int OUT>
+__device__ inline void store_o(const AttnParams &p, int x, int h, int half, const RowState &st,
+                               const f32x16 (&o)[D / 32]) {
+  const float l = st.l + __shfl_xor(st.l, 32);
+  const float inv = p.s_v / l;
+  if constexpr (OUT == SPB_F32) {
+    float *op = (float *)p.o + ((size_t)x * p.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        float4 v = {o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv, o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv};
+        *(float4 *)(op + db * 32 + gg * 8 + half * 4) = v;
+      }
+  } else {
+    uint16_t *op = (uint16_t *)p.o + ((size_t)x * p.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        u32x2 v = {pack_bf16(o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv),
+                   pack_bf16(o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv)};
+        *(u32x2 *)(op + db * 32 + gg * 8 + half * 4) = v;
+      }
+  }
+}
+
+// The chunk walk shared by both kernels.  Content chunk c (keys
+// [c*64, c*64 + 64) of the content) is two 32-key blocks, the second skipped
+// when no lane sees past key 32; branch chunk c (extended keys
+// [c*32, c*32 + 32) of the branch) is one block.  A chunk is skipped by a wave
+// none of whose lanes sees a key of it.  block(i, vis, two, masked, anc) runs
+// chunk i -- S^T, mask, softmax, O^T update over one or two blocks -- and
+// appears once in the loop, so the accumulators keep their registers;
+// advance(i) hands the LDS ring on to chunk i + 1.
+template <typename Block, typename Advance>
+__device__ __attribute__((always_inline)) inline void walk_chunks(const int2 *chunks, int nch, const SpbRow &row,
+                                                                  int half, Block &&block, Advance &&advance) {
+  for (int i = 0; i < nch; ++i) {
+    const int2 ch = chunks[i];
+    int thr;  // keys of the chunk this lane sees as a prefix
+    int anc[kMaxDepth];
+    bool any, node = false;
+#pragma unroll
+    for (int a = 0; a < kMaxDepth; ++a) anc[a] = -1000;
+    if (ch.y < 0) {
+      thr = row.cvis - (-1 - ch.y) * kChunk;
+      any = thr > 0;
+    } else {
+      const int c = ch.y & 1023;
+      const int lo = c * kBranchChunk;
+      const bool mine = row.br == ch.x - lo;
+      thr = mine ? min(min(row.e + 1, row.L) - lo, kBranchChunk) : 0;
+      any = thr > 0;
+      node = mine && row.depth > 0;
+      if (node) {
+#pragma unroll
+        for (int a = 0; a < kMaxDepth; ++a) {
+          const int e = anc_of(row, a) - lo;
+          if (a < row.depth && e >= 0 && e < kBranchChunk) {
+            anc[a] = e;
+            any = true;
+          }
+        }
+      }
+    }
+    if (__ballot(any)) {
+      const bool two = ch.y < 0 && __ballot(thr > 32);
+      const bool anc_any = __ballot(node) != 0;
+      Vis vis;
+      vis.thr = thr - 4 * half;
+#pragma unroll
+      for (int a = 0; a < kMaxDepth; ++a) vis.anc[a] = anc[a] - 4 * half;
+      const bool masked = anc_any || __ballot(thr < (two ? 64 : 32)) != 0;
+      block(i, vis, two, masked, anc_any);
+    }
+    advance(i);
+  }
+}
+
+// ------------------------------------------------------- bf16: dma kernel
+
+template <int D, int G, int HPW_, int RG_>
+struct DmaCfg {
+  static constexpr int HPW = HPW_;            // query heads per wave
+  static constexpr int HG = G / HPW;          // waves per 32-row group
+  static constexpr int RG = RG_;              // 32-row groups per work item
+  static constexpr int NW = RG * HG;          // waves
+  static constexpr int NT = 64 * NW;
+  static constexpr int ROWS = 32 * RG;
+  static constexpr int SPLITS = 128 / ROWS;   // work items per 128-row tile
+  static constexpr int ROWB = 2 * D;          // bytes per K or V row
+  static constexpr int BUF = 64 * ROWB;       // one chunk of K (or V)
+  static constexpr int NBUF = 3;              // ring depth: two chunks in flight
+  // copies per wave per tensor for a 64-key and a 32-key chunk
+  static constexpr int Q64 = 64 * ROWB / 1024 / NW;
+  static constexpr int Q32 = 32 * ROWB / 1024 / NW;
+  static_assert(G % HPW == 0 && 128 % ROWS == 0, "work item shape");
+  static_assert(Q32 >= 1 && Q32 * NW * 1024 == 32 * ROWB, "a 32-key chunk must give every wave whole copies");
+};
+
+// LDS row swizzles (16-byte chunk c of row r lives at chunk c ^ f(r)).  K: a
+// fragment read has 16 lanes on 16 consecutive rows at one chunk; V: a
+// transpose read has 32 lanes on 4 consecutive rows at 4 consecutive chunks.
+// Both spread those over all 64 banks.
+template <int ROWB>
+__device__ inline int swz_k(int r) { return ROWB == 256 ? (r & 15) : ((r >> 1) & 7); }
+template <int ROWB>
+__device__ inline int swz_v(int r) { return ROWB == 256 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+template <int D, int G, int HPW_, int RG_, int OUT>
+__global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), 1) void branch_attention_dma(AttnParams p) {
+  using C = DmaCfg<D, G, HPW_, RG_>;
+  constexpr int HPW = C::HPW;
+  constexpr int IN = SPB_BF16;
+  __shared__ __attribute__((aligned(1024))) char Ks[C::NBUF][C::BUF];
+  __shared__ __attribute__((aligned(1024))) char Vs[C::NBUF][C::BUF];
+  __shared__ int2 chunks[kMaxChunks];  // (key0, info): info < 0 content chunk -1-c; else branch << 10 | c
+  __shared__ int n_chunks_s;
+
+  const int w = blockIdx.x;
+  const int kvh = w % p.hkv;
+  const int rest = w / p.hkv;
+  const int split = rest % C::SPLITS;
+  const SpbTile tile = p.tiles[rest / C::SPLITS];
+  const int sub0 = tile.row0 + split * C::ROWS;
+  const int sub_n = min(C::ROWS, tile.row0 + tile.nrows - sub0);
+  if (sub_n <= 0) return;  // uniform over the work group
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave / C::HG, hgi = wave % C::HG;
+  const int h0 = kvh * G + hgi * HPW;  // the wave's first query head
+  const int qi = lane & 31, half = lane >> 5;
+  const int local = rg * 32 + qi;
+  const bool active = local < sub_n;
+  const int x = sub0 + local;
+
+  if (wave == 0) build_chunk_list(p, tile, sub0, sub_n, lane, chunks, &n_chunks_s);
+
+  SpbRow row;
+  if (active) {
+    row = p.rows[x];
+  } else {
+    row.cvis = 0; row.seg = 0; row.br = -1; row.e = 0; row.L = 0; row.depth = 0; row.anc01 = 0; row.anc23 = 0;
+  }
+  QFrag<D, IN> qf[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) load_q<D, IN>(qf[j], p, x, h0 + j, active, half);
+
+  // fragment offsets in the swizzled layout
+  FragOffsets<D, IN> fo;
+#pragma unroll
+  for (int t = 0; t < QFrag<D, IN>::STEPS; ++t)
+    fo.k[t][0] = qi * C::ROWB + (((2 * t + half) ^ swz_k<C::ROWB>(qi)) << 4);
+  {
+    const int g = qi >> 4, l16 = lane & 15;
+    const int rr = half * 4 + (l16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int cv = 2 * g + ((l16 & 3) >> 1) + 4 * db;
+      fo.v[db] = rr * C::ROWB + ((cv ^ swz_v<C::ROWB>(rr)) << 4) + (l16 & 1) * 8;
+    }
+  }
+
+  RowState st[HPW];
+  f32x16 o[HPW][D / 32];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    st[j] = RowState{kNegInf, 0.f};
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[j][db] = f32x16{0.f};
+  }
+
+  __syncthreads();  // chunk list ready
+  const int nch = n_chunks_s;
+  const uint32_t k_lds = lds_addr(&Ks[0][0]), v_lds = lds_addr(&Vs[0][0]);
+
+  // Copies chunk i (64 or 32 key rows; rows past the pass repeat its last
+  // row, so every slot holds finite data) into ring slot i % 3: copy q of a
+  // tensor moves slot bytes q*1024 .. +1024, so lane t fills row
+  // (q*1024 + 16t) / ROWB at chunk position (16t % ROWB) / 16.
+  auto issue = [&](int i) {
+    const int2 ch = chunks[i];
+    const int nq = ch.y < 0 ? C::Q64 : C::Q32;
+    const uint32_t slot = (uint32_t)(i % C::NBUF) * C::BUF;
+    for (int qq = 0; qq < nq; ++qq) {
+      const int q = wave * nq + qq;
+      const int b = q * 1024 + lane * 16;
+      const int r = b / C::ROWB, pos = (b % C::ROWB) >> 4;
+      const int y = min(ch.x + r, p.n_tokens - 1);
+      const uint32_t rowoff = (uint32_t)(((size_t)y * p.hkv + kvh) * C::ROWB);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + (uint32_t)q * 1024);
+      dma16(p.k, rowoff + ((pos ^ swz_k<C::ROWB>(r)) << 4), k_lds + dst);
+      dma16(p.v, rowoff + ((pos ^ swz_v<C::ROWB>(r)) << 4), v_lds + dst);
+    }
+  };
+  // waits for this wave's copies of chunk i + 1, leaving chunk i + 2's in flight
+  auto wait_next = [&](int i) {
+    if (i + 2 < nch) {
+      if (chunks[i + 2].y < 0)
+        wait_vmcnt<2 * C::Q64>();
+      else
+        wait_vmcnt<2 * C::Q32>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+  };
+
+  if (nch > 0) {
+    issue(0);
+    if (nch > 1) issue(1);
+    wait_next(-1);
+  }
+
+  auto block = [&](int i, const Vis &vis, bool two, bool masked, bool anc) {
+    const char *Kb = Ks[i % C::NBUF];
+    const char *Vb = Vs[i % C::NBUF];
+    f32x16 s0[HPW], s1[HPW];
+    qk_block<D, IN, HPW>(Kb, fo, qf, s0);
+    if (two) qk_block<D, IN, HPW>(Kb + 32 * C::ROWB, fo, qf, s1);
+    if (masked) {
+      if (anc) {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) mask_block<1>(s0[j], vis);
+      } else {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) mask_block<0>(s0[j], vis);
+        if (two) {
+          Vis v1 = vis;
+          v1.thr -= 32;
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) mask_block<0>(s1[j], v1);
+        }
+      }
+    }
+    uint32_t pk[HPW][2][8];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) softmax_chunk<D>(s0[j], s1[j], two, p.sc, st[j], o[j], pk[j]);
+    {
+      uint32_t pb[HPW][8];
+#pragma unroll
+      for (int j = 0; j < HPW; ++j)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) pb[j][r] = pk[j][0][r];
+      pv_block<D, IN, HPW, C::ROWB>(Vb, fo, pb, o);
+    }
+    if (two) {
+      uint32_t pb[HPW][8];
+#pragma unroll
+      for (int j = 0; j < HPW; ++j)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) pb[j][r] = pk[j][1][r];
+      pv_block<D, IN, HPW, C::ROWB>(Vb + 32 * C::ROWB, fo, pb, o);
+    }
+  };
+  // Chunk i + 2 goes into the slot chunk i - 1 left (every wave passed the
+  // barrier after reading it); then chunk i + 1 is awaited for the next trip.
+  auto advance = [&](int i) {
+    if (i + 2 < nch) issue(i + 2);
+    wait_next(i);
+  };
+  walk_chunks(chunks, nch, row, half, block, advance);
+
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) store_o<D, OUT>(p, x, h0 + j, half, st[j], o[j]);
+  }
+}
+
+// ------------------------------------------------- f32 / fp8: staged kernel
+
 template <int D, int G, int IN>
-struct Cfg {
+struct StagedCfg {
   static constexpr bool FP8 = IN == SPB_FP8_E4M3;
   static constexpr int RW = G == 4 ? 2 : 4;   // 32-row groups per work item
-  static constexpr int NW = RW * G;           // waves
+  static constexpr int NW = RW * G;           // waves, one query head each
   static constexpr int NT = NW * 64;
   static constexpr int ROWS = 32 * RW;
   static constexpr int SPLITS = 128 / ROWS;   // work items per 128-row tile
@@ -101,22 +621,17 @@ struct Cfg {
   static constexpr int VPITCH = 2 * D + 64;
 };
 
-template <int D, int IN>
-struct QFrag {
-  static constexpr int STEPS = IN == SPB_FP8_E4M3 ? D / 64 : D / 16;
-  typename std::conditional<IN == SPB_FP8_E4M3, i32x8, bf16x8_t>::type f[STEPS];
-};
-
 template <int D, int G, int IN>
 struct Stage {  // one chunk's K and V units held by this thread
-  u32x4 k[Cfg<D, G, IN>::KPT];
-  u32x4 v[Cfg<D, G, IN>::VPT];
+  u32x4 k[StagedCfg<D, G, IN>::KPT];
+  u32x4 v[StagedCfg<D, G, IN>::VPT];
 };
 
-// Global -> registers: rows key0 .. key0 + nrows of K and V for KV head kvh.
+// Global -> registers: rows key0 .. key0 + nrows of K and V for KV head kvh;
+// rows past nrows (or past the pass) are zeros.
 template <int D, int G, int IN>
 __device__ inline void stage_load(Stage<D, G, IN> &st, const AttnParams &p, int kvh, int key0, int nrows) {
-  using C = Cfg<D, G, IN>;
+  using C = StagedCfg<D, G, IN>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < C::KPT; ++i) {
@@ -170,153 +685,30 @@ __device__ inline void stage_load(Stage<D, G, IN> &st, const AttnParams &p, int 
   }
 }
 
-// registers -> LDS buffers (swizzled)
+// registers -> LDS buffers; every one of the 64 rows is written (zeros past
+// the chunk), so no slot ever holds a stale or uninitialised value.
 template <int D, int G, int IN>
-__device__ inline void stage_store(const Stage<D, G, IN> &st, char *Ks, char *Vs, int nrows) {
-  using C = Cfg<D, G, IN>;
+__device__ inline void stage_store(const Stage<D, G, IN> &st, char *Ks, char *Vs) {
+  using C = StagedCfg<D, G, IN>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < C::KPT; ++i) {
     const int u = tid + i * C::NT;
-    const int r = u / C::KCH, c = u % C::KCH;
-    if (r < nrows) *(u32x4 *)(Ks + r * C::KPITCH + c * 16) = st.k[i];
+    if (u < 64 * C::KCH) *(u32x4 *)(Ks + (u / C::KCH) * C::KPITCH + (u % C::KCH) * 16) = st.k[i];
   }
 #pragma unroll
   for (int i = 0; i < C::VPT; ++i) {
     const int u = tid + i * C::NT;
-    const int r = u / C::VCH, c = u % C::VCH;
-    if (r < nrows) *(u32x4 *)(Vs + r * C::VPITCH + c * 16) = st.v[i];
+    if (u < 64 * C::VCH) *(u32x4 *)(Vs + (u / C::VCH) * C::VPITCH + (u % C::VCH) * 16) = st.v[i];
   }
 }
-
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-struct RowState {
-  float m;  // running max of the scaled (base-2) logits
-  float l;  // this lane's partial row sum
-};
-
-// Which keys of a chunk this lane's query sees.  Register r of block kb
-// holds chunk key kb*32 + (r/4)*8 + half*4 + r%4; with the lane's half folded
-// into the thresholds, every test compares a compile-time slot offset
-// kb*32 + (r/4)*8 + r%4 against per-lane values:
-//   visible = slot < thr  ||  slot is one of anc[0..3]  (ANC only)
-struct Vis {
-  int thr;        // keys [0, thr + 4*half) visible
-  int anc[kMaxDepth];  // option-trie ancestor keys minus 4*half, or -1000
-};
-
-// One chunk of NKB*32 keys.  MODE 0: every key visible to every lane;
-// 1: prefix test only; 2: prefix test and ancestor keys.
-template <int D, int G, int IN, int NKB, int MODE>
-__device__ inline void chunk_step(const char *Ks, const char *Vs, const QFrag<D, IN> &qf, const Vis &vis,
-                                  float sc, RowState &st, f32x16 (&o)[D / 32]) {
-  using C = Cfg<D, G, IN>;
-  const int lane = threadIdx.x & 63;
-  const int qi = lane & 31, half = lane >> 5;
-  f32x16 s[NKB];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    asm volatile("" ::: "memory");  // keeps each block's LDS reads next to its MFMAs
-    s[kb] = f32x16{0.f};
-    const int r = kb * 32 + qi;
-    if constexpr (C::FP8) {
-#pragma unroll
-      for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-        const char *src = Ks + r * C::KPITCH + t * 64 + half * 32;
-        u32x4 a0 = *(const u32x4 *)src, a1 = *(const u32x4 *)(src + 16);
-        i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf.f[t], s[kb], 0, 0, 0, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-        u32x4 u = *(const u32x4 *)(Ks + r * C::KPITCH + t * 32 + half * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(bf16x8_t *)&u, qf.f[t], s[kb], 0, 0, 0);
-      }
-    }
-  }
-  // online softmax: lane owns query qi; register r of block kb holds key
-  // kb*32 + (r/4)*8 + half*4 + r%4
-  if constexpr (MODE != 0) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int slot = kb * 32 + (r >> 2) * 8 + (r & 3);
-        bool v = slot < vis.thr;
-        if constexpr (MODE == 2) {
-#pragma unroll
-          for (int a = 0; a < kMaxDepth; ++a) v = v || slot == vis.anc[a];
-        }
-        s[kb][r] = v ? s[kb][r] : kNegInf;
-      }
-  }
-  float mloc = kNegInf;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kb][r]);
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  const float mnew = fmaxf(st.m, mloc * sc);
-  const bool none = mnew == kNegInf;  // nothing visible yet: p = 0, alpha = 1
-  const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(st.m - mnew);
-  const float negm = none ? 0.f : -mnew;
-  uint32_t pk[NKB][8];
-  float lsum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sc, negm));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], sc, negm));
-      lsum += p0;
-      lsum += p1;
-      pk[kb][r >> 1] = pack_bf16(p0, p1);
-    }
-  st.l = st.l * alpha + lsum;
-  st.m = mnew;
-  if (__ballot(alpha != 1.f)) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-  }
-  // O^T += V^T P^T.  k-step j covers keys 16j + half*4 + {0..3} and
-  // 16j + 8 + half*4 + {0..3}: the P^T operand is registers 8(j%2) .. +8 of
-  // block j/2, the V^T operand two transpose reads of 4 rows each.
-  const int g = qi >> 4, l16 = lane & 15;
-#pragma unroll
-  for (int j = 0; j < 2 * NKB; ++j) {
-    asm volatile("" ::: "memory");
-    const int kb = j >> 1, rb = (j & 1) * 4;
-    union {
-      uint32_t u[4];
-      bf16x8_t v;
-    } b;
-    b.u[0] = pk[kb][rb]; b.u[1] = pk[kb][rb + 1]; b.u[2] = pk[kb][rb + 2]; b.u[3] = pk[kb][rb + 3];
-    // lane reads 4 bf16 at row 16j + half*4 + l16/4 (and +8), column
-    // db*32 + g*16 + 4*(l16%4); the transpose hands it column db*32 + qi
-    const char *vrow = Vs + (16 * j + half * 4 + (l16 >> 2)) * C::VPITCH + (g * 16 + 4 * (l16 & 3)) * 2;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      union {
-        i16x4 h[2];
-        bf16x8_t v;
-      } a;
-      a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + db * 64));
-      a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vrow + 8 * C::VPITCH + db * 64));
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, o[db], 0, 0, 0);
-    }
-  }
-}
-
-// ----------------------------------------------------------------- kernel
 
 template <int D, int G, int IN, int OUT>
-__global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(AttnParams p) {
-  using C = Cfg<D, G, IN>;
+__global__ __launch_bounds__((StagedCfg<D, G, IN>::NT)) void branch_attention_staged(AttnParams p) {
+  using C = StagedCfg<D, G, IN>;
   __shared__ __attribute__((aligned(16))) char Ks[2][64 * C::KPITCH];
   __shared__ __attribute__((aligned(16))) char Vs[2][64 * C::VPITCH];
-  __shared__ int2 chunks[kMaxChunks];  // (key0, info): info < 0 content chunk -1-c; else branch << 10 | c
+  __shared__ int2 chunks[kMaxChunks];
   __shared__ int n_chunks_s;
 
   const int w = blockIdx.x;
@@ -336,35 +728,7 @@ __global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(A
   const bool active = local < sub_n;
   const int x = sub0 + local;
 
-  // chunk list (wave 0): content chunks, then the chunks of each branch that
-  // meets rows [sub0, sub0 + sub_n)
-  if (wave == 0) {
-    for (int c = lane; c < tile.ncc && c < kMaxChunks; c += 64) chunks[c] = int2{tile.seg + c * kChunk, -1 - c};
-    int n = tile.ncc;
-    for (int b0 = tile.b_lo; b0 < tile.b_hi; b0 += 64) {
-      const int b = b0 + lane;
-      int cnt = 0, start = 0;
-      if (b < tile.b_hi) {
-        const SpbBranch br = p.branches[b];
-        start = br.start;
-        if (br.start + br.E > sub0 && br.start < sub0 + sub_n) {
-          const int last = min(br.start + br.E, sub0 + sub_n) - 1 - br.start;
-          cnt = last / kBranchChunk + 1;
-        }
-      }
-      int incl = cnt;  // inclusive prefix sum over the wave
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
-      const int base = n + incl - cnt;
-      for (int c = 0; c < cnt; ++c)
-        if (base + c < kMaxChunks) chunks[base + c] = int2{start + c * kBranchChunk, (b << 10) | c};
-      n += __shfl(incl, 63);
-    }
-    if (lane == 0) n_chunks_s = n < kMaxChunks ? n : kMaxChunks;
-  }
+  if (wave == 0) build_chunk_list(p, tile, sub0, sub_n, lane, chunks, &n_chunks_s);
 
   SpbRow row;
   if (active) {
@@ -372,43 +736,30 @@ __global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(A
   } else {
     row.cvis = 0; row.seg = 0; row.br = -1; row.e = 0; row.L = 0; row.depth = 0; row.anc01 = 0; row.anc23 = 0;
   }
+  QFrag<D, IN> qf[1];
+  load_q<D, IN>(qf[0], p, x, h, active, half);
 
-  QFrag<D, IN> qf;
-  if constexpr (C::FP8) {
-    const unsigned char *qp = (const unsigned char *)p.q + ((size_t)x * p.hq + h) * D;
+  FragOffsets<D, IN> fo;
 #pragma unroll
-    for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-      if (active) {
-        a0 = *(const u32x4 *)(qp + t * 64 + half * 32);
-        a1 = *(const u32x4 *)(qp + t * 64 + half * 32 + 16);
-      }
-      qf.f[t] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
-      u32x4 a = {0u, 0u, 0u, 0u};
-      if (active) {
-        if constexpr (IN == SPB_BF16) {
-          a = *(const u32x4 *)((const uint16_t *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8);
-        } else {
-          const float *src = (const float *)p.q + ((size_t)x * p.hq + h) * D + t * 16 + half * 8;
-          u32x4 f0 = *(const u32x4 *)src, f1 = *(const u32x4 *)(src + 4);
-          a = u32x4{pack_bf16(__uint_as_float(f0.x), __uint_as_float(f0.y)),
-                    pack_bf16(__uint_as_float(f0.z), __uint_as_float(f0.w)),
-                    pack_bf16(__uint_as_float(f1.x), __uint_as_float(f1.y)),
-                    pack_bf16(__uint_as_float(f1.z), __uint_as_float(f1.w))};
-        }
-      }
-      qf.f[t] = *(bf16x8_t *)&a;
+  for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
+    if constexpr (C::FP8) {
+      fo.k[t][0] = qi * C::KPITCH + t * 64 + half * 32;
+      fo.k[t][1] = fo.k[t][0] + 16;
+    } else {
+      fo.k[t][0] = qi * C::KPITCH + t * 32 + half * 16;
     }
   }
-
-  RowState st{kNegInf, 0.f};
-  f32x16 o[D / 32];
+  {
+    const int g = qi >> 4, l16 = lane & 15;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{0.f};
+    for (int db = 0; db < D / 32; ++db)
+      fo.v[db] = (half * 4 + (l16 >> 2)) * C::VPITCH + (g * 16 + 4 * (l16 & 3)) * 2 + db * 64;
+  }
+
+  RowState st[1] = {RowState{kNegInf, 0.f}};
+  f32x16 o[1][D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[0][db] = f32x16{0.f};
 
   __syncthreads();  // chunk list ready
   const int nch = n_chunks_s;
@@ -420,89 +771,59 @@ __global__ __launch_bounds__((Cfg<D, G, IN>::NT)) void branch_attention_kernel(A
   Stage<D, G, IN> stg;
   if (nch > 0) {
     stage_load<D, G, IN>(stg, p, kvh, chunks[0].x, nrows_of(0));
-    stage_store<D, G, IN>(stg, Ks[0], Vs[0], nrows_of(0));
+    stage_store<D, G, IN>(stg, Ks[0], Vs[0]);
     lds_barrier();
     const int i1 = min(1, nch - 1);
     stage_load<D, G, IN>(stg, p, kvh, chunks[i1].x, nrows_of(i1));
   }
 
-  for (int i = 0; i < nch; ++i) {
-    const int buf = i & 1;
-    const int2 ch = chunks[i];
-    Vis vis;
-#pragma unroll
-    for (int a = 0; a < kMaxDepth; ++a) vis.anc[a] = -1000;
-    if (ch.y < 0) {  // content chunk c: keys [c*64, c*64 + 64) of the content
-      const int c = -1 - ch.y;
-      const int nvis = row.cvis - c * kChunk;
-      vis.thr = nvis - 4 * half;
-      if (__ballot(nvis > 0)) {
-        if (__ballot(nvis < kChunk))
-          chunk_step<D, G, IN, 2, 1>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
-        else
-          chunk_step<D, G, IN, 2, 0>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
-      }
-    } else {  // branch chunk c: extended keys [c*32, c*32 + 32) of the branch
-      const int c = ch.y & 1023;
-      const int lo = c * kBranchChunk;
-      const bool mine = row.br == ch.x - lo;
-      int nt = mine ? min(min(row.e + 1, row.L) - lo, kBranchChunk) : 0;
-      bool any = nt > 0;
-      const bool node = mine && row.depth > 0;
-      if (node) {
-#pragma unroll
-        for (int a = 0; a < kMaxDepth; ++a) {
-          const int e = anc_of(row, a) - lo;
-          if (a < row.depth && e >= 0 && e < kBranchChunk) {
-            vis.anc[a] = e - 4 * half;
-            any = true;
-          }
+  auto block = [&](int i, const Vis &vis, bool two, bool masked, bool anc) {
+    const char *Kb = Ks[i & 1];
+    const char *Vb = Vs[i & 1];
+    f32x16 s0[1], s1[1];
+    qk_block<D, IN, 1>(Kb, fo, qf, s0);
+    if (two) qk_block<D, IN, 1>(Kb + 32 * C::KPITCH, fo, qf, s1);
+    if (masked) {
+      if (anc) {
+        mask_block<1>(s0[0], vis);
+      } else {
+        mask_block<0>(s0[0], vis);
+        if (two) {
+          Vis v1 = vis;
+          v1.thr -= 32;
+          mask_block<0>(s1[0], v1);
         }
       }
-      vis.thr = nt - 4 * half;
-      if (__ballot(any)) {
-        if (__ballot(node))
-          chunk_step<D, G, IN, 1, 2>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
-        else
-          chunk_step<D, G, IN, 1, 1>(Ks[buf], Vs[buf], qf, vis, p.sc, st, o);
-      }
     }
-    const int i1 = min(i + 1, nch - 1), i2 = min(i + 2, nch - 1);
-    stage_store<D, G, IN>(stg, Ks[buf ^ 1], Vs[buf ^ 1], nrows_of(i1));
+    uint32_t pk[2][8];
+    softmax_chunk<D>(s0[0], s1[0], two, p.sc, st[0], o[0], pk);
+    {
+      uint32_t pb[1][8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) pb[0][r] = pk[0][r];
+      pv_block<D, IN, 1, C::VPITCH>(Vb, fo, pb, o);
+    }
+    if (two) {
+      uint32_t pb[1][8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) pb[0][r] = pk[1][r];
+      pv_block<D, IN, 1, C::VPITCH>(Vb + 32 * C::VPITCH, fo, pb, o);
+    }
+  };
+  auto advance = [&](int i) {  // stage chunk i+1 into the other buffer, start loading chunk i+2
+    const int i2 = min(i + 2, nch - 1);
+    stage_store<D, G, IN>(stg, Ks[(i & 1) ^ 1], Vs[(i & 1) ^ 1]);
     lds_barrier();
     stage_load<D, G, IN>(stg, p, kvh, chunks[i2].x, nrows_of(i2));
-  }
+  };
+  walk_chunks(chunks, nch, row, half, block, advance);
 
-  // normalise and store: lane holds d = db*32 + (r/4)*8 + half*4 + r%4
-  const float l = st.l + __shfl_xor(st.l, 32);
-  const float inv = p.s_v / l;
-  if (active) {
-    if constexpr (OUT == SPB_F32) {
-      float *op = (float *)p.o + ((size_t)x * p.hq + h) * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          float4 v = {o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv, o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv};
-          *(float4 *)(op + db * 32 + gg * 8 + half * 4) = v;
-        }
-    } else {
-      uint16_t *op = (uint16_t *)p.o + ((size_t)x * p.hq + h) * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          u32x2 v = {pack_bf16(o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv),
-                     pack_bf16(o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv)};
-          *(u32x2 *)(op + db * 32 + gg * 8 + half * 4) = v;
-        }
-    }
-  }
+  if (active) store_o<D, OUT>(p, x, h, half, st[0], o[0]);
 }
 
-template <int D, int G, int IN, int OUT>
-int launch_t(const AttnLaunch &a, hipStream_t s) {
-  using C = Cfg<D, G, IN>;
+// ------------------------------------------------------------------ launch
+
+AttnParams make_params(const AttnLaunch &a) {
   AttnParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o;
   p.hq = a.hq; p.hkv = a.hkv; p.n_tokens = a.n_tokens;
@@ -511,21 +832,52 @@ int launch_t(const AttnLaunch &a, hipStream_t s) {
   p.rows = (const SpbRow *)a.rows;
   p.tiles = (const SpbTile *)a.tiles;
   p.branches = (const SpbBranch *)a.branches;
+  return p;
+}
+
+// Work-item shapes of the dma kernel: (query heads per wave, 32-row groups).
+// One head per wave and up to eight waves (two per SIMD); d = 64 rows are too
+// short for eight waves to split a 32-key chunk into whole copies, so there
+// the two heads of a wave share the K/V reads and four waves suffice.
+template <int D, int G>
+struct DmaShape {
+  static constexpr int HPW = (G >= 2 && D == 64) ? 2 : 1;
+  static constexpr int RG = ((G / HPW) >= 4 || (D == 64 && (G / HPW) >= 2)) ? 2 : 4;
+};
+
+template <int D, int G, int OUT>
+int launch_dma(const AttnLaunch &a, hipStream_t s) {
+  using Sh = DmaShape<D, G>;
+  using C = DmaCfg<D, G, Sh::HPW, Sh::RG>;
   long long items = (long long)a.n_tiles * C::SPLITS * a.hkv;
   if (items > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL((branch_attention_kernel<D, G, IN, OUT>), dim3((unsigned)items), dim3(C::NT), 0, s, p);
+  // the copies address K/V with 32-bit byte offsets
+  if ((long long)a.n_tokens * a.hkv * C::ROWB > 0xFFFFFFFFll) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL((branch_attention_dma<D, G, Sh::HPW, Sh::RG, OUT>), dim3((unsigned)items), dim3(C::NT), 0, s,
+                     make_params(a));
+  return (int)hipGetLastError();
+}
+
+template <int D, int G, int IN, int OUT>
+int launch_staged(const AttnLaunch &a, hipStream_t s) {
+  using C = StagedCfg<D, G, IN>;
+  long long items = (long long)a.n_tiles * C::SPLITS * a.hkv;
+  if (items > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL((branch_attention_staged<D, G, IN, OUT>), dim3((unsigned)items), dim3(C::NT), 0, s,
+                     make_params(a));
   return (int)hipGetLastError();
 }
 
 template <int D, int G>
 int launch_dtypes(const AttnLaunch &a, hipStream_t s) {
   if (a.in_dtype == SPB_BF16)
-    return a.out_dtype == SPB_F32 ? launch_t<D, G, SPB_BF16, SPB_F32>(a, s) : launch_t<D, G, SPB_BF16, SPB_BF16>(a, s);
+    return a.out_dtype == SPB_F32 ? launch_dma<D, G, SPB_F32>(a, s) : launch_dma<D, G, SPB_BF16>(a, s);
   if (a.in_dtype == SPB_F32)
-    return a.out_dtype == SPB_F32 ? launch_t<D, G, SPB_F32, SPB_F32>(a, s) : launch_t<D, G, SPB_F32, SPB_BF16>(a, s);
+    return a.out_dtype == SPB_F32 ? launch_staged<D, G, SPB_F32, SPB_F32>(a, s)
+                                  : launch_staged<D, G, SPB_F32, SPB_BF16>(a, s);
   if constexpr (D == 128)
-    return a.out_dtype == SPB_F32 ? launch_t<D, G, SPB_FP8_E4M3, SPB_F32>(a, s)
-                                  : launch_t<D, G, SPB_FP8_E4M3, SPB_BF16>(a, s);
+    return a.out_dtype == SPB_F32 ? launch_staged<D, G, SPB_FP8_E4M3, SPB_F32>(a, s)
+                                  : launch_staged<D, G, SPB_FP8_E4M3, SPB_BF16>(a, s);
   return (int)hipErrorInvalidValue;
 }
 

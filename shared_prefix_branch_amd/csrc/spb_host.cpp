@@ -724,6 +724,9 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
   if (!(sq > 0.f) || !(sk > 0.f) || !(sv > 0.f) || !std::isfinite(sq * sk * sv))
     return fail(SPB_ERR_ARG, "fp8 scales must be finite and > 0");
   if ((uintptr_t)d_meta % 256) return fail(SPB_ERR_ARG, "d_meta must be 256-byte aligned");
+  if (a->in_dtype == SPB_BF16 && (uint64_t)h.n_tokens * (uint64_t)a->hkv * (uint64_t)a->head_dim * 2u > 0xFFFFFFFFull)
+    return fail(SPB_ERR_LIMIT, "a bf16 pass's K/V (%d tokens x %d heads x %d) must stay under 4 GiB", h.n_tokens, a->hkv,
+                a->head_dim);
   if (h.n_tiles == 0) return ok();
   for (const SpbTile &t : P.tiles)
     if (t.cost > kMaxTileChunks)

@@ -28,6 +28,7 @@
 #define SPB_HD __host__ __device__
 #include "spb_meta.h"
 #include "spb_launch.h"
+#include "spb_dev.h"
 #include "../../include/spb.h"
 
 #include <hip/hip_runtime.h>
@@ -96,9 +97,6 @@ struct HeadParams {
   float *part, *tz;
 };
 
-// barrier for the LDS hand-off that leaves outstanding global loads in flight
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 template <int MW>
 struct HeadTile {
   static constexpr int TM = 64 * MW;                // scored rows per work group
@@ -110,29 +108,6 @@ struct HeadTile {
   static constexpr int NW = 8;                      // W copies per wave per stage
   static constexpr int NH = 2 * MW;                 // h copies per wave per stage
 };
-
-// Asynchronous copy of 16 bytes per lane from global memory into LDS: lane i
-// writes lds + 16 i.  Issued from inline assembly so that the compiler does
-// not wait on it before unrelated LDS reads; the kernel orders it with
-// explicit vmcnt waits and barriers.  m0 (the LDS address operand) is saved
-// and restored around the copy.
-__device__ inline void dma16(const void *base, uint32_t voff, uint32_t lds) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "s"(lds), "v"(voff), "s"(base)
-      : "memory");
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Fragments of one 16-element K step: A = 4 vocabulary blocks, B = MW
 // scored-row blocks.
@@ -220,8 +195,7 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
     const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
     hoff[i] = ((uint32_t)(m0 + r) * (uint32_t)p.H + c * 8) * 2;
   }
-  const uint32_t lds0 =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&lds[0]);
+  const uint32_t lds0 = lds_addr(&lds[0]);
   auto issue_w = [&](int stage, int sl) {
     const uint32_t kb = (uint32_t)stage * kKT * 2;
     const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
