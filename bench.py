@@ -5,9 +5,11 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 pack the batch into token-budget passes (host C++), and per pass upload the
 metadata, run branch attention and the scored-row lm head (GPU); then copy
-the option scores back and join the floors (host).  The host packs the next
-step's batch while the GPU runs the current one.  Inputs (Q/K/V, hidden
-states, lm head) are resident in HBM before timing starts.
+the option scores back and join the floors (host).  Steps are pipelined: the
+host enqueues step i, then packs and stages batch i+1 and joins step i-1's
+scores while the GPU runs step i; the last step's join is inside the timed
+region.  Inputs (Q/K/V, hidden states, lm head) are resident in HBM before
+timing starts.
 
 Prints one JSON line: whole-job packed tokens/s as `value`, plus scored
 questions/s, per-kernel timings from HIP events recorded on the launch stream
@@ -135,15 +137,21 @@ def main():
     questions = int(info["n_content_branches"])
     tokens = int(info["n_tokens"])
 
-    def step(next_plan_holder, marks=None):
-        # enqueue every pass, pack the next batch on the host meanwhile,
-        # then bring the scores back and join the floors
-        p = next_plan_holder[0]
-        job.plan = p
-        job.run(W, stream=stream, marks=marks)
-        next_plan_holder[0] = spb.pack_pass(prob, token_budget=budget)
-        res = job.finalize()   # synchronises on the copies back
-        return res
+    def step(state, marks=None):
+        # enqueue every pass of the batch staged last and the copy of its
+        # scores back; while the GPU runs them, pack the next batch, stage its
+        # metadata in pinned memory and join the previous step's scores
+        job.run(W, stream=stream, marks=marks, staged=state["next"])
+        slot = job.last_slot
+        state["next"] = job.stage_host(spb.pack_pass(prob, token_budget=budget))
+        if state["prev"] is not None:
+            state["res"] = job.finalize(state["prev"])
+        state["prev"] = slot
+
+    def drain(state):
+        if state["prev"] is not None:
+            state["res"] = job.finalize(state["prev"])
+            state["prev"] = None
 
     # HIP events on the launch stream, created up front (a torch event exists
     # once recorded), recorded inside the timed steps
@@ -155,15 +163,18 @@ def main():
                 ev.record(stream)
     torch.cuda.synchronize()
 
-    holder = [spb.pack_pass(prob, token_budget=budget)]
+    state = {"next": job.stage_host(spb.pack_pass(prob, token_budget=budget)), "prev": None, "res": None}
     for _ in range(args.warmup):
-        step(holder)
+        step(state)
+    drain(state)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        res = step(holder, marks[i])
+        step(state, marks[i])
+    drain(state)   # the last step's scores are joined inside the timed region
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    res = state["res"]
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     att_ms = np.zeros(n_pass)

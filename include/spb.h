@@ -155,6 +155,11 @@ spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int
 /* Copies the pass's device metadata (meta_bytes) from host to d_meta on the
  * stream.  d_meta: device memory, 256-byte aligned, caller-owned. */
 spb_status spb_plan_upload(const spb_plan *plan, int32_t pass, void *d_meta, size_t bytes, void *stream);
+/* Host-to-host copy of the same metadata bytes into caller memory (bytes >=
+ * meta_bytes), e.g. pinned memory from which the caller uploads the pass
+ * asynchronously on a copy stream, overlapping the previous pass's kernels.
+ * The device layout is identical to what spb_plan_upload writes. */
+spb_status spb_plan_meta_copy(const spb_plan *plan, int32_t pass, void *host_dst, size_t bytes);
 
 /* ------------------------------------------------------------------ attention
  * For every packed row x and query head h:

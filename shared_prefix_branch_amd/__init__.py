@@ -16,6 +16,7 @@ import numpy as np
 
 __all__ = [
     "SpbError", "lib", "library_path", "fingerprint", "Plan", "pack_pass", "branch_attention",
+    "PreparedAttention", "PreparedScore",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
     "EXPORTED_SYMBOLS",
 ]
@@ -28,7 +29,7 @@ EXPORTED_SYMBOLS = [
     "spb_last_error", "spb_fingerprint", "spb_pack_opts_default", "spb_pack_pass", "spb_plan_free",
     "spb_plan_num_passes", "spb_plan_info", "spb_plan_rows", "spb_plan_branches", "spb_plan_inputs",
     "spb_plan_visible",
-    "spb_plan_upload", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
+    "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
     "spb_score_finalize",
 ]
 
@@ -105,6 +106,7 @@ def lib() -> ctypes.CDLL:
         L.spb_plan_inputs.argtypes = [ctypes.c_void_p, _i64p, _i32p]
         L.spb_plan_visible.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p]
         L.spb_plan_upload.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.spb_plan_meta_copy.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]
         L.spb_branch_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.POINTER(_AttnArgs), ctypes.c_void_p]
         L.spb_score_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -198,6 +200,14 @@ class Plan:
         _check(lib().spb_plan_upload(self._h, pass_, ctypes.c_void_p(d_meta.data_ptr()),
                                      d_meta.numel() * d_meta.element_size(), ctypes.c_void_p(_stream_handle(stream))))
 
+    def meta_copy(self, pass_: int, host_dst):
+        """Copies pass metadata into a host buffer (a CPU tensor, e.g. pinned, or a numpy array)."""
+        if hasattr(host_dst, "data_ptr"):
+            ptr, n = host_dst.data_ptr(), host_dst.numel() * host_dst.element_size()
+        else:
+            ptr, n = host_dst.ctypes.data, host_dst.nbytes
+        _check(lib().spb_plan_meta_copy(self._h, pass_, ctypes.c_void_p(ptr), n))
+
 
 def pack_pass(problem, token_budget: int = 16384, floors: bool = True, **limits) -> Plan:
     """Packs a logical problem (any object with the CSR fields of spb_problem)."""
@@ -231,26 +241,41 @@ def _dtype_code(t) -> int:
     raise SpbError(-3, f"unsupported tensor dtype {t.dtype}")
 
 
+class PreparedAttention:
+    """spb_branch_attention with its arguments marshalled once: calling it
+    with a plan (same pass shapes) and a stream only enqueues the kernel."""
+
+    def __init__(self, pass_: int, d_meta, q, k, v, o, softmax_scale: float = 0.0,
+                 scales: Sequence[float] = (1.0, 1.0, 1.0)):
+        for t in (q, k, v, o):
+            if not t.is_contiguous():
+                raise SpbError(-1, "tensors must be contiguous")
+        A = _AttnArgs()
+        A.q, A.k, A.v, A.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+        A.in_dtype = _dtype_code(q)
+        if _dtype_code(k) != A.in_dtype or _dtype_code(v) != A.in_dtype:
+            raise SpbError(-3, "q, k and v must share one dtype")
+        A.out_dtype = _dtype_code(o)
+        A.hq, A.hkv, A.head_dim = int(q.shape[1]), int(k.shape[1]), int(q.shape[2])
+        if k.shape[2] != A.head_dim or o.shape[1] != A.hq or o.shape[2] != A.head_dim or v.shape != k.shape:
+            raise SpbError(-1, "q/k/v/o shapes disagree")
+        A.softmax_scale = float(softmax_scale)
+        A.s_q, A.s_k, A.s_v = (float(s) for s in scales)
+        A.rows = int(min(q.shape[0], k.shape[0], v.shape[0], o.shape[0]))
+        self.args = A
+        self.pass_ = pass_
+        self.meta = ctypes.c_void_p(d_meta.data_ptr())
+        self.fn = lib().spb_branch_attention
+
+    def __call__(self, plan: Plan, stream=None):
+        _check(self.fn(plan.handle, self.pass_, self.meta, ctypes.byref(self.args),
+                       ctypes.c_void_p(_stream_handle(stream))))
+
+
 def branch_attention(plan: Plan, pass_: int, d_meta, q, k, v, o, softmax_scale: float = 0.0,
                      scales: Sequence[float] = (1.0, 1.0, 1.0), stream=None):
     """q [rows, hq, d], k/v [rows, hkv, d], o [rows, hq, d]: contiguous device tensors."""
-    for t in (q, k, v, o):
-        if not t.is_contiguous():
-            raise SpbError(-1, "tensors must be contiguous")
-    A = _AttnArgs()
-    A.q, A.k, A.v, A.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
-    A.in_dtype = _dtype_code(q)
-    if _dtype_code(k) != A.in_dtype or _dtype_code(v) != A.in_dtype:
-        raise SpbError(-3, "q, k and v must share one dtype")
-    A.out_dtype = _dtype_code(o)
-    A.hq, A.hkv, A.head_dim = int(q.shape[1]), int(k.shape[1]), int(q.shape[2])
-    if k.shape[2] != A.head_dim or o.shape[1] != A.hq or o.shape[2] != A.head_dim or v.shape != k.shape:
-        raise SpbError(-1, "q/k/v/o shapes disagree")
-    A.softmax_scale = float(softmax_scale)
-    A.s_q, A.s_k, A.s_v = (float(s) for s in scales)
-    A.rows = int(min(q.shape[0], k.shape[0], v.shape[0], o.shape[0]))
-    _check(lib().spb_branch_attention(plan.handle, pass_, ctypes.c_void_p(d_meta.data_ptr()), ctypes.byref(A),
-                                      ctypes.c_void_p(_stream_handle(stream))))
+    PreparedAttention(pass_, d_meta, q, k, v, o, softmax_scale, scales)(plan, stream)
 
 
 def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int) -> int:
@@ -259,40 +284,54 @@ def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int) -
     return int(n.value)
 
 
+class PreparedScore:
+    """spb_score_options with its arguments marshalled once."""
+
+    def __init__(self, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual):
+        import torch
+        if lm_head.dtype != torch.bfloat16:
+            raise SpbError(-3, "lm_head must be bfloat16")
+        for t in (lp, p, residual):
+            if t.dtype != torch.float32:
+                raise SpbError(-3, "outputs must be float32")
+        S = _ScoreArgs()
+        S.hidden = hidden.data_ptr()
+        S.h_dtype = _dtype_code(hidden)
+        S.hidden_dim = int(hidden.shape[1])
+        S.rows = int(hidden.shape[0])
+        if int(lm_head.shape[1]) != S.hidden_dim:
+            raise SpbError(-1, "lm_head and hidden disagree on the hidden size")
+        S.lm_head = lm_head.data_ptr()
+        S.vocab = int(lm_head.shape[0])
+        S.workspace = workspace.data_ptr()
+        S.workspace_bytes = workspace.numel() * workspace.element_size()
+        S.lp = ctypes.cast(ctypes.c_void_p(lp.data_ptr()), _f32p)
+        S.p = ctypes.cast(ctypes.c_void_p(p.data_ptr()), _f32p)
+        S.residual = ctypes.cast(ctypes.c_void_p(residual.data_ptr()), _f32p)
+        self.args = S
+        self.pass_ = pass_
+        self.meta = ctypes.c_void_p(d_meta.data_ptr())
+        self.fn = lib().spb_score_options
+
+    def __call__(self, plan: Plan, stream=None, gemm_events=None):
+        S = self.args
+        if gemm_events is not None:
+            for ev in gemm_events:
+                if not ev.cuda_event:
+                    raise SpbError(-1, "timing events must be created (recorded once) before use")
+            S.gemm_event_begin, S.gemm_event_end = gemm_events[0].cuda_event, gemm_events[1].cuda_event
+        else:
+            S.gemm_event_begin = S.gemm_event_end = None
+        _check(self.fn(plan.handle, self.pass_, self.meta, ctypes.byref(S), ctypes.c_void_p(_stream_handle(stream))))
+
+
 def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual, stream=None,
                   gemm_events=None):
     """hidden [rows, H] (bf16/f32), lm_head [V, H] bf16, workspace uint8 device buffer,
     lp/p [n_options] and residual [n_branches] float32 device tensors.
     gemm_events: optional pair of created ``torch.cuda.Event`` recorded on the
     stream around the lm-head GEMM kernel."""
-    import torch
-    if lm_head.dtype != torch.bfloat16:
-        raise SpbError(-3, "lm_head must be bfloat16")
-    for t in (lp, p, residual):
-        if t.dtype != torch.float32:
-            raise SpbError(-3, "outputs must be float32")
-    S = _ScoreArgs()
-    S.hidden = hidden.data_ptr()
-    S.h_dtype = _dtype_code(hidden)
-    S.hidden_dim = int(hidden.shape[1])
-    S.rows = int(hidden.shape[0])
-    if int(lm_head.shape[1]) != S.hidden_dim:
-        raise SpbError(-1, "lm_head and hidden disagree on the hidden size")
-    S.lm_head = lm_head.data_ptr()
-    S.vocab = int(lm_head.shape[0])
-    S.workspace = workspace.data_ptr()
-    S.workspace_bytes = workspace.numel() * workspace.element_size()
-    S.lp = ctypes.cast(ctypes.c_void_p(lp.data_ptr()), _f32p)
-    S.p = ctypes.cast(ctypes.c_void_p(p.data_ptr()), _f32p)
-    S.residual = ctypes.cast(ctypes.c_void_p(residual.data_ptr()), _f32p)
-    if gemm_events is not None:
-        for ev in gemm_events:
-            if not ev.cuda_event:
-                raise SpbError(-1, "timing events must be created (recorded once) before use")
-        S.gemm_event_begin = gemm_events[0].cuda_event
-        S.gemm_event_end = gemm_events[1].cuda_event
-    _check(lib().spb_score_options(plan.handle, pass_, ctypes.c_void_p(d_meta.data_ptr()), ctypes.byref(S),
-                                   ctypes.c_void_p(_stream_handle(stream))))
+    PreparedScore(pass_, d_meta, hidden, lm_head, workspace, lp, p, residual)(plan, stream, gemm_events)
 
 
 def score_finalize(plan: Plan, lp_per_pass, p_per_pass, res_per_pass) -> dict:

@@ -426,10 +426,10 @@ void build_blob(PassPlan &P, int pass) {
 // Workspace of spb_score_options: slice partials, captured logits, LSE per
 // row, gathered hidden states.  Returns the total; off[] gets the offsets.
 size_t score_workspace_layout(int n_scored, int n_targets, int vocab, int hidden_dim, size_t *off) {
-  int n_chunks = 0, mw = 0;
-  head_m_layout(n_scored, &n_chunks, &mw);
+  int n_chunks = 0, mb = 0;
+  head_m_layout(n_scored, &n_chunks, &mb);
   size_t sizes[4] = {(size_t)n_scored * n_vocab_slices(vocab) * 2 * sizeof(float), (size_t)n_targets * sizeof(float),
-                     (size_t)n_scored * sizeof(float), (size_t)n_chunks * 64 * mw * (size_t)hidden_dim * 2};
+                     (size_t)n_scored * sizeof(float), (size_t)n_chunks * 32 * mb * (size_t)hidden_dim * 2};
   size_t o = 0;
   for (int i = 0; i < 4; ++i) {
     if (off) off[i] = o;
@@ -698,6 +698,16 @@ spb_status spb_plan_upload(const spb_plan *plan, int32_t pass, void *d_meta, siz
   if (bytes < P.blob.size()) return fail(SPB_ERR_SIZE, "metadata needs %zu bytes, buffer has %zu", P.blob.size(), bytes);
   hipError_t e = hipMemcpyAsync(d_meta, P.blob.data(), P.blob.size(), hipMemcpyHostToDevice, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SPB_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  return ok();
+}
+
+spb_status spb_plan_meta_copy(const spb_plan *plan, int32_t pass, void *host_dst, size_t bytes) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  const PassPlan &P = plan->passes[pass];
+  if (!host_dst) return fail(SPB_ERR_ARG, "host_dst is NULL");
+  if (bytes < P.blob.size()) return fail(SPB_ERR_SIZE, "metadata needs %zu bytes, buffer has %zu", P.blob.size(), bytes);
+  std::memcpy(host_dst, P.blob.data(), P.blob.size());
   return ok();
 }
 

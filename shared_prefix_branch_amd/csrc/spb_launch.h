@@ -36,15 +36,15 @@ struct ScoreLaunch {
 
 inline int n_vocab_slices(int vocab) { return (vocab + 255) / 256; }
 
-// Scored rows per lm-head work group: n_chunks chunks of 64*mw rows (mw in
-// 1..4), the fewest chunks of at most 256 rows, each as small as possible.
-inline void head_m_layout(int M, int *n_chunks, int *mw) {
+// Scored rows per lm-head work group: n_chunks chunks of 32*mb rows (mb in
+// 1..8), the fewest chunks of at most 256 rows, each as small as possible.
+inline void head_m_layout(int M, int *n_chunks, int *mb) {
   int n = (M + 255) / 256;
   if (n < 1) n = 1;
   int per = (M + n - 1) / n;
-  int w = (per + 63) / 64;
+  int b = (per + 31) / 32;
   *n_chunks = n;
-  *mw = w < 1 ? 1 : (w > 4 ? 4 : w);
+  *mb = b < 1 ? 1 : (b > 8 ? 8 : b);
 }
 
 int launch_attention(const AttnLaunch &a, void *stream);

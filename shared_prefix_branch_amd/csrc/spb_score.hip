@@ -13,11 +13,12 @@
 //   bf16 rows, zero-padded to the GEMM's row tiling.
 // Kernel 1 (head_lse_kernel): Z^T[v, m] = W[v, :] . h[m, :] on MFMA 32x32x16
 //   bf16 with f32 accumulation, one work group per (256-row vocabulary slice,
-//   64..256 scored rows); W and h tiles of 32 hidden elements are staged
-//   through registers two stages ahead into a double-buffered, XOR-swizzled
-//   LDS ring.  Logits never leave registers: the epilogue writes, per (row,
-//   slice), the slice max and sum of exp(z - max), and stores the logits of
-//   the option tokens the row predicts.
+//   32..256 scored rows), each wave a 64-row vocabulary strip against all the
+//   group's rows; W and h tiles of 64 hidden elements are copied global ->
+//   LDS asynchronously into XOR-swizzled rings.  Logits never leave
+//   registers: the epilogue writes, per (row, slice), the slice max and sum
+//   of exp(z - max), and stores the logits of the option tokens the row
+//   predicts.
 // Kernel 2 (finalize_kernel): one wave per branch merges a row's slices in
 //   slice order into LSE, sums each option's chain of log-probabilities in
 //   token order, and renormalises.
@@ -97,67 +98,69 @@ struct HeadParams {
   float *part, *tz;
 };
 
-template <int MW>
+// Work group: 256 vocabulary rows x TM = 32*MB scored rows; wave w owns
+// vocabulary rows w*64 .. +64 (two 32-row blocks) against all TM rows, so
+// only the h tile is shared between waves.
+template <int MB>
 struct HeadTile {
-  static constexpr int TM = 64 * MW;                // scored rows per work group
+  static constexpr int TM = 32 * MB;                // scored rows per work group
   static constexpr int WBYTES = kVocabTile * 128;   // W stage: 256 rows x 64 bf16
   static constexpr int HBYTES = TM * 128;           // h stage: TM rows x 64 bf16
   static constexpr int RW = 3;                      // W ring: two stages in flight
   static constexpr int RH = 2;                      // h ring: one stage in flight (L2-resident)
-  static constexpr int LDS = RW * WBYTES + RH * HBYTES;  // 112..160 KB
-  static constexpr int NW = 8;                      // W copies per wave per stage
-  static constexpr int NH = 2 * MW;                 // h copies per wave per stage
+  static constexpr int LDS = RW * WBYTES + RH * HBYTES;  // <= 160 KB
+  static constexpr int NW = 8;                      // W copies per wave per stage (its own 64 rows)
+  static constexpr int NH = MB;                     // h copies per wave per stage
+  static_assert(LDS <= 160 * 1024, "LDS ring too large");
+  static_assert(4 * TM * 2 * 4 <= LDS, "epilogue buffer must fit in the ring");
 };
 
-// Fragments of one 16-element K step: A = 4 vocabulary blocks, B = MW
-// scored-row blocks.
-template <int MW>
+// Fragments of one 16-element K step: A = the wave's 2 vocabulary blocks,
+// B = the MB scored-row blocks.
+template <int MB>
 struct Frags {
-  bf16x8_t a[4];
-  bf16x8_t b[MW];
+  bf16x8_t a[2];
+  bf16x8_t b[MB];
 };
 
 // K step ks (0..3) of a 64-element stage: lane (qi, half) takes elements
 // 16 ks + 8 half .. +8 of its row, i.e. chunk 2 ks + half.
-template <int MW>
-__device__ __attribute__((always_inline)) inline void head_frags(Frags<MW> &f, const u32x4 *Wb, const u32x4 *Hb,
-                                                                 int ks, int wv, int wm, int qi, int half) {
+template <int MB>
+__device__ __attribute__((always_inline)) inline void head_frags(Frags<MB> &f, const u32x4 *Wb, const u32x4 *Hb,
+                                                                 int ks, int wave, int qi, int half) {
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) {
-    u32x4 u = Wb[swz(wv * 128 + vb * 32 + qi, ks * 2 + half)];
+  for (int vb = 0; vb < 2; ++vb) {
+    u32x4 u = Wb[swz(wave * 64 + vb * 32 + qi, ks * 2 + half)];
     f.a[vb] = *(bf16x8_t *)&u;
   }
 #pragma unroll
-  for (int mb = 0; mb < MW; ++mb) {
-    u32x4 u = Hb[swz(wm * 32 * MW + mb * 32 + qi, ks * 2 + half)];
+  for (int mb = 0; mb < MB; ++mb) {
+    u32x4 u = Hb[swz(mb * 32 + qi, ks * 2 + half)];
     f.b[mb] = *(bf16x8_t *)&u;
   }
 }
 
-template <int MW>
-__device__ __attribute__((always_inline)) inline void head_mfma(f32x16 (&acc)[4][MW], const Frags<MW> &f) {
+template <int MB>
+__device__ __attribute__((always_inline)) inline void head_mfma(f32x16 (&acc)[2][MB], const Frags<MB> &f) {
 #pragma unroll
-  for (int mb = 0; mb < MW; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+    for (int vb = 0; vb < 2; ++vb)
       acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0);
 }
 
-// MW: 32-row m blocks per wave; a work group covers 256 vocabulary rows x
-// 64*MW scored rows.  Wave (wv, wm) owns vocabulary rows wv*128 .. +128 and
-// scored rows wm*32*MW .. +32*MW.
-//
 // Pipeline over stages of 64 hidden elements (four 16-element K steps), so
 // every row of a stage is one whole 128-byte line and each global request
 // carries a full line.  Stage j's W tile is copied straight into LDS slot
-// j % 3 two stages ahead of use; its h tile (small and shared by every work
-// group, so L2-resident) into slot j % 2 one stage ahead.  Within a stage the
-// fragments of K step t+1 are read while step t is multiplied.
-template <int MW>
+// j % 3 two stages ahead of use (each wave copies the 64 rows it alone
+// reads); its h tile (small and shared by every work group, so L2-resident)
+// into slot j % 2 one stage ahead.  Within a stage the fragments of K step
+// t+1 are read while step t is multiplied.
+template <int MB>
 __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
-  using T = HeadTile<MW>;
+  using T = HeadTile<MB>;
   constexpr int TM = T::TM;
-  __shared__ __attribute__((aligned(16))) char lds[T::LDS];
+  __shared__ __attribute__((aligned(1024))) char lds[T::LDS];
   char *const wring = lds;
   char *const hring = lds + T::RW * T::WBYTES;
 
@@ -173,7 +176,6 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform within the wave
   const int qi = lane & 31, half = lane >> 5;
-  const int wv = wave & 1, wm = wave >> 1;
   const int v0 = slice * kVocabTile;
   const int m0 = mchunk * TM;
 
@@ -211,18 +213,17 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
       dma16(p.hg, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
   };
 
-  f32x16 acc[4][MW];
+  f32x16 acc[2][MB];
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb)
+  for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-    for (int mb = 0; mb < MW; ++mb) acc[vb][mb] = f32x16{0.f};
+    for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x16{0.f};
 
   const int S = p.H / kKT;
   const int last = S - 1;
   // Copies past the last stage reload it into a slot nothing reads again, so
-  // the count of copies in flight is the same on every trip.  Issue order
-  // per trip s: h(s+1), then W(s+2); at the trip's end only W(s+2) may still
-  // be in flight.
+  // the count of copies in flight is the same on every trip.
+  // Trip s issues h(s+1) then W(s+2); at its end only W(s+2) may be in flight.
   issue_h(0, 0);
   issue_w(0, 0);
   issue_w(min(1, last), 1);
@@ -233,24 +234,24 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   for (int s = 0; s < S; ++s) {
     const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
     const u32x4 *Hb = (const u32x4 *)(hring + sh * T::HBYTES);
-    Frags<MW> f0, f1;
-    head_frags<MW>(f0, Wb, Hb, 0, wv, wm, qi, half);
+    Frags<MB> f0, f1;
+    head_frags<MB>(f0, Wb, Hb, 0, wave, qi, half);
     const int sw2 = sw == 0 ? 2 : sw - 1;  // slot of stage s + 2 (= s - 1 mod 3)
     issue_h(min(s + 1, last), sh ^ 1);
     issue_w(min(s + 2, last), sw2);
-    head_frags<MW>(f1, Wb, Hb, 1, wv, wm, qi, half);
+    head_frags<MB>(f1, Wb, Hb, 1, wave, qi, half);
     __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MW>(acc, f0);
+    head_mfma<MB>(acc, f0);
     __builtin_amdgcn_sched_barrier(0);
-    head_frags<MW>(f0, Wb, Hb, 2, wv, wm, qi, half);
+    head_frags<MB>(f0, Wb, Hb, 2, wave, qi, half);
     __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MW>(acc, f1);
+    head_mfma<MB>(acc, f1);
     __builtin_amdgcn_sched_barrier(0);
-    head_frags<MW>(f1, Wb, Hb, 3, wv, wm, qi, half);
+    head_frags<MB>(f1, Wb, Hb, 3, wave, qi, half);
     __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MW>(acc, f0);
+    head_mfma<MB>(acc, f0);
     __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MW>(acc, f1);
+    head_mfma<MB>(acc, f1);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<T::NW>();  // h(s+1) and W(s+1) landed
     lds_barrier();
@@ -259,18 +260,17 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   }
   wait_vmcnt<0>();  // no copy may land after the ring is reused or released
   lds_barrier();
-  float (*red)[TM][2] = (float (*)[TM][2])lds;  // [2][TM][2], reusing the ring
+  float (*red)[TM][2] = (float (*)[TM][2])lds;  // [4][TM][2], reusing the ring
 
-  // epilogue.  Lane holds column m = m0 + wm*32*MW + mb*32 + qi; register r
-  // of block vb holds vocabulary row v0 + wv*128 + vb*32 + (r/4)*8 + half*4 + r%4.
-  const int vw0 = v0 + wv * 128;
+  // epilogue.  Lane holds column m = m0 + mb*32 + qi; register r of block vb
+  // holds vocabulary row v0 + wave*64 + vb*32 + (r/4)*8 + half*4 + r%4.
+  const int vw0 = v0 + wave * 64;
+  const int nvalid = p.V - vw0;  // rows past the vocabulary (last slice only) are excluded
 #pragma unroll
-  for (int mb = 0; mb < MW; ++mb) {
-    // rows past the vocabulary (last slice only) are excluded
-    const int nvalid = p.V - vw0;
+  for (int mb = 0; mb < MB; ++mb) {
     float mx = kNegInf;
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+    for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
     float se = 0.f;
     if (mx != kNegInf) {
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb)
+      for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
@@ -288,10 +288,10 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
         }
     }
     se = se + __shfl_xor(se, 32);
-    const int ml = wm * 32 * MW + mb * 32 + qi;
+    const int ml = mb * 32 + qi;
     if (half == 0) {
-      red[wv][ml][0] = mx;
-      red[wv][ml][1] = se;
+      red[wave][ml][0] = mx;
+      red[wave][ml][1] = se;
     }
     // capture the logits of the tokens this row predicts
     const int m = m0 + ml;
@@ -299,13 +299,13 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
       const int t0 = p.tgt_off[m], t1 = p.tgt_off[m + 1];
       for (int t = t0; t < t1; ++t) {
         const int rel = p.tgt_tok[t] - vw0;
-        if (rel < 0 || rel >= 128) continue;
+        if (rel < 0 || rel >= 64) continue;
         const int rr = rel & 31;
         if (((rr >> 2) & 1) != half) continue;
         const int vbt = rel >> 5, rt = (rr >> 3) * 4 + (rr & 3);
         float val = 0.f;
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb)
+        for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) val = (vb == vbt && r == rt) ? acc[vb][mb][r] : val;
         p.tz[t] = val;
@@ -313,16 +313,21 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
     }
   }
   __syncthreads();
+  // merge the four waves' (max, sum) in wave order
   for (int ml = tid; ml < TM; ml += kThreads) {
     const int m = m0 + ml;
     if (m < p.M) {
-      const float a = red[0][ml][0], c = red[1][ml][0];
-      const float M = fmaxf(a, c);
-      const float Ssum = (a == kNegInf ? 0.f : red[0][ml][1] * __expf(a - M)) +
-                         (c == kNegInf ? 0.f : red[1][ml][1] * __expf(c - M));
+      float M = red[0][ml][0], S = red[0][ml][1];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float a = red[w][ml][0];
+        const float Mn = fmaxf(M, a);
+        S = (M == kNegInf ? 0.f : S * __expf(M - Mn)) + (a == kNegInf ? 0.f : red[w][ml][1] * __expf(a - Mn));
+        M = Mn;
+      }
       float *dst = p.part + ((size_t)m * p.n_slices + slice) * 2;
       dst[0] = M;
-      dst[1] = Ssum;
+      dst[1] = S;
     }
   }
 }
@@ -387,9 +392,9 @@ __global__ __launch_bounds__(64) void finalize_kernel(FinParams f) {
 
 int launch_score(const ScoreLaunch &a, void *stream) {
   hipStream_t s = (hipStream_t)stream;
-  int n_chunks = 0, mw = 0;
-  head_m_layout(a.n_scored, &n_chunks, &mw);
-  const int m_pad = n_chunks * 64 * mw;
+  int n_chunks = 0, mb = 0;
+  head_m_layout(a.n_scored, &n_chunks, &mb);
+  const int m_pad = n_chunks * 32 * mb;
   GatherParams g;
   g.hidden = a.hidden;
   g.scored = (const int32_t *)a.scored;
@@ -425,11 +430,15 @@ int launch_score(const ScoreLaunch &a, void *stream) {
     e = (int)hipEventRecord((hipEvent_t)a.ev_begin, s);
     if (e) return e;
   }
-  switch (mw) {
+  switch (mb) {
     case 1: hipLaunchKernelGGL(head_lse_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(head_lse_kernel<2>, grid, block, 0, s, p); break;
     case 3: hipLaunchKernelGGL(head_lse_kernel<3>, grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL(head_lse_kernel<4>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(head_lse_kernel<4>, grid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL(head_lse_kernel<5>, grid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL(head_lse_kernel<6>, grid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL(head_lse_kernel<7>, grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL(head_lse_kernel<8>, grid, block, 0, s, p); break;
   }
   e = (int)hipGetLastError();
   if (e) return e;

@@ -6,6 +6,14 @@ the lm head.  ``Job`` assembles each pass's token-major buffers from them by
 the plan's placement, then per pass enqueues: metadata upload, branch
 attention, option scoring.  The host floor join runs after all passes.
 Nothing here computes the method: every step runs in libspb.
+
+Transfers and pipelining: every pass's metadata is staged in pinned host
+memory and uploaded on a copy stream; pass k's upload waits only until the
+previous run's pass k has finished with the buffer, and pass k's kernels wait
+only for that upload, so uploads overlap other passes' kernels.  All passes
+write their option scores into one device buffer, copied back in one transfer
+at the end of the run; results are double-buffered, so a caller may enqueue
+run i+1 before it joins run i and the GPU never waits on the host.
 """
 from __future__ import annotations
 
@@ -14,7 +22,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from . import Plan, branch_attention, score_finalize, score_options, score_workspace_bytes
+from . import Plan, PreparedAttention, PreparedScore, score_finalize, score_workspace_bytes
 
 
 @dataclasses.dataclass
@@ -27,9 +35,10 @@ class PassBuffers:
     hidden: object
     meta: object
     workspace: object
-    lp: object
+    lp: object        # score outputs of the result slot the last run wrote
     p: object
     residual: object
+    slots: list = None  # per result slot: (lp, p, residual) device views
 
 
 Provider = Callable[[int], Tuple[object, object, object, object]]
@@ -49,6 +58,24 @@ class Job:
         self.scales = tuple(scales)
         self.row_off, self.floor_q = plan.inputs()
         self.passes: List[PassBuffers] = []
+        self.copy_stream = None
+        self._set = 0                  # pinned metadata set staged last
+        self._set_done = [None, None]  # per metadata set: event after its last upload
+        self._slot = 1                 # result slot of the last run
+        self._slot_plan = [None, None]
+        self._slot_done = [None, None]  # per result slot: event after its copy back
+        self._pass_done: List = []      # per pass: event after the last run's kernels
+        self._head = None               # lm head the prepared score calls point at
+        self._attn: List = []
+        self._score: List = []
+
+    # -- buffers ---------------------------------------------------------------
+    def _result_sizes(self):
+        out = []
+        for k in range(self.plan.n_passes):
+            inf = self.plan.info(k)
+            out.append((max(1, inf["n_options"]), max(1, inf["n_branches"])))
+        return out
 
     def _alloc(self, k: int) -> PassBuffers:
         t = self.torch
@@ -64,10 +91,7 @@ class Job:
             t.empty((n, self.hkv, self.d), dtype=self.qkv_dtype, device=dev),
             t.empty((n, self.hq, self.d), dtype=self.out_dtype, device=dev),
             t.empty((n, self.H), dtype=self.hidden_dtype, device=dev),
-            meta, ws,
-            t.empty(max(1, inf["n_options"]), dtype=t.float32, device=dev),
-            t.empty(max(1, inf["n_options"]), dtype=t.float32, device=dev),
-            t.empty(max(1, inf["n_branches"]), dtype=t.float32, device=dev))
+            meta, ws, None, None, None, [])
 
     def fill(self, k: int, buf: PassBuffers, provider: Provider, cache: Dict[int, tuple]):
         """Gathers pass k's rows from the per-input activations."""
@@ -93,43 +117,143 @@ class Job:
 
     def load(self, provider: Provider):
         """Allocates and fills every pass."""
+        t = self.torch
         cache: Dict[int, tuple] = {}
+        sizes = self._result_sizes()
+        total = sum(2 * no + nb for no, nb in sizes)
+        self.results = [t.empty(total, dtype=t.float32, device=self.device) for _ in range(2)]
+        self.results_host = [t.empty(total, dtype=t.float32, pin_memory=True) for _ in range(2)]
+        # two pinned metadata sets: the next batch is staged into one while
+        # the other may still be uploading
+        self.meta_host = [[t.empty(self.plan.info(k)["meta_bytes"], dtype=t.uint8, pin_memory=True)
+                           for k in range(self.plan.n_passes)] for _ in range(2)]
         self.passes = []
+        off = 0
         for k in range(self.plan.n_passes):
             buf = self._alloc(k)
+            no, nb = sizes[k]
+            for r in range(2):
+                res = self.results[r]
+                buf.slots.append((res[off:off + no], res[off + no:off + 2 * no], res[off + 2 * no:off + 2 * no + nb]))
+            buf.lp, buf.p, buf.residual = buf.slots[0]
+            off += 2 * no + nb
             self.fill(k, buf, provider, cache)
             self.passes.append(buf)
+        self._attn = [PreparedAttention(k, b.meta, b.q, b.k, b.v, b.o, scales=self.scales)
+                      for k, b in enumerate(self.passes)]
+        self._pass_done = [None] * len(self.passes)
 
-    def run_pass(self, k: int, lm_head, stream=None, attention=True, scoring=True, marks=None):
-        """Enqueues pass k.  ``marks``, if given, holds four created events:
-        recorded on ``stream`` around the attention kernel (0, 1) and, by the
-        library, around the lm-head GEMM kernel (2, 3)."""
-        buf = self.passes[k]
-        self.plan.upload(k, buf.meta, stream)
-        if marks is not None:
-            marks[0].record(stream)
-        if attention:
-            branch_attention(self.plan, k, buf.meta, buf.q, buf.k, buf.v, buf.o, scales=self.scales, stream=stream)
-        if marks is not None:
-            marks[1].record(stream)
-        if scoring:
-            score_options(self.plan, k, buf.meta, buf.hidden, lm_head, buf.workspace, buf.lp, buf.p, buf.residual,
-                          stream=stream, gemm_events=None if marks is None else (marks[2], marks[3]))
+    def _prepare_head(self, lm_head):
+        if self._head is not lm_head:
+            self._score = [[PreparedScore(k, b.meta, b.hidden, lm_head, b.workspace, *b.slots[r]) for r in range(2)]
+                           for k, b in enumerate(self.passes)]
+            self._head = lm_head
 
-    def run(self, lm_head, stream=None, attention=True, scoring=True, marks=None):
-        for k in range(self.plan.n_passes):
-            self.run_pass(k, lm_head, stream, attention, scoring, None if marks is None else marks[k])
+    # -- metadata ------------------------------------------------------------
+    def stage_host(self, plan: Optional[Plan] = None):
+        """Copies a plan's metadata (by default the job's) into the pinned set
+        not staged last; host work that can run while the GPU is busy.  The
+        plan must have this job's pass shapes.  Returns the token ``run``
+        takes."""
+        plan = self.plan if plan is None else plan
+        self._set ^= 1
+        if self._set_done[self._set] is not None:
+            self._set_done[self._set].synchronize()  # its previous upload has left the buffers
+        for k in range(plan.n_passes):
+            plan.meta_copy(k, self.meta_host[self._set][k])
+        return plan, self._set
 
-    def pass_outputs(self, k: int):
-        """Host copies of pass k's lp, p, residual."""
-        inf = self.plan.info(k)
-        b = self.passes[k]
-        return (b.lp[:inf["n_options"]].cpu().numpy(), b.p[:inf["n_options"]].cpu().numpy(),
-                b.residual[:inf["n_branches"]].cpu().numpy())
+    def _upload(self, which: int, stream):
+        """Uploads pinned set ``which`` on the copy stream, pass k after the
+        previous run's pass-k kernels (which read the old metadata); returns
+        one event per pass."""
+        t = self.torch
+        if self.copy_stream is None:
+            self.copy_stream = t.cuda.Stream(device=self.device)
+        cs = self.copy_stream
+        events = []
+        with t.cuda.stream(cs):
+            for k in range(len(self.passes)):
+                if self._pass_done[k] is not None:
+                    cs.wait_event(self._pass_done[k])
+                else:
+                    cs.wait_stream(stream)
+                self.passes[k].meta.copy_(self.meta_host[which][k], non_blocking=True)
+                ev = t.cuda.Event()
+                ev.record(cs)
+                events.append(ev)
+        if events:
+            self._set_done[which] = events[-1]
+        return events
 
-    def finalize(self) -> dict:
-        outs = [self.pass_outputs(k) for k in range(self.plan.n_passes)]
-        return score_finalize(self.plan, [o[0] for o in outs], [o[1] for o in outs], [o[2] for o in outs])
+    # -- running -------------------------------------------------------------
+    def run(self, lm_head, stream=None, attention=True, scoring=True, marks=None, staged=None):
+        """Enqueues every pass of a plan, then the copy of its scores back.
+        ``staged``: a ``stage_host`` token (the plan to run and its pinned
+        metadata); None stages the job's plan now.  ``marks``, if given, holds
+        per pass four created events: recorded on ``stream`` around the
+        attention kernel (0, 1) and, by the library, around the lm-head GEMM
+        kernel (2, 3)."""
+        t = self.torch
+        stream = stream if stream is not None else t.cuda.current_stream()
+        if staged is None:
+            staged = self.stage_host()
+        plan, which = staged
+        self.plan = plan
+        self._prepare_head(lm_head)
+        r = self._slot ^ 1
+        if self._slot_done[r] is not None:
+            self._slot_done[r].synchronize()  # its previous copy back has landed
+        uploaded = self._upload(which, stream)
+        for k, buf in enumerate(self.passes):
+            stream.wait_event(uploaded[k])
+            mk = None if marks is None else marks[k]
+            if mk is not None:
+                mk[0].record(stream)
+            if attention:
+                self._attn[k](plan, stream)
+            if mk is not None:
+                mk[1].record(stream)
+            if scoring:
+                self._score[k][r](plan, stream, None if mk is None else (mk[2], mk[3]))
+            done = t.cuda.Event()
+            done.record(stream)
+            self._pass_done[k] = done
+            buf.lp, buf.p, buf.residual = buf.slots[r]
+        with t.cuda.stream(stream):
+            self.results_host[r].copy_(self.results[r], non_blocking=True)
+        ev = t.cuda.Event()
+        ev.record(stream)
+        self._slot, self._slot_plan[r], self._slot_done[r] = r, plan, ev
+
+    def finalize(self, slot: Optional[int] = None, copy: bool = False) -> dict:
+        """Waits for a run's scores (by default the last run's) and joins the
+        floors on the host.  copy: fetch the slot's device scores again (after
+        the caller rewrote them)."""
+        t = self.torch
+        r = self._slot if slot is None else slot
+        if copy:
+            stream = t.cuda.current_stream()
+            with t.cuda.stream(stream):
+                self.results_host[r].copy_(self.results[r], non_blocking=True)
+            stream.synchronize()
+        else:
+            self._slot_done[r].synchronize()
+        plan = self._slot_plan[r]
+        host = self.results_host[r].numpy()
+        lps, ps, rs = [], [], []
+        off = 0
+        for k, (no, nb) in enumerate(self._result_sizes()):
+            inf = plan.info(k)
+            lps.append(host[off:off + inf["n_options"]])
+            ps.append(host[off + no:off + no + inf["n_options"]])
+            rs.append(host[off + 2 * no:off + 2 * no + inf["n_branches"]])
+            off += 2 * no + nb
+        return score_finalize(plan, lps, ps, rs)
+
+    @property
+    def last_slot(self) -> int:
+        return self._slot
 
     def attention_by_logical_row(self, rows: Sequence[int]) -> Dict[int, object]:
         """Attention output rows (host float32 [hq, d]) keyed by logical row; a

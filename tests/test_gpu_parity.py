@@ -44,7 +44,7 @@ def test_tiny_config_chained_hidden_is_attention_output():
     hid = buf.o.reshape(buf.o.shape[0], -1).contiguous()
     spb.score_options(case.plan, 0, buf.meta, hid, W, buf.workspace, buf.lp, buf.p, buf.residual)
     torch.cuda.synchronize()
-    res = job.finalize()
+    res = job.finalize(copy=True)
     lay = OT.build_layout(case.prob, floors=True)
     att = {}
     for n, li in enumerate(lay.inputs):

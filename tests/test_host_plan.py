@@ -209,6 +209,28 @@ def test_upload_rejects_small_or_misaligned_buffers():
     assert L.spb_plan_upload(plan.handle, 0, ctypes.c_void_p(4097), need, None) == -1
 
 
+def test_meta_copy_matches_the_pass_layout():
+    # the host copy carries the same metadata blob spb_plan_upload sends: header
+    # magic "SPB1", the pass index and its counts, and the plan's row placement
+    prob = synth.make_problem("random", 17, vocab=32, n_inputs=4, n_questions=3, max_content=20,
+                              max_len=5, max_options=3, max_option_tokens=2)
+    plan = spb.pack_pass(prob, token_budget=60)
+    for k in range(plan.n_passes):
+        inf = plan.info(k)
+        buf = np.zeros(inf["meta_bytes"] + 64, np.uint8)
+        plan.meta_copy(k, buf)
+        head = buf[:48].view(np.int32)
+        assert head[0] == 0x53504231 and head[2] == k
+        assert head[3] == inf["n_tokens"] and head[4] == inf["n_tiles"]
+        assert head[5] == inf["n_branches"] and head[6] == inf["n_options"] and head[7] == inf["n_scored_rows"]
+        assert not buf[inf["meta_bytes"]:].any()  # nothing written past meta_bytes
+    L = spb.lib()
+    small = np.zeros(plan.info(0)["meta_bytes"] - 1, np.uint8)
+    assert L.spb_plan_meta_copy(plan.handle, 0, ctypes.c_void_p(small.ctypes.data), small.nbytes) == -4
+    assert L.spb_plan_meta_copy(plan.handle, 0, None, 1 << 20) == -1
+    assert L.spb_plan_meta_copy(plan.handle, plan.n_passes, ctypes.c_void_p(small.ctypes.data), small.nbytes) == -1
+
+
 def test_score_finalize_joins_floors_in_logical_order():
     prob = synth.make_problem("random", 41, vocab=16, n_inputs=5, n_questions=3, max_content=10,
                               max_len=4, max_options=3, max_option_tokens=2)
