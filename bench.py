@@ -22,6 +22,11 @@ summary in profiles/ (null when the kernel source has changed since).
 
 runs only a plain 1 GiB device-to-device copy, three times, for scaling the
 FETCH_SIZE / WRITE_SIZE counters.
+
+    python bench.py --head-sweep 8,16,56,128,256 [--steps K --warmup W]
+
+times the lm head alone (news head shape) at each scored-row count and prints
+one JSON line per count with its HBM and MFMA fractions.
 """
 from __future__ import annotations
 
@@ -37,6 +42,8 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# lm-head ridge in scored rows per W stream: the head does M flop per W byte
+HEAD_RIDGE_ROWS = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # 312.5
 HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = ("shared_prefix_branch_amd/csrc/spb_score.hip", "shared_prefix_branch_amd/csrc/spb_launch.h")
 TRAFFIC_SUMMARY = "profiles/head_lse_kernel_news_traffic.md"
@@ -52,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-sample-inputs", type=int, default=0,
                     help="contents in the oracle's sample (0: all of the workload's)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--head-sweep", default="",
+                    help="comma-separated scored-row counts: time the lm head alone on the news head shape")
     return ap.parse_args()
 
 
@@ -100,6 +109,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.head_sweep:
+        head_sweep([int(x) for x in args.head_sweep.split(",")], args.steps, args.warmup)
         return
     import torch
     import synth
@@ -192,7 +204,7 @@ def main():
     att_tflops = att_flops.sum() / (att_ms.sum() * 1e-3) / 1e12
     head_tflops = head_flops.sum() / (head_ms.sum() * 1e-3) / 1e12
     head_gbs = head_bytes.sum() / (head_ms.sum() * 1e-3) / 1e9
-    head_bound = "mfma" if M.mean() > PEAK_BF16_TFLOPS / PEAK_HBM_GBS else "hbm"
+    head_bound = "mfma" if M.mean() > HEAD_RIDGE_ROWS else "hbm"
     traffic, traffic_src = measured_traffic() if args.workload == "news" else (None, "counters taken on news only")
     if head_bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(head_tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -232,6 +244,59 @@ def main():
         n_cpu = args.cpu_sample_inputs if args.cpu_sample_inputs > 0 else prob.n_inputs
         line["cpu_baseline"] = cpu_baseline(wl, W, scales, min(n_cpu, prob.n_inputs))
     print(json.dumps(line), flush=True)
+
+
+def head_sweep(ms, steps, warmup):
+    """The scored-row lm head alone on the news head shape (262,144 x 3,840
+    bf16) for M scored rows: one content-free input with M one-token
+    questions of two single-token options, so the pass scores exactly M rows.
+    One JSON line per M: GEMM-kernel time from HIP events on the launch
+    stream, W streaming rate against HBM peak, and MFMA rate."""
+    import torch
+    import synth
+    import shared_prefix_branch_amd as spb
+    wl = synth.make_workload("news")
+    V, H = wl.dims.vocab, wl.dims.hidden
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    W = synth.lm_head(wl, device=dev)
+    stream = torch.cuda.current_stream()
+    for M in ms:
+        prob = synth.Problem(np.array([0], np.int32), np.array([0, M], np.int32), np.arange(M, dtype=np.int32),
+                             np.ones(M, np.int32), np.arange(0, 2 * M + 1, 2, dtype=np.int32),
+                             np.arange(2 * M + 1, dtype=np.int32), (np.arange(2 * M) * 97 % V).astype(np.int32), V)
+        plan = spb.pack_pass(prob, floors=False)
+        inf = plan.info(0)
+        assert inf["n_scored_rows"] == M and plan.n_passes == 1
+        g = torch.Generator(device=dev)
+        g.manual_seed(M)
+        hid = (torch.randn((inf["n_tokens"], H), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)
+        meta = torch.empty(inf["meta_bytes"], dtype=torch.uint8, device=dev)
+        ws = torch.empty(spb.score_workspace_bytes(plan, 0, V, H), dtype=torch.uint8, device=dev)
+        lp = torch.empty(inf["n_options"], device=dev)
+        p = torch.empty_like(lp)
+        res = torch.empty(inf["n_branches"], device=dev)
+        plan.upload(0, meta, stream)
+        call = spb.PreparedScore(0, meta, hid, W, ws, lp, p, res)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in evs:
+            e[0].record(stream)
+            e[1].record(stream)
+        for _ in range(warmup):
+            call(plan, stream)
+        for e in evs:
+            call(plan, stream, (e[0], e[1]))
+        torch.cuda.synchronize()
+        ms_k = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        w_bytes = 2.0 * V * H + 2.0 * H * M
+        flops = 2.0 * H * V * M
+        gbs = w_bytes / (ms_k * 1e-3) / 1e9
+        tfl = flops / (ms_k * 1e-3) / 1e12
+        print(json.dumps({"head_sweep": {"scored_rows": M, "ms": round(ms_k, 4), "algorithmic_bytes": int(w_bytes),
+                                         "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                                         "tflops": round(tfl, 2), "mfma_frac": round(tfl / PEAK_BF16_TFLOPS, 4),
+                                         "bound": "hbm" if M <= HEAD_RIDGE_ROWS else "mfma"}}),
+              flush=True)
 
 
 def cpu_baseline(wl, W, scales, n_inputs):
