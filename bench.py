@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--cpu-sample-inputs", type=int, default=0,
                     help="contents in the oracle's sample (0: all of the workload's)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--head-batch", action="store_true",
+                    help="one lm-head launch for all passes of the step (spb_score_options_batch) "
+                         "instead of one per pass")
     ap.add_argument("--head-sweep", default="",
                     help="comma-separated scored-row counts: time the lm head alone on the news head shape")
     return ap.parse_args()
@@ -72,15 +75,16 @@ def gemm_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per lm-head GEMM launch from the committed counter summary,
-    or None when it is missing or was taken on other kernel sources."""
+def measured_traffic(mode: str):
+    """HBM bytes per lm-head GEMM launch (mode "batched": one launch for all
+    passes of the step; "per_pass") from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
     path = os.path.join(HERE, TRAFFIC_SUMMARY)
     if not os.path.exists(path):
         return None, "no counter summary"
     text = open(path).read()
     m_src = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
-    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch\[" + mode + r"\]:\s*([0-9.eE+]+)", text)
     if not (m_src and m_val):
         return None, "counter summary unreadable"
     if m_src.group(1) != gemm_source_hash():
@@ -139,7 +143,9 @@ def main():
         qc, kc, vc = synth.cast_inputs(wl, q, k, v, scales)
         return qc, kc, vc, h.to(hid_dt)
 
-    job = Job(plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv_dt, out_dt, hid_dt, device=dev, scales=scales)
+    batch_head = args.head_batch and plan.n_passes <= 64
+    job = Job(plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv_dt, out_dt, hid_dt, device=dev, scales=scales,
+              batch_head=batch_head)
     job.load(provider)
     W = synth.lm_head(wl, device=dev)
     torch.cuda.synchronize()
@@ -190,14 +196,18 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     att_ms = np.zeros(n_pass)
-    head_ms = np.zeros(n_pass)
+    n_head = 1 if batch_head else n_pass   # lm-head launches per step
+    head_ms = np.zeros(n_head)
     for ms in marks:
         for k, mk in enumerate(ms):
             att_ms[k] += mk[0].elapsed_time(mk[1]) / args.steps
-            head_ms[k] += mk[2].elapsed_time(mk[3]) / args.steps
+            if k < n_head:
+                head_ms[k] += mk[2].elapsed_time(mk[3]) / args.steps
     pair_flops = 4.0 * d.head_dim * d.hq
     att_flops = np.array([plan.info(k)["unmasked_pairs"] * pair_flops for k in range(n_pass)])
     M = np.array([plan.info(k)["n_scored_rows"] for k in range(n_pass)], dtype=np.float64)
+    if batch_head:
+        M = np.array([M.sum()])
     head_flops = 2.0 * d.hidden * d.vocab * M
     w_bytes = 2.0 * d.hidden * d.vocab
     head_bytes = w_bytes + M * d.hidden * 2.0
@@ -205,7 +215,8 @@ def main():
     head_tflops = head_flops.sum() / (head_ms.sum() * 1e-3) / 1e12
     head_gbs = head_bytes.sum() / (head_ms.sum() * 1e-3) / 1e9
     head_bound = "mfma" if M.mean() > HEAD_RIDGE_ROWS else "hbm"
-    traffic, traffic_src = measured_traffic() if args.workload == "news" else (None, "counters taken on news only")
+    traffic, traffic_src = (measured_traffic("batched" if batch_head else "per_pass") if args.workload == "news"
+                            else (None, "counters taken on news only"))
     if head_bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(head_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(head_tflops / PEAK_BF16_TFLOPS, 4)}
@@ -230,7 +241,8 @@ def main():
         "config": {"workload": f"{args.workload}: {prob.n_inputs} contents x {len(prob.q_len)} questions, "
                                f"token budget {budget}, {n_pass} passes",
                    "packed_tokens": tokens, "questions": questions, "token_budget": budget,
-                   "hq": d.hq, "hkv": d.hkv, "head_dim": d.head_dim, "hidden": d.hidden, "vocab": d.vocab},
+                   "hq": d.hq, "hkv": d.hkv, "head_dim": d.head_dim, "hidden": d.hidden, "vocab": d.vocab,
+                   "lm_head_launches_per_step": n_head},
         "questions_per_s": round(questions / (ms_step * 1e-3), 1),
         "attention": {"ms": round(float(att_ms.sum()), 4), "tflops": round(att_tflops, 2),
                       "mfma_util": round(att_tflops / PEAK_BF16_TFLOPS, 4),

@@ -229,6 +229,24 @@ spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t
 spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *args,
                              void *stream);
 
+/* Several passes' scored rows through ONE lm-head stream: W is read once for
+ * the whole batch instead of once per pass (for passes whose scored rows alone
+ * leave the head HBM-bound, this moves the head toward its MFMA roofline).
+ * Every output equals, bit for bit, what spb_score_options gives pass by
+ * pass: each logit depends only on its W row and hidden row (fixed K order)
+ * and each row's vocabulary-slice merge runs in a fixed order.
+ * passes[0..n): distinct passes of the plan (n <= 64); d_metas[i]: the upload
+ * of passes[i]; args[i]: hidden, rows, lp, p, residual of passes[i] (all
+ * entries must agree on h_dtype, hidden_dim, lm_head and vocab; the
+ * workspace fields and the timing events are read from args[0] only, the
+ * events bracketing the single GEMM launch).  workspace: device memory of
+ * spb_score_batch_workspace_bytes, 256-byte aligned. */
+spb_status spb_score_batch_workspace_bytes(const spb_plan *plan, int32_t n, const int32_t *passes, int32_t vocab,
+                                           int32_t hidden_dim, size_t *out);
+spb_status spb_score_options_batch(const spb_plan *plan, int32_t n, const int32_t *passes, const void *const *d_metas,
+                                   const spb_score_args *args, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* Host, after all passes: gathers each content branch's results into logical
  * order and joins the floors.  *_per_pass[k] are host copies of pass k's lp,
  * p and residual outputs.  Outputs (host, caller-owned): lp, p, floor_p, lift

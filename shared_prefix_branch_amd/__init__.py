@@ -16,7 +16,8 @@ import numpy as np
 
 __all__ = [
     "SpbError", "lib", "library_path", "fingerprint", "Plan", "pack_pass", "branch_attention",
-    "PreparedAttention", "PreparedScore",
+    "PreparedAttention", "PreparedScore", "PreparedScoreBatch", "score_batch_workspace_bytes",
+    "score_options_batch",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
     "EXPORTED_SYMBOLS",
 ]
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = [
     "spb_plan_num_passes", "spb_plan_info", "spb_plan_rows", "spb_plan_branches", "spb_plan_inputs",
     "spb_plan_visible",
     "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
+    "spb_score_batch_workspace_bytes", "spb_score_options_batch",
     "spb_score_finalize",
 ]
 
@@ -113,6 +115,11 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_options.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.POINTER(_ScoreArgs), ctypes.c_void_p]
+        L.spb_score_batch_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.spb_score_options_batch.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.POINTER(ctypes.c_void_p),
+                                              ctypes.POINTER(_ScoreArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.c_void_p]
         fpp = ctypes.POINTER(_f32p)
         L.spb_score_finalize.argtypes = [ctypes.c_void_p, fpp, fpp, fpp, _f32p, _f32p, _f32p, _f32p, _f32p]
         for name in EXPORTED_SYMBOLS:
@@ -332,6 +339,52 @@ def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp
     gemm_events: optional pair of created ``torch.cuda.Event`` recorded on the
     stream around the lm-head GEMM kernel."""
     PreparedScore(pass_, d_meta, hidden, lm_head, workspace, lp, p, residual)(plan, stream, gemm_events)
+
+
+def score_batch_workspace_bytes(plan: Plan, passes: Sequence[int], vocab: int, hidden_dim: int) -> int:
+    ps = np.ascontiguousarray(passes, dtype=np.int32)
+    n = ctypes.c_size_t()
+    _check(lib().spb_score_batch_workspace_bytes(plan.handle, len(ps), _ptr(ps, _i32p), int(vocab), int(hidden_dim),
+                                                 ctypes.byref(n)))
+    return int(n.value)
+
+
+class PreparedScoreBatch:
+    """spb_score_options_batch with its arguments marshalled once: passes[i]
+    reads hiddens[i] and writes outs[i] = (lp, p, residual); one lm-head
+    stream serves them all."""
+
+    def __init__(self, passes: Sequence[int], d_metas, hiddens, lm_head, workspace, outs):
+        n = len(passes)
+        if not (len(d_metas) == len(hiddens) == len(outs) == n):
+            raise SpbError(-1, "passes, d_metas, hiddens and outs must have one entry per pass")
+        self.passes = np.ascontiguousarray(passes, dtype=np.int32)
+        self.metas = (ctypes.c_void_p * n)(*[m.data_ptr() for m in d_metas])
+        self.args = (_ScoreArgs * n)()
+        for i in range(n):
+            one = PreparedScore(int(passes[i]), d_metas[i], hiddens[i], lm_head, workspace, *outs[i])
+            self.args[i] = one.args
+        self.workspace = ctypes.c_void_p(workspace.data_ptr())
+        self.workspace_bytes = workspace.numel() * workspace.element_size()
+        self.fn = lib().spb_score_options_batch
+
+    def __call__(self, plan: Plan, stream=None, gemm_events=None):
+        A = self.args[0]
+        if gemm_events is not None:
+            for ev in gemm_events:
+                if not ev.cuda_event:
+                    raise SpbError(-1, "timing events must be created (recorded once) before use")
+            A.gemm_event_begin, A.gemm_event_end = gemm_events[0].cuda_event, gemm_events[1].cuda_event
+        else:
+            A.gemm_event_begin = A.gemm_event_end = None
+        _check(self.fn(plan.handle, len(self.passes), _ptr(self.passes, _i32p), self.metas, self.args,
+                       self.workspace, self.workspace_bytes, ctypes.c_void_p(_stream_handle(stream))))
+
+
+def score_options_batch(plan: Plan, passes: Sequence[int], d_metas, hiddens, lm_head, workspace, outs, stream=None,
+                        gemm_events=None):
+    """One lm-head stream for several passes' scored rows (see spb_score_options_batch)."""
+    PreparedScoreBatch(passes, d_metas, hiddens, lm_head, workspace, outs)(plan, stream, gemm_events)
 
 
 def score_finalize(plan: Plan, lp_per_pass, p_per_pass, res_per_pass) -> dict:

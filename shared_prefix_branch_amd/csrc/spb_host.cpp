@@ -438,6 +438,21 @@ size_t score_workspace_layout(int n_scored, int n_targets, int vocab, int hidden
   return o;
 }
 
+// Workspace of spb_score_options_batch: the single-pass layout over the
+// combined rows and targets, then the combined target CSR (offsets, tokens).
+size_t score_batch_workspace_layout(int m_tot, int t_tot, int vocab, int hidden_dim, size_t *off) {
+  size_t o4[4];
+  size_t o = score_workspace_layout(m_tot, t_tot, vocab, hidden_dim, o4);
+  if (off) {
+    for (int i = 0; i < 4; ++i) off[i] = o4[i];
+    off[4] = o;
+  }
+  o += align256((size_t)(m_tot + 1) * sizeof(int32_t));
+  if (off) off[5] = o;
+  o += align256((size_t)(t_tot > 0 ? t_tot : 1) * sizeof(int32_t));
+  return o;
+}
+
 const SpbMetaHeader &header(const PassPlan &P) { return *reinterpret_cast<const SpbMetaHeader *>(P.blob.data()); }
 
 spb_status check_pass(const spb_plan *plan, int32_t pass) {
@@ -812,6 +827,115 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   L.ev_begin = a->gemm_event_begin; L.ev_end = a->gemm_event_end;
   int e = launch_score(L, stream);
   if (e) return fail(SPB_ERR_HIP, "score launch: %s", hip_error_string(e));
+  return ok();
+}
+
+namespace {
+
+// Distinct, valid pass indices; sums of scored rows and targets.
+spb_status check_batch(const spb_plan *plan, int32_t n, const int32_t *passes, int64_t *m_tot, int64_t *t_tot) {
+  if (!plan) return fail(SPB_ERR_ARG, "plan is NULL");
+  if (n < 1 || n > kMaxBatchPasses) return fail(SPB_ERR_LIMIT, "a batch holds 1..%d passes, got %d", kMaxBatchPasses, n);
+  if (!passes) return fail(SPB_ERR_ARG, "passes is NULL");
+  std::vector<char> seen(plan->passes.size(), 0);
+  *m_tot = *t_tot = 0;
+  for (int i = 0; i < n; ++i) {
+    spb_status st = check_pass(plan, passes[i]);
+    if (st != SPB_OK) return st;
+    if (seen[passes[i]]++) return fail(SPB_ERR_ARG, "pass %d appears twice in the batch", passes[i]);
+    const SpbMetaHeader &h = header(plan->passes[passes[i]]);
+    *m_tot += h.n_scored;
+    *t_tot += h.n_targets;
+  }
+  if (*m_tot > INT32_MAX / 2 || *t_tot > INT32_MAX / 2) return fail(SPB_ERR_LIMIT, "batch too large");
+  return ok();
+}
+
+}  // namespace
+
+spb_status spb_score_batch_workspace_bytes(const spb_plan *plan, int32_t n, const int32_t *passes, int32_t vocab,
+                                           int32_t hidden_dim, size_t *out) {
+  int64_t m_tot = 0, t_tot = 0;
+  spb_status st = check_batch(plan, n, passes, &m_tot, &t_tot);
+  if (st != SPB_OK) return st;
+  if (!out || vocab < 1 || hidden_dim < 1) return fail(SPB_ERR_ARG, "bad argument");
+  *out = score_batch_workspace_layout((int)m_tot, (int)t_tot, vocab, hidden_dim, nullptr);
+  return ok();
+}
+
+spb_status spb_score_options_batch(const spb_plan *plan, int32_t n, const int32_t *passes, const void *const *d_metas,
+                                   const spb_score_args *args, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  int64_t m_tot = 0, t_tot = 0;
+  spb_status st = check_batch(plan, n, passes, &m_tot, &t_tot);
+  if (st != SPB_OK) return st;
+  if (!d_metas || !args) return fail(SPB_ERR_ARG, "NULL argument");
+  const spb_score_args &a0 = args[0];
+  if (a0.h_dtype != SPB_BF16 && a0.h_dtype != SPB_F32) return fail(SPB_ERR_DTYPE, "h_dtype %d unsupported", a0.h_dtype);
+  if (a0.hidden_dim < 64 || a0.hidden_dim % 64)
+    return fail(SPB_ERR_DTYPE, "hidden_dim %d not a positive multiple of 64", a0.hidden_dim);
+  if (a0.vocab < 1) return fail(SPB_ERR_ARG, "vocab %d < 1", a0.vocab);
+  if ((int64_t)a0.vocab * a0.hidden_dim * 2 > (int64_t)UINT32_MAX)
+    return fail(SPB_ERR_DTYPE, "the lm head (%lld bytes) exceeds 4 GiB", (long long)a0.vocab * a0.hidden_dim * 2);
+  const size_t need = score_batch_workspace_layout((int)m_tot, (int)t_tot, a0.vocab, a0.hidden_dim, nullptr);
+  if (workspace_bytes < need) return fail(SPB_ERR_SIZE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (m_tot > 0 && (!workspace || !a0.lm_head)) return fail(SPB_ERR_ARG, "NULL workspace or lm head");
+  if ((uintptr_t)workspace % 256) return fail(SPB_ERR_ARG, "workspace must be 256-byte aligned");
+  std::unique_ptr<ScoreBatchLaunch> B(new ScoreBatchLaunch());
+  ScoreBatchLaunch &L = *B;
+  L.n = 0;
+  int m_off = 0, t_off = 0;
+  for (int i = 0; i < n; ++i) {
+    const spb_score_args &a = args[i];
+    const PassPlan &P = plan->passes[passes[i]];
+    const SpbMetaHeader &h = header(P);
+    if (a.h_dtype != a0.h_dtype || a.hidden_dim != a0.hidden_dim || a.vocab != a0.vocab || a.lm_head != a0.lm_head)
+      return fail(SPB_ERR_ARG, "batch entry %d disagrees with entry 0 on the hidden dtype/size or the lm head", i);
+    for (int t : P.tgt_tok)
+      if (t >= a.vocab) return fail(SPB_ERR_ARG, "option token %d >= vocab %d", t, a.vocab);
+    if (a.rows < h.n_tokens)
+      return fail(SPB_ERR_SIZE, "hidden of pass %d holds %lld rows, the pass has %d", passes[i], (long long)a.rows, h.n_tokens);
+    if (!d_metas[i] || (uintptr_t)d_metas[i] % 256) return fail(SPB_ERR_ARG, "d_metas[%d] NULL or not 256-byte aligned", i);
+    if (h.n_scored == 0) continue;  // no branches either: nothing to score
+    if (!a.hidden || !a.lp || !a.p || !a.residual) return fail(SPB_ERR_ARG, "NULL tensor in batch entry %d", i);
+    ScoreLaunch &S = L.pass[L.n];
+    S.hidden = a.hidden;
+    S.n_scored = h.n_scored; S.n_targets = h.n_targets; S.n_branches = h.n_branches; S.n_options = h.n_options;
+    const char *base = (const char *)d_metas[i];
+    S.scored = base + h.off_scored;
+    S.tgt_off = base + h.off_tgt_off;
+    S.tgt_tok = base + h.off_tgt_tok;
+    S.branches = base + h.off_branches;
+    S.opt_step_off = base + h.off_opt_step_off;
+    S.step_slot = base + h.off_step_slot;
+    S.step_row = base + h.off_step_row;
+    S.lp = a.lp; S.p = a.p; S.residual = a.residual;
+    L.m_off[L.n] = m_off;
+    L.t_off[L.n] = t_off;
+    m_off += h.n_scored;
+    t_off += h.n_targets;
+    ++L.n;
+  }
+  if (L.n == 0) return ok();
+  L.m_tot = m_off;
+  L.t_tot = t_off;
+  L.h_dtype = a0.h_dtype;
+  L.hidden_dim = a0.hidden_dim;
+  L.lm_head = a0.lm_head;
+  L.vocab = a0.vocab;
+  size_t off[6];
+  score_batch_workspace_layout(L.m_tot, L.t_tot, a0.vocab, a0.hidden_dim, off);
+  char *ws = (char *)workspace;
+  L.part = (float *)(ws + off[0]);
+  L.tz = (float *)(ws + off[1]);
+  L.lse = (float *)(ws + off[2]);
+  L.hg = ws + off[3];
+  L.ctgt_off = (int32_t *)(ws + off[4]);
+  L.ctgt_tok = (int32_t *)(ws + off[5]);
+  L.ev_begin = a0.gemm_event_begin;
+  L.ev_end = a0.gemm_event_end;
+  int e = launch_score_batch(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "batched score launch: %s", hip_error_string(e));
   return ok();
 }
 

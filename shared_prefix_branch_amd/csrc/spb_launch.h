@@ -47,8 +47,28 @@ inline void head_m_layout(int M, int *n_chunks, int *mb) {
   *mb = b < 1 ? 1 : (b > 8 ? 8 : b);
 }
 
+// Several passes' scored rows through one lm-head stream: pass i's rows
+// occupy combined rows m_off[i] .. +n_scored and its targets combined
+// targets t_off[i] .. (the per-pass fields of pass[i] describe its
+// metadata and outputs; its workspace fields are unused).
+constexpr int kMaxBatchPasses = 64;
+struct ScoreBatchLaunch {
+  int n;
+  ScoreLaunch pass[kMaxBatchPasses];
+  int m_off[kMaxBatchPasses], t_off[kMaxBatchPasses];
+  int m_tot, t_tot;
+  int h_dtype, hidden_dim;
+  const void *lm_head;
+  int vocab;
+  float *part, *tz, *lse;  // workspace, combined rows / targets
+  void *hg;
+  int32_t *ctgt_off, *ctgt_tok;  // workspace: combined target CSR
+  void *ev_begin, *ev_end;
+};
+
 int launch_attention(const AttnLaunch &a, void *stream);
 int launch_score(const ScoreLaunch &a, void *stream);
+int launch_score_batch(const ScoreBatchLaunch &a, void *stream);
 const char *hip_error_string(int err);
 
 }  // namespace spb

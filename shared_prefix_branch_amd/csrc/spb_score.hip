@@ -62,15 +62,23 @@ struct GatherParams {
   const void *hidden;
   const int32_t *scored;
   uint16_t *hg;
-  int H, M, M_pad;
+  int H, M;        // this call's scored rows
+  int row0;        // their first row in hg
+  int zero_end;    // rows row0 + M .. zero_end are zeroed (padding)
+  // batched calls: copy this pass's target CSR into the combined one
+  const int32_t *tgt_off, *tgt_tok;
+  int32_t *ctgt_off, *ctgt_tok;
+  int t_base, t_end;  // the pass's first target in the combined CSR; total targets (last pass only: -1 otherwise)
 };
 
-// hg[m] = bf16(hidden[scored[m]]) for m < M, zero rows up to M_pad.
+// hg[row0 + m] = bf16(hidden[scored[m]]) for m < M, zero rows up to
+// zero_end; with a combined CSR, also its rows' target ranges and tokens.
 template <int HIN>
 __global__ __launch_bounds__(256) void gather_hidden_kernel(GatherParams g) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // one 8-element unit
   const int per_row = g.H / 8;
-  if (i >= (long long)g.M_pad * per_row) return;
+  const int n_rows = g.zero_end - g.row0;
+  if (i >= (long long)n_rows * per_row) return;
   const int m = (int)(i / per_row), k = (int)(i % per_row) * 8;
   uint4 v = {0u, 0u, 0u, 0u};
   if (m < g.M) {
@@ -85,8 +93,14 @@ __global__ __launch_bounds__(256) void gather_hidden_kernel(GatherParams g) {
       v.z = f2bf(b.x) | (f2bf(b.y) << 16);
       v.w = f2bf(b.z) | (f2bf(b.w) << 16);
     }
+    if (g.ctgt_off && k == 0) {
+      const int t0 = g.tgt_off[m], t1 = g.tgt_off[m + 1];
+      g.ctgt_off[g.row0 + m] = g.t_base + t0;
+      for (int t = t0; t < t1; ++t) g.ctgt_tok[g.t_base + t] = g.tgt_tok[t];
+      if (m == g.M - 1 && g.t_end >= 0) g.ctgt_off[g.row0 + g.M] = g.t_end;
+    }
   }
-  *(uint4 *)(g.hg + (long long)m * g.H + k) = v;
+  *(uint4 *)(g.hg + (long long)(g.row0 + m) * g.H + k) = v;
 }
 
 struct HeadParams {
@@ -390,44 +404,29 @@ __global__ __launch_bounds__(64) void finalize_kernel(FinParams f) {
 
 }  // namespace
 
-int launch_score(const ScoreLaunch &a, void *stream) {
-  hipStream_t s = (hipStream_t)stream;
-  int n_chunks = 0, mb = 0;
-  head_m_layout(a.n_scored, &n_chunks, &mb);
-  const int m_pad = n_chunks * 32 * mb;
-  GatherParams g;
-  g.hidden = a.hidden;
-  g.scored = (const int32_t *)a.scored;
-  g.hg = (uint16_t *)a.hg;
-  g.H = a.hidden_dim;
-  g.M = a.n_scored;
-  g.M_pad = m_pad;
-  long long units = (long long)m_pad * (a.hidden_dim / 8);
-  unsigned gblocks = (unsigned)((units + 255) / 256);
-  if (a.h_dtype == SPB_BF16)
-    hipLaunchKernelGGL(gather_hidden_kernel<SPB_BF16>, dim3(gblocks), dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL(gather_hidden_kernel<SPB_F32>, dim3(gblocks), dim3(256), 0, s, g);
-  int e = (int)hipGetLastError();
-  if (e) return e;
+namespace {
 
-  HeadParams p;
-  p.hg = (const uint16_t *)a.hg;
-  p.W = (const uint16_t *)a.lm_head;
-  p.H = a.hidden_dim;
-  p.V = a.vocab;
-  p.M = a.n_scored;
-  p.n_slices = n_vocab_slices(a.vocab);
-  p.n_mchunks = n_chunks;
-  p.tgt_off = (const int32_t *)a.tgt_off;
-  p.tgt_tok = (const int32_t *)a.tgt_tok;
-  p.part = a.part;
-  p.tz = a.tz;
+int launch_gather(const GatherParams &g, int h_dtype, hipStream_t s) {
+  const long long units = (long long)(g.zero_end - g.row0) * (g.H / 8);
+  if (units <= 0) return 0;
+  const unsigned blocks = (unsigned)((units + 255) / 256);
+  if (h_dtype == SPB_BF16)
+    hipLaunchKernelGGL(gather_hidden_kernel<SPB_BF16>, dim3(blocks), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL(gather_hidden_kernel<SPB_F32>, dim3(blocks), dim3(256), 0, s, g);
+  return (int)hipGetLastError();
+}
+
+// The GEMM + slice partials over M gathered rows, bracketed by the optional
+// timing events.
+int launch_head(const HeadParams &p0, int mb, void *ev_begin, void *ev_end, hipStream_t s) {
+  HeadParams p = p0;
   long long groups = (long long)((p.n_slices + 7) / 8) * 8 * p.n_mchunks;
   if (groups > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
   dim3 grid((unsigned)groups), block(kThreads);
-  if (a.ev_begin) {
-    e = (int)hipEventRecord((hipEvent_t)a.ev_begin, s);
+  int e;
+  if (ev_begin) {
+    e = (int)hipEventRecord((hipEvent_t)ev_begin, s);
     if (e) return e;
   }
   switch (mb) {
@@ -442,10 +441,51 @@ int launch_score(const ScoreLaunch &a, void *stream) {
   }
   e = (int)hipGetLastError();
   if (e) return e;
-  if (a.ev_end) {
-    e = (int)hipEventRecord((hipEvent_t)a.ev_end, s);
+  if (ev_end) {
+    e = (int)hipEventRecord((hipEvent_t)ev_end, s);
     if (e) return e;
   }
+  return 0;
+}
+
+int launch_finalize(const FinParams &f, int n_branches, hipStream_t s) {
+  if (n_branches <= 0) return 0;
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)n_branches), dim3(64), 0, s, f);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_score(const ScoreLaunch &a, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  int n_chunks = 0, mb = 0;
+  head_m_layout(a.n_scored, &n_chunks, &mb);
+  GatherParams g{};
+  g.hidden = a.hidden;
+  g.scored = (const int32_t *)a.scored;
+  g.hg = (uint16_t *)a.hg;
+  g.H = a.hidden_dim;
+  g.M = a.n_scored;
+  g.row0 = 0;
+  g.zero_end = n_chunks * 32 * mb;
+  int e = launch_gather(g, a.h_dtype, s);
+  if (e) return e;
+
+  HeadParams p;
+  p.hg = (const uint16_t *)a.hg;
+  p.W = (const uint16_t *)a.lm_head;
+  p.H = a.hidden_dim;
+  p.V = a.vocab;
+  p.M = a.n_scored;
+  p.n_slices = n_vocab_slices(a.vocab);
+  p.n_mchunks = n_chunks;
+  p.tgt_off = (const int32_t *)a.tgt_off;
+  p.tgt_tok = (const int32_t *)a.tgt_tok;
+  p.part = a.part;
+  p.tz = a.tz;
+  e = launch_head(p, mb, a.ev_begin, a.ev_end, s);
+  if (e) return e;
+
   FinParams f;
   f.n_slices = p.n_slices;
   f.branches = (const SpbBranch *)a.branches;
@@ -458,8 +498,67 @@ int launch_score(const ScoreLaunch &a, void *stream) {
   f.lp = a.lp;
   f.p = a.p;
   f.residual = a.residual;
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.n_branches), dim3(64), 0, s, f);
-  return (int)hipGetLastError();
+  return launch_finalize(f, a.n_branches, s);
+}
+
+int launch_score_batch(const ScoreBatchLaunch &a, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  int n_chunks = 0, mb = 0;
+  head_m_layout(a.m_tot, &n_chunks, &mb);
+  const int m_pad = n_chunks * 32 * mb;
+  int e;
+  for (int i = 0; i < a.n; ++i) {
+    const ScoreLaunch &P = a.pass[i];
+    const bool last = i == a.n - 1;
+    GatherParams g{};
+    g.hidden = P.hidden;
+    g.scored = (const int32_t *)P.scored;
+    g.hg = (uint16_t *)a.hg;
+    g.H = a.hidden_dim;
+    g.M = P.n_scored;
+    g.row0 = a.m_off[i];
+    g.zero_end = last ? m_pad : a.m_off[i] + P.n_scored;
+    g.tgt_off = (const int32_t *)P.tgt_off;
+    g.tgt_tok = (const int32_t *)P.tgt_tok;
+    g.ctgt_off = a.ctgt_off;
+    g.ctgt_tok = a.ctgt_tok;
+    g.t_base = a.t_off[i];
+    g.t_end = last ? a.t_tot : -1;
+    e = launch_gather(g, a.h_dtype, s);
+    if (e) return e;
+  }
+  HeadParams p;
+  p.hg = (const uint16_t *)a.hg;
+  p.W = (const uint16_t *)a.lm_head;
+  p.H = a.hidden_dim;
+  p.V = a.vocab;
+  p.M = a.m_tot;
+  p.n_slices = n_vocab_slices(a.vocab);
+  p.n_mchunks = n_chunks;
+  p.tgt_off = a.ctgt_off;
+  p.tgt_tok = a.ctgt_tok;
+  p.part = a.part;
+  p.tz = a.tz;
+  e = launch_head(p, mb, a.ev_begin, a.ev_end, s);
+  if (e) return e;
+  for (int i = 0; i < a.n; ++i) {
+    const ScoreLaunch &P = a.pass[i];
+    FinParams f;
+    f.n_slices = p.n_slices;
+    f.branches = (const SpbBranch *)P.branches;
+    f.opt_step_off = (const int32_t *)P.opt_step_off;
+    f.step_slot = (const int32_t *)P.step_slot;
+    f.step_row = (const int32_t *)P.step_row;
+    f.part = a.part + (size_t)a.m_off[i] * p.n_slices * 2;
+    f.tz = a.tz + a.t_off[i];
+    f.lse = a.lse + a.m_off[i];
+    f.lp = P.lp;
+    f.p = P.p;
+    f.residual = P.residual;
+    e = launch_finalize(f, P.n_branches, s);
+    if (e) return e;
+  }
+  return 0;
 }
 
 }  // namespace spb

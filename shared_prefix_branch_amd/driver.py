@@ -14,6 +14,10 @@ only for that upload, so uploads overlap other passes' kernels.  All passes
 write their option scores into one device buffer, copied back in one transfer
 at the end of the run; results are double-buffered, so a caller may enqueue
 run i+1 before it joins run i and the GPU never waits on the host.
+
+With ``batch_head`` the scored rows of all passes go through one lm-head
+launch after the passes' attention (W streamed once per run instead of once
+per pass); the scores are bit-identical to the per-pass head.
 """
 from __future__ import annotations
 
@@ -22,7 +26,8 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from . import Plan, PreparedAttention, PreparedScore, score_finalize, score_workspace_bytes
+from . import (Plan, PreparedAttention, PreparedScore, PreparedScoreBatch, score_batch_workspace_bytes,
+               score_finalize, score_workspace_bytes)
 
 
 @dataclasses.dataclass
@@ -48,7 +53,8 @@ class Job:
     """All passes of a plan, resident on one device."""
 
     def __init__(self, plan: Plan, hq: int, hkv: int, head_dim: int, hidden_dim: int, vocab: int,
-                 qkv_dtype, out_dtype, hidden_dtype, device="cuda", scales=(1.0, 1.0, 1.0)):
+                 qkv_dtype, out_dtype, hidden_dtype, device="cuda", scales=(1.0, 1.0, 1.0),
+                 batch_head: bool = False):
         import torch
         self.torch = torch
         self.plan = plan
@@ -68,6 +74,9 @@ class Job:
         self._head = None               # lm head the prepared score calls point at
         self._attn: List = []
         self._score: List = []
+        self.batch_head = bool(batch_head)
+        if self.batch_head and plan.n_passes > 64:
+            raise ValueError("batch_head covers at most 64 passes")
 
     # -- buffers ---------------------------------------------------------------
     def _result_sizes(self):
@@ -83,7 +92,8 @@ class Job:
         n = max(1, inf["n_tokens"])
         dev = self.device
         meta = t.empty(inf["meta_bytes"], dtype=t.uint8, device=dev)
-        ws = t.empty(max(256, score_workspace_bytes(self.plan, k, self.V, self.H)), dtype=t.uint8, device=dev)
+        ws_bytes = 256 if self.batch_head else max(256, score_workspace_bytes(self.plan, k, self.V, self.H))
+        ws = t.empty(ws_bytes, dtype=t.uint8, device=dev)
         return PassBuffers(
             inf["n_tokens"],
             t.empty((n, self.hq, self.d), dtype=self.qkv_dtype, device=dev),
@@ -141,12 +151,21 @@ class Job:
             self.passes.append(buf)
         self._attn = [PreparedAttention(k, b.meta, b.q, b.k, b.v, b.o, scales=self.scales)
                       for k, b in enumerate(self.passes)]
+        if self.batch_head:
+            nb = score_batch_workspace_bytes(self.plan, list(range(self.plan.n_passes)), self.V, self.H)
+            self.batch_ws = t.empty(max(256, nb), dtype=t.uint8, device=self.device)
         self._pass_done = [None] * len(self.passes)
 
     def _prepare_head(self, lm_head):
         if self._head is not lm_head:
-            self._score = [[PreparedScore(k, b.meta, b.hidden, lm_head, b.workspace, *b.slots[r]) for r in range(2)]
-                           for k, b in enumerate(self.passes)]
+            if self.batch_head:
+                ks = list(range(len(self.passes)))
+                self._score = [PreparedScoreBatch(ks, [b.meta for b in self.passes], [b.hidden for b in self.passes],
+                                                  lm_head, self.batch_ws, [b.slots[r] for b in self.passes])
+                               for r in range(2)]
+            else:
+                self._score = [[PreparedScore(k, b.meta, b.hidden, lm_head, b.workspace, *b.slots[r])
+                                for r in range(2)] for k, b in enumerate(self.passes)]
             self._head = lm_head
 
     # -- metadata ------------------------------------------------------------
@@ -214,12 +233,19 @@ class Job:
                 self._attn[k](plan, stream)
             if mk is not None:
                 mk[1].record(stream)
-            if scoring:
+            if scoring and not self.batch_head:
                 self._score[k][r](plan, stream, None if mk is None else (mk[2], mk[3]))
+            if not self.batch_head:
+                done = t.cuda.Event()
+                done.record(stream)
+                self._pass_done[k] = done
+            buf.lp, buf.p, buf.residual = buf.slots[r]
+        if self.batch_head:
+            if scoring:
+                self._score[r](plan, stream, None if marks is None else (marks[0][2], marks[0][3]))
             done = t.cuda.Event()
             done.record(stream)
-            self._pass_done[k] = done
-            buf.lp, buf.p, buf.residual = buf.slots[r]
+            self._pass_done = [done] * len(self.passes)
         with t.cuda.stream(stream):
             self.results_host[r].copy_(self.results[r], non_blocking=True)
         ev = t.cuda.Event()

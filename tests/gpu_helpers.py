@@ -29,7 +29,7 @@ class Case:
 
     def __init__(self, wl: synth.Workload, budget: int, inputs: Optional[Sequence[int]] = None,
                  floors: bool = True, peaked: bool = False, device: str = "cuda", gen_device: str = "cuda",
-                 chained: bool = False, cache: Optional[dict] = None):
+                 chained: bool = False, cache: Optional[dict] = None, batch_head: bool = False):
         import torch
         self.torch = torch
         self.wl = wl
@@ -48,6 +48,7 @@ class Case:
         self.dims = wl.dims
         self.scales = synth.fp8_scales(wl) if wl.dims.dtype == "fp8" else (1.0, 1.0, 1.0)
         self._blocks: Dict[tuple, tuple] = {} if cache is None else cache  # activations by identity
+        self.batch_head = batch_head
 
     # -- inputs --------------------------------------------------------------
     def block(self, ident):
@@ -70,7 +71,7 @@ class Case:
         out = t.float32 if d.dtype == "f32" else t.bfloat16
         hid = t.float32 if d.dtype == "f32" else t.bfloat16
         self.job = Job(self.plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv, out, hid,
-                       device=self.device, scales=self.scales)
+                       device=self.device, scales=self.scales, batch_head=self.batch_head)
         self.job.load(self.provider)
         self.job.run(W)
         t.cuda.synchronize()

@@ -209,6 +209,59 @@ def test_upload_rejects_small_or_misaligned_buffers():
     assert L.spb_plan_upload(plan.handle, 0, ctypes.c_void_p(4097), need, None) == -1
 
 
+def test_batched_score_validation():
+    # host-side checks of the one-stream head for several passes; no GPU work
+    prob = synth.make_problem("random", 23, vocab=64, n_inputs=6, n_questions=3, max_content=20,
+                              max_len=5, max_options=3, max_option_tokens=2)
+    plan = spb.pack_pass(prob, token_budget=40)
+    assert plan.n_passes >= 3
+    L = spb.lib()
+    ps = np.arange(plan.n_passes, dtype=np.int32)
+    n = ctypes.c_size_t()
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    assert L.spb_score_batch_workspace_bytes(plan.handle, len(ps), ps.ctypes.data_as(i32), 64, 128,
+                                             ctypes.byref(n)) == 0
+    tot_m = sum(plan.info(k)["n_scored_rows"] for k in range(plan.n_passes))
+    tot_t = sum(plan.info(k)["n_targets"] for k in range(plan.n_passes))
+    assert n.value >= tot_m * 4 * 2 + tot_t * 4 + tot_m * 4 + tot_m * 128 * 2 + (tot_m + 1) * 4 + tot_t * 4
+    # same answer through the binding
+    assert spb.score_batch_workspace_bytes(plan, list(range(plan.n_passes)), 64, 128) == n.value
+    dup = np.array([0, 0], np.int32)
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 2, dup.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -1
+    bad = np.array([plan.n_passes], np.int32)
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 1, bad.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -1
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 0, ps.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -2
+    big = np.zeros(65, np.int32)
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 65, big.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -2
+    # argument checks before any launch (fake device pointers are never touched)
+    k = len(ps)
+    metas = (ctypes.c_void_p * k)(*[4096 * (i + 1) for i in range(k)])
+    A = (spb._ScoreArgs * k)()
+    for i in range(k):
+        A[i].hidden, A[i].h_dtype, A[i].hidden_dim, A[i].rows = 1 << 20, spb.BF16, 128, 1 << 20
+        A[i].lm_head, A[i].vocab = 1 << 21, 64
+        A[i].lp = A[i].p = A[i].residual = ctypes.cast(ctypes.c_void_p(1 << 22), ctypes.POINTER(ctypes.c_float))
+    ws_ok = n.value
+    call = lambda ws, nbytes: L.spb_score_options_batch(plan.handle, k, ps.ctypes.data_as(i32), metas, A,
+                                                        ctypes.c_void_p(ws), nbytes, None)
+    L.spb_score_batch_workspace_bytes(plan.handle, k, ps.ctypes.data_as(i32), 64, 128, ctypes.byref(n))
+    assert call(1 << 23, n.value - 1) == -4                 # workspace too small
+    assert call((1 << 23) + 4, n.value) == -1               # workspace misaligned
+    A[1].hidden_dim = 192
+    assert call(1 << 23, n.value) == -1                     # entries disagree
+    A[1].hidden_dim = 128
+    for i in range(k):
+        A[i].vocab = 8
+    assert call(1 << 23, 1 << 30) == -1                     # a token >= vocab
+    for i in range(k):
+        A[i].vocab = 64
+    A[2].rows = 1
+    assert call(1 << 23, ws_ok) == -4                       # hidden too short
+    A[2].rows = 1 << 20
+    metas[1] = 4096 + 8
+    assert call(1 << 23, ws_ok) == -1                       # metadata misaligned
+
+
 def test_meta_copy_matches_the_pass_layout():
     # the host copy carries the same metadata blob spb_plan_upload sends: header
     # magic "SPB1", the pass index and its counts, and the plan's row placement
