@@ -44,7 +44,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kKT = 64;        // hidden elements per K stage (128-byte LDS rows: one cache line)
-constexpr int kThreads = 256;  // 2 x 2 waves: vocabulary halves x scored-row halves
+constexpr int kThreads = 256;  // 4 waves, each a 64-row strip of the 256-row vocabulary slice
 
 __device__ inline uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
