@@ -9,10 +9,10 @@
 // and scale"].
 //
 // Work item: up to 128 consecutive rows of one 128-row tile (rows of one
-// segment) and one KV head.  Keys are visited as a list of chunks built per
-// work item: content chunks of 64 keys aligned to the content start, then for
-// each branch that meets the work item's rows, chunks of 32 keys aligned to
-// the branch start (template rows, then option-trie nodes).  Per chunk:
+// segment) and one KV head.  Keys are visited as a list of chunks per work
+// item: content chunks of 64 keys aligned to the content start, then for each
+// branch that meets the work item's rows, chunks of 32 keys aligned to the
+// branch start (template rows, then option-trie nodes).  Per chunk:
 //   S^T = K Q^T      (MFMA 32x32x16 bf16, or 32x32x64 OCP e4m3 for fp8 Q/K)
 //   online softmax   (each lane owns one query; f32, base-2 exponent, the
 //                     exponent reference moved lazily)
@@ -20,13 +20,17 @@
 //                     read from row-major V with the LDS transpose read)
 //
 // Two kernels share that chunk step:
-//  * bf16 inputs (dma kernel): K and V rows are copied straight from global
-//    memory into a 3-deep LDS ring (XOR-swizzled rows, no staging registers),
-//    two chunks ahead; a wave owns 32 query rows of one query head (two heads
-//    for d = 64, sharing every K/V fragment read and visibility test).
+//  * bf16 inputs (dma kernel): four waves, two work groups per CU.  The work
+//    item's chunk list comes from the pass metadata (items of 32, 64 or 128
+//    rows).  K and V rows are copied straight from global memory into a
+//    two-slot LDS ring (XOR-swizzled rows, no staging registers), one chunk
+//    ahead; every LDS fragment read is issued ahead of the MFMAs that use it.
+//    A wave owns 32 query rows of one query head (two heads for d = 64,
+//    sharing every K/V fragment read and visibility test).
 //  * f32 / fp8 inputs (staged kernel): K and V pass through registers, where
 //    f32 is rounded to bf16 and e4m3 V is widened to bf16, into a
-//    double-buffered padded LDS layout; one head per wave.
+//    double-buffered padded LDS layout; one head per wave; the chunk list is
+//    built in the kernel from the tile and branch tables.
 // Both run one chunk step per chunk (a single instance in the loop, so the
 // O accumulators keep their registers).
 //
@@ -88,6 +92,9 @@ struct AttnParams {
   const SpbRow *rows;
   const SpbTile *tiles;
   const SpbBranch *branches;
+  const SpbItem *items;      // bf16 kernel: the item table of its row granularity
+  const SpbChunk *bchunks;   // bf16 kernel: branch chunks of the items
+  int n_work;                // bf16 kernel: items x KV heads
 };
 
 template <int D, int IN>
@@ -136,6 +143,13 @@ __device__ __attribute__((always_inline)) inline void mask_block(f32x16 &s, cons
   }
 }
 
+// max over the lane pair (i, i ^ 32): v_permlane32_swap hands each lane its
+// partner's value without an LDS round trip
+__device__ __attribute__((always_inline)) inline float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Online softmax over one chunk -- one 32-key block, or two when `two`
 // (runtime, uniform over the wave) -- for one head, with a lazily moved
 // reference: the row's exponent reference m changes only when the chunk's max
@@ -157,7 +171,7 @@ __device__ __attribute__((always_inline)) inline void softmax_chunk(const f32x16
 #pragma unroll
     for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s1[r]);
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sc;
+  mloc = half_max(mloc) * sc;
   const bool first = st.m == kNegInf;
   const bool move = !first && mloc > st.m + kLazy;
   const float mnew = (first || move) ? mloc : st.m;
@@ -261,6 +275,102 @@ __device__ __attribute__((always_inline)) inline void pv_block(const char *Vblk,
   }
 }
 
+// bf16 with K and V in 16-byte-swizzled LDS rows of ROWB bytes: the chunk's
+// S^T (one or two 32-key blocks) and its O^T update with every LDS read
+// issued ahead of the MFMAs that use it.  K fragments go in groups of four
+// 16-element steps, the next group read while the current one multiplies; V^T
+// fragments go one 16-key k-step ahead, the first k-step read before the
+// softmax (read_v_step).  Each output element accumulates in the same order
+// as in qk_block / pv_block.
+template <int D>
+struct VStep {
+  bf16x8_t v[D / 32];
+};
+
+template <int D, int ROWB>
+__device__ __attribute__((always_inline)) inline void read_k_group(const char *Kb, const FragOffsets<D, SPB_BF16> &fo,
+                                                                   int gi, u32x4 (&a)[4]) {
+  constexpr int NG = D / 64;  // groups per 32-key block
+  const char *base = Kb + (gi / NG) * 32 * ROWB;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a[t] = *(const u32x4 *)(base + fo.k[(gi % NG) * 4 + t][0]);
+}
+
+template <int D, int HPW, int ROWB>
+__device__ __attribute__((always_inline)) inline void qk_chunk(const char *Kb, const FragOffsets<D, SPB_BF16> &fo,
+                                                               const QFrag<D, SPB_BF16> (&qf)[HPW], f32x16 (&s0)[HPW],
+                                                               f32x16 (&s1)[HPW], bool two) {
+  constexpr int NG = D / 64;
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) s0[j] = f32x16{0.f};
+  if (two) {
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) s1[j] = f32x16{0.f};
+  }
+  u32x4 a[2][4];
+  read_k_group<D, ROWB>(Kb, fo, 0, a[0]);
+#pragma unroll
+  for (int gi = 0; gi < 2 * NG; ++gi) {
+    if (gi == NG && !two) break;
+    asm volatile("" ::: "memory");  // reads of group gi + 2 stay behind this point
+    if (gi + 1 < NG || (gi + 1 < 2 * NG && two)) read_k_group<D, ROWB>(Kb, fo, gi + 1, a[(gi + 1) & 1]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        const bf16x8_t av = *(const bf16x8_t *)&a[gi & 1][t];
+        if (gi < NG)
+          s0[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[j].f[(gi % NG) * 4 + t], s0[j], 0, 0, 0);
+        else
+          s1[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[j].f[(gi % NG) * 4 + t], s1[j], 0, 0, 0);
+      }
+  }
+}
+
+// V^T operands of k-step ks (keys 16 ks .. 16 ks + 16 of the chunk)
+template <int D, int ROWB>
+__device__ __attribute__((always_inline)) inline void read_v_step(const char *Vb, const FragOffsets<D, SPB_BF16> &fo,
+                                                                  int ks, VStep<D> &f) {
+  const char *vstep = Vb + 16 * ks * ROWB;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    union {
+      i16x4 h[2];
+      bf16x8_t v;
+    } a;
+    a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vstep + fo.v[db]));
+    a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vstep + fo.v[db] + 8 * ROWB));
+    f.v[db] = a.v;
+  }
+}
+
+template <int D, int HPW, int ROWB>
+__device__ __attribute__((always_inline)) inline void pv_chunk(const char *Vb, const FragOffsets<D, SPB_BF16> &fo,
+                                                               const uint32_t (&pk)[HPW][2][8],
+                                                               f32x16 (&o)[HPW][D / 32], bool two,
+                                                               const VStep<D> &first) {
+  VStep<D> f[2];
+  f[0] = first;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks == 2 && !two) break;
+    asm volatile("" ::: "memory");  // reads of k-step ks + 2 stay behind this point
+    if (ks + 1 < 2 || (ks + 1 < 4 && two)) read_v_step<D, ROWB>(Vb, fo, ks + 1, f[(ks + 1) & 1]);
+    const int blk = ks >> 1, rb = (ks & 1) * 4;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        union {
+          uint32_t u[4];
+          bf16x8_t v;
+        } b;
+        b.u[0] = pk[h][blk][rb]; b.u[1] = pk[h][blk][rb + 1]; b.u[2] = pk[h][blk][rb + 2]; b.u[3] = pk[h][blk][rb + 3];
+        o[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].v[db], b.v, o[h][db], 0, 0, 0);
+      }
+  }
+}
+
 // Chunk list of the work item (built by wave 0): content chunks, then the
 // chunks of each branch that meets rows [sub0, sub0 + sub_n).
 __device__ inline void build_chunk_list(const AttnParams &p, const SpbTile &tile, int sub0, int sub_n, int lane,
@@ -355,55 +465,68 @@ __device__ inline void store_o(const AttnParams &p, int x, int h, int half, cons
   }
 }
 
-// The chunk walk shared by both kernels.  Content chunk c (keys
-// [c*64, c*64 + 64) of the content) is two 32-key blocks, the second skipped
-// when no lane sees past key 32; branch chunk c (extended keys
-// [c*32, c*32 + 32) of the branch) is one block.  A chunk is skipped by a wave
-// none of whose lanes sees a key of it.  block(i, vis, two, masked, anc) runs
+// What one wave does with one chunk.  Content chunk c (keys [c*64, c*64 + 64)
+// of the content) is two 32-key blocks, the second skipped when no lane sees
+// past key 32; branch chunk c (extended keys [c*32, c*32 + 32) of the branch)
+// is one block.  A chunk is skipped by a wave none of whose lanes sees a key
+// of it.  ch = (first key row, info): info < 0 for content chunk -1 - info,
+// else branch << 10 | c.  Calls ballots: every lane of the wave takes part.
+struct ChunkStep {
+  bool run;     // some lane sees a key of the chunk
+  bool two;     // content chunk whose second block some lane sees
+  bool masked;  // some lane sees only part of the chunk
+  bool anc;     // some lane is an option-trie node of the chunk's branch
+  Vis vis;
+};
+
+__device__ __attribute__((always_inline)) inline ChunkStep chunk_step(int2 ch, const SpbRow &row, int half) {
+  int thr;  // keys of the chunk this lane sees as a prefix
+  int anc[kMaxDepth];
+  bool any, node = false;
+#pragma unroll
+  for (int a = 0; a < kMaxDepth; ++a) anc[a] = -1000;
+  if (ch.y < 0) {
+    thr = row.cvis - (-1 - ch.y) * kChunk;
+    any = thr > 0;
+  } else {
+    const int c = ch.y & 1023;
+    const int lo = c * kBranchChunk;
+    const bool mine = row.br == ch.x - lo;
+    thr = mine ? min(min(row.e + 1, row.L) - lo, kBranchChunk) : 0;
+    any = thr > 0;
+    node = mine && row.depth > 0;
+    if (node) {
+#pragma unroll
+      for (int a = 0; a < kMaxDepth; ++a) {
+        const int e = anc_of(row, a) - lo;
+        if (a < row.depth && e >= 0 && e < kBranchChunk) {
+          anc[a] = e;
+          any = true;
+        }
+      }
+    }
+  }
+  ChunkStep cs;
+  cs.run = __ballot(any) != 0;
+  cs.two = ch.y < 0 && __ballot(thr > 32) != 0;
+  cs.anc = __ballot(node) != 0;
+  cs.vis.thr = thr - 4 * half;
+#pragma unroll
+  for (int a = 0; a < kMaxDepth; ++a) cs.vis.anc[a] = anc[a] - 4 * half;
+  cs.masked = cs.anc || __ballot(thr < (cs.two ? 64 : 32)) != 0;
+  return cs;
+}
+
+// The chunk walk of the staged kernel: block(i, vis, two, masked, anc) runs
 // chunk i -- S^T, mask, softmax, O^T update over one or two blocks -- and
 // appears once in the loop, so the accumulators keep their registers;
-// advance(i) hands the LDS ring on to chunk i + 1.
+// advance(i) hands the LDS buffers on to chunk i + 1.
 template <typename Block, typename Advance>
 __device__ __attribute__((always_inline)) inline void walk_chunks(const int2 *chunks, int nch, const SpbRow &row,
                                                                   int half, Block &&block, Advance &&advance) {
   for (int i = 0; i < nch; ++i) {
-    const int2 ch = chunks[i];
-    int thr;  // keys of the chunk this lane sees as a prefix
-    int anc[kMaxDepth];
-    bool any, node = false;
-#pragma unroll
-    for (int a = 0; a < kMaxDepth; ++a) anc[a] = -1000;
-    if (ch.y < 0) {
-      thr = row.cvis - (-1 - ch.y) * kChunk;
-      any = thr > 0;
-    } else {
-      const int c = ch.y & 1023;
-      const int lo = c * kBranchChunk;
-      const bool mine = row.br == ch.x - lo;
-      thr = mine ? min(min(row.e + 1, row.L) - lo, kBranchChunk) : 0;
-      any = thr > 0;
-      node = mine && row.depth > 0;
-      if (node) {
-#pragma unroll
-        for (int a = 0; a < kMaxDepth; ++a) {
-          const int e = anc_of(row, a) - lo;
-          if (a < row.depth && e >= 0 && e < kBranchChunk) {
-            anc[a] = e;
-            any = true;
-          }
-        }
-      }
-    }
-    if (__ballot(any)) {
-      const bool two = ch.y < 0 && __ballot(thr > 32);
-      const bool anc_any = __ballot(node) != 0;
-      Vis vis;
-      vis.thr = thr - 4 * half;
-#pragma unroll
-      for (int a = 0; a < kMaxDepth; ++a) vis.anc[a] = anc[a] - 4 * half;
-      const bool masked = anc_any || __ballot(thr < (two ? 64 : 32)) != 0;
-      block(i, vis, two, masked, anc_any);
-    }
+    const ChunkStep cs = chunk_step(chunks[i], row, half);
+    if (cs.run) block(i, cs.vis, cs.two, cs.masked, cs.anc);
     advance(i);
   }
 }
@@ -417,15 +540,16 @@ struct DmaCfg {
   static constexpr int RG = RG_;              // 32-row groups per work item
   static constexpr int NW = RG * HG;          // waves
   static constexpr int NT = 64 * NW;
-  static constexpr int ROWS = 32 * RG;
-  static constexpr int SPLITS = 128 / ROWS;   // work items per 128-row tile
+  static constexpr int GRAN = RG == 1 ? 0 : RG == 2 ? 1 : 2;  // work items of 32 << GRAN rows
   static constexpr int ROWB = 2 * D;          // bytes per K or V row
   static constexpr int BUF = 64 * ROWB;       // one chunk of K (or V)
-  static constexpr int NBUF = 3;              // ring depth: two chunks in flight
   // copies per wave per tensor for a 64-key and a 32-key chunk
   static constexpr int Q64 = 64 * ROWB / 1024 / NW;
   static constexpr int Q32 = 32 * ROWB / 1024 / NW;
-  static_assert(G % HPW == 0 && 128 % ROWS == 0, "work item shape");
+  // work groups per CU the registers are budgeted for: two (at most 256 per
+  // lane) with one query head per wave
+  static constexpr int MINWG = HPW == 1 ? 2 : 1;
+  static_assert(G % HPW == 0 && (RG == 1 || RG == 2 || RG == 4), "work item shape");
   static_assert(Q32 >= 1 && Q32 * NW * 1024 == 32 * ROWB, "a 32-key chunk must give every wave whole copies");
 };
 
@@ -438,24 +562,25 @@ __device__ inline int swz_k(int r) { return ROWB == 256 ? (r & 15) : ((r >> 1) &
 template <int ROWB>
 __device__ inline int swz_v(int r) { return ROWB == 256 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
+// One work item (an item of the table, one KV head) per work group, two
+// work groups per CU.  The item's chunk list (content chunks, then the
+// chunks of the branches meeting its rows) is taken from the item table.  K
+// and V of the chunks are copied global -> LDS into a two-slot ring, the copy
+// of chunk i + 1 running while chunk i is computed.
 template <int D, int G, int HPW_, int RG_, int OUT>
-__global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), 1) void branch_attention_dma(AttnParams p) {
+__global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, RG_>::MINWG)) void branch_attention_dma(
+    AttnParams p) {
   using C = DmaCfg<D, G, HPW_, RG_>;
   constexpr int HPW = C::HPW;
   constexpr int IN = SPB_BF16;
-  __shared__ __attribute__((aligned(1024))) char Ks[C::NBUF][C::BUF];
-  __shared__ __attribute__((aligned(1024))) char Vs[C::NBUF][C::BUF];
-  __shared__ int2 chunks[kMaxChunks];  // (key0, info): info < 0 content chunk -1-c; else branch << 10 | c
-  __shared__ int n_chunks_s;
+  __shared__ __attribute__((aligned(1024))) char Ks[2][C::BUF];
+  __shared__ __attribute__((aligned(1024))) char Vs[2][C::BUF];
+  __shared__ int2 chunks[kMaxChunks];  // (first key row, info): info < 0 content chunk -1-c; else branch << 10 | c
 
   const int w = blockIdx.x;
   const int kvh = w % p.hkv;
-  const int rest = w / p.hkv;
-  const int split = rest % C::SPLITS;
-  const SpbTile tile = p.tiles[rest / C::SPLITS];
-  const int sub0 = tile.row0 + split * C::ROWS;
-  const int sub_n = min(C::ROWS, tile.row0 + tile.nrows - sub0);
-  if (sub_n <= 0) return;  // uniform over the work group
+  const SpbItem it = p.items[w / p.hkv];
+  const int nch = it.ncc + it.bn;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -463,11 +588,17 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), 1) void branch_atten
   const int h0 = kvh * G + hgi * HPW;  // the wave's first query head
   const int qi = lane & 31, half = lane >> 5;
   const int local = rg * 32 + qi;
-  const bool active = local < sub_n;
-  const int x = sub0 + local;
+  const bool active = local < it.nrows;
+  const int x = it.row0 + local;
 
-  if (wave == 0) build_chunk_list(p, tile, sub0, sub_n, lane, chunks, &n_chunks_s);
-
+  for (int i = tid; i < nch; i += C::NT) {
+    if (i < it.ncc) {
+      chunks[i] = int2{it.seg + i * kChunk, -1 - i};
+    } else {
+      const SpbChunk c = p.bchunks[it.boff + i - it.ncc];
+      chunks[i] = int2{c.key0, c.info};
+    }
+  }
   SpbRow row;
   if (active) {
     row = p.rows[x];
@@ -501,55 +632,51 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), 1) void branch_atten
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[j][db] = f32x16{0.f};
   }
-
-  __syncthreads();  // chunk list ready
-  const int nch = n_chunks_s;
   const uint32_t k_lds = lds_addr(&Ks[0][0]), v_lds = lds_addr(&Vs[0][0]);
 
   // Copies chunk i (64 or 32 key rows; rows past the pass repeat its last
-  // row, so every slot holds finite data) into ring slot i % 3: copy q of a
-  // tensor moves slot bytes q*1024 .. +1024, so lane t fills row
-  // (q*1024 + 16t) / ROWB at chunk position (16t % ROWB) / 16.
+  // row, so every slot holds finite data) into ring slot i % 2.  Copy qq of
+  // this wave moves slot bytes (qq*NW + wave)*1024 .. +1024 of each tensor:
+  // lane t fills row r0 + qq*RSTEP at 16-byte position pos, where r0 and pos
+  // do not depend on qq, and neither does the row swizzle (RSTEP is a
+  // multiple of its period), so only the source row changes per copy.
+  constexpr int RSTEP = C::NW * 1024 / C::ROWB;
+  static_assert(RSTEP % 16 == 0, "copy rounds must keep the swizzle phase");
+  const int r0 = (wave * 1024 + lane * 16) / C::ROWB;
+  const int pos = ((lane * 16) % C::ROWB) >> 4;
+  const uint32_t kofs = (uint32_t)(kvh * C::ROWB + ((pos ^ swz_k<C::ROWB>(r0)) << 4));
+  const uint32_t vofs = (uint32_t)(kvh * C::ROWB + ((pos ^ swz_v<C::ROWB>(r0)) << 4));
+  const uint32_t ystride = (uint32_t)(p.hkv * C::ROWB);
+  auto copy_rows = [&](int key0, uint32_t slot, int qq) {
+    const int y = min(key0 + r0 + qq * RSTEP, p.n_tokens - 1);
+    const uint32_t rowoff = (uint32_t)y * ystride;
+    const uint32_t dst = slot + (uint32_t)(qq * C::NW + wave) * 1024;
+    dma16(p.k, rowoff + kofs, k_lds + dst);
+    dma16(p.v, rowoff + vofs, v_lds + dst);
+  };
   auto issue = [&](int i) {
     const int2 ch = chunks[i];
-    const int nq = ch.y < 0 ? C::Q64 : C::Q32;
-    const uint32_t slot = (uint32_t)(i % C::NBUF) * C::BUF;
-    for (int qq = 0; qq < nq; ++qq) {
-      const int q = wave * nq + qq;
-      const int b = q * 1024 + lane * 16;
-      const int r = b / C::ROWB, pos = (b % C::ROWB) >> 4;
-      const int y = min(ch.x + r, p.n_tokens - 1);
-      const uint32_t rowoff = (uint32_t)(((size_t)y * p.hkv + kvh) * C::ROWB);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + (uint32_t)q * 1024);
-      dma16(p.k, rowoff + ((pos ^ swz_k<C::ROWB>(r)) << 4), k_lds + dst);
-      dma16(p.v, rowoff + ((pos ^ swz_v<C::ROWB>(r)) << 4), v_lds + dst);
-    }
-  };
-  // waits for this wave's copies of chunk i + 1, leaving chunk i + 2's in flight
-  auto wait_next = [&](int i) {
-    if (i + 2 < nch) {
-      if (chunks[i + 2].y < 0)
-        wait_vmcnt<2 * C::Q64>();
-      else
-        wait_vmcnt<2 * C::Q32>();
+    const uint32_t slot = (uint32_t)(i & 1) * C::BUF;
+    if (ch.y < 0) {
+#pragma unroll
+      for (int qq = 0; qq < C::Q64; ++qq) copy_rows(ch.x, slot, qq);
     } else {
-      wait_vmcnt<0>();
+#pragma unroll
+      for (int qq = 0; qq < C::Q32; ++qq) copy_rows(ch.x, slot, qq);
     }
-    lds_barrier();
   };
 
-  if (nch > 0) {
-    issue(0);
-    if (nch > 1) issue(1);
-    wait_next(-1);
-  }
+  __syncthreads();  // chunk list in LDS
+  issue(0);
+  wait_vmcnt<0>();
+  lds_barrier();
+  if (nch > 1) issue(1);
 
-  auto block = [&](int i, const Vis &vis, bool two, bool masked, bool anc) {
-    const char *Kb = Ks[i % C::NBUF];
-    const char *Vb = Vs[i % C::NBUF];
+  auto block = [&](int slot, const Vis &vis, bool two, bool masked, bool anc) {
+    const char *Kb = Ks[slot];
+    const char *Vb = Vs[slot];
     f32x16 s0[HPW], s1[HPW];
-    qk_block<D, IN, HPW>(Kb, fo, qf, s0);
-    if (two) qk_block<D, IN, HPW>(Kb + 32 * C::ROWB, fo, qf, s1);
+    qk_chunk<D, HPW, C::ROWB>(Kb, fo, qf, s0, s1, two);
     if (masked) {
       if (anc) {
 #pragma unroll
@@ -565,33 +692,22 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), 1) void branch_atten
         }
       }
     }
+    VStep<D> v0;
+    read_v_step<D, C::ROWB>(Vb, fo, 0, v0);
     uint32_t pk[HPW][2][8];
 #pragma unroll
     for (int j = 0; j < HPW; ++j) softmax_chunk<D>(s0[j], s1[j], two, p.sc, st[j], o[j], pk[j]);
-    {
-      uint32_t pb[HPW][8];
-#pragma unroll
-      for (int j = 0; j < HPW; ++j)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) pb[j][r] = pk[j][0][r];
-      pv_block<D, IN, HPW, C::ROWB>(Vb, fo, pb, o);
-    }
-    if (two) {
-      uint32_t pb[HPW][8];
-#pragma unroll
-      for (int j = 0; j < HPW; ++j)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) pb[j][r] = pk[j][1][r];
-      pv_block<D, IN, HPW, C::ROWB>(Vb + 32 * C::ROWB, fo, pb, o);
-    }
+    pv_chunk<D, HPW, C::ROWB>(Vb, fo, pk, o, two, v0);
   };
-  // Chunk i + 2 goes into the slot chunk i - 1 left (every wave passed the
-  // barrier after reading it); then chunk i + 1 is awaited for the next trip.
-  auto advance = [&](int i) {
+
+  for (int i = 0; i < nch; ++i) {
+    const ChunkStep cs = chunk_step(chunks[i], row, half);
+    if (cs.run) block(i & 1, cs.vis, cs.two, cs.masked, cs.anc);
+    // chunk i + 1 has landed and every wave is done with slot i % 2
+    wait_vmcnt<0>();
+    lds_barrier();
     if (i + 2 < nch) issue(i + 2);
-    wait_next(i);
-  };
-  walk_chunks(chunks, nch, row, half, block, advance);
+  }
 
   if (active) {
 #pragma unroll
@@ -840,21 +956,25 @@ AttnParams make_params(const AttnLaunch &a) {
 // short for eight waves to split a 32-key chunk into whole copies, so there
 // the two heads of a wave share the K/V reads and four waves suffice.
 template <int D, int G>
-struct DmaShape {
+struct DmaShape {  // four waves per work group
   static constexpr int HPW = (G >= 2 && D == 64) ? 2 : 1;
-  static constexpr int RG = ((G / HPW) >= 4 || (D == 64 && (G / HPW) >= 2)) ? 2 : 4;
+  static constexpr int RG = 4 / (G / HPW);
 };
 
 template <int D, int G, int OUT>
 int launch_dma(const AttnLaunch &a, hipStream_t s) {
   using Sh = DmaShape<D, G>;
   using C = DmaCfg<D, G, Sh::HPW, Sh::RG>;
-  long long items = (long long)a.n_tiles * C::SPLITS * a.hkv;
-  if (items > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  const long long work = (long long)a.n_items[C::GRAN] * a.hkv;
+  if (work > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  if (work == 0) return 0;
   // the copies address K/V with 32-bit byte offsets
   if ((long long)a.n_tokens * a.hkv * C::ROWB > 0xFFFFFFFFll) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL((branch_attention_dma<D, G, Sh::HPW, Sh::RG, OUT>), dim3((unsigned)items), dim3(C::NT), 0, s,
-                     make_params(a));
+  AttnParams p = make_params(a);
+  p.items = (const SpbItem *)a.items[C::GRAN];
+  p.bchunks = (const SpbChunk *)a.bchunks;
+  p.n_work = (int)work;
+  hipLaunchKernelGGL((branch_attention_dma<D, G, Sh::HPW, Sh::RG, OUT>), dim3((unsigned)work), dim3(C::NT), 0, s, p);
   return (int)hipGetLastError();
 }
 

@@ -152,6 +152,8 @@ struct PassPlan {
   std::vector<SpbRow> rows;
   std::vector<SpbTile> tiles;
   std::vector<SpbBranch> branches;
+  std::vector<SpbItem> items[3];
+  std::vector<SpbChunk> bchunks;
   std::vector<int32_t> logical_branch;
   std::vector<int32_t> scored, tgt_off, tgt_tok, opt_step_off, step_slot, step_row;
   std::vector<unsigned char> blob;
@@ -350,6 +352,49 @@ void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, co
   std::stable_sort(P.tiles.begin(), P.tiles.end(), [](const SpbTile &a, const SpbTile &b) { return a.cost > b.cost; });
 }
 
+// Work items of the bf16 attention kernel at 32, 64 and 128 rows: each tile
+// split into row ranges, each with the content chunks its own rows see and the
+// chunks of the branches meeting its rows, longest first.
+void build_items(PassPlan &P) {
+  for (int g = 0; g < 3; ++g) {
+    const int rows_per = 32 << g;
+    std::vector<SpbItem> items;
+    std::vector<std::vector<SpbChunk>> lists;
+    for (const SpbTile &t : P.tiles) {
+      for (int r0 = t.row0; r0 < t.row0 + t.nrows; r0 += rows_per) {
+        SpbItem it{};
+        it.row0 = r0;
+        it.nrows = std::min(rows_per, t.row0 + t.nrows - r0);
+        it.seg = t.seg;
+        int maxc = 0;
+        for (int r = r0; r < r0 + it.nrows; ++r) maxc = std::max(maxc, P.rows[r].cvis);
+        it.ncc = (maxc + kChunk - 1) / kChunk;
+        std::vector<SpbChunk> list;
+        for (int b = t.b_lo; b < t.b_hi; ++b) {
+          const SpbBranch &B = P.branches[b];
+          if (B.start + B.E <= r0 || B.start >= r0 + it.nrows) continue;
+          const int last = std::min(B.start + B.E, r0 + it.nrows) - 1 - B.start;
+          for (int c = 0; c <= last / kBranchChunk; ++c) list.push_back(SpbChunk{B.start + c * kBranchChunk, (b << 10) | c});
+        }
+        it.bn = (int)list.size();
+        it.cost = it.ncc + it.bn;
+        items.push_back(it);
+        lists.push_back(std::move(list));
+      }
+    }
+    std::vector<int> order(items.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return items[a].cost > items[b].cost; });
+    P.items[g].clear();
+    for (int i : order) {
+      SpbItem it = items[i];
+      it.boff = (int)P.bchunks.size();
+      P.bchunks.insert(P.bchunks.end(), lists[i].begin(), lists[i].end());
+      P.items[g].push_back(it);
+    }
+  }
+}
+
 void build_scoring(PassPlan &P, const std::vector<Question> &Q) {
   int opt = 0;
   P.tgt_off.push_back(0);
@@ -408,6 +453,12 @@ void build_blob(PassPlan &P, int pass) {
   place(h.off_opt_step_off, P.opt_step_off.size() * 4);
   place(h.off_step_slot, P.step_slot.size() * 4);
   place(h.off_step_row, P.step_row.size() * 4);
+  for (int g = 0; g < 3; ++g) {
+    h.n_items[g] = (int)P.items[g].size();
+    place(h.off_items[g], P.items[g].size() * sizeof(SpbItem));
+  }
+  h.n_bchunks = (int)P.bchunks.size();
+  place(h.off_bchunks, P.bchunks.size() * sizeof(SpbChunk));
   h.total_bytes = (int64_t)off;
   P.blob.assign(off, 0);
   memcpy(P.blob.data(), &h, sizeof h);
@@ -420,6 +471,8 @@ void build_blob(PassPlan &P, int pass) {
   put(P.blob, h.off_opt_step_off, P.opt_step_off);
   put(P.blob, h.off_step_slot, P.step_slot);
   put(P.blob, h.off_step_row, P.step_row);
+  for (int g = 0; g < 3; ++g) put(P.blob, h.off_items[g], P.items[g]);
+  put(P.blob, h.off_bchunks, P.bchunks);
   P.n_tokens = h.n_tokens;
 }
 
@@ -604,6 +657,7 @@ spb_status spb_pack_pass(const spb_problem *P, const spb_pack_opts *opts, spb_pl
   for (size_t k = 0; k < pk.passes.size(); ++k) {
     PassPlan &pp = pk.passes[k];
     build_tiles(pp, pk.pass_groups[k], pk.pass_group_seg[k]);
+    build_items(pp);
     build_scoring(pp, Q);
     build_blob(pp, (int)k);
   }
@@ -768,6 +822,11 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
   L.rows = base + h.off_rows;
   L.tiles = base + h.off_tiles;
   L.branches = base + h.off_branches;
+  for (int g = 0; g < 3; ++g) {
+    L.items[g] = base + h.off_items[g];
+    L.n_items[g] = h.n_items[g];
+  }
+  L.bchunks = base + h.off_bchunks;
   int e = launch_attention(L, stream);
   if (e) return fail(SPB_ERR_HIP, "branch attention launch: %s", hip_error_string(e));
   return ok();

@@ -17,6 +17,8 @@ struct AttnLaunch {
   float s_q, s_k, s_v;       // fp8 dequantisation scales (1 otherwise)
   int n_tokens, n_tiles;
   const void *rows, *tiles, *branches;  // device pointers into the metadata blob
+  const void *items[3], *bchunks;       // work items at 32, 64, 128 rows; their branch chunks
+  int n_items[3];
 };
 
 struct ScoreLaunch {

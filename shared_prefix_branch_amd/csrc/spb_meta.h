@@ -16,7 +16,7 @@
 namespace spb {
 
 constexpr int32_t kMetaMagic = 0x53504231;  // "SPB1"
-constexpr int32_t kMetaVersion = 1;
+constexpr int32_t kMetaVersion = 2;
 constexpr int kTileRows = 128;  // rows per attention tile (one to two work groups)
 constexpr int kChunk = 64;      // keys per content chunk, chunks start at the content start
 constexpr int kBranchChunk = 32;  // keys per branch chunk, chunks start at the branch start
@@ -51,6 +51,26 @@ struct SpbTile {
   int32_t pad;
 };
 
+// One work item of the bf16 attention kernel at a row granularity of 32 << g
+// (g = 0, 1, 2): rows [row0, row0 + nrows) of one tile, the content chunks
+// its rows see (chunk c holds content keys [64c, 64c + 64)), and the branch
+// chunks of the branches meeting its rows, entries [boff, boff + bn) of the
+// pass's branch-chunk list.  Items of one granularity are ordered longest
+// first (cost = ncc + bn).
+struct SpbItem {
+  int32_t row0, nrows;
+  int32_t seg;    // content start (pass row)
+  int32_t ncc;    // content chunks: ceil(max cvis over the item's rows / kChunk)
+  int32_t boff, bn;
+  int32_t cost, pad;
+};
+
+// A branch chunk: keys [key0, key0 + kBranchChunk) of branch `b`, chunk c of
+// it (key0 = start + c * kBranchChunk); info = b << 10 | c.
+struct SpbChunk {
+  int32_t key0, info;
+};
+
 struct SpbBranch {
   int32_t start;   // pass row of template token 0
   int32_t L, E;    // template length; template + trie nodes
@@ -69,6 +89,8 @@ struct SpbMetaHeader {
   int64_t off_rows, off_tiles, off_branches, off_scored;
   int64_t off_tgt_off, off_tgt_tok, off_opt_step_off, off_step_slot;
   int64_t off_step_row, total_bytes, pad2, pad3;
+  int64_t off_items[3], off_bchunks;  // work items at 32, 64, 128 rows; their branch chunks
+  int32_t n_items[3], n_bchunks;
 };
 
 SPB_HD inline int anc_of(const SpbRow &r, int i) {

@@ -336,3 +336,57 @@ def test_score_workspace_covers_gathered_hidden_rows():
     assert small >= M * 64 * 2 + M * 4 * 2 * 4  # hidden rows + (max, sum) per 256-row vocabulary slice
     with pytest.raises(spb.SpbError):
         spb.score_workspace_bytes(plan, 0, 1000, 0)
+
+
+def _meta_arrays(buf):
+    """Header fields and arrays of a pass metadata blob (layout of spb_meta.h)."""
+    i32 = buf[:48].view(np.int32)
+    i64 = buf[48:48 + 16 * 8].view(np.int64)
+    tail = buf[48 + 16 * 8:48 + 16 * 8 + 16].view(np.int32)
+    n_tokens, n_branches = int(i32[3]), int(i32[5])
+    off_rows, off_branches = int(i64[0]), int(i64[2])
+    rows = buf[off_rows:off_rows + 32 * n_tokens].view(np.int32).reshape(-1, 8)
+    br = buf[off_branches:off_branches + 32 * n_branches].view(np.int32).reshape(-1, 8)
+    items = []
+    for g in range(3):
+        off, n = int(i64[12 + g]), int(tail[g])
+        items.append(buf[off:off + 32 * n].view(np.int32).reshape(-1, 8))
+    off_bc, n_bc = int(i64[15]), int(tail[3])
+    bchunks = buf[off_bc:off_bc + 8 * n_bc].view(np.int32).reshape(-1, 2)
+    return n_tokens, rows, br, items, bchunks
+
+
+@pytest.mark.parametrize("budget", [120, 200, 600])
+def test_attention_work_items_cover_rows_and_visible_chunks(budget):
+    # the bf16 attention kernel walks, per work item, the content chunks its
+    # rows see and the chunks of every branch meeting its rows; derive both
+    # from the rows' own visibility fields and compare
+    prob = synth.make_problem("random", 23, vocab=64, n_inputs=6, n_questions=5, max_content=70,
+                              max_len=40, max_options=3, max_option_tokens=3)
+    plan = spb.pack_pass(prob, token_budget=budget)
+    for k in range(plan.n_passes):
+        buf = np.zeros(plan.info(k)["meta_bytes"], np.uint8)
+        plan.meta_copy(k, buf)
+        n, rows, br, items, bchunks = _meta_arrays(buf)
+        start_of = {int(s): b for b, s in enumerate(br[:, 0])}
+        for g in range(3):
+            per = 32 << g
+            seen = np.zeros(n, np.int32)
+            costs = []
+            for it in items[g]:
+                row0, nrows, seg, ncc, boff, bn, cost = (int(v) for v in it[:7])
+                assert 1 <= nrows <= per and cost == ncc + bn
+                costs.append(cost)
+                seen[row0:row0 + nrows] += 1
+                r = rows[row0:row0 + nrows]
+                # rows that see content see the item's segment (floor rows see none)
+                assert (r[r[:, 0] > 0, 1] == seg).all()
+                assert ncc == -(-int(r[:, 0].max()) // 64)
+                want = []
+                for b0 in sorted(set(int(v) for v in r[:, 2] if v >= 0)):
+                    emax = int(r[r[:, 2] == b0, 3].max())
+                    want += [(b0 + 32 * c, (start_of[b0] << 10) | c) for c in range(emax // 32 + 1)]
+                got = [tuple(int(v) for v in e) for e in bchunks[boff:boff + bn]]
+                assert got == want
+            assert (seen == 1).all()  # every row in exactly one item
+            assert costs == sorted(costs, reverse=True)
