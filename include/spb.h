@@ -193,8 +193,16 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
 
 /* ------------------------------------------------------------------ scoring
  * For every scored row r (each template's last row and each trie node):
- *   z_r = W h_r over the whole vocabulary, f32 (the "f32out" lm head [man
- *   PARAMETERS --lm-head]); LSE_r = log sum exp z_r.
+ *   z_r = W h_r over the whole vocabulary; LSE_r = log sum exp z_r.
+ * The lm head's output kind [man page "spinf-serve", PARAMETERS --lm-head]:
+ *   SPB_HEAD_F32OUT (0, default): bf16 W times bf16 h (an f32 hidden row is
+ *     rounded to bf16), f32 logits;
+ *   SPB_HEAD_BF16 (1): the same product, each logit rounded to bf16 (nearest
+ *     even) before the log-sum-exp and the option gather;
+ *   SPB_HEAD_FP32 (2): bf16 W (exact in f32) times the f32 hidden row without
+ *     rounding it: h is split into three bf16 terms whose sum is h, each
+ *     multiplied on the bf16 MFMA with f32 accumulation (three times the
+ *     f32out work; for bf16 hidden rows it equals f32out).
  * For option o of a branch with tokens t_1..t_n:
  *   lp_o = sum_k z_{r_{k-1}}[t_k] - LSE_{r_{k-1}}  (r_0 = template's last row,
  *          r_k = trie node of t_1..t_k);
@@ -205,8 +213,10 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
  * only scored rows are read; lm_head [vocab, hidden_dim] bf16 row-major;
  * hidden_dim % 64 == 0.  Outputs (device, f32): lp and p [n_options],
  * residual [n_branches], in the pass's slot order.  workspace: device memory
- * of spb_score_workspace_bytes, 256-byte aligned; no state is kept in it
- * between calls. */
+ * of spb_score_workspace_bytes for the same lm_head_kind, 256-byte aligned;
+ * no state is kept in it between calls.  An lm_head_kind outside 0..2 is
+ * SPB_ERR_ARG. */
+enum { SPB_HEAD_F32OUT = 0, SPB_HEAD_BF16 = 1, SPB_HEAD_FP32 = 2 };
 typedef struct {
   const void *hidden;
   int32_t h_dtype;
@@ -221,11 +231,13 @@ typedef struct {
    * on the stream right before and right after the lm-head GEMM kernel, so a
    * caller can time that kernel alone.  NULL: not recorded. */
   void *gemm_event_begin, *gemm_event_end;
+  int32_t lm_head_kind; /* SPB_HEAD_*; 0 (f32out) in a zero-initialised struct */
 } spb_score_args;
 
-/* Workspace bytes spb_score_options needs for this pass, vocabulary and hidden size. */
+/* Workspace bytes spb_score_options needs for this pass, vocabulary, hidden
+ * size and lm-head kind. */
 spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, int32_t hidden_dim,
-                                     size_t *out);
+                                     int32_t lm_head_kind, size_t *out);
 spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *args,
                              void *stream);
 
@@ -237,12 +249,12 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
  * and each row's vocabulary-slice merge runs in a fixed order.
  * passes[0..n): distinct passes of the plan (n <= 64); d_metas[i]: the upload
  * of passes[i]; args[i]: hidden, rows, lp, p, residual of passes[i] (all
- * entries must agree on h_dtype, hidden_dim, lm_head and vocab; the
- * workspace fields and the timing events are read from args[0] only, the
- * events bracketing the single GEMM launch).  workspace: device memory of
- * spb_score_batch_workspace_bytes, 256-byte aligned. */
+ * entries must agree on h_dtype, hidden_dim, lm_head, vocab and
+ * lm_head_kind; the workspace fields and the timing events are read from
+ * args[0] only, the events bracketing the single GEMM launch).  workspace:
+ * device memory of spb_score_batch_workspace_bytes, 256-byte aligned. */
 spb_status spb_score_batch_workspace_bytes(const spb_plan *plan, int32_t n, const int32_t *passes, int32_t vocab,
-                                           int32_t hidden_dim, size_t *out);
+                                           int32_t hidden_dim, int32_t lm_head_kind, size_t *out);
 spb_status spb_score_options_batch(const spb_plan *plan, int32_t n, const int32_t *passes, const void *const *d_metas,
                                    const spb_score_args *args, void *workspace, size_t workspace_bytes,
                                    void *stream);

@@ -64,3 +64,17 @@ def to_f64(x, scale: float = 1.0) -> np.ndarray:
     if a.dtype == np.uint8:
         return e4m3_bytes_to_f64(a, scale)
     return a.astype(np.float64) * float(scale)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """The bf16 value nearest to each float64 (ties to the even significand),
+    as float64.  bf16 keeps 8 significant bits and the exponent range of
+    binary32: normal values from 2**-126, subnormal spacing 2**-133, largest
+    finite (2 - 2**-7) * 2**127 (beyond it: infinity)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m 2**e, 0.5 <= |m| < 1
+    y = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    tiny = np.abs(x) < 2.0 ** -126
+    y = np.where(tiny, np.rint(x * 2.0 ** 133) * 2.0 ** -133, y)
+    big = np.abs(y) > (2 - 2.0 ** -7) * 2.0 ** 127
+    return np.where(big, np.copysign(np.inf, x), y)

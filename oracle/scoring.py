@@ -13,8 +13,13 @@ GPU", the response example and the paragraph after it; PyPI "spinf-serve
     one minus the options' total probability;
   * ``floor_p`` is ``p`` for the same question on empty content; ``p - floor_p``
     is what the content added (the lift).
-The lm head's output precision defaults to f32 logits [man page "spinf-serve",
-PARAMETERS: --lm-head]; the oracle keeps float64 throughout.
+The lm head's output precision [man page "spinf-serve", PARAMETERS: --lm-head]
+is one of f32out (the default: f32 logits), bf16 or fp32.  The oracle keeps
+float64 throughout and models the kinds as: f32out and fp32, the exact
+product of the hidden rows it is given with W (the caller passes bf16-rounded
+rows for f32out, unrounded f32 rows for fp32); bf16, that product rounded to
+the nearest bf16 before the log-sum-exp and the option gather (reading: the
+logits themselves are bf16).
 
 Readings (pages silent): a multi-token option's log-probability is the chain
 rule along its trie path, sum over k of log softmax(z_{k-1})[t_k], where
@@ -28,7 +33,7 @@ from typing import Callable, Dict, List, Sequence, Tuple
 
 import numpy as np
 
-from .numerics import to_f64
+from .numerics import round_to_bf16, to_f64
 from .tree import Layout, LBranch
 
 
@@ -88,13 +93,18 @@ def residual(lp: np.ndarray) -> float:
     return float(-np.expm1(m + np.log(np.sum(np.exp(lp - m)))))
 
 
+LM_HEAD_KINDS = ("f32out", "bf16", "fp32")
+
+
 def score_branches(layout: Layout, hidden: Callable[[Sequence[int]], np.ndarray], W,
-                   branches: Sequence[LBranch] = None) -> Dict[Tuple[int, int], BranchScores]:
+                   branches: Sequence[LBranch] = None, lm_head: str = "f32out") -> Dict[Tuple[int, int], BranchScores]:
     """Scores of the listed branches (default: all), keyed (input number, question).
 
     ``hidden(rows)`` returns the float64 hidden states [len(rows), H] of the
-    given logical rows.
+    given logical rows.  ``lm_head``: the output kind (see the header).
     """
+    if lm_head not in LM_HEAD_KINDS:
+        raise ValueError(f"lm_head must be one of {LM_HEAD_KINDS}")
     if branches is None:
         branches = list(layout.branches())
     rows: List[int] = []
@@ -104,6 +114,8 @@ def score_branches(layout: Layout, hidden: Callable[[Sequence[int]], np.ndarray]
     rows = sorted(set(rows))
     at = {r: i for i, r in enumerate(rows)}
     z = logits(W, hidden(rows))
+    if lm_head == "bf16":
+        z = round_to_bf16(z)
     lse_v = logsumexp(z)
     lse = {r: float(lse_v[at[r]]) for r in rows}
 

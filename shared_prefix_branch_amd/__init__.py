@@ -19,10 +19,12 @@ __all__ = [
     "PreparedAttention", "PreparedScore", "PreparedScoreBatch", "score_batch_workspace_bytes",
     "score_options_batch",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
+    "HEAD_F32OUT", "HEAD_BF16", "HEAD_FP32",
     "EXPORTED_SYMBOLS",
 ]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
+HEAD_F32OUT, HEAD_BF16, HEAD_FP32 = 0, 1, 2  # lm-head output kinds
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libspb.so")
 
@@ -81,7 +83,8 @@ class _ScoreArgs(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("lm_head", ctypes.c_void_p), ("vocab", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("lp", _f32p), ("p", _f32p), ("residual", _f32p),
-                ("gemm_event_begin", ctypes.c_void_p), ("gemm_event_end", ctypes.c_void_p)]
+                ("gemm_event_begin", ctypes.c_void_p), ("gemm_event_end", ctypes.c_void_p),
+                ("lm_head_kind", ctypes.c_int32)]
 
 
 _lib = None
@@ -112,11 +115,11 @@ def lib() -> ctypes.CDLL:
         L.spb_branch_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.POINTER(_AttnArgs), ctypes.c_void_p]
         L.spb_score_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                ctypes.POINTER(ctypes.c_size_t)]
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_options.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.POINTER(_ScoreArgs), ctypes.c_void_p]
         L.spb_score_batch_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32,
-                                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+                                                      ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_options_batch.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.POINTER(ctypes.c_void_p),
                                               ctypes.POINTER(_ScoreArgs), ctypes.c_void_p, ctypes.c_size_t,
                                               ctypes.c_void_p]
@@ -285,16 +288,17 @@ def branch_attention(plan: Plan, pass_: int, d_meta, q, k, v, o, softmax_scale: 
     PreparedAttention(pass_, d_meta, q, k, v, o, softmax_scale, scales)(plan, stream)
 
 
-def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int) -> int:
+def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int, lm_head_kind: int = 0) -> int:
     n = ctypes.c_size_t()
-    _check(lib().spb_score_workspace_bytes(plan.handle, pass_, int(vocab), int(hidden_dim), ctypes.byref(n)))
+    _check(lib().spb_score_workspace_bytes(plan.handle, pass_, int(vocab), int(hidden_dim), int(lm_head_kind),
+                                           ctypes.byref(n)))
     return int(n.value)
 
 
 class PreparedScore:
     """spb_score_options with its arguments marshalled once."""
 
-    def __init__(self, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual):
+    def __init__(self, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual, lm_head_kind: int = 0):
         import torch
         if lm_head.dtype != torch.bfloat16:
             raise SpbError(-3, "lm_head must be bfloat16")
@@ -315,6 +319,7 @@ class PreparedScore:
         S.lp = ctypes.cast(ctypes.c_void_p(lp.data_ptr()), _f32p)
         S.p = ctypes.cast(ctypes.c_void_p(p.data_ptr()), _f32p)
         S.residual = ctypes.cast(ctypes.c_void_p(residual.data_ptr()), _f32p)
+        S.lm_head_kind = int(lm_head_kind)
         self.args = S
         self.pass_ = pass_
         self.meta = ctypes.c_void_p(d_meta.data_ptr())
@@ -333,19 +338,22 @@ class PreparedScore:
 
 
 def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual, stream=None,
-                  gemm_events=None):
+                  gemm_events=None, lm_head_kind: int = 0):
     """hidden [rows, H] (bf16/f32), lm_head [V, H] bf16, workspace uint8 device buffer,
     lp/p [n_options] and residual [n_branches] float32 device tensors.
     gemm_events: optional pair of created ``torch.cuda.Event`` recorded on the
-    stream around the lm-head GEMM kernel."""
-    PreparedScore(pass_, d_meta, hidden, lm_head, workspace, lp, p, residual)(plan, stream, gemm_events)
+    stream around the lm-head GEMM kernel.  lm_head_kind: HEAD_F32OUT,
+    HEAD_BF16 or HEAD_FP32."""
+    PreparedScore(pass_, d_meta, hidden, lm_head, workspace, lp, p, residual, lm_head_kind)(plan, stream,
+                                                                                               gemm_events)
 
 
-def score_batch_workspace_bytes(plan: Plan, passes: Sequence[int], vocab: int, hidden_dim: int) -> int:
+def score_batch_workspace_bytes(plan: Plan, passes: Sequence[int], vocab: int, hidden_dim: int,
+                                lm_head_kind: int = 0) -> int:
     ps = np.ascontiguousarray(passes, dtype=np.int32)
     n = ctypes.c_size_t()
     _check(lib().spb_score_batch_workspace_bytes(plan.handle, len(ps), _ptr(ps, _i32p), int(vocab), int(hidden_dim),
-                                                 ctypes.byref(n)))
+                                                 int(lm_head_kind), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -354,7 +362,7 @@ class PreparedScoreBatch:
     reads hiddens[i] and writes outs[i] = (lp, p, residual); one lm-head
     stream serves them all."""
 
-    def __init__(self, passes: Sequence[int], d_metas, hiddens, lm_head, workspace, outs):
+    def __init__(self, passes: Sequence[int], d_metas, hiddens, lm_head, workspace, outs, lm_head_kind: int = 0):
         n = len(passes)
         if not (len(d_metas) == len(hiddens) == len(outs) == n):
             raise SpbError(-1, "passes, d_metas, hiddens and outs must have one entry per pass")
@@ -362,7 +370,8 @@ class PreparedScoreBatch:
         self.metas = (ctypes.c_void_p * n)(*[m.data_ptr() for m in d_metas])
         self.args = (_ScoreArgs * n)()
         for i in range(n):
-            one = PreparedScore(int(passes[i]), d_metas[i], hiddens[i], lm_head, workspace, *outs[i])
+            one = PreparedScore(int(passes[i]), d_metas[i], hiddens[i], lm_head, workspace, *outs[i],
+                                lm_head_kind=lm_head_kind)
             self.args[i] = one.args
         self.workspace = ctypes.c_void_p(workspace.data_ptr())
         self.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -382,9 +391,9 @@ class PreparedScoreBatch:
 
 
 def score_options_batch(plan: Plan, passes: Sequence[int], d_metas, hiddens, lm_head, workspace, outs, stream=None,
-                        gemm_events=None):
+                        gemm_events=None, lm_head_kind: int = 0):
     """One lm-head stream for several passes' scored rows (see spb_score_options_batch)."""
-    PreparedScoreBatch(passes, d_metas, hiddens, lm_head, workspace, outs)(plan, stream, gemm_events)
+    PreparedScoreBatch(passes, d_metas, hiddens, lm_head, workspace, outs, lm_head_kind)(plan, stream, gemm_events)
 
 
 def score_finalize(plan: Plan, lp_per_pass, p_per_pass, res_per_pass) -> dict:

@@ -478,11 +478,12 @@ void build_blob(PassPlan &P, int pass) {
 
 // Workspace of spb_score_options: slice partials, captured logits, LSE per
 // row, gathered hidden states.  Returns the total; off[] gets the offsets.
-size_t score_workspace_layout(int n_scored, int n_targets, int vocab, int hidden_dim, size_t *off) {
+size_t score_workspace_layout(int n_scored, int n_targets, int vocab, int hidden_dim, int kind, size_t *off) {
   int n_chunks = 0, mb = 0;
   head_m_layout(n_scored, &n_chunks, &mb);
   size_t sizes[4] = {(size_t)n_scored * n_vocab_slices(vocab) * 2 * sizeof(float), (size_t)n_targets * sizeof(float),
-                     (size_t)n_scored * sizeof(float), (size_t)n_chunks * 32 * mb * (size_t)hidden_dim * 2};
+                     (size_t)n_scored * sizeof(float),
+                     (size_t)n_chunks * 32 * mb * (size_t)hidden_dim * 2 * head_planes(kind)};
   size_t o = 0;
   for (int i = 0; i < 4; ++i) {
     if (off) off[i] = o;
@@ -493,9 +494,9 @@ size_t score_workspace_layout(int n_scored, int n_targets, int vocab, int hidden
 
 // Workspace of spb_score_options_batch: the single-pass layout over the
 // combined rows and targets, then the combined target CSR (offsets, tokens).
-size_t score_batch_workspace_layout(int m_tot, int t_tot, int vocab, int hidden_dim, size_t *off) {
+size_t score_batch_workspace_layout(int m_tot, int t_tot, int vocab, int hidden_dim, int kind, size_t *off) {
   size_t o4[4];
-  size_t o = score_workspace_layout(m_tot, t_tot, vocab, hidden_dim, o4);
+  size_t o = score_workspace_layout(m_tot, t_tot, vocab, hidden_dim, kind, o4);
   if (off) {
     for (int i = 0; i < 4; ++i) off[i] = o4[i];
     off[4] = o;
@@ -833,12 +834,14 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
 }
 
 spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t vocab, int32_t hidden_dim,
-                                     size_t *out) {
+                                     int32_t lm_head_kind, size_t *out) {
   spb_status st = check_pass(plan, pass);
   if (st != SPB_OK) return st;
   if (!out || vocab < 1 || hidden_dim < 1) return fail(SPB_ERR_ARG, "bad argument");
+  if (lm_head_kind < SPB_HEAD_F32OUT || lm_head_kind > SPB_HEAD_FP32)
+    return fail(SPB_ERR_ARG, "lm_head_kind %d outside 0..2", lm_head_kind);
   const SpbMetaHeader &h = header(plan->passes[pass]);
-  *out = score_workspace_layout(h.n_scored, h.n_targets, vocab, hidden_dim, nullptr);
+  *out = score_workspace_layout(h.n_scored, h.n_targets, vocab, hidden_dim, lm_head_kind, nullptr);
   return ok();
 }
 
@@ -857,7 +860,9 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   for (int t : P.tgt_tok)
     if (t >= a->vocab) return fail(SPB_ERR_ARG, "option token %d >= vocab %d", t, a->vocab);
   if (a->rows < h.n_tokens) return fail(SPB_ERR_SIZE, "hidden holds %lld rows, the pass has %d", (long long)a->rows, h.n_tokens);
-  const size_t need = score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, nullptr);
+  if (a->lm_head_kind < SPB_HEAD_F32OUT || a->lm_head_kind > SPB_HEAD_FP32)
+    return fail(SPB_ERR_ARG, "lm_head_kind %d outside 0..2", a->lm_head_kind);
+  const size_t need = score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, a->lm_head_kind, nullptr);
   if (a->workspace_bytes < need) return fail(SPB_ERR_SIZE, "workspace needs %zu bytes, got %zu", need, a->workspace_bytes);
   if (h.n_scored > 0 && (!a->hidden || !a->lm_head || !a->workspace || !a->lp || !a->p || !a->residual))
     return fail(SPB_ERR_ARG, "NULL tensor");
@@ -876,7 +881,7 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   L.step_slot = base + h.off_step_slot;
   L.step_row = base + h.off_step_row;
   size_t off[4];
-  score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, off);
+  score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, a->lm_head_kind, off);
   char *ws = (char *)a->workspace;
   L.part = (float *)(ws + off[0]);
   L.tz = (float *)(ws + off[1]);
@@ -884,6 +889,7 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   L.hg = ws + off[3];
   L.lp = a->lp; L.p = a->p; L.residual = a->residual;
   L.ev_begin = a->gemm_event_begin; L.ev_end = a->gemm_event_end;
+  L.kind = a->lm_head_kind;
   int e = launch_score(L, stream);
   if (e) return fail(SPB_ERR_HIP, "score launch: %s", hip_error_string(e));
   return ok();
@@ -913,12 +919,14 @@ spb_status check_batch(const spb_plan *plan, int32_t n, const int32_t *passes, i
 }  // namespace
 
 spb_status spb_score_batch_workspace_bytes(const spb_plan *plan, int32_t n, const int32_t *passes, int32_t vocab,
-                                           int32_t hidden_dim, size_t *out) {
+                                           int32_t hidden_dim, int32_t lm_head_kind, size_t *out) {
   int64_t m_tot = 0, t_tot = 0;
   spb_status st = check_batch(plan, n, passes, &m_tot, &t_tot);
   if (st != SPB_OK) return st;
   if (!out || vocab < 1 || hidden_dim < 1) return fail(SPB_ERR_ARG, "bad argument");
-  *out = score_batch_workspace_layout((int)m_tot, (int)t_tot, vocab, hidden_dim, nullptr);
+  if (lm_head_kind < SPB_HEAD_F32OUT || lm_head_kind > SPB_HEAD_FP32)
+    return fail(SPB_ERR_ARG, "lm_head_kind %d outside 0..2", lm_head_kind);
+  *out = score_batch_workspace_layout((int)m_tot, (int)t_tot, vocab, hidden_dim, lm_head_kind, nullptr);
   return ok();
 }
 
@@ -936,7 +944,10 @@ spb_status spb_score_options_batch(const spb_plan *plan, int32_t n, const int32_
   if (a0.vocab < 1) return fail(SPB_ERR_ARG, "vocab %d < 1", a0.vocab);
   if ((int64_t)a0.vocab * a0.hidden_dim * 2 > (int64_t)UINT32_MAX)
     return fail(SPB_ERR_DTYPE, "the lm head (%lld bytes) exceeds 4 GiB", (long long)a0.vocab * a0.hidden_dim * 2);
-  const size_t need = score_batch_workspace_layout((int)m_tot, (int)t_tot, a0.vocab, a0.hidden_dim, nullptr);
+  if (a0.lm_head_kind < SPB_HEAD_F32OUT || a0.lm_head_kind > SPB_HEAD_FP32)
+    return fail(SPB_ERR_ARG, "lm_head_kind %d outside 0..2", a0.lm_head_kind);
+  const size_t need =
+      score_batch_workspace_layout((int)m_tot, (int)t_tot, a0.vocab, a0.hidden_dim, a0.lm_head_kind, nullptr);
   if (workspace_bytes < need) return fail(SPB_ERR_SIZE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (m_tot > 0 && (!workspace || !a0.lm_head)) return fail(SPB_ERR_ARG, "NULL workspace or lm head");
   if ((uintptr_t)workspace % 256) return fail(SPB_ERR_ARG, "workspace must be 256-byte aligned");
@@ -948,7 +959,8 @@ spb_status spb_score_options_batch(const spb_plan *plan, int32_t n, const int32_
     const spb_score_args &a = args[i];
     const PassPlan &P = plan->passes[passes[i]];
     const SpbMetaHeader &h = header(P);
-    if (a.h_dtype != a0.h_dtype || a.hidden_dim != a0.hidden_dim || a.vocab != a0.vocab || a.lm_head != a0.lm_head)
+    if (a.h_dtype != a0.h_dtype || a.hidden_dim != a0.hidden_dim || a.vocab != a0.vocab || a.lm_head != a0.lm_head ||
+        a.lm_head_kind != a0.lm_head_kind)
       return fail(SPB_ERR_ARG, "batch entry %d disagrees with entry 0 on the hidden dtype/size or the lm head", i);
     for (int t : P.tgt_tok)
       if (t >= a.vocab) return fail(SPB_ERR_ARG, "option token %d >= vocab %d", t, a.vocab);
@@ -982,8 +994,9 @@ spb_status spb_score_options_batch(const spb_plan *plan, int32_t n, const int32_
   L.hidden_dim = a0.hidden_dim;
   L.lm_head = a0.lm_head;
   L.vocab = a0.vocab;
+  L.kind = a0.lm_head_kind;
   size_t off[6];
-  score_batch_workspace_layout(L.m_tot, L.t_tot, a0.vocab, a0.hidden_dim, off);
+  score_batch_workspace_layout(L.m_tot, L.t_tot, a0.vocab, a0.hidden_dim, a0.lm_head_kind, off);
   char *ws = (char *)workspace;
   L.part = (float *)(ws + off[0]);
   L.tz = (float *)(ws + off[1]);

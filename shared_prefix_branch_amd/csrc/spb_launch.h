@@ -34,9 +34,12 @@ struct ScoreLaunch {
   void *hg;      // workspace: gathered hidden states, bf16 [m_pad][hidden_dim]
   float *lp, *p, *residual;
   void *ev_begin, *ev_end;  // optional hipEvent_t around the GEMM kernel
+  int kind;                 // lm-head output kind (SPB_HEAD_*)
 };
 
 inline int n_vocab_slices(int vocab) { return (vocab + 255) / 256; }
+// bf16 planes of a gathered hidden row: three (hi, mid, lo) for the fp32 head
+inline int head_planes(int kind) { return kind == 2 ? 3 : 1; }
 
 // Scored rows per lm-head work group: n_chunks chunks of 32*mb rows (mb in
 // 1..8), the fewest chunks of at most 256 rows, each as small as possible.
@@ -65,6 +68,7 @@ struct ScoreBatchLaunch {
   float *part, *tz, *lse;  // workspace, combined rows / targets
   void *hg;
   int32_t *ctgt_off, *ctgt_tok;  // workspace: combined target CSR
+  int kind;                      // lm-head output kind (SPB_HEAD_*)
   void *ev_begin, *ev_end;
 };
 

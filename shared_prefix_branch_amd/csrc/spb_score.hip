@@ -63,6 +63,7 @@ struct GatherParams {
   const int32_t *scored;
   uint16_t *hg;
   int H, M;        // this call's scored rows
+  int planes;      // bf16 planes per gathered row: 1, or 3 (hi, mid, lo) for the fp32 head
   int row0;        // their first row in hg
   int zero_end;    // rows row0 + M .. zero_end are zeroed (padding)
   // batched calls: copy this pass's target CSR into the combined one
@@ -71,8 +72,21 @@ struct GatherParams {
   int t_base, t_end;  // the pass's first target in the combined CSR; total targets (last pass only: -1 otherwise)
 };
 
+__device__ inline float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x = hi + mid + lo exactly for an f32 x: each term is the bf16 (nearest
+// even) of what the previous ones left; the differences are exact in f32.
+__device__ inline void split3(float x, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+  hi = f2bf(x);
+  const float r1 = x - bf2f(hi);
+  mid = f2bf(r1);
+  lo = f2bf(r1 - bf2f(mid));
+}
+
 // hg[row0 + m] = bf16(hidden[scored[m]]) for m < M, zero rows up to
-// zero_end; with a combined CSR, also its rows' target ranges and tokens.
+// zero_end; with three planes, row m holds hi | mid | lo of the f32 row (a
+// bf16 row: itself | 0 | 0).  With a combined CSR, also its rows' target
+// ranges and tokens.
 template <int HIN>
 __global__ __launch_bounds__(256) void gather_hidden_kernel(GatherParams g) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // one 8-element unit
@@ -80,18 +94,28 @@ __global__ __launch_bounds__(256) void gather_hidden_kernel(GatherParams g) {
   const int n_rows = g.zero_end - g.row0;
   if (i >= (long long)n_rows * per_row) return;
   const int m = (int)(i / per_row), k = (int)(i % per_row) * 8;
-  uint4 v = {0u, 0u, 0u, 0u};
+  uint4 v = {0u, 0u, 0u, 0u}, v2 = {0u, 0u, 0u, 0u}, v3 = {0u, 0u, 0u, 0u};
   if (m < g.M) {
     const long long row = g.scored[m];
     if constexpr (HIN == SPB_BF16) {
       v = *(const uint4 *)((const uint16_t *)g.hidden + row * g.H + k);
     } else {
       const float4 *s = (const float4 *)((const float *)g.hidden + row * g.H + k);
-      float4 a = s[0], b = s[1];
-      v.x = f2bf(a.x) | (f2bf(a.y) << 16);
-      v.y = f2bf(a.z) | (f2bf(a.w) << 16);
-      v.z = f2bf(b.x) | (f2bf(b.y) << 16);
-      v.w = f2bf(b.z) | (f2bf(b.w) << 16);
+      const float4 a = s[0], b = s[1];
+      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t h[8], md[8], lw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (g.planes == 3) {
+          split3(x[j], h[j], md[j], lw[j]);
+        } else {
+          h[j] = f2bf(x[j]);
+          md[j] = lw[j] = 0u;
+        }
+      }
+      v = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      v2 = uint4{md[0] | (md[1] << 16), md[2] | (md[3] << 16), md[4] | (md[5] << 16), md[6] | (md[7] << 16)};
+      v3 = uint4{lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16), lw[4] | (lw[5] << 16), lw[6] | (lw[7] << 16)};
     }
     if (g.ctgt_off && k == 0) {
       const int t0 = g.tgt_off[m], t1 = g.tgt_off[m + 1];
@@ -100,13 +124,21 @@ __global__ __launch_bounds__(256) void gather_hidden_kernel(GatherParams g) {
       if (m == g.M - 1 && g.t_end >= 0) g.ctgt_off[g.row0 + g.M] = g.t_end;
     }
   }
-  *(uint4 *)(g.hg + (long long)(g.row0 + m) * g.H + k) = v;
+  uint16_t *dst = g.hg + (long long)(g.row0 + m) * g.planes * g.H + k;
+  *(uint4 *)dst = v;
+  if (g.planes == 3) {
+    *(uint4 *)(dst + g.H) = v2;
+    *(uint4 *)(dst + 2 * g.H) = v3;
+  }
 }
 
 struct HeadParams {
-  const uint16_t *hg;  // gathered hidden states [M_pad][H] bf16
+  const uint16_t *hg;  // gathered hidden states [M_pad][Hrow] bf16
   const uint16_t *W;
   int H, V, M;
+  int Hrow;       // hg row length: H, or 3H (planes hi | mid | lo) for the fp32 head
+  int SW;         // stages per sweep of W (H / 64); Hrow / 64 stages in all
+  int round_bf16; // bf16 head: each logit rounded to bf16 before the epilogue uses it
   int n_slices, n_mchunks;
   const int32_t *tgt_off, *tgt_tok;
   float *part, *tz;
@@ -209,11 +241,14 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   for (int i = 0; i < T::NH; ++i) {
     const int r = (wave * T::NH + i) * 8 + dr;
     const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
-    hoff[i] = ((uint32_t)(m0 + r) * (uint32_t)p.H + c * 8) * 2;
+    hoff[i] = ((uint32_t)(m0 + r) * (uint32_t)p.Hrow + c * 8) * 2;
   }
   const uint32_t lds0 = lds_addr(&lds[0]);
   auto issue_w = [&](int stage, int sl) {
-    const uint32_t kb = (uint32_t)stage * kKT * 2;
+    int ws = stage;  // stage within the sweep of W (stage < 3 SW)
+    if (ws >= p.SW) ws -= p.SW;
+    if (ws >= p.SW) ws -= p.SW;
+    const uint32_t kb = (uint32_t)ws * kKT * 2;
     const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
 #pragma unroll
     for (int i = 0; i < T::NW; ++i)
@@ -233,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x16{0.f};
 
-  const int S = p.H / kKT;
+  const int S = p.Hrow / kKT;
   const int last = S - 1;
   // Copies past the last stage reload it into a slot nothing reads again, so
   // the count of copies in flight is the same on every trip.
@@ -275,6 +310,14 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   wait_vmcnt<0>();  // no copy may land after the ring is reused or released
   lds_barrier();
   float (*red)[TM][2] = (float (*)[TM][2])lds;  // [4][TM][2], reusing the ring
+  if (p.round_bf16) {
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[vb][mb][r] = bf2f(f2bf(acc[vb][mb][r]));
+  }
 
   // epilogue.  Lane holds column m = m0 + mb*32 + qi; register r of block vb
   // holds vocabulary row v0 + wave*64 + vb*32 + (r/4)*8 + half*4 + r%4.
@@ -466,6 +509,7 @@ int launch_score(const ScoreLaunch &a, void *stream) {
   g.hg = (uint16_t *)a.hg;
   g.H = a.hidden_dim;
   g.M = a.n_scored;
+  g.planes = head_planes(a.kind);
   g.row0 = 0;
   g.zero_end = n_chunks * 32 * mb;
   int e = launch_gather(g, a.h_dtype, s);
@@ -477,6 +521,9 @@ int launch_score(const ScoreLaunch &a, void *stream) {
   p.H = a.hidden_dim;
   p.V = a.vocab;
   p.M = a.n_scored;
+  p.Hrow = a.hidden_dim * head_planes(a.kind);
+  p.SW = a.hidden_dim / kKT;
+  p.round_bf16 = a.kind == SPB_HEAD_BF16;
   p.n_slices = n_vocab_slices(a.vocab);
   p.n_mchunks = n_chunks;
   p.tgt_off = (const int32_t *)a.tgt_off;
@@ -516,6 +563,7 @@ int launch_score_batch(const ScoreBatchLaunch &a, void *stream) {
     g.hg = (uint16_t *)a.hg;
     g.H = a.hidden_dim;
     g.M = P.n_scored;
+    g.planes = head_planes(a.kind);
     g.row0 = a.m_off[i];
     g.zero_end = last ? m_pad : a.m_off[i] + P.n_scored;
     g.tgt_off = (const int32_t *)P.tgt_off;
@@ -533,6 +581,9 @@ int launch_score_batch(const ScoreBatchLaunch &a, void *stream) {
   p.H = a.hidden_dim;
   p.V = a.vocab;
   p.M = a.m_tot;
+  p.Hrow = a.hidden_dim * head_planes(a.kind);
+  p.SW = a.hidden_dim / kKT;
+  p.round_bf16 = a.kind == SPB_HEAD_BF16;
   p.n_slices = n_vocab_slices(a.vocab);
   p.n_mchunks = n_chunks;
   p.tgt_off = a.ctgt_off;

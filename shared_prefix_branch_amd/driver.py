@@ -54,7 +54,7 @@ class Job:
 
     def __init__(self, plan: Plan, hq: int, hkv: int, head_dim: int, hidden_dim: int, vocab: int,
                  qkv_dtype, out_dtype, hidden_dtype, device="cuda", scales=(1.0, 1.0, 1.0),
-                 batch_head: bool = False):
+                 batch_head: bool = False, lm_head_kind: int = 0):
         import torch
         self.torch = torch
         self.plan = plan
@@ -75,6 +75,7 @@ class Job:
         self._attn: List = []
         self._score: List = []
         self.batch_head = bool(batch_head)
+        self.lm_head_kind = int(lm_head_kind)
         if self.batch_head and plan.n_passes > 64:
             raise ValueError("batch_head covers at most 64 passes")
 
@@ -92,7 +93,8 @@ class Job:
         n = max(1, inf["n_tokens"])
         dev = self.device
         meta = t.empty(inf["meta_bytes"], dtype=t.uint8, device=dev)
-        ws_bytes = 256 if self.batch_head else max(256, score_workspace_bytes(self.plan, k, self.V, self.H))
+        ws_bytes = 256 if self.batch_head else max(256, score_workspace_bytes(self.plan, k, self.V, self.H,
+                                                                              self.lm_head_kind))
         ws = t.empty(ws_bytes, dtype=t.uint8, device=dev)
         return PassBuffers(
             inf["n_tokens"],
@@ -152,7 +154,8 @@ class Job:
         self._attn = [PreparedAttention(k, b.meta, b.q, b.k, b.v, b.o, scales=self.scales)
                       for k, b in enumerate(self.passes)]
         if self.batch_head:
-            nb = score_batch_workspace_bytes(self.plan, list(range(self.plan.n_passes)), self.V, self.H)
+            nb = score_batch_workspace_bytes(self.plan, list(range(self.plan.n_passes)), self.V, self.H,
+                                             self.lm_head_kind)
             self.batch_ws = t.empty(max(256, nb), dtype=t.uint8, device=self.device)
         self._pass_done = [None] * len(self.passes)
 
@@ -161,10 +164,12 @@ class Job:
             if self.batch_head:
                 ks = list(range(len(self.passes)))
                 self._score = [PreparedScoreBatch(ks, [b.meta for b in self.passes], [b.hidden for b in self.passes],
-                                                  lm_head, self.batch_ws, [b.slots[r] for b in self.passes])
+                                                  lm_head, self.batch_ws, [b.slots[r] for b in self.passes],
+                                                  self.lm_head_kind)
                                for r in range(2)]
             else:
-                self._score = [[PreparedScore(k, b.meta, b.hidden, lm_head, b.workspace, *b.slots[r])
+                self._score = [[PreparedScore(k, b.meta, b.hidden, lm_head, b.workspace, *b.slots[r],
+                                              lm_head_kind=self.lm_head_kind)
                                 for r in range(2)] for k, b in enumerate(self.passes)]
             self._head = lm_head
 

@@ -29,7 +29,8 @@ class Case:
 
     def __init__(self, wl: synth.Workload, budget: int, inputs: Optional[Sequence[int]] = None,
                  floors: bool = True, peaked: bool = False, device: str = "cuda", gen_device: str = "cuda",
-                 chained: bool = False, cache: Optional[dict] = None, batch_head: bool = False):
+                 chained: bool = False, cache: Optional[dict] = None, batch_head: bool = False,
+                 lm_head_kind: int = 0):
         import torch
         self.torch = torch
         self.wl = wl
@@ -49,6 +50,7 @@ class Case:
         self.scales = synth.fp8_scales(wl) if wl.dims.dtype == "fp8" else (1.0, 1.0, 1.0)
         self._blocks: Dict[tuple, tuple] = {} if cache is None else cache  # activations by identity
         self.batch_head = batch_head
+        self.lm_head_kind = lm_head_kind
 
     # -- inputs --------------------------------------------------------------
     def block(self, ident):
@@ -71,7 +73,8 @@ class Case:
         out = t.float32 if d.dtype == "f32" else t.bfloat16
         hid = t.float32 if d.dtype == "f32" else t.bfloat16
         self.job = Job(self.plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv, out, hid,
-                       device=self.device, scales=self.scales, batch_head=self.batch_head)
+                       device=self.device, scales=self.scales, batch_head=self.batch_head,
+                       lm_head_kind=self.lm_head_kind)
         self.job.load(self.provider)
         self.job.run(W)
         t.cuda.synchronize()
@@ -133,17 +136,25 @@ def check_attention(case: Case, inputs: Sequence[int] = None, branches_per_input
     return worst
 
 
+KIND_NAME = {0: "f32out", 1: "bf16", 2: "fp32"}
+
+
 def oracle_scores(case: Case, W, branch_keys: Sequence[tuple] = None):
-    """Oracle scores (with floors joined) for content branches keyed (input number, question)."""
+    """Oracle scores (with floors joined) for content branches keyed (input number, question),
+    for the case's lm-head kind.  The f32out and bf16 heads take f32 hidden rows
+    rounded to bf16 (the library rounds them on load); the fp32 head takes them
+    as they are."""
     lay = OT.build_layout(case.prob, floors=case.floors)
     hid_cache = {}
+    kind = KIND_NAME[case.lm_head_kind]
 
     def hidden(rows):
         out = []
         for r in rows:
             n = int(lay.row_input[r])
             if n not in hid_cache:
-                hid_cache[n] = case.oracle_inputs(n)[3]
+                h = case.oracle_inputs(n)[3]
+                hid_cache[n] = h if kind == "fp32" else ON.round_to_bf16(h)
             out.append(hid_cache[n][r - lay.inputs[n].first_row])
         return np.stack(out)
 
@@ -158,7 +169,7 @@ def oracle_scores(case: Case, W, branch_keys: Sequence[tuple] = None):
     for b in lay.branches():
         if b.is_floor and b.question in floors_needed:
             branches.append(b)
-    sc = OS.score_branches(lay, hidden, W, branches)
+    sc = OS.score_branches(lay, hidden, W, branches, lm_head=kind)
     OS.join_floors(lay, sc)
     return {k: v for k, v in sc.items() if lay.inputs[k[0]].kind == "input"}
 

@@ -199,6 +199,28 @@ def test_kernel_entry_points_validate_before_any_hip_call():
     S.vocab = 8
     S.workspace_bytes = 16
     assert L.spb_score_options(plan.handle, 0, meta, ctypes.byref(S), None) == -4      # workspace
+    S.workspace_bytes = 1 << 30
+    S.lm_head_kind = 3
+    assert L.spb_score_options(plan.handle, 0, meta, ctypes.byref(S), None) == -1      # lm-head kind
+    S.lm_head_kind = spb.HEAD_FP32
+    need = spb.score_workspace_bytes(plan, 0, 8, 128, spb.HEAD_FP32)
+    S.workspace_bytes = need - 1
+    assert L.spb_score_options(plan.handle, 0, meta, ctypes.byref(S), None) == -4      # fp32 workspace
+
+
+def test_lm_head_kind_workspace():
+    # the fp32 head keeps three bf16 planes of every gathered row; the other
+    # kinds one; kinds outside 0..2 are rejected
+    plan = spb.pack_pass(_prob())
+    f32out = spb.score_workspace_bytes(plan, 0, 1000, 256, spb.HEAD_F32OUT)
+    assert spb.score_workspace_bytes(plan, 0, 1000, 256, spb.HEAD_BF16) == f32out
+    fp32 = spb.score_workspace_bytes(plan, 0, 1000, 256, spb.HEAD_FP32)
+    m = plan.info(0)["n_scored_rows"]
+    assert fp32 - f32out >= 2 * m * 256 * 2
+    with pytest.raises(spb.SpbError):
+        spb.score_workspace_bytes(plan, 0, 1000, 256, 3)
+    with pytest.raises(spb.SpbError):
+        spb.score_batch_workspace_bytes(plan, [0], 1000, 256, -1)
 
 
 def test_upload_rejects_small_or_misaligned_buffers():
@@ -219,7 +241,7 @@ def test_batched_score_validation():
     ps = np.arange(plan.n_passes, dtype=np.int32)
     n = ctypes.c_size_t()
     i32 = ctypes.POINTER(ctypes.c_int32)
-    assert L.spb_score_batch_workspace_bytes(plan.handle, len(ps), ps.ctypes.data_as(i32), 64, 128,
+    assert L.spb_score_batch_workspace_bytes(plan.handle, len(ps), ps.ctypes.data_as(i32), 64, 128, 0,
                                              ctypes.byref(n)) == 0
     tot_m = sum(plan.info(k)["n_scored_rows"] for k in range(plan.n_passes))
     tot_t = sum(plan.info(k)["n_targets"] for k in range(plan.n_passes))
@@ -227,12 +249,12 @@ def test_batched_score_validation():
     # same answer through the binding
     assert spb.score_batch_workspace_bytes(plan, list(range(plan.n_passes)), 64, 128) == n.value
     dup = np.array([0, 0], np.int32)
-    assert L.spb_score_batch_workspace_bytes(plan.handle, 2, dup.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -1
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 2, dup.ctypes.data_as(i32), 64, 128, 0, ctypes.byref(n)) == -1
     bad = np.array([plan.n_passes], np.int32)
-    assert L.spb_score_batch_workspace_bytes(plan.handle, 1, bad.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -1
-    assert L.spb_score_batch_workspace_bytes(plan.handle, 0, ps.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -2
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 1, bad.ctypes.data_as(i32), 64, 128, 0, ctypes.byref(n)) == -1
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 0, ps.ctypes.data_as(i32), 64, 128, 0, ctypes.byref(n)) == -2
     big = np.zeros(65, np.int32)
-    assert L.spb_score_batch_workspace_bytes(plan.handle, 65, big.ctypes.data_as(i32), 64, 128, ctypes.byref(n)) == -2
+    assert L.spb_score_batch_workspace_bytes(plan.handle, 65, big.ctypes.data_as(i32), 64, 128, 0, ctypes.byref(n)) == -2
     # argument checks before any launch (fake device pointers are never touched)
     k = len(ps)
     metas = (ctypes.c_void_p * k)(*[4096 * (i + 1) for i in range(k)])
@@ -244,12 +266,15 @@ def test_batched_score_validation():
     ws_ok = n.value
     call = lambda ws, nbytes: L.spb_score_options_batch(plan.handle, k, ps.ctypes.data_as(i32), metas, A,
                                                         ctypes.c_void_p(ws), nbytes, None)
-    L.spb_score_batch_workspace_bytes(plan.handle, k, ps.ctypes.data_as(i32), 64, 128, ctypes.byref(n))
+    L.spb_score_batch_workspace_bytes(plan.handle, k, ps.ctypes.data_as(i32), 64, 128, 0, ctypes.byref(n))
     assert call(1 << 23, n.value - 1) == -4                 # workspace too small
     assert call((1 << 23) + 4, n.value) == -1               # workspace misaligned
     A[1].hidden_dim = 192
     assert call(1 << 23, n.value) == -1                     # entries disagree
     A[1].hidden_dim = 128
+    A[1].lm_head_kind = spb.HEAD_BF16
+    assert call(1 << 23, n.value) == -1                     # entries disagree on the lm-head kind
+    A[1].lm_head_kind = 0
     for i in range(k):
         A[i].vocab = 8
     assert call(1 << 23, 1 << 30) == -1                     # a token >= vocab

@@ -87,7 +87,44 @@ def test_bf16_decode_exact():
     assert np.array_equal(ON.to_f64(x), x.double().numpy())
 
 
+def test_round_to_bf16_matches_torch_with_ties():
+    # random f32 values plus exact midpoints between neighbouring bf16 values
+    # (representable in f32), which must go to the even significand
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=4096).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 4096).astype(np.float32)
+    b = torch.from_numpy(rng.normal(size=2048).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    ulp = np.ldexp(1.0, np.frexp(b.astype(np.float64))[1] - 8)
+    mid = (b.astype(np.float64) + ulp / 2).astype(np.float32)  # exact in f32
+    x = np.concatenate([x, mid, np.float32([0.0, -0.0, 2.0 ** -130, -(2.0 ** -140)])])
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(ON.round_to_bf16(x.astype(np.float64)), want)
+    # by hand: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> 1 (even);
+    # 1 + 3 2^-8 halfway between 1 + 2^-7 and 1 + 2^-6 -> 1 + 2^-6 (even)
+    assert ON.round_to_bf16(1 + 2.0 ** -8) == 1.0
+    assert ON.round_to_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+
+
 # ----------------------------------------------------------------------------- scoring closed forms
+
+def test_bf16_lm_head_rounds_the_logits():
+    # vocabulary of 3, hidden size 1, h = 1: the logits are W itself.
+    # z0 = 1 + 2^-9 is not a bf16 value and rounds to 1.
+    prob, lay = _layout_one_branch(0, 1, [(0,), (1,)], 3)
+    W = np.array([[1 + 2.0 ** -9], [0.5], [-1.0]])
+    hid = np.ones((lay.n_rows, 1))
+    def by_hand(z):
+        lse = math.log(sum(math.exp(v) for v in z))
+        return [z[0] - lse, z[1] - lse]
+    for kind, z in (("f32out", [1 + 2.0 ** -9, 0.5, -1.0]), ("fp32", [1 + 2.0 ** -9, 0.5, -1.0]),
+                    ("bf16", [1.0, 0.5, -1.0])):
+        sc = OS.score_branches(lay, lambda rows: hid[rows], W, lm_head=kind)[(0, 0)]
+        assert np.allclose(sc.lp, by_hand(z), rtol=0, atol=1e-15), kind
+        e = np.exp(by_hand(z))
+        assert np.allclose(sc.p, e / e.sum(), rtol=0, atol=1e-15)
+        assert sc.residual == pytest.approx(1 - e.sum(), abs=1e-15)
+    with pytest.raises(ValueError):
+        OS.score_branches(lay, lambda rows: hid[rows], W, lm_head="f16")
+
 
 def _layout_one_branch(C, L, options, vocab, floors=False):
     opts_flat = [t for o in options for t in o]
