@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--head-batch", action="store_true",
                     help="one lm-head launch for all passes of the step (spb_score_options_batch) "
                          "instead of one per pass")
+    ap.add_argument("--lm-head", default="f32out", choices=["f32out", "bf16", "fp32"],
+                    help="lm-head output kind (f32out is the default of the engine the pages describe)")
     ap.add_argument("--head-sweep", default="",
                     help="comma-separated scored-row counts: time the lm head alone on the news head shape")
     return ap.parse_args()
@@ -144,8 +146,9 @@ def main():
         return qc, kc, vc, h.to(hid_dt)
 
     batch_head = args.head_batch and plan.n_passes <= 64
+    head_kind = {"f32out": 0, "bf16": 1, "fp32": 2}[args.lm_head]
     job = Job(plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv_dt, out_dt, hid_dt, device=dev, scales=scales,
-              batch_head=batch_head)
+              batch_head=batch_head, lm_head_kind=head_kind)
     job.load(provider)
     W = synth.lm_head(wl, device=dev)
     torch.cuda.synchronize()
@@ -215,8 +218,12 @@ def main():
     head_tflops = head_flops.sum() / (head_ms.sum() * 1e-3) / 1e12
     head_gbs = head_bytes.sum() / (head_ms.sum() * 1e-3) / 1e9
     head_bound = "mfma" if M.mean() > HEAD_RIDGE_ROWS else "hbm"
-    traffic, traffic_src = (measured_traffic("batched" if batch_head else "per_pass") if args.workload == "news"
-                            else (None, "counters taken on news only"))
+    if args.workload != "news":
+        traffic, traffic_src = None, "counters taken on news only"
+    elif head_kind != 0:
+        traffic, traffic_src = None, "counters taken for the f32out lm head only"
+    else:
+        traffic, traffic_src = measured_traffic("batched" if batch_head else "per_pass")
     if head_bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(head_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(head_tflops / PEAK_BF16_TFLOPS, 4)}
@@ -226,6 +233,8 @@ def main():
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["traffic_source"] = traffic_src
     roof["kernel"] = "head_lse_kernel (lm-head GEMM with fused log-sum-exp, in spb_score_options)"
+    # the fp32 head runs three bf16 products per logit term (hi, mid, lo planes of h)
+    roof["mfma_products_per_term"] = 3 if head_kind == 2 else 1
     roof["per_launch"] = {"ms": [round(x, 4) for x in head_ms], "scored_rows": M.astype(int).tolist(),
                           "flops_per_scored_row": 2 * d.hidden * d.vocab,
                           "algorithmic_bytes": [int(x) for x in head_bytes]}
@@ -242,7 +251,7 @@ def main():
                                f"token budget {budget}, {n_pass} passes",
                    "packed_tokens": tokens, "questions": questions, "token_budget": budget,
                    "hq": d.hq, "hkv": d.hkv, "head_dim": d.head_dim, "hidden": d.hidden, "vocab": d.vocab,
-                   "lm_head_launches_per_step": n_head},
+                   "lm_head": args.lm_head, "lm_head_launches_per_step": n_head},
         "questions_per_s": round(questions / (ms_step * 1e-3), 1),
         "attention": {"ms": round(float(att_ms.sum()), 4), "tflops": round(att_tflops, 2),
                       "mfma_util": round(att_tflops / PEAK_BF16_TFLOPS, 4),
