@@ -81,9 +81,11 @@ def attention_input(layout: Layout, li: LInput, q: np.ndarray, k: np.ndarray, v:
     want = range(len(li.branches)) if branches is None else branches
     for bi in want:
         b = li.branches[bi]
-        t0 = b.first_row - base
-        seq = np.r_[0:C, t0:t0 + b.L]
-        out[t0:t0 + b.L] = causal_attention_tail(q[t0:t0 + b.L], k[seq], v[seq], scale)
+        # content then the whole template (shared tokens first): every template
+        # token attends causally along this sequence
+        tmpl = np.asarray(b.template_rows, np.int64) - base
+        seq = np.r_[0:C, tmpl]
+        out[tmpl] = causal_attention_tail(q[tmpl], k[seq], v[seq], scale)
         for ni in range(len(b.trie.prefixes)):
             x = b.node_row0 + ni
             path = np.asarray(root_path(layout, x)) - base
@@ -103,6 +105,7 @@ def dense_mask(layout: Layout) -> np.ndarray:
         for bi, b in enumerate(li.branches):
             for ni, p in enumerate(b.trie.prefixes):
                 prefix[b.node_row0 + ni] = p
+    tp = layout.row_tprefix
     M = np.zeros((N, N), dtype=bool)
     for i in range(N):
         for j in range(N):
@@ -110,6 +113,18 @@ def dense_mask(layout: Layout) -> np.ndarray:
                 continue
             if kind[j] == 0:
                 M[i, j] = (pos[j] <= pos[i]) if kind[i] == 0 else True
+            elif kind[j] == 1 and br[j] < 0:
+                # a shared template token: seen by the shared tokens whose prefix
+                # extends its own, and by the template tokens and trie nodes of
+                # every question whose template starts with its prefix and goes
+                # on past it (a question's last token is never shared)
+                if kind[i] == 0 or len(tp[j]) > len(tp[i]) or tp[i][:len(tp[j])] != tp[j]:
+                    continue
+                if br[i] >= 0:
+                    full = len(layout.inputs[inp[i]].branches[br[i]].template_rows)
+                    M[i, j] = len(tp[j]) < full
+                else:
+                    M[i, j] = True
             elif kind[j] == 1:
                 if kind[i] == 0 or br[i] != br[j]:
                     continue

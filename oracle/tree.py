@@ -25,6 +25,19 @@ attends to, itself last) is the chain of ancestors:
   template token j    -> template token j-1
   trie node, depth 1  -> last template token
   trie node, depth k  -> the trie node of its first k-1 tokens
+
+Template tries [PyPI "Layout": templates to token tries; "What it does":
+placeholders turn one template into a grid of questions].  When the
+templates' token ids are given, the questions of one input share the tokens
+of common template prefixes.  Reading taken: a prefix of a question's template
+up to (not including) its last token is shared when at least two of the
+input's questions start with it; the last token -- the answer slot -- is
+always the question's own.  A shared token is one logical token (one row, one
+set of activations) whose parent is the shared token before it (or the last
+content token); a question's own template tokens follow its last shared token.
+Logical rows of an input: the content, then for each question in order the
+shared tokens of its template not yet numbered, its own template tokens and
+its option-trie nodes.  Without template token ids nothing is shared.
 """
 from __future__ import annotations
 
@@ -67,11 +80,17 @@ def build_trie(options: List[tuple]) -> Trie:
 class LBranch:
     input_no: int         # logical input number (row-numbering order)
     question: int
-    first_row: int        # logical row of template token 0
-    L: int
+    first_row: int        # logical row of the question's first own template token
+    L: int                # own template tokens (the whole template when nothing is shared)
     node_row0: int        # logical row of trie node 0
     trie: Trie
     is_floor: bool
+    stem_rows: List[int] = dataclasses.field(default_factory=list)  # shared template tokens, in order
+
+    @property
+    def template_rows(self) -> List[int]:
+        """Logical rows of the whole template, in order (shared, then own)."""
+        return list(self.stem_rows) + list(range(self.first_row, self.first_row + self.L))
 
     @property
     def last_row(self) -> int:
@@ -99,8 +118,12 @@ class Layout:
     #           position: content index / template index / node index)
     row_input: np.ndarray
     row_kind: np.ndarray  # 0 content, 1 template, 2 trie node
-    row_branch: np.ndarray
-    row_pos: np.ndarray
+    row_branch: np.ndarray  # branch index within the input; -1 for content and shared template tokens
+    row_pos: np.ndarray   # content index / template index / trie node index
+    # per row: the template token ids from the template's start through this
+    # row (template rows), the whole template (trie nodes), None (content);
+    # only when template token ids are given
+    row_tprefix: list = None
 
     def branches(self):
         for li in self.inputs:
@@ -129,32 +152,69 @@ def build_layout(problem, floors: bool = True) -> Layout:
         for q in sorted(set(int(q) for q in problem.branch_q)):
             plan.append(("floor", q, 0, [q]))
 
-    parent, r_in, r_kind, r_br, r_pos = [], [], [], [], []
+    has_tmpl = getattr(problem, "tmpl_tok", None) is not None
+
+    def template(q):
+        off = int(np.sum(problem.q_len[:q]))
+        return tuple(int(x) for x in problem.tmpl_tok[off:off + int(problem.q_len[q])])
+
+    parent, r_in, r_kind, r_br, r_pos, r_tp = [], [], [], [], [], []
     inputs = []
     row = 0
     for n, (kind, ident, C, qs) in enumerate(plan):
         li = LInput(kind, ident, row, C, [])
         for t in range(C):
             parent.append(row + t - 1 if t > 0 else -1)
-            r_in.append(n); r_kind.append(0); r_br.append(-1); r_pos.append(t)
+            r_in.append(n); r_kind.append(0); r_br.append(-1); r_pos.append(t); r_tp.append(None)
         row += C
         last_content = li.first_row + C - 1 if C > 0 else -1
+        # shared template prefixes: those at least two of the input's
+        # questions start with, never including a question's last token
+        shared = [0] * len(qs)
+        if has_tmpl:
+            count = {}
+            for q in qs:
+                T = template(q)
+                for k in range(1, len(T)):
+                    count[T[:k]] = count.get(T[:k], 0) + 1
+            for bi, q in enumerate(qs):
+                T = template(q)
+                s = 0
+                while s < len(T) - 1 and count[T[:s + 1]] >= 2:
+                    s += 1
+                shared[bi] = s
+        stem_row = {}
         for bi, q in enumerate(qs):
             L = int(problem.q_len[q])
+            T = template(q) if has_tmpl else None
+            s = shared[bi]
+            stem = []
+            for k in range(1, s + 1):
+                p = T[:k]
+                if p not in stem_row:
+                    stem_row[p] = row
+                    parent.append(stem_row[T[:k - 1]] if k > 1 else last_content)
+                    r_in.append(n); r_kind.append(1); r_br.append(-1); r_pos.append(k - 1); r_tp.append(p)
+                    row += 1
+                stem.append(stem_row[p])
             tr = trie_of(q)
-            b = LBranch(n, q, row, L, row + L, tr, kind == "floor")
-            for j in range(L):
-                parent.append(row + j - 1 if j > 0 else last_content)
-                r_in.append(n); r_kind.append(1); r_br.append(bi); r_pos.append(j)
+            own = L - s
+            b = LBranch(n, q, row, own, row + own, tr, kind == "floor", stem)
+            for j in range(own):
+                parent.append(row + j - 1 if j > 0 else (stem[-1] if stem else last_content))
+                r_in.append(n); r_kind.append(1); r_br.append(bi); r_pos.append(s + j)
+                r_tp.append(T[:s + j + 1] if has_tmpl else None)
             for ni, p in enumerate(tr.prefixes):
                 par = b.last_row if len(p) == 1 else b.node_row0 + tr.index[p[:-1]]
                 parent.append(par)
                 r_in.append(n); r_kind.append(2); r_br.append(bi); r_pos.append(ni)
-            row += L + len(tr.prefixes)
+                r_tp.append(T if has_tmpl else None)
+            row += own + len(tr.prefixes)
             li.branches.append(b)
         inputs.append(li)
     return Layout(inputs, row, np.asarray(parent, np.int64), np.asarray(r_in, np.int64),
-                  np.asarray(r_kind, np.int64), np.asarray(r_br, np.int64), np.asarray(r_pos, np.int64))
+                  np.asarray(r_kind, np.int64), np.asarray(r_br, np.int64), np.asarray(r_pos, np.int64),
+                  r_tp if has_tmpl else None)
 
 
 def root_path(layout: Layout, x: int) -> List[int]:

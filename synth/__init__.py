@@ -47,6 +47,9 @@ class Problem:
     tok_off: np.ndarray       # int32 [n_options + 1]
     tok: np.ndarray           # int32 [n_option_tokens]
     vocab: int
+    # template token ids, question after question (q_len[q] each); None: the
+    # templates' tokens are not given and no template tokens are shared
+    tmpl_tok: Optional[np.ndarray] = None
 
     @property
     def n_inputs(self) -> int:
@@ -65,6 +68,11 @@ class Problem:
     def questions_of(self, i: int) -> List[int]:
         return [int(q) for q in self.branch_q[self.branch_off[i]:self.branch_off[i + 1]]]
 
+    def template_of(self, q: int) -> tuple:
+        """Template token ids of question q (requires tmpl_tok)."""
+        off = int(np.sum(self.q_len[:q]))
+        return tuple(int(t) for t in self.tmpl_tok[off:off + int(self.q_len[q])])
+
     def subset(self, inputs: Sequence[int]) -> "Problem":
         """The same questions, asked only by the listed inputs (in that order)."""
         cl = np.asarray([self.content_len[i] for i in inputs], np.int32)
@@ -73,7 +81,7 @@ class Problem:
             bq.extend(self.questions_of(i))
             off.append(len(bq))
         return Problem(cl, np.asarray(off, np.int32), np.asarray(bq, np.int32),
-                       self.q_len, self.opt_off, self.tok_off, self.tok, self.vocab)
+                       self.q_len, self.opt_off, self.tok_off, self.tok, self.vocab, self.tmpl_tok)
 
 
 @dataclasses.dataclass
@@ -117,7 +125,9 @@ def logical_inputs(problem: Problem, floors: bool) -> List[tuple]:
 
 
 def input_rows(problem: Problem, which: tuple) -> int:
-    """Logical rows owned by one logical input (content + templates + trie nodes)."""
+    """Logical rows owned by one logical input (content + templates + trie nodes)
+    when no template tokens are shared; an upper bound otherwise (activation
+    blocks are drawn at this size and a layout uses their first rows)."""
     kind, idx = which
     if kind == "input":
         qs = problem.questions_of(idx)
@@ -175,14 +185,37 @@ def _label_options(rng, n_opts, max_len, vocab, lead_pool=3):
             return opts
 
 
-def _assemble(content_len, asks, q_len, q_opts, vocab) -> Problem:
+def _assemble(content_len, asks, q_len, q_opts, vocab, templates=None) -> Problem:
     branch_off, branch_q = _csr(asks)
     opt_counts = [len(o) for o in q_opts]
     opt_off = np.concatenate([[0], np.cumsum(opt_counts)]).astype(np.int32)
     flat_opts = [o for opts in q_opts for o in opts]
     tok_off, tok = _csr(flat_opts)
+    tmpl = None
+    if templates is not None:
+        assert [len(x) for x in templates] == [int(n) for n in q_len]
+        tmpl = np.asarray([t for x in templates for t in x], np.int32)
     return Problem(np.asarray(content_len, np.int32), branch_off, branch_q,
-                   np.asarray(q_len, np.int32), opt_off, tok_off, tok, int(vocab))
+                   np.asarray(q_len, np.int32), opt_off, tok_off, tok, int(vocab), tmpl)
+
+
+def _distinct_seqs(rng, n, max_len, vocab):
+    """n token sequences of 1..max_len tokens with distinct first tokens."""
+    firsts = rng.choice(vocab, size=n, replace=False)
+    return [tuple([int(f)] + [int(x) for x in rng.integers(0, vocab, size=int(rng.integers(0, max_len)))])
+            for f in firsts]
+
+
+def _grid_templates(rng, vocab, lead=(8, 14), n_a=(3, 5), n_b=(3, 5)):
+    """One template with two placeholders expanded into a grid of questions:
+    lead-in, value of A (1-3 tokens), connector, value of B (1-2 tokens), a
+    closing run ending in the answer slot."""
+    lead_in = [int(x) for x in rng.integers(0, vocab, size=int(rng.integers(lead[0], lead[1] + 1)))]
+    a_vals = _distinct_seqs(rng, int(rng.integers(n_a[0], n_a[1] + 1)), 3, vocab)
+    mid = [int(x) for x in rng.integers(0, vocab, size=int(rng.integers(2, 5)))]
+    b_vals = _distinct_seqs(rng, int(rng.integers(n_b[0], n_b[1] + 1)), 2, vocab)
+    tail = [int(x) for x in rng.integers(0, vocab, size=int(rng.integers(1, 4)))]
+    return [tuple(lead_in + list(a) + mid + list(b) + tail) for a in a_vals for b in b_vals]
 
 
 def make_problem(name: str, cfg_seed: int, **over) -> Problem:
@@ -231,6 +264,41 @@ def make_problem(name: str, cfg_seed: int, **over) -> Problem:
             k = int(rng.integers(20, 81))
             asks.append(sorted(int(q) for q in rng.choice(nq, size=k, replace=False)))
         return _assemble(cl, asks, q_len, q_opts, V)
+    if name == "grid":
+        # questions from placeholder templates: every content asks the grids of
+        # a few templates, whose questions share lead-ins and partial fillings
+        V = over.get("vocab", 262144)
+        n_in = over.get("n_inputs", 16)
+        templates = []
+        for _ in range(over.get("n_templates", 3)):
+            templates += _grid_templates(rng, V)
+        nq = len(templates)
+        q_opts = [_single_token_options(rng, 2, V) for _ in range(nq)]
+        cl = rng.integers(over.get("min_content", 200), over.get("max_content", 400) + 1, size=n_in)
+        return _assemble(cl, [list(range(nq))] * n_in, [len(x) for x in templates], q_opts, V, templates)
+    if name == "random_shared":
+        # small random problems whose templates share lead-ins (a pool of two)
+        V = over.get("vocab", 64)
+        n_in = over.get("n_inputs", 3)
+        nq = over.get("n_questions", 6)
+        max_c = over.get("max_content", 20)
+        leads = [[int(x) for x in rng.integers(0, V, size=int(rng.integers(1, over.get("max_lead", 5) + 1)))]
+                 for _ in range(2)]
+        templates = []
+        for _ in range(nq):
+            lead = leads[int(rng.integers(0, 2))][:int(rng.integers(0, over.get("max_lead", 5) + 1))]
+            rest = [int(x) for x in rng.integers(0, over.get("tail_vocab", V), size=int(rng.integers(1, 4)))]
+            templates.append(tuple(lead + rest))
+        q_opts = []
+        for _ in range(nq):
+            n_o = int(rng.integers(1, over.get("max_options", 3) + 1))
+            q_opts.append(_label_options(rng, n_o, over.get("max_option_tokens", 3), V, lead_pool=min(3, V)))
+        cl = rng.integers(over.get("min_content", 0), max_c + 1, size=n_in)
+        asks = []
+        for _ in range(n_in):
+            k = int(rng.integers(1, nq + 1))
+            asks.append(sorted(int(q) for q in rng.choice(nq, size=k, replace=False)))
+        return _assemble(cl, asks, [len(x) for x in templates], q_opts, V, templates)
     if name == "random":
         # small random problems for oracle self-tests and packer tests
         V = over.get("vocab", 64)
@@ -260,6 +328,8 @@ CONFIGS: Dict[str, dict] = {
     "moderation": dict(cfg_seed=3, dims=Dims(32, 16, 128, 3840, 262144, "bf16"), budgets=[16384]),
     "extreme": dict(cfg_seed=4, dims=Dims(32, 8, 128, 3840, 262144, "bf16"), budgets=[16384]),
     "fp8": dict(cfg_seed=5, dims=Dims(32, 8, 128, 3840, 262144, "fp8"), budgets=[8192, 16384, 32768]),
+    # template tries (grids of placeholder questions sharing template prefixes)
+    "grid": dict(cfg_seed=6, dims=Dims(32, 16, 128, 3840, 262144, "bf16"), budgets=[16384]),
 }
 
 

@@ -258,6 +258,110 @@ def test_per_sequence_equals_dense_mask(seed):
         assert np.allclose(per, dense[lo:hi], atol=1e-12)
 
 
+def _shared_problem(seed, **kw):
+    args = dict(vocab=16, n_inputs=3, n_questions=6, max_content=8, max_lead=4, tail_vocab=4,
+                max_options=3, max_option_tokens=3)
+    args.update(kw)
+    return synth.make_problem("random_shared", seed, **args)
+
+
+def test_shared_template_layout_by_hand():
+    # one input (C = 2) asking (1,2,3), (1,2,4), (1,5), (6,): the proper prefixes
+    # (1) [3 questions] and (1,2) [2 questions] are shared; last tokens never
+    prob = synth.Problem(np.array([2], np.int32), np.array([0, 4], np.int32), np.array([0, 1, 2, 3], np.int32),
+                         np.array([3, 3, 2, 1], np.int32), np.arange(5, dtype=np.int32),
+                         np.arange(5, dtype=np.int32), np.array([7, 8, 9, 10], np.int32), 16,
+                         np.array([1, 2, 3, 1, 2, 4, 1, 5, 6], np.int32))
+    lay = OT.build_layout(prob, floors=False)
+    # rows: content 0,1 | (1) 2, (1,2) 3, q0 own "3" 4 | q1 own "4" 5 | q2 own "5" 6 | q3 own "6" 7
+    assert lay.n_rows == 8
+    assert lay.parent.tolist() == [-1, 0, 1, 2, 3, 3, 2, 1]
+    b = lay.inputs[0].branches
+    assert [x.template_rows for x in b] == [[2, 3, 4], [2, 3, 5], [2, 6], [7]]
+    assert [x.last_row for x in b] == [4, 5, 6, 7]
+    assert lay.row_branch.tolist() == [-1, -1, -1, -1, 0, 1, 2, 3]
+    M = OA.dense_mask(lay)
+    assert np.nonzero(M[4])[0].tolist() == [0, 1, 2, 3, 4]
+    assert np.nonzero(M[6])[0].tolist() == [0, 1, 2, 6]
+    assert np.nonzero(M[7])[0].tolist() == [0, 1, 7]
+    # a template that is a proper prefix of two others keeps its last token:
+    # (1,2) alone; (1,2,3) and (1,2,4) share (1) and (1,2)
+    prob2 = synth.Problem(np.array([0], np.int32), np.array([0, 3], np.int32), np.array([0, 1, 2], np.int32),
+                          np.array([2, 3, 3], np.int32), np.arange(4, dtype=np.int32),
+                          np.arange(4, dtype=np.int32), np.array([7, 8, 9], np.int32), 16,
+                          np.array([1, 2, 1, 2, 3, 1, 2, 4], np.int32))
+    lay2 = OT.build_layout(prob2, floors=False)
+    b2 = lay2.inputs[0].branches
+    assert [x.template_rows for x in b2] == [[0, 1], [0, 2, 3], [0, 2, 4]]
+    M2 = OA.dense_mask(lay2)
+    assert np.nonzero(M2[1])[0].tolist() == [0, 1]        # q0's last token does not see (1,2)
+    for x in range(lay2.n_rows):
+        assert set(np.nonzero(M2[x])[0].tolist()) == set(OT.root_path(lay2, x))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_shared_templates_per_sequence_equals_dense_mask(seed):
+    prob = _shared_problem(200 + seed)
+    lay = OT.build_layout(prob, floors=True)
+    assert any(b.stem_rows for b in lay.branches())
+    M = OA.dense_mask(lay)
+    for x in range(lay.n_rows):
+        assert set(np.nonzero(M[x])[0].tolist()) == set(OT.root_path(lay, x))
+    rng = np.random.default_rng(seed)
+    n = lay.n_rows
+    q = rng.normal(size=(n, 4, 8)); k = rng.normal(size=(n, 2, 8)); v = rng.normal(size=(n, 2, 8))
+    dense = OA.attention_dense(lay, q, k, v, mask=M)
+    for li in lay.inputs:
+        lo = li.first_row
+        hi = lo + int((lay.row_input == lay.row_input[lo]).sum())
+        per = OA.attention_input(lay, li, q[lo:hi], k[lo:hi], v[lo:hi])
+        assert np.allclose(per, dense[lo:hi], atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_sharing_template_tokens_only_packs_them_once(seed):
+    # the same problem without template token ids gives every question its own
+    # copy of its template; copies that carry the shared tokens' activations give
+    # the same attention rows and the same scores
+    prob = _shared_problem(300 + seed)
+    unshared = synth.Problem(prob.content_len, prob.branch_off, prob.branch_q, prob.q_len, prob.opt_off,
+                             prob.tok_off, prob.tok, prob.vocab)
+    S = OT.build_layout(prob, floors=True)
+    U = OT.build_layout(unshared, floors=True)
+    assert S.n_rows < U.n_rows
+    # U row -> S row carrying the same token
+    to_s = np.empty(U.n_rows, np.int64)
+    for ls, lu in zip(S.inputs, U.inputs):
+        for t in range(lu.C):
+            to_s[lu.first_row + t] = ls.first_row + t
+        for bs, bu in zip(ls.branches, lu.branches):
+            assert bu.L == len(bs.template_rows)
+            to_s[bu.first_row:bu.first_row + bu.L] = bs.template_rows
+            nn = len(bu.trie.prefixes)
+            to_s[bu.node_row0:bu.node_row0 + nn] = np.arange(bs.node_row0, bs.node_row0 + nn)
+    rng = np.random.default_rng(seed)
+    n, H = S.n_rows, 6
+    q = rng.normal(size=(n, 4, 8)); k = rng.normal(size=(n, 2, 8)); v = rng.normal(size=(n, 2, 8))
+    hid = rng.normal(size=(n, H)); W = rng.normal(size=(prob.vocab, H))
+
+    def att(lay, q, k, v):
+        out = []
+        for li in lay.inputs:
+            lo = li.first_row
+            hi = lo + int((lay.row_input == lay.row_input[lo]).sum())
+            out.append(OA.attention_input(lay, li, q[lo:hi], k[lo:hi], v[lo:hi]))
+        return np.concatenate(out)
+
+    a_s = att(S, q, k, v)
+    a_u = att(U, q[to_s], k[to_s], v[to_s])
+    assert np.allclose(a_u, a_s[to_s], atol=1e-12)
+    sc_s = OS.score_branches(S, lambda rows: hid[rows], W)
+    sc_u = OS.score_branches(U, lambda rows: hid[to_s[rows]], W)
+    for key in sc_u:
+        assert np.allclose(sc_u[key].lp, sc_s[key].lp, atol=1e-12)
+        assert np.allclose(sc_u[key].p, sc_s[key].p, atol=1e-12)
+
+
 def test_dense_mask_matches_root_paths():
     prob = synth.make_problem("random", 7, vocab=8, n_inputs=2, n_questions=3, max_content=6,
                               max_len=4, max_options=4, max_option_tokens=4)
