@@ -79,7 +79,18 @@ const char *spb_fingerprint(void);
  * id; inside an input its content rows, then per branch the template rows
  * followed by the option-trie nodes of its question.  Trie nodes are the
  * distinct proper prefixes of the options in first-appearance order (options
- * in order, each option's prefixes by increasing length). */
+ * in order, each option's prefixes by increasing length).
+ *
+ * Template tries [PyPI "Layout": templates to token tries; "What it does":
+ * placeholders turn one template into a grid of questions]: with tmpl_tok
+ * (the template token ids, question after question, q_len[q] each; NULL: none
+ * given), the questions of one input share the tokens of every template prefix
+ * that at least two of them start with, except that a question's last
+ * template token is always its own.  A shared token is one logical row; the
+ * shared rows of a branch's template come, in template order, right before
+ * its first own template row in the numbering when they have not appeared
+ * earlier in that input.  Token ids are only compared, never bounds-checked
+ * against the vocabulary. */
 typedef struct {
   int32_t n_inputs;
   const int32_t *content_len; /* [n_inputs], >= 0                  */
@@ -91,6 +102,7 @@ typedef struct {
   const int32_t *tok_off;     /* [opt_off[n_questions] + 1]        */
   const int32_t *tok;         /* [tok_off[n_options]], < vocab     */
   int32_t vocab;
+  const int32_t *tmpl_tok;    /* [sum q_len] or NULL (no sharing)  */
 } spb_problem;
 
 /* Packing options; request limits default to the man page's [man PARAMETERS]. */

@@ -52,7 +52,8 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 class _Problem(ctypes.Structure):
     _fields_ = [("n_inputs", ctypes.c_int32), ("content_len", _i32p), ("branch_off", _i32p),
                 ("branch_q", _i32p), ("n_questions", ctypes.c_int32), ("q_len", _i32p),
-                ("opt_off", _i32p), ("tok_off", _i32p), ("tok", _i32p), ("vocab", ctypes.c_int32)]
+                ("opt_off", _i32p), ("tok_off", _i32p), ("tok", _i32p), ("vocab", ctypes.c_int32),
+                ("tmpl_tok", _i32p)]
 
 
 class _PackOpts(ctypes.Structure):
@@ -229,6 +230,12 @@ def pack_pass(problem, token_budget: int = 16384, floors: bool = True, **limits)
     for f, a in arrs.items():
         setattr(P, f, _ptr(a, _i32p))
     P.vocab = int(problem.vocab)
+    tmpl = getattr(problem, "tmpl_tok", None)
+    if tmpl is not None:
+        arrs["tmpl_tok"] = np.ascontiguousarray(tmpl, dtype=np.int32)
+        if arrs["tmpl_tok"].shape[0] != int(arrs["q_len"].sum()):
+            raise SpbError(-1, "tmpl_tok must hold sum(q_len) token ids")
+        P.tmpl_tok = _ptr(arrs["tmpl_tok"], _i32p)
     O = _PackOpts()
     lib().spb_pack_opts_default(ctypes.byref(O))
     O.token_budget = int(token_budget)

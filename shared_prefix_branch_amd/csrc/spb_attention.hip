@@ -90,11 +90,9 @@ struct AttnParams {
   float sc;   // softmax scale * log2(e) * s_q * s_k
   float s_v;  // applied to the output
   const SpbRow *rows;
-  const SpbTile *tiles;
-  const SpbBranch *branches;
-  const SpbItem *items;      // bf16 kernel: the item table of its row granularity
-  const SpbChunk *bchunks;   // bf16 kernel: branch chunks of the items
-  int n_work;                // bf16 kernel: items x KV heads
+  const SpbItem *items;      // the item table of the kernel's row granularity
+  const SpbChunk *bchunks;   // stem and branch chunks of the items
+  int n_work;                // items x KV heads
 };
 
 template <int D, int IN>
@@ -371,35 +369,29 @@ __device__ __attribute__((always_inline)) inline void pv_chunk(const char *Vb, c
   }
 }
 
-// Chunk list of the work item (built by wave 0): content chunks, then the
-// chunks of each branch that meets rows [sub0, sub0 + sub_n).
-__device__ inline void build_chunk_list(const AttnParams &p, const SpbTile &tile, int sub0, int sub_n, int lane,
-                                        int2 *chunks, int *n_chunks) {
-  for (int c = lane; c < tile.ncc && c < kMaxChunks; c += 64) chunks[c] = int2{tile.seg + c * kChunk, -1 - c};
-  int n = tile.ncc;
-  for (int b0 = tile.b_lo; b0 < tile.b_hi; b0 += 64) {
-    const int b = b0 + lane;
-    int cnt = 0, start = 0;
-    if (b < tile.b_hi) {
-      const SpbBranch br = p.branches[b];
-      start = br.start;
-      if (br.start + br.E > sub0 && br.start < sub0 + sub_n) {
-        const int last = min(br.start + br.E, sub0 + sub_n) - 1 - br.start;
-        cnt = last / kBranchChunk + 1;
-      }
+// Chunk list of a work item in LDS: its content chunks, then its stem and
+// branch chunks from the item table.  Entry: (first key row, info, pre,
+// post | nvis << 24); info < 0 for content chunk -1 - info, else the table's.
+__device__ inline void load_chunk_list(const AttnParams &p, const SpbItem &it, int4 *chunks, int tid, int nt) {
+  const int nch = it.ncc + it.bn;
+  for (int i = tid; i < nch; i += nt) {
+    if (i < it.ncc) {
+      chunks[i] = int4{it.seg + i * kChunk, -1 - i, 0, 0};
+    } else {
+      const SpbChunk c = p.bchunks[it.boff + i - it.ncc];
+      chunks[i] = int4{c.key0, c.info, c.pre, c.post_nvis};
     }
-    int incl = cnt;  // inclusive prefix sum over the wave
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
-    }
-    const int base = n + incl - cnt;
-    for (int c = 0; c < cnt; ++c)
-      if (base + c < kMaxChunks) chunks[base + c] = int2{start + c * kBranchChunk, (b << 10) | c};
-    n += __shfl(incl, 63);
   }
-  if (lane == 0) *n_chunks = n < kMaxChunks ? n : kMaxChunks;
+}
+
+// The row a lane works on; lanes past the item's rows get a row that sees
+// nothing (no content, no stem, no branch).
+__device__ inline SpbRow load_row(const AttnParams &p, int x, bool active) {
+  if (active) return p.rows[x];
+  SpbRow r{};
+  r.br = -1;
+  r.spre = -1;
+  return r;
 }
 
 // Q fragments of row x, query head h (zeros for inactive lanes).
@@ -467,9 +459,13 @@ __device__ inline void store_o(const AttnParams &p, int x, int h, int half, cons
 
 // What one wave does with one chunk.  Content chunk c (keys [c*64, c*64 + 64)
 // of the content) is two 32-key blocks, the second skipped when no lane sees
-// past key 32; branch chunk c (extended keys [c*32, c*32 + 32) of the branch)
-// is one block.  A chunk is skipped by a wave none of whose lanes sees a key
-// of it.  ch = (first key row, info): info < 0 for content chunk -1 - info,
+// past key 32; stem chunk c (tokens [c*32, c*32 + nvis) of a shared template
+// stem) and branch chunk c (extended keys [c*32, c*32 + 32) of the branch)
+// are one block each.  A stem row sees its own stem causally; a row whose
+// path runs through a stem (its DFS number falls in the stem's interval) sees
+// all of it.  A chunk is skipped by a wave none of whose lanes sees a key of
+// it.  ch = (first key row, info, pre, post | nvis << 24): info < 0 for
+// content chunk -1 - info, kStemChunk | stem << 10 | c for a stem chunk,
 // else branch << 10 | c.  Calls ballots: every lane of the wave takes part.
 struct ChunkStep {
   bool run;     // some lane sees a key of the chunk
@@ -479,7 +475,7 @@ struct ChunkStep {
   Vis vis;
 };
 
-__device__ __attribute__((always_inline)) inline ChunkStep chunk_step(int2 ch, const SpbRow &row, int half) {
+__device__ __attribute__((always_inline)) inline ChunkStep chunk_step(int4 ch, const SpbRow &row, int half) {
   int thr;  // keys of the chunk this lane sees as a prefix
   int anc[kMaxDepth];
   bool any, node = false;
@@ -487,6 +483,13 @@ __device__ __attribute__((always_inline)) inline ChunkStep chunk_step(int2 ch, c
   for (int a = 0; a < kMaxDepth; ++a) anc[a] = -1000;
   if (ch.y < 0) {
     thr = row.cvis - (-1 - ch.y) * kChunk;
+    any = thr > 0;
+  } else if (ch.y & kStemChunk) {
+    const int lo = (ch.y & 1023) * kBranchChunk;
+    const int nvis = (int)((uint32_t)ch.w >> 24);
+    const bool own = row.br == ch.x - lo;
+    const bool below = ch.z <= row.spre && row.spre < (ch.w & 0xFFFFFF);
+    thr = own ? min(row.e + 1 - lo, nvis) : below ? nvis : 0;
     any = thr > 0;
   } else {
     const int c = ch.y & 1023;
@@ -522,7 +525,7 @@ __device__ __attribute__((always_inline)) inline ChunkStep chunk_step(int2 ch, c
 // appears once in the loop, so the accumulators keep their registers;
 // advance(i) hands the LDS buffers on to chunk i + 1.
 template <typename Block, typename Advance>
-__device__ __attribute__((always_inline)) inline void walk_chunks(const int2 *chunks, int nch, const SpbRow &row,
+__device__ __attribute__((always_inline)) inline void walk_chunks(const int4 *chunks, int nch, const SpbRow &row,
                                                                   int half, Block &&block, Advance &&advance) {
   for (int i = 0; i < nch; ++i) {
     const ChunkStep cs = chunk_step(chunks[i], row, half);
@@ -575,7 +578,7 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
   constexpr int IN = SPB_BF16;
   __shared__ __attribute__((aligned(1024))) char Ks[2][C::BUF];
   __shared__ __attribute__((aligned(1024))) char Vs[2][C::BUF];
-  __shared__ int2 chunks[kMaxChunks];  // (first key row, info): info < 0 content chunk -1-c; else branch << 10 | c
+  __shared__ int4 chunks[kMaxChunks];
 
   const int w = blockIdx.x;
   const int kvh = w % p.hkv;
@@ -591,20 +594,8 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
   const bool active = local < it.nrows;
   const int x = it.row0 + local;
 
-  for (int i = tid; i < nch; i += C::NT) {
-    if (i < it.ncc) {
-      chunks[i] = int2{it.seg + i * kChunk, -1 - i};
-    } else {
-      const SpbChunk c = p.bchunks[it.boff + i - it.ncc];
-      chunks[i] = int2{c.key0, c.info};
-    }
-  }
-  SpbRow row;
-  if (active) {
-    row = p.rows[x];
-  } else {
-    row.cvis = 0; row.seg = 0; row.br = -1; row.e = 0; row.L = 0; row.depth = 0; row.anc01 = 0; row.anc23 = 0;
-  }
+  load_chunk_list(p, it, chunks, tid, C::NT);
+  const SpbRow row = load_row(p, x, active);
   QFrag<D, IN> qf[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) load_q<D, IN>(qf[j], p, x, h0 + j, active, half);
@@ -655,7 +646,7 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
     dma16(p.v, rowoff + vofs, v_lds + dst);
   };
   auto issue = [&](int i) {
-    const int2 ch = chunks[i];
+    const int2 ch = int2{chunks[i].x, chunks[i].y};
     const uint32_t slot = (uint32_t)(i & 1) * C::BUF;
     if (ch.y < 0) {
 #pragma unroll
@@ -724,7 +715,7 @@ struct StagedCfg {
   static constexpr int NW = RW * G;           // waves, one query head each
   static constexpr int NT = NW * 64;
   static constexpr int ROWS = 32 * RW;
-  static constexpr int SPLITS = 128 / ROWS;   // work items per 128-row tile
+  static constexpr int GRAN = RW == 2 ? 1 : 2;  // work items of 32 << GRAN rows
   static constexpr int KROWB = FP8 ? D : 2 * D;  // bytes per staged K row
   static constexpr int KCH = KROWB / 16;         // 16-byte chunks per K row
   static constexpr int VCH = 2 * D / 16;         // V is staged as bf16
@@ -824,17 +815,13 @@ __global__ __launch_bounds__((StagedCfg<D, G, IN>::NT)) void branch_attention_st
   using C = StagedCfg<D, G, IN>;
   __shared__ __attribute__((aligned(16))) char Ks[2][64 * C::KPITCH];
   __shared__ __attribute__((aligned(16))) char Vs[2][64 * C::VPITCH];
-  __shared__ int2 chunks[kMaxChunks];
-  __shared__ int n_chunks_s;
+  __shared__ int4 chunks[kMaxChunks];
 
   const int w = blockIdx.x;
   const int kvh = w % p.hkv;
-  const int rest = w / p.hkv;
-  const int split = rest % C::SPLITS;
-  const SpbTile tile = p.tiles[rest / C::SPLITS];
-  const int sub0 = tile.row0 + split * C::ROWS;
-  const int sub_n = min(C::ROWS, tile.row0 + tile.nrows - sub0);
-  if (sub_n <= 0) return;  // uniform over the work group
+  const SpbItem it = p.items[w / p.hkv];
+  const int nch = it.ncc + it.bn;
+  const int sub0 = it.row0, sub_n = it.nrows;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rw = wave / G, gh = wave % G;
@@ -844,14 +831,8 @@ __global__ __launch_bounds__((StagedCfg<D, G, IN>::NT)) void branch_attention_st
   const bool active = local < sub_n;
   const int x = sub0 + local;
 
-  if (wave == 0) build_chunk_list(p, tile, sub0, sub_n, lane, chunks, &n_chunks_s);
-
-  SpbRow row;
-  if (active) {
-    row = p.rows[x];
-  } else {
-    row.cvis = 0; row.seg = 0; row.br = -1; row.e = 0; row.L = 0; row.depth = 0; row.anc01 = 0; row.anc23 = 0;
-  }
+  load_chunk_list(p, it, chunks, tid, C::NT);
+  const SpbRow row = load_row(p, x, active);
   QFrag<D, IN> qf[1];
   load_q<D, IN>(qf[0], p, x, h, active, half);
 
@@ -878,7 +859,6 @@ __global__ __launch_bounds__((StagedCfg<D, G, IN>::NT)) void branch_attention_st
   for (int db = 0; db < D / 32; ++db) o[0][db] = f32x16{0.f};
 
   __syncthreads();  // chunk list ready
-  const int nch = n_chunks_s;
 
   // Prefetch loads are issued on every trip (past the end they reload the
   // last chunk), so no branch changes the count of outstanding loads and each
@@ -946,8 +926,7 @@ AttnParams make_params(const AttnLaunch &a) {
   p.sc = a.scale * kLog2e * a.s_q * a.s_k;
   p.s_v = a.s_v;
   p.rows = (const SpbRow *)a.rows;
-  p.tiles = (const SpbTile *)a.tiles;
-  p.branches = (const SpbBranch *)a.branches;
+  p.bchunks = (const SpbChunk *)a.bchunks;
   return p;
 }
 
@@ -972,7 +951,6 @@ int launch_dma(const AttnLaunch &a, hipStream_t s) {
   if ((long long)a.n_tokens * a.hkv * C::ROWB > 0xFFFFFFFFll) return (int)hipErrorInvalidValue;
   AttnParams p = make_params(a);
   p.items = (const SpbItem *)a.items[C::GRAN];
-  p.bchunks = (const SpbChunk *)a.bchunks;
   p.n_work = (int)work;
   hipLaunchKernelGGL((branch_attention_dma<D, G, Sh::HPW, Sh::RG, OUT>), dim3((unsigned)work), dim3(C::NT), 0, s, p);
   return (int)hipGetLastError();
@@ -981,10 +959,13 @@ int launch_dma(const AttnLaunch &a, hipStream_t s) {
 template <int D, int G, int IN, int OUT>
 int launch_staged(const AttnLaunch &a, hipStream_t s) {
   using C = StagedCfg<D, G, IN>;
-  long long items = (long long)a.n_tiles * C::SPLITS * a.hkv;
-  if (items > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL((branch_attention_staged<D, G, IN, OUT>), dim3((unsigned)items), dim3(C::NT), 0, s,
-                     make_params(a));
+  const long long work = (long long)a.n_items[C::GRAN] * a.hkv;
+  if (work > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  if (work == 0) return 0;
+  AttnParams p = make_params(a);
+  p.items = (const SpbItem *)a.items[C::GRAN];
+  p.n_work = (int)work;
+  hipLaunchKernelGGL((branch_attention_staged<D, G, IN, OUT>), dim3((unsigned)work), dim3(C::NT), 0, s, p);
   return (int)hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ struct Question {
   int n_nodes = 0;
   int n_opt = 0;
   std::vector<int> node_depth;                  // [n_nodes]
-  std::vector<std::vector<int>> node_anc;       // [n_nodes][depth]: extended indices, self last
+  std::vector<std::vector<int>> node_anc;       // [n_nodes][depth]: node indices of the ancestors, self last
   // scored rows of one branch: 0 = template's last row, 1 + i = node i
   std::vector<std::vector<int>> targets;        // [1 + n_nodes]: distinct next tokens
   // per option: (local scored row, index into that row's targets) per token
@@ -117,7 +117,7 @@ spb_status compile_question(const spb_problem &P, int q, const spb_pack_opts &o,
     Q.node_depth[i] = (int)pre.size();
     for (size_t k = 1; k <= pre.size(); ++k) {
       std::vector<int> a(pre.begin(), pre.begin() + k);
-      Q.node_anc[i].push_back(Q.L + node_of[a]);
+      Q.node_anc[i].push_back(node_of[a]);
     }
   }
   Q.targets.assign(1 + Q.n_nodes, {});
@@ -154,6 +154,11 @@ struct PassPlan {
   std::vector<SpbBranch> branches;
   std::vector<SpbItem> items[3];
   std::vector<SpbChunk> bchunks;
+  struct HostStem {
+    int start, L, pre, post, parent;  // parent: index in stems, -1 none
+  };
+  std::vector<HostStem> stems;  // stems placed in this pass, in placement order
+  int stem_base = 0;            // next free DFS number in this pass
   std::vector<int32_t> logical_branch;
   std::vector<int32_t> scored, tgt_off, tgt_tok, opt_step_off, step_slot, step_row;
   std::vector<unsigned char> blob;
@@ -175,13 +180,110 @@ struct spb_plan {
 
 namespace {
 
+// A run of template tokens shared by several of one input's questions.
+struct Stem {
+  int len;            // tokens
+  int parent;         // index of the enclosing stem, -1 = none (below the content)
+  int pre, post;      // DFS interval among the input's stems (pre < post)
+  int64_t first_row;  // logical row of its first token
+  int chain_len;      // tokens of its ancestors (not counting itself)
+};
+
 struct Unit {  // one logical input to place
   int C;
   int64_t first_row;                 // logical row of its first token
   std::vector<int> qs;               // questions (branches) in order
   std::vector<int> lbs;              // logical branch id of each branch
-  std::vector<int64_t> br_first_row; // logical row of each branch's template token 0
+  std::vector<int64_t> br_first_row; // logical row of each branch's own template token 0
+  std::vector<int> own_L;            // per branch: own template tokens (after its shared ones)
+  std::vector<int> br_stem;          // per branch: deepest stem on its path, -1 none
+  std::vector<Stem> stems;
+  int E(size_t bi, const std::vector<Question> &Q) const { return own_L[bi] + Q[qs[bi]].n_nodes; }
+  int chain(size_t bi) const { return br_stem[bi] < 0 ? 0 : stems[br_stem[bi]].chain_len + stems[br_stem[bi]].len; }
 };
+
+// Shared template prefixes of an input: a proper prefix (never the last token)
+// of a question's template is shared when at least two of the input's
+// questions start with it.  Shared tokens form stems, each a run that ends
+// where a question leaves the shared part or the shared trie branches; stems
+// are numbered (and their tokens given logical rows) at first appearance in
+// question order.  tmpl: the template of each question (empty: none given).
+void build_stems(Unit &u, const std::vector<Question> &Q, const std::vector<std::vector<int>> &tmpl) {
+  const size_t nb = u.qs.size();
+  u.own_L.assign(nb, 0);
+  u.br_stem.assign(nb, -1);
+  for (size_t b = 0; b < nb; ++b) u.own_L[b] = Q[u.qs[b]].L;
+  if (tmpl.empty() || nb < 2) return;
+  std::map<std::vector<int>, int> count;
+  for (size_t b = 0; b < nb; ++b) {
+    const auto &T = tmpl[u.qs[b]];
+    for (size_t k = 1; k < T.size(); ++k) count[std::vector<int>(T.begin(), T.begin() + k)]++;
+  }
+  std::vector<int> s(nb, 0);
+  for (size_t b = 0; b < nb; ++b) {
+    const auto &T = tmpl[u.qs[b]];
+    while (s[b] + 1 < (int)T.size() && count[std::vector<int>(T.begin(), T.begin() + s[b] + 1)] >= 2) ++s[b];
+  }
+  // per shared node: distinct shared children, and whether a question leaves there
+  std::map<std::vector<int>, std::set<int>> kids;
+  std::set<std::vector<int>> exits;
+  for (size_t b = 0; b < nb; ++b) {
+    const auto &T = tmpl[u.qs[b]];
+    for (int k = 1; k <= s[b]; ++k)
+      if (k > 1) kids[std::vector<int>(T.begin(), T.begin() + k - 1)].insert(T[k - 1]);
+    if (s[b] > 0) exits.insert(std::vector<int>(T.begin(), T.begin() + s[b]));
+  }
+  std::map<std::vector<int>, int> seg_of;  // shared node -> stem index
+  for (size_t b = 0; b < nb; ++b) {
+    const auto &T = tmpl[u.qs[b]];
+    for (int k = 1; k <= s[b]; ++k) {
+      std::vector<int> p(T.begin(), T.begin() + k);
+      if (seg_of.count(p)) continue;
+      int par = -1;
+      if (k > 1) {
+        std::vector<int> up(T.begin(), T.begin() + k - 1);
+        const int ps = seg_of[up];
+        if (!exits.count(up) && kids[up].size() == 1) {  // the run continues
+          seg_of[p] = ps;
+          u.stems[ps].len++;
+          continue;
+        }
+        par = ps;
+      }
+      Stem st{};
+      st.len = 1;
+      st.parent = par;
+      seg_of[p] = (int)u.stems.size();
+      u.stems.push_back(st);
+    }
+    if (s[b] > 0) u.br_stem[b] = seg_of[std::vector<int>(T.begin(), T.begin() + s[b])];
+    u.own_L[b] = (int)T.size() - s[b];
+  }
+  // DFS numbering (children in creation order) and ancestor token counts
+  const int ns = (int)u.stems.size();
+  std::vector<std::vector<int>> ch(ns);
+  std::vector<int> roots;
+  for (int i = 0; i < ns; ++i) (u.stems[i].parent < 0 ? roots : ch[u.stems[i].parent]).push_back(i);
+  int clock = 0;
+  std::vector<std::pair<int, int>> stack;  // (stem, next child)
+  for (int r : roots) {
+    u.stems[r].pre = clock++;
+    u.stems[r].chain_len = 0;
+    stack.push_back({r, 0});
+    while (!stack.empty()) {
+      auto &top = stack.back();
+      if (top.second < (int)ch[top.first].size()) {
+        const int c = ch[top.first][top.second++];
+        u.stems[c].pre = clock++;
+        u.stems[c].chain_len = u.stems[top.first].chain_len + u.stems[top.first].len;
+        stack.push_back({c, 0});
+      } else {
+        u.stems[top.first].post = clock++;
+        stack.pop_back();
+      }
+    }
+  }
+}
 
 struct Packer {
   const std::vector<Question> &Q;
@@ -230,6 +332,7 @@ struct Packer {
       r.seg = seg;
       r.br = -1;
       r.e = t;
+      r.spre = -1;
       P.rows.push_back(r);
       P.logical_row.push_back(u.first_row + t);
       P.pairs += t + 1;
@@ -238,72 +341,122 @@ struct Packer {
     end_rows();
   }
 
+  // Stem placement state of the unit being placed in the current pass: the
+  // pass row of each stem placed (-1 not yet) and the pass's DFS base.
+  std::vector<int> stem_start, stem_index;
+  int stem_base = 0;
+  void reset_stems(const Unit &u) {
+    stem_start.assign(u.stems.size(), -1);
+    stem_index.assign(u.stems.size(), -1);
+    stem_base = cur().stem_base;
+    cur().stem_base += 2 * (int)u.stems.size();
+  }
+  // places stem s (after its ancestors) unless the pass already holds it
+  void place_stem(const Unit &u, int s, int seg) {
+    if (stem_start[s] >= 0) return;
+    const Stem &st = u.stems[s];
+    if (st.parent >= 0) place_stem(u, st.parent, seg);
+    PassPlan &P = cur();
+    const int start = fill();
+    stem_start[s] = start;
+    stem_index[s] = (int)P.stems.size();
+    P.stems.push_back({start, st.len, stem_base + st.pre, stem_base + st.post,
+                       st.parent >= 0 ? stem_index[st.parent] : -1});
+    for (int j = 0; j < st.len; ++j) {
+      SpbRow r{};
+      r.cvis = u.C;
+      r.seg = u.C > 0 ? seg : start;
+      r.br = start;
+      r.e = j;
+      r.L = st.len;
+      r.spre = stem_base + st.pre;
+      r.stem = 1;
+      P.rows.push_back(r);
+      P.logical_row.push_back(st.first_row + j);
+      P.pairs += u.C + st.chain_len + j + 1;
+    }
+    end_rows();
+  }
+  // stems not yet in the pass that branch bi needs
+  int stems_needed(const Unit &u, int bi) const {
+    int n = 0;
+    for (int s = u.br_stem[bi]; s >= 0; s = u.stems[s].parent)
+      if (stem_start[s] < 0) n += u.stems[s].len;
+    return n;
+  }
+
   void place_branch(const Unit &u, int bi, int seg, std::vector<int> &lb_pass, std::vector<int> &lb_slot) {
+    if (u.br_stem[bi] >= 0) place_stem(u, u.br_stem[bi], seg);
     PassPlan &P = cur();
     const Question &q = Q[u.qs[bi]];
+    const int L = u.own_L[bi];
+    const int chain = u.chain(bi);
+    const int spre = u.br_stem[bi] >= 0 ? stem_base + u.stems[u.br_stem[bi]].pre : -1;
     int start = fill();
     SpbBranch b{};
     b.start = start;
-    b.L = q.L;
-    b.E = q.E();
+    b.L = L;
+    b.E = L + q.n_nodes;
     b.n_opt = q.n_opt;
     b.question = u.qs[bi];
     lb_pass[u.lbs[bi]] = (int)passes.size() - 1;
     lb_slot[u.lbs[bi]] = (int)P.branches.size();
     P.branches.push_back(b);
     P.logical_branch.push_back(u.lbs[bi]);
-    for (int j = 0; j < q.L; ++j) {
+    for (int j = 0; j < L; ++j) {
       SpbRow r{};
       r.cvis = u.C;
       r.seg = u.C > 0 ? seg : start;
       r.br = start;
       r.e = j;
-      r.L = q.L;
+      r.L = L;
+      r.spre = spre;
       P.rows.push_back(r);
       P.logical_row.push_back(u.br_first_row[bi] + j);
-      P.pairs += u.C + j + 1;
+      P.pairs += u.C + chain + j + 1;
     }
     for (int i = 0; i < q.n_nodes; ++i) {
       SpbRow r{};
       r.cvis = u.C;
       r.seg = u.C > 0 ? seg : start;
       r.br = start;
-      r.e = q.L + i;
-      r.L = q.L;
+      r.e = L + i;
+      r.L = L;
       r.depth = q.node_depth[i];
+      r.spre = spre;
       int a[4] = {0, 0, 0, 0};
-      for (int k = 0; k < r.depth; ++k) a[k] = q.node_anc[i][k];
+      for (int k = 0; k < r.depth; ++k) a[k] = L + q.node_anc[i][k];
       r.anc01 = (int32_t)((uint32_t)a[0] | ((uint32_t)a[1] << 16));
       r.anc23 = (int32_t)((uint32_t)a[2] | ((uint32_t)a[3] << 16));
       P.rows.push_back(r);
-      P.logical_row.push_back(u.br_first_row[bi] + q.L + i);
-      P.pairs += u.C + q.L + r.depth;
+      P.logical_row.push_back(u.br_first_row[bi] + L + i);
+      P.pairs += u.C + chain + L + r.depth;
     }
     end_rows();
   }
 
   void place(const Unit &u, std::vector<int> &lb_pass, std::vector<int> &lb_slot) {
     int64_t size = u.C;
-    for (int q : u.qs) size += Q[q].E();
+    for (size_t bi = 0; bi < u.qs.size(); ++bi) size += u.E(bi, Q);
+    for (const Stem &s : u.stems) size += s.len;
     int seg = 0;
-    if (size <= B - fill()) {
+    if (size <= B - fill() || size <= B) {
+      if (size > B - fill()) close_if_nonempty();
       place_content(u, seg);
+      reset_stems(u);
       for (size_t bi = 0; bi < u.qs.size(); ++bi) place_branch(u, (int)bi, seg, lb_pass, lb_slot);
       return;
     }
-    if (size <= B) {
-      close_if_nonempty();
-      place_content(u, seg);
-      for (size_t bi = 0; bi < u.qs.size(); ++bi) place_branch(u, (int)bi, seg, lb_pass, lb_slot);
-      return;
-    }
-    // larger than a pass: spill at branch boundaries, content re-staged
-    if (u.C + (u.qs.empty() ? 0 : Q[u.qs[0]].E()) > B - fill()) close_if_nonempty();
+    // larger than a pass: spill at branch boundaries, content and the stems a
+    // pass's branches need re-staged
+    if (u.C + (u.qs.empty() ? 0 : u.chain(0) + u.E(0, Q)) > B - fill()) close_if_nonempty();
     place_content(u, seg);
+    reset_stems(u);
     for (size_t bi = 0; bi < u.qs.size(); ++bi) {
-      if (Q[u.qs[bi]].E() > B - fill()) {
+      if (stems_needed(u, (int)bi) + u.E(bi, Q) > B - fill()) {
         open();
         place_content(u, seg);
+        reset_stems(u);
       }
       place_branch(u, (int)bi, seg, lb_pass, lb_slot);
     }
@@ -325,7 +478,7 @@ void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, co
       // branches intersecting [r0, r0 + nrows): the branch table is in row order
       int lo = -1, hi = -1;
       for (int r = r0; r < r0 + t.nrows; ++r) {
-        if (P.rows[r].br < 0) continue;
+        if (P.rows[r].br < 0 || P.rows[r].stem) continue;
         // locate by binary search on start
         int s = P.rows[r].br;
         auto it = std::lower_bound(P.branches.begin(), P.branches.end(), s,
@@ -356,6 +509,8 @@ void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, co
 // split into row ranges, each with the content chunks its own rows see and the
 // chunks of the branches meeting its rows, longest first.
 void build_items(PassPlan &P) {
+  std::map<int, int> stem_at;  // pre number -> index in P.stems
+  for (size_t s = 0; s < P.stems.size(); ++s) stem_at[P.stems[s].pre] = (int)s;
   for (int g = 0; g < 3; ++g) {
     const int rows_per = 32 << g;
     std::vector<SpbItem> items;
@@ -370,11 +525,29 @@ void build_items(PassPlan &P) {
         for (int r = r0; r < r0 + it.nrows; ++r) maxc = std::max(maxc, P.rows[r].cvis);
         it.ncc = (maxc + kChunk - 1) / kChunk;
         std::vector<SpbChunk> list;
+        // stems on the paths of the item's rows (a stem row's own stem, a
+        // branch row's deepest stem, and their ancestors), root first
+        std::set<std::pair<int, int>> stems;  // (pre, index)
+        for (int r = r0; r < r0 + it.nrows; ++r) {
+          const SpbRow &R = P.rows[r];
+          if (R.br < 0 || R.spre < 0) continue;
+          int s = stem_at.at(R.spre);
+          for (; s >= 0; s = P.stems[s].parent) stems.insert({P.stems[s].pre, s});
+        }
+        for (auto &ps : stems) {
+          const auto &S = P.stems[ps.second];
+          for (int c = 0; c * kBranchChunk < S.L; ++c) {
+            const int nvis = std::min(S.L - c * kBranchChunk, kBranchChunk);
+            list.push_back(SpbChunk{S.start + c * kBranchChunk, kStemChunk | (ps.second << 10) | c, S.pre,
+                                    S.post | (nvis << 24)});
+          }
+        }
         for (int b = t.b_lo; b < t.b_hi; ++b) {
           const SpbBranch &B = P.branches[b];
           if (B.start + B.E <= r0 || B.start >= r0 + it.nrows) continue;
           const int last = std::min(B.start + B.E, r0 + it.nrows) - 1 - B.start;
-          for (int c = 0; c <= last / kBranchChunk; ++c) list.push_back(SpbChunk{B.start + c * kBranchChunk, (b << 10) | c});
+          for (int c = 0; c <= last / kBranchChunk; ++c)
+            list.push_back(SpbChunk{B.start + c * kBranchChunk, (b << 10) | c, 0, 0});
         }
         it.bn = (int)list.size();
         it.cost = it.ncc + it.bn;
@@ -404,8 +577,8 @@ void build_scoring(PassPlan &P, const std::vector<Question> &Q) {
     b.opt0 = opt;
     b.scored0 = (int)P.scored.size();
     b.n_scored = 1 + q.n_nodes;
-    P.scored.push_back(b.start + q.L - 1);
-    for (int i = 0; i < q.n_nodes; ++i) P.scored.push_back(b.start + q.L + i);
+    P.scored.push_back(b.start + b.L - 1);
+    for (int i = 0; i < q.n_nodes; ++i) P.scored.push_back(b.start + b.L + i);
     for (int s = 0; s <= q.n_nodes; ++s) {
       for (int t : q.targets[s]) P.tgt_tok.push_back(t);
       P.tgt_off.push_back((int)P.tgt_tok.size());
@@ -568,6 +741,15 @@ spb_status spb_pack_pass(const spb_problem *P, const spb_pack_opts *opts, spb_pl
     spb_status s = compile_question(*P, q, o, Q[q]);
     if (s != SPB_OK) return s;
   }
+  std::vector<std::vector<int>> tmpl;  // template token ids per question (empty: not given)
+  if (P->tmpl_tok) {
+    tmpl.resize(P->n_questions);
+    int64_t off = 0;
+    for (int q = 0; q < P->n_questions; ++q) {
+      tmpl[q].assign(P->tmpl_tok + off, P->tmpl_tok + off + Q[q].L);
+      off += Q[q].L;
+    }
+  }
   std::unique_ptr<spb_plan> plan(new (std::nothrow) spb_plan());
   if (!plan) return fail(SPB_ERR_ARG, "out of host memory");
   plan->floors = o.floors != 0;
@@ -605,9 +787,23 @@ spb_status spb_pack_pass(const spb_problem *P, const spb_pack_opts *opts, spb_pl
                     q, Q[q].E(), o.token_budget);
       u.qs.push_back(q);
       u.lbs.push_back(lb++);
-      u.br_first_row.push_back(row);
-      row += Q[q].E();
       plan->lb_question.push_back(q);
+    }
+    build_stems(u, Q, tmpl);
+    // logical rows: per branch, the shared tokens of its template not yet
+    // numbered (stems root first), then its own template and trie nodes
+    std::vector<char> numbered(u.stems.size(), 0);
+    for (size_t bi = 0; bi < u.qs.size(); ++bi) {
+      std::vector<int> chain;
+      for (int s = u.br_stem[bi]; s >= 0; s = u.stems[s].parent) chain.push_back(s);
+      for (auto it = chain.rbegin(); it != chain.rend(); ++it)
+        if (!numbered[*it]) {
+          numbered[*it] = 1;
+          u.stems[*it].first_row = row;
+          row += u.stems[*it].len;
+        }
+      u.br_first_row.push_back(row);
+      row += u.E(bi, Q);
     }
     units.push_back(std::move(u));
   }
@@ -627,6 +823,7 @@ spb_status spb_pack_pass(const spb_problem *P, const spb_pack_opts *opts, spb_pl
       u.qs.push_back(q);
       u.lbs.push_back(lb);
       u.br_first_row.push_back(row);
+      build_stems(u, Q, tmpl);  // one question: nothing shared
       plan->floor_lb_of_q[q] = lb++;
       plan->lb_question.push_back(q);
       row += Q[q].E();
@@ -747,7 +944,18 @@ spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int
     ++n;
   };
   for (int j = 0; j < r.cvis; ++j) emit(r.seg + j);
-  if (r.br >= 0) {
+  // stems on the row's path, root first: all their tokens, the row's own stem
+  // causally
+  std::vector<std::pair<int, const PassPlan::HostStem *>> path;
+  for (auto &s : P.stems)
+    if (r.br >= 0 && s.pre <= r.spre && r.spre < s.post) path.push_back({s.pre, &s});
+  std::sort(path.begin(), path.end(), [](auto &a, auto &b) { return a.first < b.first; });
+  for (auto &ps : path) {
+    const bool own = r.stem && ps.second->start == r.br;
+    const int n = own ? r.e + 1 : ps.second->L;
+    for (int j = 0; j < n; ++j) emit(ps.second->start + j);
+  }
+  if (r.br >= 0 && !r.stem) {
     int E = r.L;
     for (auto &b : P.branches)
       if (b.start == r.br) E = b.E;
@@ -808,9 +1016,14 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
     return fail(SPB_ERR_LIMIT, "a bf16 pass's K/V (%d tokens x %d heads x %d) must stay under 4 GiB", h.n_tokens, a->hkv,
                 a->head_dim);
   if (h.n_tiles == 0) return ok();
-  for (const SpbTile &t : P.tiles)
-    if (t.cost > kMaxTileChunks)
-      return fail(SPB_ERR_LIMIT, "an attention tile needs %d key chunks, more than %d", t.cost, kMaxTileChunks);
+  // stem chunk fields: stem index below bit 20 of the info word (below the
+  // stem flag), DFS numbers below 2^24
+  if (P.stems.size() >= (1u << 20) || P.stem_base >= (1 << 24))
+    return fail(SPB_ERR_LIMIT, "a pass holds %zu shared template stems, too many", P.stems.size());
+  for (int g = 0; g < 3; ++g)
+    for (const SpbItem &it : P.items[g])
+      if (it.cost > kMaxTileChunks)
+        return fail(SPB_ERR_LIMIT, "an attention tile needs %d key chunks, more than %d", it.cost, kMaxTileChunks);
   AttnLaunch L{};
   L.q = a->q; L.k = a->k; L.v = a->v; L.o = a->o;
   L.in_dtype = a->in_dtype; L.out_dtype = a->out_dtype;

@@ -16,7 +16,7 @@
 namespace spb {
 
 constexpr int32_t kMetaMagic = 0x53504231;  // "SPB1"
-constexpr int32_t kMetaVersion = 2;
+constexpr int32_t kMetaVersion = 3;
 constexpr int kTileRows = 128;  // rows per attention tile (one to two work groups)
 constexpr int kChunk = 64;      // keys per content chunk, chunks start at the content start
 constexpr int kBranchChunk = 32;  // keys per branch chunk, chunks start at the branch start
@@ -26,18 +26,26 @@ constexpr int kVocabTile = 256; // vocabulary rows per lm-head slice (LSE partia
 
 // One per pass row.  Visibility of key row y from query row x:
 //   content key: y in [x.seg, x.seg + x.cvis)
-//   branch key:  x.br >= 0 and y in [x.br, x.br + E) with e' = y - x.br:
+//   stem key (a shared template token, of stem s with DFS interval
+//     [pre_s, post_s)): visible iff pre_s <= x.spre < post_s, and, when x is
+//     a row of s itself (x.stem and y in s), iff y <= x (causal)
+//   branch key:  x.br >= 0, !x.stem and y in [x.br, x.br + E) with e' = y - x.br:
 //     e' <  x.L : visible iff e' <= x.e  (template rows causal; nodes see all)
 //     e' >= x.L : visible iff e' is one of the node's ancestors anc[0..depth)
 struct SpbRow {
-  int32_t cvis;   // content keys visible (content row t: t+1; branch rows: C)
+  int32_t cvis;   // content keys visible (content row t: t+1; branch and stem rows: C)
   int32_t seg;    // pass row of the segment's first content token
-  int32_t br;     // pass row of the branch's template token 0; -1 for content rows
-  int32_t e;      // extended index in the branch (template j or L + node index); content: t
-  int32_t L;      // template length of the branch (0 for content rows)
-  int32_t depth;  // option-trie depth (0 for content and template rows)
+  int32_t br;     // pass row of the branch's own template token 0 (stem rows: of the
+                  // stem's first token); -1 for content rows
+  int32_t e;      // extended index in the branch or stem (template j or L + node index); content: t
+  int32_t L;      // own template length of the branch, or the stem's length (0 for content rows)
+  int32_t depth;  // option-trie depth (0 for content, template and stem rows)
   int32_t anc01;  // extended indices of ancestors at depth 1 and 2 (low / high 16 bits)
   int32_t anc23;  // depth 3 and 4; anc[depth-1] is the node itself
+  int32_t spre;   // pre number of the deepest stem on the row's path (its own stem for a
+                  // stem row); -1: none
+  int32_t stem;   // 1 for a stem row
+  int32_t pad0, pad1;
 };
 
 // One attention work item: at most kTileRows consecutive rows of one segment
@@ -66,9 +74,15 @@ struct SpbItem {
 };
 
 // A branch chunk: keys [key0, key0 + kBranchChunk) of branch `b`, chunk c of
-// it (key0 = start + c * kBranchChunk); info = b << 10 | c.
+// it (key0 = start + c * kBranchChunk); info = b << 10 | c.  A stem chunk:
+// keys [key0, key0 + kBranchChunk) of stem s, info = kStemChunk | s << 10 | c,
+// pre / post its DFS interval, nvis its keys (up to kBranchChunk; all of them
+// are seen by a row below the stem).
+constexpr int32_t kStemChunk = 1 << 30;
 struct SpbChunk {
   int32_t key0, info;
+  int32_t pre;
+  int32_t post_nvis;  // post | nvis << 24
 };
 
 struct SpbBranch {

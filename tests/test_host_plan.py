@@ -36,21 +36,21 @@ def _placements(plan):
 def _check_plan(prob, plan, budget, floors=True):
     lay = OT.build_layout(prob, floors=floors)
     seen = collections.Counter()
-    content_rows = set(np.nonzero(lay.row_kind == 0)[0].tolist())
+    # content and shared template rows may be re-staged in several passes
+    restaged = set(np.nonzero((lay.row_kind == 0) | ((lay.row_kind == 1) & (lay.row_branch < 0)))[0].tolist())
+    scored = set(OT.scored_rows(lay))
     for k in range(plan.n_passes):
         lr, sr = plan.rows(k)
         assert len(lr) <= budget
         assert len(set(lr.tolist())) == len(lr)          # no row twice in one pass
         seen.update(lr.tolist())
         # scored rows: the template's last row and every trie node
-        want = sorted(x for x in range(len(lr)) if lay.row_kind[lr[x]] == 2 or
-                      (lay.row_kind[lr[x]] == 1 and
-                       lay.row_pos[lr[x]] == lay.inputs[lay.row_input[lr[x]]].branches[lay.row_branch[lr[x]]].L - 1))
+        want = sorted(x for x in range(len(lr)) if int(lr[x]) in scored)
         assert sorted(sr.tolist()) == want
     # every branch row exactly once; content rows at least once, and in every
     # pass that holds one of the input's branches
     for r in range(lay.n_rows):
-        if r in content_rows:
+        if r in restaged:
             assert seen[r] >= 1
         else:
             assert seen[r] == 1, r
@@ -370,14 +370,14 @@ def _meta_arrays(buf):
     tail = buf[48 + 16 * 8:48 + 16 * 8 + 16].view(np.int32)
     n_tokens, n_branches = int(i32[3]), int(i32[5])
     off_rows, off_branches = int(i64[0]), int(i64[2])
-    rows = buf[off_rows:off_rows + 32 * n_tokens].view(np.int32).reshape(-1, 8)
+    rows = buf[off_rows:off_rows + 48 * n_tokens].view(np.int32).reshape(-1, 12)
     br = buf[off_branches:off_branches + 32 * n_branches].view(np.int32).reshape(-1, 8)
     items = []
     for g in range(3):
         off, n = int(i64[12 + g]), int(tail[g])
         items.append(buf[off:off + 32 * n].view(np.int32).reshape(-1, 8))
     off_bc, n_bc = int(i64[15]), int(tail[3])
-    bchunks = buf[off_bc:off_bc + 8 * n_bc].view(np.int32).reshape(-1, 2)
+    bchunks = buf[off_bc:off_bc + 16 * n_bc].view(np.int32).reshape(-1, 4)
     return n_tokens, rows, br, items, bchunks
 
 
@@ -411,7 +411,7 @@ def test_attention_work_items_cover_rows_and_visible_chunks(budget):
                 for b0 in sorted(set(int(v) for v in r[:, 2] if v >= 0)):
                     emax = int(r[r[:, 2] == b0, 3].max())
                     want += [(b0 + 32 * c, (start_of[b0] << 10) | c) for c in range(emax // 32 + 1)]
-                got = [tuple(int(v) for v in e) for e in bchunks[boff:boff + bn]]
+                got = [tuple(int(v) for v in e[:2]) for e in bchunks[boff:boff + bn]]
                 assert got == want
             assert (seen == 1).all()  # every row in exactly one item
             assert costs == sorted(costs, reverse=True)
