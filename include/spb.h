@@ -81,8 +81,9 @@ const char *spb_fingerprint(void);
  * distinct proper prefixes of the options in first-appearance order (options
  * in order, each option's prefixes by increasing length).
  *
- * Template tries [PyPI "Layout": templates to token tries; "What it does":
- * placeholders turn one template into a grid of questions]: with tmpl_tok
+ * Template tries [PyPI "Layout": the engine compiles templates into token
+ * tries; "What it does": placeholder values expand one template into many
+ * questions]: with tmpl_tok
  * (the template token ids, question after question, q_len[q] each; NULL: none
  * given), the questions of one input share the tokens of every template prefix
  * that at least two of them start with, except that a question's last

@@ -9,10 +9,10 @@ GPU", the response example and the paragraph after it; PyPI "spinf-serve
     distribution (``logprob``);
   * ``p`` is the probability among the given options: the options'
     probabilities renormalised to sum to one;
-  * ``residual`` is the probability that went to tokens outside the options:
+  * ``residual`` is the probability mass left to tokens other than the options:
     one minus the options' total probability;
-  * ``floor_p`` is ``p`` for the same question on empty content; ``p - floor_p``
-    is what the content added (the lift).
+  * ``floor_p`` is ``p`` for the same question on empty content; the lift,
+    ``p - floor_p``, measures the content's own contribution.
 The lm head's output precision [man page "spinf-serve", PARAMETERS: --lm-head]
 is one of f32out (the default: f32 logits), bf16 or fp32.  The oracle keeps
 float64 throughout and models the kinds as: f32out and fp32, the exact

@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY -- see the package header.
 
 What the pages fix, restated:
   * one input is a content read once, with every question laid out as a branch
-    of that read; a question's template ends where the answer goes
+    of that read; a question's template stops at the position of its answer
     [PyPI "spinf-serve 0.1.1", "What it does": Scoring; Many questions, one read];
   * templates and options are compiled to token tries, and scoring is one packed
     forward over them [PyPI, "Layout": protocol/compiler/packer/scorer];
@@ -26,8 +26,9 @@ attends to, itself last) is the chain of ancestors:
   trie node, depth 1  -> last template token
   trie node, depth k  -> the trie node of its first k-1 tokens
 
-Template tries [PyPI "Layout": templates to token tries; "What it does":
-placeholders turn one template into a grid of questions].  When the
+Template tries [PyPI "Layout": the engine compiles templates into token
+tries; "What it does": placeholder values expand one template into many
+questions].  When the
 templates' token ids are given, the questions of one input share the tokens
 of common template prefixes.  Reading taken: a prefix of a question's template
 up to (not including) its last token is shared when at least two of the

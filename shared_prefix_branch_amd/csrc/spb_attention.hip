@@ -3,8 +3,8 @@
 // Computes, for every packed row x and query head h, softmax attention over
 // the keys on x's root path only: its own content (causal for content rows,
 // all of it for branch rows), its own template prefix and its own option-trie
-// ancestors.  This is the pages' "content read once, every question a branch
-// of the same pass" [PyPI "spinf-serve 0.1.1", "What it does"], with answers
+// ancestors.  So each content is read once and all of its questions ride in
+// the same pass as branches [PyPI "spinf-serve 0.1.1", "What it does"], with answers
 // equal to running each content + question as its own prompt [PyPI, "Speed
 // and scale"].
 //
