@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="news")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-template-sharing", action="store_true",
+                    help="drop the template token ids, so questions share no template prefix")
     ap.add_argument("--cpu-sample-inputs", type=int, default=0,
                     help="contents in the oracle's sample (0: all of the workload's)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -130,6 +132,8 @@ def main():
     d = wl.dims
     budget = wl.budgets[0]
     prob = wl.problem
+    if args.no_template_sharing:
+        prob = synth.Problem(**{**prob.__dict__, "tmpl_tok": None})
 
     # ---- inputs resident in HBM
     plan = spb.pack_pass(prob, token_budget=budget)
@@ -251,7 +255,8 @@ def main():
                                f"token budget {budget}, {n_pass} passes",
                    "packed_tokens": tokens, "questions": questions, "token_budget": budget,
                    "hq": d.hq, "hkv": d.hkv, "head_dim": d.head_dim, "hidden": d.hidden, "vocab": d.vocab,
-                   "lm_head": args.lm_head, "lm_head_launches_per_step": n_head},
+                   "lm_head": args.lm_head, "lm_head_launches_per_step": n_head,
+                   "template_sharing": prob.tmpl_tok is not None},
         "questions_per_s": round(questions / (ms_step * 1e-3), 1),
         "attention": {"ms": round(float(att_ms.sum()), 4), "tflops": round(att_tflops, 2),
                       "mfma_util": round(att_tflops / PEAK_BF16_TFLOPS, 4),

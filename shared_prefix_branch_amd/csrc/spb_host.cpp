@@ -13,12 +13,14 @@
 #include "../../include/spb.h"
 
 #include <algorithm>
+#include <unordered_map>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <new>
 #include <set>
 #include <string>
@@ -144,16 +146,94 @@ spb_status compile_question(const spb_problem &P, int q, const spb_pack_opts &o,
 
 // ----------------------------------------------------------------- plan
 
+// Large host buffers of a plan (rows, item tables, metadata) come from a
+// process-wide cache of freed blocks, so a serving loop that packs one batch
+// after another reuses memory that is already mapped instead of faulting in
+// fresh pages on every pack.  Blocks of 64 KiB .. 64 MiB, in power-of-two
+// classes; at most 256 MiB are kept; smaller requests go to operator new.
+class BlockCache {
+ public:
+  static constexpr int kMinLog = 16, kMaxLog = 26;
+  static constexpr size_t kKeepBytes = size_t(256) << 20;
+  static int cls(size_t bytes) {
+    int c = kMinLog;
+    while (c <= kMaxLog && (size_t(1) << c) < bytes) ++c;
+    return c;
+  }
+  static void *get(size_t bytes) {
+    const int c = cls(bytes);
+    if (bytes < (size_t(1) << kMinLog) || c > kMaxLog) return ::operator new(bytes);
+    {
+      std::lock_guard<std::mutex> g(m());
+      auto &fl = lists()[c - kMinLog];
+      if (!fl.empty()) {
+        void *p = fl.back();
+        fl.pop_back();
+        kept() -= size_t(1) << c;
+        return p;
+      }
+    }
+    return ::operator new(size_t(1) << c);
+  }
+  static void put(void *p, size_t bytes) {
+    const int c = cls(bytes);
+    if (bytes < (size_t(1) << kMinLog) || c > kMaxLog) {
+      ::operator delete(p);
+      return;
+    }
+    {
+      std::lock_guard<std::mutex> g(m());
+      if (kept() + (size_t(1) << c) <= kKeepBytes) {
+        lists()[c - kMinLog].push_back(p);
+        kept() += size_t(1) << c;
+        return;
+      }
+    }
+    ::operator delete(p);
+  }
+
+ private:
+  // never destroyed: plans may be freed while the process exits
+  static std::mutex &m() {
+    static std::mutex *mu = new std::mutex;
+    return *mu;
+  }
+  static std::vector<void *> *lists() {
+    static std::vector<void *> *l = new std::vector<void *>[kMaxLog - kMinLog + 1];
+    return l;
+  }
+  static size_t &kept() {
+    static size_t k = 0;
+    return k;
+  }
+};
+
+template <class T>
+struct CachedAlloc {
+  using value_type = T;
+  CachedAlloc() = default;
+  template <class U>
+  CachedAlloc(const CachedAlloc<U> &) {}
+  T *allocate(size_t n) { return static_cast<T *>(BlockCache::get(n * sizeof(T))); }
+  void deallocate(T *p, size_t n) { BlockCache::put(p, n * sizeof(T)); }
+  template <class U>
+  bool operator==(const CachedAlloc<U> &) const { return true; }
+  template <class U>
+  bool operator!=(const CachedAlloc<U> &) const { return false; }
+};
+template <class T>
+using cvec = std::vector<T, CachedAlloc<T>>;
+
 struct PassPlan {
   int n_tokens = 0;
   int n_segments = 0;
   int64_t pairs = 0;
-  std::vector<int64_t> logical_row;
-  std::vector<SpbRow> rows;
-  std::vector<SpbTile> tiles;
+  cvec<int64_t> logical_row;
+  cvec<SpbRow> rows;
+  cvec<SpbTile> tiles;
   std::vector<SpbBranch> branches;
-  std::vector<SpbItem> items[3];
-  std::vector<SpbChunk> bchunks;
+  cvec<SpbItem> items[3];
+  cvec<SpbChunk> bchunks;
   struct HostStem {
     int start, L, pre, post, parent;  // parent: index in stems, -1 none
   };
@@ -161,7 +241,33 @@ struct PassPlan {
   int stem_base = 0;            // next free DFS number in this pass
   std::vector<int32_t> logical_branch;
   std::vector<int32_t> scored, tgt_off, tgt_tok, opt_step_off, step_slot, step_row;
-  std::vector<unsigned char> blob;
+  struct Blob {  // the pass metadata, allocated without a zero fill
+    unsigned char *p = nullptr;
+    size_t n = 0;
+    Blob() = default;
+    Blob(const Blob &) = delete;
+    Blob &operator=(const Blob &) = delete;
+    Blob(Blob &&o) noexcept : p(o.p), n(o.n) { o.p = nullptr; o.n = 0; }
+    Blob &operator=(Blob &&o) noexcept {
+      if (this != &o) {
+        reset(0);
+        p = o.p;
+        n = o.n;
+        o.p = nullptr;
+        o.n = 0;
+      }
+      return *this;
+    }
+    ~Blob() { reset(0); }
+    void reset(size_t bytes) {
+      if (p) BlockCache::put(p, n);
+      p = bytes ? static_cast<unsigned char *>(BlockCache::get(bytes)) : nullptr;
+      n = bytes;
+    }
+    unsigned char *data() { return p; }
+    const unsigned char *data() const { return p; }
+    size_t size() const { return n; }
+  } blob;
 };
 
 }  // namespace
@@ -214,50 +320,63 @@ void build_stems(Unit &u, const std::vector<Question> &Q, const std::vector<std:
   u.br_stem.assign(nb, -1);
   for (size_t b = 0; b < nb; ++b) u.own_L[b] = Q[u.qs[b]].L;
   if (tmpl.empty() || nb < 2) return;
-  std::map<std::vector<int>, int> count;
+  // trie of the questions' proper template prefixes (node 0: the empty
+  // prefix); cnt[n]: questions of which node n's prefix is a proper prefix.
+  // cnt never grows along a path, so a question's shared tokens are the
+  // leading nodes of its path with cnt >= 2.
+  std::unordered_map<uint64_t, int> child;
+  std::vector<int> cnt(1, 0), par(1, -1);
+  std::vector<std::vector<int>> path(nb);
   for (size_t b = 0; b < nb; ++b) {
     const auto &T = tmpl[u.qs[b]];
-    for (size_t k = 1; k < T.size(); ++k) count[std::vector<int>(T.begin(), T.begin() + k)]++;
+    int n = 0;
+    for (size_t k = 0; k + 1 < T.size(); ++k) {
+      const uint64_t key = ((uint64_t)(uint32_t)n << 32) | (uint32_t)T[k];
+      auto it = child.find(key);
+      if (it == child.end()) {
+        it = child.emplace(key, (int)cnt.size()).first;
+        cnt.push_back(0);
+        par.push_back(n);
+      }
+      n = it->second;
+      cnt[n]++;
+      path[b].push_back(n);
+    }
   }
+  const int nn = (int)cnt.size();
   std::vector<int> s(nb, 0);
+  for (size_t b = 0; b < nb; ++b)
+    while (s[b] < (int)path[b].size() && cnt[path[b][s[b]]] >= 2) ++s[b];
+  // per shared node: its shared children, and whether some question's shared
+  // part ends there
+  std::vector<int> nkids(nn, 0), seg_of(nn, -1);
+  std::vector<char> exits(nn, 0);
+  for (int n = 1; n < nn; ++n)
+    if (cnt[n] >= 2) nkids[par[n]]++;
+  for (size_t b = 0; b < nb; ++b)
+    if (s[b] > 0) exits[path[b][s[b] - 1]] = 1;
   for (size_t b = 0; b < nb; ++b) {
-    const auto &T = tmpl[u.qs[b]];
-    while (s[b] + 1 < (int)T.size() && count[std::vector<int>(T.begin(), T.begin() + s[b] + 1)] >= 2) ++s[b];
-  }
-  // per shared node: distinct shared children, and whether a question leaves there
-  std::map<std::vector<int>, std::set<int>> kids;
-  std::set<std::vector<int>> exits;
-  for (size_t b = 0; b < nb; ++b) {
-    const auto &T = tmpl[u.qs[b]];
-    for (int k = 1; k <= s[b]; ++k)
-      if (k > 1) kids[std::vector<int>(T.begin(), T.begin() + k - 1)].insert(T[k - 1]);
-    if (s[b] > 0) exits.insert(std::vector<int>(T.begin(), T.begin() + s[b]));
-  }
-  std::map<std::vector<int>, int> seg_of;  // shared node -> stem index
-  for (size_t b = 0; b < nb; ++b) {
-    const auto &T = tmpl[u.qs[b]];
     for (int k = 1; k <= s[b]; ++k) {
-      std::vector<int> p(T.begin(), T.begin() + k);
-      if (seg_of.count(p)) continue;
-      int par = -1;
+      const int n = path[b][k - 1];
+      if (seg_of[n] >= 0) continue;
+      int parent = -1;
       if (k > 1) {
-        std::vector<int> up(T.begin(), T.begin() + k - 1);
-        const int ps = seg_of[up];
-        if (!exits.count(up) && kids[up].size() == 1) {  // the run continues
-          seg_of[p] = ps;
-          u.stems[ps].len++;
+        const int up = path[b][k - 2];
+        if (!exits[up] && nkids[up] == 1) {  // the run continues
+          seg_of[n] = seg_of[up];
+          u.stems[seg_of[up]].len++;
           continue;
         }
-        par = ps;
+        parent = seg_of[up];
       }
       Stem st{};
       st.len = 1;
-      st.parent = par;
-      seg_of[p] = (int)u.stems.size();
+      st.parent = parent;
+      seg_of[n] = (int)u.stems.size();
       u.stems.push_back(st);
     }
-    if (s[b] > 0) u.br_stem[b] = seg_of[std::vector<int>(T.begin(), T.begin() + s[b])];
-    u.own_L[b] = (int)T.size() - s[b];
+    if (s[b] > 0) u.br_stem[b] = seg_of[path[b][s[b] - 1]];
+    u.own_L[b] = (int)tmpl[u.qs[b]].size() - s[b];
   }
   // DFS numbering (children in creation order) and ancestor token counts
   const int ns = (int)u.stems.size();
@@ -303,6 +422,8 @@ struct Packer {
 
   void open() {
     passes.emplace_back();
+    passes.back().rows.reserve((size_t)std::min(B, 1 << 16));
+    passes.back().logical_row.reserve((size_t)std::min(B, 1 << 16));
     pass_groups.emplace_back();
     pass_group_seg.emplace_back();
   }
@@ -464,6 +585,8 @@ struct Packer {
 };
 
 void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, const std::vector<int> &gseg) {
+  std::vector<int> branch_at(P.rows.size(), -1);  // branch start row -> index in the branch table
+  for (size_t b = 0; b < P.branches.size(); ++b) branch_at[P.branches[b].start] = (int)b;
   for (size_t g = 0; g < groups.size(); ++g) {
     int g0 = groups[g].first, g1 = groups[g].second;
     for (int r0 = g0; r0 < g1; r0 += kTileRows) {
@@ -479,11 +602,7 @@ void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, co
       int lo = -1, hi = -1;
       for (int r = r0; r < r0 + t.nrows; ++r) {
         if (P.rows[r].br < 0 || P.rows[r].stem) continue;
-        // locate by binary search on start
-        int s = P.rows[r].br;
-        auto it = std::lower_bound(P.branches.begin(), P.branches.end(), s,
-                                   [](const SpbBranch &b, int v) { return b.start < v; });
-        int bi = (int)(it - P.branches.begin());
+        const int bi = branch_at[P.rows[r].br];
         if (lo < 0) lo = bi;
         hi = bi;
       }
@@ -509,36 +628,43 @@ void build_tiles(PassPlan &P, const std::vector<std::pair<int, int>> &groups, co
 // split into row ranges, each with the content chunks its own rows see and the
 // chunks of the branches meeting its rows, longest first.
 void build_items(PassPlan &P) {
-  std::map<int, int> stem_at;  // pre number -> index in P.stems
+  std::unordered_map<int, int> stem_at;  // pre number -> index in P.stems
   for (size_t s = 0; s < P.stems.size(); ++s) stem_at[P.stems[s].pre] = (int)s;
+  cvec<SpbItem> items;
+  cvec<SpbChunk> flat;                // chunk lists of the items, in item order
+  std::vector<std::pair<int, int>> stems;  // (pre, index) of an item's stems
+  std::vector<int> order;
   for (int g = 0; g < 3; ++g) {
     const int rows_per = 32 << g;
-    std::vector<SpbItem> items;
-    std::vector<std::vector<SpbChunk>> lists;
+    items.clear();
+    flat.clear();
     for (const SpbTile &t : P.tiles) {
       for (int r0 = t.row0; r0 < t.row0 + t.nrows; r0 += rows_per) {
         SpbItem it{};
         it.row0 = r0;
         it.nrows = std::min(rows_per, t.row0 + t.nrows - r0);
         it.seg = t.seg;
+        it.boff = (int)flat.size();
         int maxc = 0;
-        for (int r = r0; r < r0 + it.nrows; ++r) maxc = std::max(maxc, P.rows[r].cvis);
-        it.ncc = (maxc + kChunk - 1) / kChunk;
-        std::vector<SpbChunk> list;
         // stems on the paths of the item's rows (a stem row's own stem, a
         // branch row's deepest stem, and their ancestors), root first
-        std::set<std::pair<int, int>> stems;  // (pre, index)
+        stems.clear();
+        int last_spre = -1;
         for (int r = r0; r < r0 + it.nrows; ++r) {
           const SpbRow &R = P.rows[r];
-          if (R.br < 0 || R.spre < 0) continue;
-          int s = stem_at.at(R.spre);
-          for (; s >= 0; s = P.stems[s].parent) stems.insert({P.stems[s].pre, s});
+          maxc = std::max(maxc, R.cvis);
+          if (R.br < 0 || R.spre < 0 || R.spre == last_spre) continue;
+          last_spre = R.spre;
+          for (int s = stem_at.at(R.spre); s >= 0; s = P.stems[s].parent) stems.push_back({P.stems[s].pre, s});
         }
+        it.ncc = (maxc + kChunk - 1) / kChunk;
+        std::sort(stems.begin(), stems.end());
+        stems.erase(std::unique(stems.begin(), stems.end()), stems.end());
         for (auto &ps : stems) {
           const auto &S = P.stems[ps.second];
           for (int c = 0; c * kBranchChunk < S.L; ++c) {
             const int nvis = std::min(S.L - c * kBranchChunk, kBranchChunk);
-            list.push_back(SpbChunk{S.start + c * kBranchChunk, kStemChunk | (ps.second << 10) | c, S.pre,
+            flat.push_back(SpbChunk{S.start + c * kBranchChunk, kStemChunk | (ps.second << 10) | c, S.pre,
                                     S.post | (nvis << 24)});
           }
         }
@@ -547,22 +673,25 @@ void build_items(PassPlan &P) {
           if (B.start + B.E <= r0 || B.start >= r0 + it.nrows) continue;
           const int last = std::min(B.start + B.E, r0 + it.nrows) - 1 - B.start;
           for (int c = 0; c <= last / kBranchChunk; ++c)
-            list.push_back(SpbChunk{B.start + c * kBranchChunk, (b << 10) | c, 0, 0});
+            flat.push_back(SpbChunk{B.start + c * kBranchChunk, (b << 10) | c, 0, 0});
         }
-        it.bn = (int)list.size();
+        it.bn = (int)flat.size() - it.boff;
         it.cost = it.ncc + it.bn;
         items.push_back(it);
-        lists.push_back(std::move(list));
       }
     }
-    std::vector<int> order(items.size());
+    // longest first (stable: ties keep row order)
+    order.resize(items.size());
     for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return items[a].cost > items[b].cost; });
     P.items[g].clear();
+    P.items[g].reserve(items.size());
+    P.bchunks.reserve(P.bchunks.size() + flat.size());
     for (int i : order) {
       SpbItem it = items[i];
+      const int src = it.boff;
       it.boff = (int)P.bchunks.size();
-      P.bchunks.insert(P.bchunks.end(), lists[i].begin(), lists[i].end());
+      P.bchunks.insert(P.bchunks.end(), flat.begin() + src, flat.begin() + src + it.bn);
       P.items[g].push_back(it);
     }
   }
@@ -595,9 +724,9 @@ void build_scoring(PassPlan &P, const std::vector<Question> &Q) {
   }
 }
 
-template <class T>
-void put(std::vector<unsigned char> &blob, size_t off, const std::vector<T> &v) {
-  if (!v.empty()) memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
+template <class V>
+void put(unsigned char *blob, size_t off, const V &v) {
+  if (!v.empty()) memcpy(blob + off, v.data(), v.size() * sizeof(v[0]));
 }
 
 void build_blob(PassPlan &P, int pass) {
@@ -613,8 +742,10 @@ void build_blob(PassPlan &P, int pass) {
   h.n_targets = (int)P.tgt_tok.size();
   h.n_steps = (int)P.step_slot.size();
   size_t off = align256(sizeof(SpbMetaHeader));
+  std::vector<std::pair<size_t, size_t>> gaps{{sizeof(SpbMetaHeader), off}};  // padding, zeroed below
   auto place = [&](int64_t &field, size_t bytes) {
     field = (int64_t)off;
+    gaps.push_back({off + bytes, align256(off + bytes)});
     off = align256(off + bytes);
   };
   place(h.off_rows, P.rows.size() * sizeof(SpbRow));
@@ -633,19 +764,21 @@ void build_blob(PassPlan &P, int pass) {
   h.n_bchunks = (int)P.bchunks.size();
   place(h.off_bchunks, P.bchunks.size() * sizeof(SpbChunk));
   h.total_bytes = (int64_t)off;
-  P.blob.assign(off, 0);
-  memcpy(P.blob.data(), &h, sizeof h);
-  put(P.blob, h.off_rows, P.rows);
-  put(P.blob, h.off_tiles, P.tiles);
-  put(P.blob, h.off_branches, P.branches);
-  put(P.blob, h.off_scored, P.scored);
-  put(P.blob, h.off_tgt_off, P.tgt_off);
-  put(P.blob, h.off_tgt_tok, P.tgt_tok);
-  put(P.blob, h.off_opt_step_off, P.opt_step_off);
-  put(P.blob, h.off_step_slot, P.step_slot);
-  put(P.blob, h.off_step_row, P.step_row);
-  for (int g = 0; g < 3; ++g) put(P.blob, h.off_items[g], P.items[g]);
-  put(P.blob, h.off_bchunks, P.bchunks);
+  P.blob.reset(off);
+  unsigned char *B = P.blob.data();
+  for (auto &g : gaps) memset(B + g.first, 0, g.second - g.first);
+  memcpy(B, &h, sizeof h);
+  put(B, h.off_rows, P.rows);
+  put(B, h.off_tiles, P.tiles);
+  put(B, h.off_branches, P.branches);
+  put(B, h.off_scored, P.scored);
+  put(B, h.off_tgt_off, P.tgt_off);
+  put(B, h.off_tgt_tok, P.tgt_tok);
+  put(B, h.off_opt_step_off, P.opt_step_off);
+  put(B, h.off_step_slot, P.step_slot);
+  put(B, h.off_step_row, P.step_row);
+  for (int g = 0; g < 3; ++g) put(B, h.off_items[g], P.items[g]);
+  put(B, h.off_bchunks, P.bchunks);
   P.n_tokens = h.n_tokens;
 }
 

@@ -415,3 +415,26 @@ def test_attention_work_items_cover_rows_and_visible_chunks(budget):
                 assert got == want
             assert (seen == 1).all()  # every row in exactly one item
             assert costs == sorted(costs, reverse=True)
+
+
+def test_repacking_gives_identical_metadata():
+    # plans reuse freed host blocks; every byte of a pass's metadata is
+    # written on each pack, so a block that held another plan leaves no trace
+    news = synth.make_workload("news").problem
+    other = synth.make_problem("random_shared", 5, vocab=1000, n_inputs=40, n_questions=30, max_content=400,
+                               max_lead=30)
+
+    def blobs(prob):
+        plan = spb.pack_pass(prob, token_budget=16384)
+        out = []
+        for k in range(plan.n_passes):
+            b = np.zeros(plan.info(k)["meta_bytes"], np.uint8)
+            plan.meta_copy(k, b)
+            out.append(b.tobytes())
+        del plan
+        return out
+
+    first = blobs(news)
+    blobs(other)
+    assert blobs(news) == first
+    assert blobs(other) == blobs(other)
