@@ -32,9 +32,11 @@ __all__ = [
     "Problem", "Dims", "Workload", "CONFIGS", "make_workload", "make_problem",
     "count_trie_nodes", "logical_inputs", "seed_for", "STREAM_INPUT",
     "STREAM_FLOOR", "STREAM_LM_HEAD", "STREAM_CALIB", "STREAM_HIDDEN",
+    "ModelDims", "model_weights", "embed_block",
 ]
 
 STREAM_INPUT, STREAM_FLOOR, STREAM_LM_HEAD, STREAM_CALIB, STREAM_HIDDEN = 0, 1, 2, 3, 4
+STREAM_MODEL, STREAM_EMBED = 5, 6
 
 
 @dataclasses.dataclass
@@ -429,3 +431,63 @@ def cast_inputs(wl: Workload, q, k, v, scales=None):
         sq, sk, sv = scales
         return to_e4m3(q, sq), to_e4m3(k, sk), to_e4m3(v, sv)
     raise ValueError(dt)
+
+
+# ----------------------------------------------------------------------------- decoder stack
+
+@dataclasses.dataclass
+class ModelDims:
+    """A decoder stack over the packed pass (synthetic weights)."""
+    hidden: int
+    hq: int
+    hkv: int
+    head_dim: int
+    ffn: int          # gated MLP width
+    layers: int
+    rope_base: float = 10000.0
+    eps: float = 1e-6
+
+
+MODEL_CONFIGS = {
+    # the news attention shape with a 4x gated MLP
+    "news": ModelDims(3840, 32, 16, 128, 15360, 2),
+    # small shapes the oracle runs in seconds
+    "small": ModelDims(256, 4, 2, 64, 512, 2),
+    "small_d128": ModelDims(512, 8, 4, 128, 768, 2),
+}
+
+
+def model_weights(md: ModelDims, seed: int, device="cpu"):
+    """Per layer: wq [Hq*d, H], wk / wv [Hkv*d, H], wo [H, Hq*d], wg / wu [F, H],
+    wd [H, F], each ~ N(0, 1/fan_in) and cast to bf16 (RNE); RMS gains g_attn,
+    g_mlp [H] ~ U(0.5, 1.5) as bf16; and the final gain g_final.  Returns
+    (list of per-layer dicts, g_final)."""
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(seed, STREAM_MODEL, 0))
+    H, F = md.hidden, md.ffn
+    qd, kd = md.hq * md.head_dim, md.hkv * md.head_dim
+
+    def mat(rows, fan_in):
+        return (torch.randn((rows, fan_in), generator=g, device=device) / np.sqrt(fan_in)).to(torch.bfloat16)
+
+    def gain():
+        return (0.5 + torch.rand((H,), generator=g, device=device)).to(torch.bfloat16)
+
+    layers = []
+    for _ in range(md.layers):
+        layers.append(dict(wq=mat(qd, H), wk=mat(kd, H), wv=mat(kd, H), wo=mat(H, qd),
+                           wg=mat(F, H), wu=mat(F, H), wd=mat(H, F), g_attn=gain(), g_mlp=gain()))
+    return layers, gain()
+
+
+def embed_block(wl: Workload, md: ModelDims, which: tuple, device="cpu"):
+    """Input embeddings x0 [rows, H] ~ N(0, 1) (float32) for every logical row
+    of one logical input, from its own seed (a stand-in for token embeddings:
+    the problem carries no content token ids)."""
+    torch = _torch()
+    stream, ident = input_ident(which)
+    n = input_rows(wl.problem, which)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(wl.cfg_seed, STREAM_EMBED, ident if stream == STREAM_INPUT else 10_000_000 + ident))
+    return torch.randn((n, md.hidden), generator=g, device=device)
