@@ -284,6 +284,79 @@ spb_status spb_score_finalize(const spb_plan *plan, const float *const *lp_per_p
                               const float *const *residual_per_pass, float *lp, float *p, float *residual,
                               float *floor_p, float *lift);
 
+/* ------------------------------------------------------------ decoder stack
+ * The engine runs a whole decoder model over the packed pass and hands its
+ * last hidden states to the head [PyPI "spinf-serve 0.1.1", "Layout": one
+ * packed forward; models/ one stack per architecture family].  The pages do
+ * not spell out the layer, so these calls build the plain pre-norm decoder
+ * layer around spb_branch_attention, on the packed rows:
+ *   h = rmsnorm(x) * g_attn;  q, k, v = h [Wq; Wk; Wv]^T, q and k rotated at
+ *   each row's position (spb_plan_positions);  x += attention(q, k, v) Wo^T;
+ *   h = rmsnorm(x) * g_mlp;  x += (silu(h Wg^T) * h Wu^T) Wd^T;
+ * and rmsnorm(x) * g_final feeds spb_score_options.  x, the residual stream,
+ * is f32; every other activation is bf16 (rounded to nearest even once, at
+ * the end of the op that makes it).  Each row's results depend only on its
+ * own root path, as for attention alone.  All calls enqueue on the stream,
+ * allocate nothing and validate every argument before any HIP call. */
+
+/* Position of each pass row on its own root path (content token t: t;
+ * template token j: C + j; trie node of depth k: C + L - 1 + k), i.e. the
+ * position the row has when its question runs as its own prompt.  host_out:
+ * [n_tokens] int32, caller-owned. */
+spb_status spb_plan_positions(const spb_plan *plan, int32_t pass, int32_t *host_out);
+
+/* Rotary embedding table [n_pos][head_dim / 2][2] = (cos, sin) of
+ * p * base^(-2i / head_dim), computed in double and rounded to f32: the
+ * rotary position embedding of Su et al. (RoFormer), pairs (2i, 2i+1).
+ * host_out: n_pos * head_dim floats, caller-owned; head_dim even. */
+spb_status spb_rope_table(float *host_out, int32_t n_pos, int32_t head_dim, double base);
+
+/* out[r] = bf16(x[r] / sqrt(mean(x[r]^2) + eps) * gain) for r < rows.
+ * x: f32 [rows][dim]; gain: bf16 [dim]; out: bf16 [rows][dim]; device
+ * memory, 16-byte aligned; dim % 4 == 0. */
+typedef struct {
+  const float *x;
+  const void *gain;
+  void *out;
+  int64_t rows;
+  int32_t dim;
+  float eps;
+} spb_rmsnorm_args;
+spb_status spb_rmsnorm(const spb_rmsnorm_args *args, void *stream);
+
+/* Linear layer on MFMA: acc = x W^T in f32 (x: bf16 [m][k], W: bf16 [n][k],
+ * both row-major), K summed in a fixed order, so a row's result does not
+ * depend on m.  Epilogues (mode):
+ *   SPB_LINEAR_BF16:      y[m][n] = bf16(acc);
+ *   SPB_LINEAR_RESIDUAL:  resid[m][n] += bf16(acc) (resid f32, in place);
+ *   SPB_LINEAR_SILU_GATE: y[m][n/2] = bf16(silu(gate) * up), with W's rows
+ *     in blocks of 64: rows 64j .. 64j+31 the gate rows 32j .. 32j+31 and
+ *     rows 64j+32 .. 64j+63 the up rows 32j .. 32j+31 (n % 64 == 0);
+ *   SPB_LINEAR_QKV_ROPE:  W = [Wq; Wk; Wv] (n = (hq + 2 hkv) head_dim); the
+ *     three column ranges go to q [m][hq*d], k [m][hkv*d], v [m][hkv*d], q
+ *     and k rotated by pos[r] with rope_table (spb_rope_table; positions
+ *     clamped into [0, n_pos)).
+ * k % 64 == 0, n % 8 == 0, m * k * 2 and n * k * 2 below 4 GiB; every
+ * tensor is device memory, 16-byte aligned, caller-owned.  gemm_event_begin /
+ * gemm_event_end: optional hipEvent_t handles recorded around the kernel. */
+enum { SPB_LINEAR_BF16 = 0, SPB_LINEAR_RESIDUAL = 1, SPB_LINEAR_SILU_GATE = 2, SPB_LINEAR_QKV_ROPE = 3 };
+typedef struct {
+  const void *x;
+  const void *w;
+  int64_t m;
+  int32_t n, k;
+  int32_t mode;
+  void *y;
+  float *resid;
+  void *q, *k_out, *v;
+  int32_t hq, hkv, head_dim;
+  const int32_t *pos;
+  const float *rope_table;
+  int32_t n_pos;
+  void *gemm_event_begin, *gemm_event_end;
+} spb_linear_args;
+spb_status spb_linear(const spb_linear_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,11 +20,14 @@ __all__ = [
     "score_options_batch",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
     "HEAD_F32OUT", "HEAD_BF16", "HEAD_FP32",
+    "LINEAR_BF16", "LINEAR_RESIDUAL", "LINEAR_SILU_GATE", "LINEAR_QKV_ROPE", "rope_table", "PreparedNorm",
+    "PreparedLinear", "rmsnorm", "linear",
     "EXPORTED_SYMBOLS",
 ]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 HEAD_F32OUT, HEAD_BF16, HEAD_FP32 = 0, 1, 2  # lm-head output kinds
+LINEAR_BF16, LINEAR_RESIDUAL, LINEAR_SILU_GATE, LINEAR_QKV_ROPE = 0, 1, 2, 3  # linear-layer epilogues
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libspb.so")
 
@@ -34,7 +37,7 @@ EXPORTED_SYMBOLS = [
     "spb_plan_visible",
     "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
     "spb_score_batch_workspace_bytes", "spb_score_options_batch",
-    "spb_score_finalize",
+    "spb_score_finalize", "spb_plan_positions", "spb_rope_table", "spb_rmsnorm", "spb_linear",
 ]
 
 
@@ -88,6 +91,20 @@ class _ScoreArgs(ctypes.Structure):
                 ("lm_head_kind", ctypes.c_int32)]
 
 
+class _NormArgs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("gain", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("dim", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class _LinearArgs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("m", ctypes.c_int64), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("mode", ctypes.c_int32), ("y", ctypes.c_void_p), ("resid", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("k_out", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("pos", ctypes.c_void_p), ("rope_table", ctypes.c_void_p), ("n_pos", ctypes.c_int32),
+                ("gemm_event_begin", ctypes.c_void_p), ("gemm_event_end", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -126,6 +143,10 @@ def lib() -> ctypes.CDLL:
                                               ctypes.c_void_p]
         fpp = ctypes.POINTER(_f32p)
         L.spb_score_finalize.argtypes = [ctypes.c_void_p, fpp, fpp, fpp, _f32p, _f32p, _f32p, _f32p, _f32p]
+        L.spb_plan_positions.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p]
+        L.spb_rope_table.argtypes = [_f32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
+        L.spb_rmsnorm.argtypes = [ctypes.POINTER(_NormArgs), ctypes.c_void_p]
+        L.spb_linear.argtypes = [ctypes.POINTER(_LinearArgs), ctypes.c_void_p]
         for name in EXPORTED_SYMBOLS:
             if name not in ("spb_last_error", "spb_fingerprint", "spb_pack_opts_default", "spb_plan_free"):
                 getattr(L, name).restype = ctypes.c_int32
@@ -185,6 +206,12 @@ class Plan:
         sr = np.empty(inf["n_scored_rows"], np.int32)
         _check(lib().spb_plan_rows(self._h, pass_, _ptr(lr, _i64p), _ptr(sr, _i32p)))
         return lr, sr
+
+    def positions(self, pass_: int) -> np.ndarray:
+        """Each pass row's position on its own root path (int32 [n_tokens])."""
+        out = np.empty(self.info(pass_)["n_tokens"], np.int32)
+        _check(lib().spb_plan_positions(self._h, pass_, _ptr(out, _i32p)))
+        return out
 
     def branches(self, pass_: int):
         inf = self.info(pass_)
@@ -426,3 +453,99 @@ def score_finalize(plan: Plan, lp_per_pass, p_per_pass, res_per_pass) -> dict:
                                     _ptr(out["residual"], _f32p), _ptr(out["floor_p"], _f32p),
                                     _ptr(out["lift"], _f32p)))
     return out
+
+
+# ---------------------------------------------------------------- decoder stack
+
+def rope_table(n_pos: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """(cos, sin) of p * base^(-2i/d): float32 [n_pos, head_dim // 2, 2]."""
+    out = np.empty((int(n_pos), int(head_dim) // 2, 2), np.float32)
+    _check(lib().spb_rope_table(_ptr(out, _f32p), int(n_pos), int(head_dim), float(base)))
+    return out
+
+
+def _dev(t, what: str, dtype=None):
+    import torch
+    if not t.is_contiguous():
+        raise SpbError(-1, f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise SpbError(-3, f"{what} must be {dtype}")
+    return t.data_ptr()
+
+
+class PreparedNorm:
+    """spb_rmsnorm with its arguments marshalled once: out = bf16(rmsnorm(x) * gain)."""
+
+    def __init__(self, x, gain, out, eps: float = 1e-6):
+        import torch
+        A = _NormArgs()
+        A.x = _dev(x, "x", torch.float32)
+        A.gain = _dev(gain, "gain", torch.bfloat16)
+        A.out = _dev(out, "out", torch.bfloat16)
+        A.rows = int(x.shape[0])
+        A.dim = int(x.shape[1])
+        if tuple(out.shape) != tuple(x.shape) or int(gain.numel()) != A.dim:
+            raise SpbError(-1, "x, gain and out disagree in shape")
+        A.eps = float(eps)
+        self.args = A
+        self._keep = (x, gain, out)
+
+    def __call__(self, stream=None):
+        _check(lib().spb_rmsnorm(ctypes.byref(self.args), ctypes.c_void_p(_stream_handle(stream))))
+
+
+class PreparedLinear:
+    """spb_linear with its arguments marshalled once.  x [m, k] and w [n, k]
+    bf16; mode LINEAR_BF16 / LINEAR_SILU_GATE: y; LINEAR_RESIDUAL: resid (f32
+    [m, n]); LINEAR_QKV_ROPE: q, k_out, v, heads, pos (int32 [m] device),
+    rope (float32 [n_pos, d/2, 2] device)."""
+
+    def __init__(self, x, w, mode: int, y=None, resid=None, q=None, k_out=None, v=None, hq: int = 0, hkv: int = 0,
+                 head_dim: int = 0, pos=None, rope=None):
+        import torch
+        A = _LinearArgs()
+        A.x = _dev(x, "x", torch.bfloat16)
+        A.w = _dev(w, "w", torch.bfloat16)
+        A.m = int(x.shape[0])
+        A.n = int(w.shape[0])
+        A.k = int(x.shape[1])
+        if int(w.shape[1]) != A.k:
+            raise SpbError(-1, "x and w disagree on k")
+        A.mode = int(mode)
+        keep = [x, w]
+        if y is not None:
+            A.y = _dev(y, "y", torch.bfloat16)
+            keep.append(y)
+        if resid is not None:
+            A.resid = _dev(resid, "resid", torch.float32)
+            keep.append(resid)
+        if q is not None:
+            A.q, A.k_out, A.v = (_dev(t, n, torch.bfloat16) for t, n in ((q, "q"), (k_out, "k"), (v, "v")))
+            A.hq, A.hkv, A.head_dim = int(hq), int(hkv), int(head_dim)
+            A.pos = _dev(pos, "pos", torch.int32)
+            A.rope_table = _dev(rope, "rope", torch.float32)
+            A.n_pos = int(rope.shape[0])
+            keep += [q, k_out, v, pos, rope]
+        self.args = A
+        self._keep = keep
+
+    def __call__(self, stream=None, events=None):
+        """events: optional (begin, end) torch.cuda.Event pair, already recorded
+        once, recorded around the kernel."""
+        A = self.args
+        if events is not None:
+            for ev in events:
+                if not ev.cuda_event:
+                    raise SpbError(-1, "timing events must be created (recorded once) before use")
+            A.gemm_event_begin, A.gemm_event_end = events[0].cuda_event, events[1].cuda_event
+        else:
+            A.gemm_event_begin = A.gemm_event_end = None
+        _check(lib().spb_linear(ctypes.byref(A), ctypes.c_void_p(_stream_handle(stream))))
+
+
+def rmsnorm(x, gain, out, eps: float = 1e-6, stream=None):
+    PreparedNorm(x, gain, out, eps)(stream)
+
+
+def linear(x, w, mode: int, stream=None, **kw):
+    PreparedLinear(x, w, mode, **kw)(stream)

@@ -229,6 +229,7 @@ struct PassPlan {
   int n_segments = 0;
   int64_t pairs = 0;
   cvec<int64_t> logical_row;
+  cvec<int32_t> pos;  // position of each row on its own root path
   cvec<SpbRow> rows;
   cvec<SpbTile> tiles;
   std::vector<SpbBranch> branches;
@@ -424,6 +425,7 @@ struct Packer {
     passes.emplace_back();
     passes.back().rows.reserve((size_t)std::min(B, 1 << 16));
     passes.back().logical_row.reserve((size_t)std::min(B, 1 << 16));
+    passes.back().pos.reserve((size_t)std::min(B, 1 << 16));
     pass_groups.emplace_back();
     pass_group_seg.emplace_back();
   }
@@ -456,6 +458,7 @@ struct Packer {
       r.spre = -1;
       P.rows.push_back(r);
       P.logical_row.push_back(u.first_row + t);
+      P.pos.push_back(t);
       P.pairs += t + 1;
     }
     if (u.C > 0) P.n_segments++;
@@ -494,6 +497,7 @@ struct Packer {
       r.stem = 1;
       P.rows.push_back(r);
       P.logical_row.push_back(st.first_row + j);
+      P.pos.push_back(u.C + st.chain_len + j);
       P.pairs += u.C + st.chain_len + j + 1;
     }
     end_rows();
@@ -534,6 +538,7 @@ struct Packer {
       r.spre = spre;
       P.rows.push_back(r);
       P.logical_row.push_back(u.br_first_row[bi] + j);
+      P.pos.push_back(u.C + chain + j);
       P.pairs += u.C + chain + j + 1;
     }
     for (int i = 0; i < q.n_nodes; ++i) {
@@ -551,6 +556,7 @@ struct Packer {
       r.anc23 = (int32_t)((uint32_t)a[2] | ((uint32_t)a[3] << 16));
       P.rows.push_back(r);
       P.logical_row.push_back(u.br_first_row[bi] + L + i);
+      P.pos.push_back(u.C + chain + L - 1 + r.depth);
       P.pairs += u.C + chain + L + r.depth;
     }
     end_rows();
@@ -1044,6 +1050,15 @@ spb_status spb_plan_rows(const spb_plan *plan, int32_t pass, int64_t *logical_ro
   return ok();
 }
 
+spb_status spb_plan_positions(const spb_plan *plan, int32_t pass, int32_t *host_out) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  if (!host_out) return fail(SPB_ERR_ARG, "host_out is NULL");
+  const PassPlan &P = plan->passes[pass];
+  if (!P.pos.empty()) memcpy(host_out, P.pos.data(), P.pos.size() * sizeof(int32_t));
+  return ok();
+}
+
 spb_status spb_plan_branches(const spb_plan *plan, int32_t pass, int32_t *logical_branch, int32_t *opt_first) {
   spb_status st = check_pass(plan, pass);
   if (st != SPB_OK) return st;
@@ -1389,6 +1404,97 @@ spb_status spb_score_finalize(const spb_plan *plan, const float *const *lp_pp, c
       if (lift) lift[dst] = F ? pv - fv : nan;
     }
   }
+  return ok();
+}
+
+spb_status spb_rope_table(float *host_out, int32_t n_pos, int32_t head_dim, double base) {
+  if (!host_out) return fail(SPB_ERR_ARG, "host_out is NULL");
+  if (n_pos < 1 || head_dim < 2 || head_dim % 2) return fail(SPB_ERR_ARG, "n_pos %d, head_dim %d", n_pos, head_dim);
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(SPB_ERR_ARG, "rope base must be finite and > 1");
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    const double theta = std::pow(base, -2.0 * i / head_dim);
+    for (int p = 0; p < n_pos; ++p) {
+      const double a = p * theta;
+      host_out[((size_t)p * half + i) * 2] = (float)std::cos(a);
+      host_out[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
+    }
+  }
+  return ok();
+}
+
+static bool misaligned16(const void *p) { return (uintptr_t)p % 16 != 0; }
+
+spb_status spb_rmsnorm(const spb_rmsnorm_args *a, void *stream) {
+  if (!a) return fail(SPB_ERR_ARG, "args is NULL");
+  if (a->rows < 0 || a->dim < 4 || a->dim % 4) return fail(SPB_ERR_ARG, "rows %lld, dim %d (dim % 4 == 0)",
+                                                             (long long)a->rows, a->dim);
+  if (!(a->eps >= 0.f) || !std::isfinite(a->eps)) return fail(SPB_ERR_ARG, "eps must be finite and >= 0");
+  if (a->rows == 0) return ok();
+  if (!a->x || !a->gain || !a->out) return fail(SPB_ERR_ARG, "NULL tensor");
+  if (misaligned16(a->x) || misaligned16(a->gain) || misaligned16(a->out))
+    return fail(SPB_ERR_ARG, "tensors must be 16-byte aligned");
+  NormLaunch L{a->x, (const uint16_t *)a->gain, (uint16_t *)a->out, (long long)a->rows, a->dim, a->eps};
+  int e = launch_rmsnorm(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "rmsnorm launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_linear(const spb_linear_args *a, void *stream) {
+  if (!a) return fail(SPB_ERR_ARG, "args is NULL");
+  if (a->mode < SPB_LINEAR_BF16 || a->mode > SPB_LINEAR_QKV_ROPE) return fail(SPB_ERR_ARG, "mode %d", a->mode);
+  if (a->m < 0 || a->m > 0x7FFFFFFF) return fail(SPB_ERR_ARG, "m %lld", (long long)a->m);
+  if (a->k < 64 || a->k % 64) return fail(SPB_ERR_ARG, "k %d must be a positive multiple of 64", a->k);
+  if (a->n < 8 || a->n % 8) return fail(SPB_ERR_ARG, "n %d must be a positive multiple of 8", a->n);
+  if ((uint64_t)a->m * (uint64_t)a->k * 2u >= (1ull << 32) || (uint64_t)a->n * (uint64_t)a->k * 2u >= (1ull << 32))
+    return fail(SPB_ERR_LIMIT, "x (%lld x %d) and W (%d x %d) must each stay under 4 GiB", (long long)a->m, a->k,
+                a->n, a->k);
+  if (a->m == 0) return ok();
+  if (!a->x || !a->w || misaligned16(a->x) || misaligned16(a->w))
+    return fail(SPB_ERR_ARG, "x and W must be non-NULL and 16-byte aligned");
+  LinearLaunch L{};
+  L.x = (const uint16_t *)a->x;
+  L.w = (const uint16_t *)a->w;
+  L.m = (int)a->m;
+  L.n = a->n;
+  L.k = a->k;
+  L.mode = a->mode;
+  switch (a->mode) {
+    case SPB_LINEAR_BF16:
+    case SPB_LINEAR_SILU_GATE:
+      if (a->mode == SPB_LINEAR_SILU_GATE && a->n % 64)
+        return fail(SPB_ERR_ARG, "silu-gate n %d must be a multiple of 64", a->n);
+      if (!a->y || misaligned16(a->y)) return fail(SPB_ERR_ARG, "y must be non-NULL and 16-byte aligned");
+      L.y = (uint16_t *)a->y;
+      break;
+    case SPB_LINEAR_RESIDUAL:
+      if (!a->resid || misaligned16(a->resid)) return fail(SPB_ERR_ARG, "resid must be non-NULL and 16-byte aligned");
+      L.resid = a->resid;
+      break;
+    case SPB_LINEAR_QKV_ROPE:
+      if (a->head_dim != 64 && a->head_dim != 128) return fail(SPB_ERR_DTYPE, "head_dim %d not in {64, 128}", a->head_dim);
+      if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv) return fail(SPB_ERR_ARG, "hq %d, hkv %d", a->hq, a->hkv);
+      if ((int64_t)(a->hq + 2 * a->hkv) * a->head_dim != a->n)
+        return fail(SPB_ERR_ARG, "n %d != (hq + 2 hkv) head_dim = %d", a->n, (a->hq + 2 * a->hkv) * a->head_dim);
+      if (!a->q || !a->k_out || !a->v || !a->pos || !a->rope_table || a->n_pos < 1)
+        return fail(SPB_ERR_ARG, "q, k, v, pos and rope_table must be non-NULL, n_pos >= 1");
+      if (misaligned16(a->q) || misaligned16(a->k_out) || misaligned16(a->v) || misaligned16(a->rope_table))
+        return fail(SPB_ERR_ARG, "q, k, v and rope_table must be 16-byte aligned");
+      L.q = (uint16_t *)a->q;
+      L.kk = (uint16_t *)a->k_out;
+      L.v = (uint16_t *)a->v;
+      L.hq = a->hq;
+      L.hkv = a->hkv;
+      L.head_dim = a->head_dim;
+      L.pos = a->pos;
+      L.rope = a->rope_table;
+      L.n_pos = a->n_pos;
+      break;
+  }
+  L.ev_begin = a->gemm_event_begin;
+  L.ev_end = a->gemm_event_end;
+  int e = launch_linear(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "linear launch: %s", hip_error_string(e));
   return ok();
 }
 

@@ -72,6 +72,37 @@ struct ScoreBatchLaunch {
   void *ev_begin, *ev_end;
 };
 
+// Decoder-stack kernels (spb_layer.hip).
+struct NormLaunch {
+  const float *x;          // [rows][dim] f32 residual stream
+  const uint16_t *gain;    // [dim] bf16
+  uint16_t *out;           // [rows][dim] bf16
+  long long rows;
+  int dim;
+  float eps;
+};
+
+// Y^T = W . X^T over tiles of 256 W rows x 32*kLinearMB X rows, then one of
+// the epilogues (SPB_LINEAR_* values).
+constexpr int kLinearMB = 7;
+struct LinearLaunch {
+  const uint16_t *x;       // [m][k] bf16
+  const uint16_t *w;       // [n][k] bf16
+  int m, n, k;
+  int mode;
+  uint16_t *y;             // BF16: [m][n]; SILU_GATE: [m][n/2]
+  float *resid;            // RESIDUAL: [m][n] f32, added to in place
+  uint16_t *q, *kk, *v;    // QKV_ROPE: [m][hq*d], [m][hkv*d], [m][hkv*d]
+  int hq, hkv, head_dim;
+  const int32_t *pos;      // QKV_ROPE: [m] positions
+  const float *rope;       // QKV_ROPE: [n_pos][d/2] (cos, sin) pairs
+  int n_pos;
+  void *ev_begin, *ev_end; // optional hipEvent_t around the kernel
+};
+
+int launch_rmsnorm(const NormLaunch &a, void *stream);
+int launch_linear(const LinearLaunch &a, void *stream);
+
 int launch_attention(const AttnLaunch &a, void *stream);
 int launch_score(const ScoreLaunch &a, void *stream);
 int launch_score_batch(const ScoreBatchLaunch &a, void *stream);

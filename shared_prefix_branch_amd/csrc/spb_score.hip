@@ -30,6 +30,7 @@
 #include "spb_meta.h"
 #include "spb_launch.h"
 #include "spb_dev.h"
+#include "spb_gemm.h"
 #include "../../include/spb.h"
 
 #include <hip/hip_runtime.h>
@@ -38,13 +39,15 @@
 namespace spb {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using gemm::bf16x8_t;
+using gemm::f32x16;
+using gemm::u32x4;
+using gemm::kKT;
+using gemm::kThreads;
+using gemm::swz;
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kKT = 64;        // hidden elements per K stage (128-byte LDS rows: one cache line)
-constexpr int kThreads = 256;  // 4 waves, each a 64-row strip of the 256-row vocabulary slice
+static_assert(gemm::kWRows == kVocabTile, "one lm-head slice per GEMM tile");
 
 __device__ inline uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
@@ -52,11 +55,6 @@ __device__ inline uint32_t f2bf(float f) {
   return u >> 16;
 }
 
-// LDS position, in 16-byte units, of chunk c (0..7) of row r of a tile with
-// 128-byte rows.  A fragment read has 16 lanes in flight on 16 consecutive
-// rows at one chunk; the XOR by (r/2)%8 puts them on 16 distinct 16-byte bank
-// groups of the 64 banks.
-__device__ inline int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 struct GatherParams {
   const void *hidden;
@@ -144,71 +142,18 @@ struct HeadParams {
   float *part, *tz;
 };
 
-// Work group: 256 vocabulary rows x TM = 32*MB scored rows; wave w owns
-// vocabulary rows w*64 .. +64 (two 32-row blocks) against all TM rows, so
-// only the h tile is shared between waves.
 template <int MB>
-struct HeadTile {
-  static constexpr int TM = 32 * MB;                // scored rows per work group
-  static constexpr int WBYTES = kVocabTile * 128;   // W stage: 256 rows x 64 bf16
-  static constexpr int HBYTES = TM * 128;           // h stage: TM rows x 64 bf16
-  static constexpr int RW = 3;                      // W ring: two stages in flight
-  static constexpr int RH = 2;                      // h ring: one stage in flight (L2-resident)
-  static constexpr int LDS = RW * WBYTES + RH * HBYTES;  // <= 160 KB
-  static constexpr int NW = 8;                      // W copies per wave per stage (its own 64 rows)
-  static constexpr int NH = MB;                     // h copies per wave per stage
-  static_assert(LDS <= 160 * 1024, "LDS ring too large");
-  static_assert(4 * TM * 2 * 4 <= LDS, "epilogue buffer must fit in the ring");
-};
+using HeadTile = gemm::Tile<MB>;
 
-// Fragments of one 16-element K step: A = the wave's 2 vocabulary blocks,
-// B = the MB scored-row blocks.
-template <int MB>
-struct Frags {
-  bf16x8_t a[2];
-  bf16x8_t b[MB];
-};
-
-// K step ks (0..3) of a 64-element stage: lane (qi, half) takes elements
-// 16 ks + 8 half .. +8 of its row, i.e. chunk 2 ks + half.
-template <int MB>
-__device__ __attribute__((always_inline)) inline void head_frags(Frags<MB> &f, const u32x4 *Wb, const u32x4 *Hb,
-                                                                 int ks, int wave, int qi, int half) {
-#pragma unroll
-  for (int vb = 0; vb < 2; ++vb) {
-    u32x4 u = Wb[swz(wave * 64 + vb * 32 + qi, ks * 2 + half)];
-    f.a[vb] = *(bf16x8_t *)&u;
-  }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    u32x4 u = Hb[swz(mb * 32 + qi, ks * 2 + half)];
-    f.b[mb] = *(bf16x8_t *)&u;
-  }
-}
-
-template <int MB>
-__device__ __attribute__((always_inline)) inline void head_mfma(f32x16 (&acc)[2][MB], const Frags<MB> &f) {
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-      acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0);
-}
-
-// Pipeline over stages of 64 hidden elements (four 16-element K steps), so
-// every row of a stage is one whole 128-byte line and each global request
-// carries a full line.  Stage j's W tile is copied straight into LDS slot
-// j % 3 two stages ahead of use (each wave copies the 64 rows it alone
-// reads); its h tile (small and shared by every work group, so L2-resident)
-// into slot j % 2 one stage ahead.  Within a stage the fragments of K step
-// t+1 are read while step t is multiplied.
+// Work group: 256 vocabulary rows x TM = 32*MB scored rows, on the shared K
+// loop (spb_gemm.h); the h tile is small and shared by every work group, so
+// L2-resident.
 template <int MB>
 __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   using T = HeadTile<MB>;
   constexpr int TM = T::TM;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS];
-  char *const wring = lds;
-  char *const hring = lds + T::RW * T::WBYTES;
+  static_assert(4 * TM * 2 * 4 <= T::LDS, "epilogue buffer must fit in the ring");
 
   // XCD-aware order: work groups are dealt round-robin to the 8 XCDs, so the
   // M chunks of one vocabulary slice get consecutive slots of one XCD and
@@ -225,90 +170,12 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   const int v0 = slice * kVocabTile;
   const int m0 = mchunk * TM;
 
-  // DMA layout: one instruction moves 8 rows x 128 bytes; lane t fills LDS
-  // position t%8 of row r = r8 + t/8 (r8 a multiple of 8), which swz() maps
-  // to chunk (t%8) ^ ((r/2)%8) of the row.
-  const int dr = lane >> 3;
-  uint32_t woff[T::NW], hoff[T::NH];
-#pragma unroll
-  for (int i = 0; i < T::NW; ++i) {
-    const int r = wave * 64 + i * 8 + dr;  // tile row
-    const int v = v0 + r;
-    const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
-    woff[i] = ((uint32_t)(v < p.V ? v : p.V - 1) * (uint32_t)p.H + c * 8) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < T::NH; ++i) {
-    const int r = (wave * T::NH + i) * 8 + dr;
-    const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
-    hoff[i] = ((uint32_t)(m0 + r) * (uint32_t)p.Hrow + c * 8) * 2;
-  }
-  const uint32_t lds0 = lds_addr(&lds[0]);
-  auto issue_w = [&](int stage, int sl) {
-    int ws = stage;  // stage within the sweep of W (stage < 3 SW)
-    if (ws >= p.SW) ws -= p.SW;
-    if (ws >= p.SW) ws -= p.SW;
-    const uint32_t kb = (uint32_t)ws * kKT * 2;
-    const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
-#pragma unroll
-    for (int i = 0; i < T::NW; ++i)
-      dma16(p.W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 8) * 128));
-  };
-  auto issue_h = [&](int stage, int sl) {
-    const uint32_t kb = (uint32_t)stage * kKT * 2;
-    const uint32_t s0 = lds0 + T::RW * T::WBYTES + (uint32_t)sl * T::HBYTES;
-#pragma unroll
-    for (int i = 0; i < T::NH; ++i)
-      dma16(p.hg, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
-  };
-
+  uint32_t woff[8], hoff[MB];
+  gemm::tile_offsets<MB>(
+      woff, hoff, [&](int r) { return v0 + r < p.V ? v0 + r : p.V - 1; }, [&](int r) { return m0 + r; }, p.H,
+      p.Hrow, wave, lane);
   f32x16 acc[2][MB];
-#pragma unroll
-  for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x16{0.f};
-
-  const int S = p.Hrow / kKT;
-  const int last = S - 1;
-  // Copies past the last stage reload it into a slot nothing reads again, so
-  // the count of copies in flight is the same on every trip.
-  // Trip s issues h(s+1) then W(s+2); at its end only W(s+2) may be in flight.
-  issue_h(0, 0);
-  issue_w(0, 0);
-  issue_w(min(1, last), 1);
-  wait_vmcnt<T::NW>();  // h(0), W(0) landed (this wave's copies)
-  lds_barrier();
-
-  int sw = 0, sh = 0;  // ring slots of stage s
-  for (int s = 0; s < S; ++s) {
-    const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
-    const u32x4 *Hb = (const u32x4 *)(hring + sh * T::HBYTES);
-    Frags<MB> f0, f1;
-    head_frags<MB>(f0, Wb, Hb, 0, wave, qi, half);
-    const int sw2 = sw == 0 ? 2 : sw - 1;  // slot of stage s + 2 (= s - 1 mod 3)
-    issue_h(min(s + 1, last), sh ^ 1);
-    issue_w(min(s + 2, last), sw2);
-    head_frags<MB>(f1, Wb, Hb, 1, wave, qi, half);
-    __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MB>(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    head_frags<MB>(f0, Wb, Hb, 2, wave, qi, half);
-    __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MB>(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    head_frags<MB>(f1, Wb, Hb, 3, wave, qi, half);
-    __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MB>(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    head_mfma<MB>(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<T::NW>();  // h(s+1) and W(s+1) landed
-    lds_barrier();
-    sw = sw == 2 ? 0 : sw + 1;
-    sh ^= 1;
-  }
-  wait_vmcnt<0>();  // no copy may land after the ring is reused or released
-  lds_barrier();
+  gemm::k_loop<MB>(acc, lds, p.W, p.hg, woff, hoff, p.Hrow / kKT, p.SW, wave, qi, half);
   float (*red)[TM][2] = (float (*)[TM][2])lds;  // [4][TM][2], reusing the ring
   if (p.round_bf16) {
 #pragma unroll

@@ -235,7 +235,7 @@ class Job:
             if mk is not None:
                 mk[0].record(stream)
             if attention:
-                self._attn[k](plan, stream)
+                self._forward(k, plan, stream)
             if mk is not None:
                 mk[1].record(stream)
             if scoring and not self.batch_head:
@@ -256,6 +256,11 @@ class Job:
         ev = t.cuda.Event()
         ev.record(stream)
         self._slot, self._slot_plan[r], self._slot_done[r] = r, plan, ev
+
+    def _forward(self, k: int, plan: Plan, stream):
+        """Pass k's rows up to the hidden states the head reads: here branch
+        attention alone (the hidden states are given)."""
+        self._attn[k](plan, stream)
 
     def finalize(self, slot: Optional[int] = None, copy: bool = False) -> dict:
         """Waits for a run's scores (by default the last run's) and joins the

@@ -1,0 +1,79 @@
+"""CPU tests of the decoder-stack host side: each pass row's position against
+the oracle's root-path positions, the rotary table against its closed form,
+and argument checks of spb_rmsnorm / spb_linear that fail before any HIP call."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import shared_prefix_branch_amd as spb
+import synth
+from oracle import forward as OF
+from oracle import tree as OT
+
+
+@pytest.mark.parametrize("kind,budget", [("random", 16384), ("random", 60), ("shared", 16384), ("shared", 40),
+                                         ("grid", 400)])
+def test_positions_equal_root_path_positions(kind, budget):
+    if kind == "random":
+        prob = synth.make_problem("random", 8, vocab=64, n_inputs=4, n_questions=5, max_content=30, max_len=6,
+                                  max_options=4, max_option_tokens=4)
+    elif kind == "shared":
+        prob = synth.make_problem("random_shared", 15, vocab=16, n_inputs=3, n_questions=6, max_content=10,
+                                  max_lead=5, tail_vocab=3, max_options=3, max_option_tokens=3)
+    else:
+        prob = synth.make_problem("grid", 6, vocab=4096, n_inputs=2, n_templates=2, min_content=30, max_content=60)
+    plan = spb.pack_pass(prob, token_budget=budget)
+    lay = OT.build_layout(prob, floors=True)
+    want = OF.positions(lay)
+    for k in range(plan.n_passes):
+        lr, _ = plan.rows(k)
+        assert plan.positions(k).tolist() == want[lr].tolist()
+
+
+def test_rope_table_closed_form():
+    t = spb.rope_table(50, 8, 10000.0)
+    assert t.shape == (50, 4, 2)
+    p = np.arange(50)[:, None]
+    ang = p * 10000.0 ** (-np.arange(4) * 2.0 / 8)[None, :]
+    assert np.array_equal(t[..., 0], np.cos(ang).astype(np.float32))
+    assert np.array_equal(t[..., 1], np.sin(ang).astype(np.float32))
+    assert t[3, 0, 0] == np.float32(math.cos(3.0)) and t[1, 1, 1] == np.float32(math.sin(0.1))
+    with pytest.raises(spb.SpbError):
+        spb.rope_table(10, 7)
+
+
+def test_layer_entry_points_validate_before_any_hip_call():
+    L = spb.lib()
+    N = spb._NormArgs()
+    N.x = N.gain = N.out = 256
+    N.rows, N.dim, N.eps = 10, 6, 1e-6
+    assert L.spb_rmsnorm(ctypes.byref(N), None) == -1          # dim % 4
+    N.dim = 8
+    N.x = 258
+    assert L.spb_rmsnorm(ctypes.byref(N), None) == -1          # alignment
+    N.x, N.rows = 256, 0
+    assert L.spb_rmsnorm(ctypes.byref(N), None) == 0           # nothing to do
+    A = spb._LinearArgs()
+    A.x = A.w = A.y = A.resid = 256
+    A.m, A.n, A.k, A.mode = 100, 256, 96, spb.LINEAR_BF16
+    assert L.spb_linear(ctypes.byref(A), None) == -1           # k % 64
+    A.k, A.n = 128, 100
+    assert L.spb_linear(ctypes.byref(A), None) == -1           # n % 8
+    A.n, A.mode = 96, spb.LINEAR_SILU_GATE
+    assert L.spb_linear(ctypes.byref(A), None) == -1           # gate blocks of 64 rows
+    A.mode = 7
+    assert L.spb_linear(ctypes.byref(A), None) == -1           # mode
+    A.mode, A.n = spb.LINEAR_QKV_ROPE, 512
+    A.hq, A.hkv, A.head_dim = 2, 1, 96
+    assert L.spb_linear(ctypes.byref(A), None) == -3           # head_dim
+    A.head_dim = 128
+    assert L.spb_linear(ctypes.byref(A), None) == -1           # n != (hq + 2 hkv) d
+    A.hq, A.hkv = 2, 1
+    A.n = 512
+    assert L.spb_linear(ctypes.byref(A), None) == -1           # q/k/v/pos/table missing
+    A.mode, A.m, A.k, A.n = spb.LINEAR_BF16, 1 << 20, 4096, 256
+    assert L.spb_linear(ctypes.byref(A), None) == -2           # x over 4 GiB
+    A.m = 0
+    assert L.spb_linear(ctypes.byref(A), None) == 0            # nothing to do
