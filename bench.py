@@ -1,6 +1,6 @@
 """Benchmark of the packed scoring pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload news] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload news] [--layers L] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 pack the batch into token-budget passes (host C++), and per pass upload the
@@ -17,6 +17,11 @@ inside the timed steps, the roofline of the dominant kernel (the lm-head GEMM)
 and the oracle timed on the host cores as `cpu_baseline`.  The roofline's
 `traffic` is the kernel's HBM bytes per launch from the committed counter
 summary in profiles/ (null when the kernel source has changed since).
+
+With --layers L the hidden states are not given: each pass first runs L
+decoder layers (synthetic bf16 weights, the news attention shape with a 4x
+gated MLP) from seeded input embeddings, and the roofline is that of the
+linear-layer GEMM kernel, which then dominates the step.
 
     python bench.py --copy-calibration
 
@@ -56,6 +61,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="news")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="decoder layers in front of the head (synthetic weights, news model dims); "
+                         "0: attention alone with given hidden states")
     ap.add_argument("--no-template-sharing", action="store_true",
                     help="drop the template token ids, so questions share no template prefix")
     ap.add_argument("--cpu-sample-inputs", type=int, default=0,
@@ -151,9 +159,23 @@ def main():
 
     batch_head = args.head_batch and plan.n_passes <= 64
     head_kind = {"f32out": 0, "bf16": 1, "fp32": 2}[args.lm_head]
-    job = Job(plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv_dt, out_dt, hid_dt, device=dev, scales=scales,
-              batch_head=batch_head, lm_head_kind=head_kind)
-    job.load(provider)
+    md = None
+    if args.layers > 0:
+        import dataclasses
+        from shared_prefix_branch_amd.stack import ForwardJob
+        if d.dtype != "bf16":
+            raise SystemExit("--layers runs bf16 workloads only")
+        md = dataclasses.replace(synth.MODEL_CONFIGS["news"], layers=args.layers, hidden=d.hidden, hq=d.hq,
+                                 hkv=d.hkv, head_dim=d.head_dim)
+        layers_w, g_final = synth.model_weights(md, wl.cfg_seed, device=dev)
+        job = ForwardJob(plan, md, layers_w, g_final, d.vocab, device=dev, batch_head=batch_head,
+                         lm_head_kind=head_kind)
+        job.load(lambda n: synth.embed_block(wl, md, ids[n], device=dev))
+        del layers_w
+    else:
+        job = Job(plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv_dt, out_dt, hid_dt, device=dev,
+                  scales=scales, batch_head=batch_head, lm_head_kind=head_kind)
+        job.load(provider)
     W = synth.lm_head(wl, device=dev)
     torch.cuda.synchronize()
 
@@ -186,6 +208,16 @@ def main():
         for mk in ms:
             for ev in mk:
                 ev.record(stream)
+    # with the stack: per step, pass and linear launch (4 per layer), a pair
+    # of events the library records around the linear kernel
+    n_lin = 4 * args.layers
+    lin_marks = [[[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n_lin)] for _ in range(n_pass)] for _ in range(args.steps)]
+    for ms in lin_marks:
+        for mk in ms:
+            for pair in mk:
+                for ev in pair:
+                    ev.record(stream)
     torch.cuda.synchronize()
 
     state = {"next": job.stage_host(spb.pack_pass(prob, token_budget=budget)), "prev": None, "res": None}
@@ -195,12 +227,16 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if n_lin:
+            job.lin_marks = lin_marks[i]
         step(state, marks[i])
     drain(state)   # the last step's scores are joined inside the timed region
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     res = state["res"]
     ms_step = (t1 - t0) * 1e3 / args.steps
+    if n_lin:
+        job.lin_marks = None
 
     att_ms = np.zeros(n_pass)
     n_head = 1 if batch_head else n_pass   # lm-head launches per step
@@ -222,6 +258,31 @@ def main():
     head_tflops = head_flops.sum() / (head_ms.sum() * 1e-3) / 1e12
     head_gbs = head_bytes.sum() / (head_ms.sum() * 1e-3) / 1e9
     head_bound = "mfma" if M.mean() > HEAD_RIDGE_ROWS else "hbm"
+    stack = None
+    if n_lin:
+        # linear launches: (n, k) per kind; m = the pass's tokens
+        kinds = [("qkv", (md.hq + 2 * md.hkv) * md.head_dim, md.hidden), ("o", md.hidden, md.hq * md.head_dim),
+                 ("gate_up", 2 * md.ffn, md.hidden), ("down", md.hidden, md.ffn)]
+        lin_ms = np.zeros((n_pass, n_lin))
+        for ms in lin_marks:
+            for k, mk in enumerate(ms):
+                for j, (b, e) in enumerate(mk):
+                    lin_ms[k, j] += b.elapsed_time(e) / args.steps
+        toks = np.array([plan.info(k)["n_tokens"] for k in range(n_pass)], dtype=np.float64)
+        lin_flops = np.array([[2.0 * toks[k] * kinds[j % 4][1] * kinds[j % 4][2] for j in range(n_lin)]
+                              for k in range(n_pass)])
+        lin_tf = lin_flops.sum() / (lin_ms.sum() * 1e-3) / 1e12
+        per_kind = {}
+        for j4, (name, n_, k_) in enumerate(kinds):
+            sel = [j for j in range(n_lin) if j % 4 == j4]
+            ms_k = float(lin_ms[:, sel].sum())
+            per_kind[name] = {"n": n_, "k": k_, "ms": round(ms_k, 4),
+                              "tflops": round(float(lin_flops[:, sel].sum()) / (ms_k * 1e-3) / 1e12, 2)}
+        stack = {"layers": md.layers, "hidden": md.hidden, "ffn": md.ffn,
+                 "forward_ms": round(float(att_ms.sum()), 4),
+                 "linear": {"ms": round(float(lin_ms.sum()), 4), "tflops": round(lin_tf, 2),
+                            "frac": round(lin_tf / PEAK_BF16_TFLOPS, 4), "launches_per_step": int(n_pass * n_lin),
+                            "per_kind": per_kind}}
     if args.workload != "news":
         traffic, traffic_src = None, "counters taken on news only"
     elif head_kind != 0:
@@ -243,6 +304,14 @@ def main():
                           "flops_per_scored_row": 2 * d.hidden * d.vocab,
                           "algorithmic_bytes": [int(x) for x in head_bytes]}
 
+    if stack is not None:
+        # the linear layers dominate the step: their GEMM kernel is the roofline
+        roof = {"bound": "mfma", "achieved": round(lin_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(lin_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "traffic_source": "counters not taken for the linear kernel",
+                "kernel": "linear_kernel (decoder-stack GEMMs with fused epilogues, spb_linear)",
+                "per_launch": {"ms_mean": round(float(lin_ms.mean()), 4),
+                               "flops_mean": float(lin_flops.mean())}}
     line = {
         "metric": "packed tokens/s + scored questions/s per MI355X; attention MFMA util",
         "value": round(tokens / (ms_step * 1e-3), 1),
@@ -256,7 +325,7 @@ def main():
                    "packed_tokens": tokens, "questions": questions, "token_budget": budget,
                    "hq": d.hq, "hkv": d.hkv, "head_dim": d.head_dim, "hidden": d.hidden, "vocab": d.vocab,
                    "lm_head": args.lm_head, "lm_head_launches_per_step": n_head,
-                   "template_sharing": prob.tmpl_tok is not None},
+                   "template_sharing": prob.tmpl_tok is not None, "decoder_layers": args.layers},
         "questions_per_s": round(questions / (ms_step * 1e-3), 1),
         "attention": {"ms": round(float(att_ms.sum()), 4), "tflops": round(att_tflops, 2),
                       "mfma_util": round(att_tflops / PEAK_BF16_TFLOPS, 4),
@@ -265,10 +334,19 @@ def main():
                  "scored_rows": int(M.sum())},
         "roofline": roof,
     }
+    if stack is not None:
+        line["stack"] = stack
+        # the pass's events bracket the whole stack, so attention has no time of its own here
+        line["attention"] = {"ms": None, "tflops": None, "mfma_util": None,
+                             "unmasked_pairs": int(info["unmasked_pairs"]),
+                             "note": "inside the decoder stack: stack.forward_ms covers every layer of each pass"}
 
     if not args.no_cpu_baseline:
-        n_cpu = args.cpu_sample_inputs if args.cpu_sample_inputs > 0 else prob.n_inputs
-        line["cpu_baseline"] = cpu_baseline(wl, W, scales, min(n_cpu, prob.n_inputs))
+        if md is not None:
+            line["cpu_baseline"] = cpu_baseline_stack(wl, md, W)
+        else:
+            n_cpu = args.cpu_sample_inputs if args.cpu_sample_inputs > 0 else prob.n_inputs
+            line["cpu_baseline"] = cpu_baseline(wl, W, scales, min(n_cpu, prob.n_inputs))
     print(json.dumps(line), flush=True)
 
 
@@ -364,6 +442,38 @@ def cpu_baseline(wl, W, scales, n_inputs):
             "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{n_inputs} contents x {len(wl.problem.q_len)} questions + {len(ids) - n_inputs} floors "
                       f"= {lay.n_rows} tokens, {qn} questions; float64 NumPy, BLAS threads {cores}"}
+
+
+def cpu_baseline_stack(wl, md, W):
+    """The float64 oracle's per-sequence forward through the decoder stack and
+    the head, on a bounded sample: one content and its first question."""
+    import torch
+    import synth
+    from oracle import forward as OF, numerics as ON, scoring as OS, tree as OT
+
+    cores = torch.get_num_threads()
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"] or [cores])
+    except Exception:
+        pass
+    sub = wl.problem.subset([0])
+    lay = OT.build_layout(sub, floors=False)
+    layers_w, g_final = synth.model_weights(md, wl.cfg_seed)
+    m = OF.Model.from_synth(md, layers_w, g_final)
+    li = lay.inputs[0]
+    x0 = ON.to_f64(synth.embed_block(wl, md, ("input", 0)))
+    t0 = time.perf_counter()
+    out = OF.forward_input(m, lay, li, x0, branches=[0], content=True)
+    b = li.branches[0]
+    sc = OS.score_branches(lay, lambda rows: out[np.asarray(rows) - li.first_row], W.cpu(), [b])
+    dt = time.perf_counter() - t0
+    assert len(sc) == 1
+    toks = li.C + len(b.template_rows) + len(b.trie.prefixes)
+    return {"value": round(toks / dt, 3), "unit": "packed tokens/s", "questions_per_s": round(1 / dt, 5),
+            "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"one content ({li.C} tokens) and its first question through {md.layers} decoder layers "
+                      f"and the head: {toks} tokens, 1 question; float64 NumPy, BLAS threads {cores}"}
 
 
 if __name__ == "__main__":

@@ -84,18 +84,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormLaunch a) {
 // ------------------------------------------------------------------ linear
 
 constexpr int kMB = kLinearMB;
-constexpr int kGroupW = 4;  // W tiles per XCD-local group (see the block mapping)
+constexpr int kGroupM = 8;  // token chunks per group of the tile order (see the block mapping)
 
 struct LinParams {
   LinearLaunch a;
-  int n_wtiles, n_mchunks, n_groups;
+  int n_wtiles, n_mchunks, per_xcd;
 };
 
 // One work group: W rows wt*256 .. +256 against tokens mchunk*224 .. +224.
-// Work groups are dealt round-robin to the 8 XCDs; W tile wt lives on XCD
-// wt % 8, and each XCD walks its tiles in groups of kGroupW, every group
-// across all token chunks, so the 32 work groups an XCD runs at once share 4
-// W tiles and 8 token chunks through its L2.
+// Tiles are ordered in groups of kGroupM token chunks x every W tile (token
+// chunk fastest), and that order is cut into 8 contiguous ranges, one per
+// XCD (work groups are dealt round-robin to the XCDs, block b to XCD b % 8).
+// So every XCD gets the same number of tiles, and the 32 work groups an XCD
+// runs at once cover 8 token chunks x 4 W tiles, sharing both through its L2.
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinParams P) {
   using T = gemm::Tile<kMB>;
@@ -104,12 +105,13 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinParams P) {
   const LinearLaunch &p = P.a;
 
   const int b = blockIdx.x;
-  const int xcd = b & 7, slot = b >> 3;
-  const int per_group = kGroupW * P.n_mchunks;
-  const int g = slot / per_group, rem = slot % per_group;
-  const int wt = (g * kGroupW + rem % kGroupW) * 8 + xcd;
-  const int mchunk = rem / kGroupW;
-  if (wt >= P.n_wtiles) return;
+  const int pid = (b & 7) * P.per_xcd + (b >> 3);
+  if (pid >= P.n_wtiles * P.n_mchunks) return;
+  const int span = kGroupM * P.n_wtiles;
+  const int first_m = (pid / span) * kGroupM;
+  const int gm = P.n_mchunks - first_m < kGroupM ? P.n_mchunks - first_m : kGroupM;
+  const int mchunk = first_m + (pid % span) % gm;
+  const int wt = (pid % span) / gm;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -214,9 +216,10 @@ int launch_linear_mode(const LinearLaunch &a, hipStream_t s) {
   P.a = a;
   P.n_wtiles = (a.n + kWRows - 1) / kWRows;
   P.n_mchunks = (a.m + 32 * kMB - 1) / (32 * kMB);
-  const int per_xcd = (P.n_wtiles + 7) / 8;
-  P.n_groups = (per_xcd + kGroupW - 1) / kGroupW;
-  const long long blocks = 8ll * P.n_groups * kGroupW * P.n_mchunks;
+  const long long tiles = (long long)P.n_wtiles * P.n_mchunks;
+  if (tiles > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  P.per_xcd = (int)((tiles + 7) / 8);
+  const long long blocks = 8ll * P.per_xcd;
   if (blocks > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
   if (a.ev_begin) {
     hipError_t e = hipEventRecord((hipEvent_t)a.ev_begin, s);
