@@ -19,9 +19,10 @@ Modules:
   scoring   -- logits, log-softmax, option log-probs, p, residual, floors, lift
   forward   -- the decoder stack around branch attention (rmsnorm, RoPE,
                projections, gated MLP) on synthetic weights
+  decode    -- searched decoding of extraction slots (beam search)
 
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test against
 something other than itself (the worked example on the article, closed forms,
 library special cases, brute force on tiny inputs).  None is unpinned.
 """
-from . import numerics, tree, attention, scoring, forward  # noqa: F401
+from . import numerics, tree, attention, scoring, forward, decode  # noqa: F401
