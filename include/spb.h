@@ -332,6 +332,7 @@ spb_status spb_rmsnorm(const spb_rmsnorm_args *args, void *stream);
  *   SPB_LINEAR_SILU_GATE: y[m][n/2] = bf16(silu(gate) * up), with W's rows
  *     in blocks of 64: rows 64j .. 64j+31 the gate rows 32j .. 32j+31 and
  *     rows 64j+32 .. 64j+63 the up rows 32j .. 32j+31 (n % 64 == 0);
+ *   SPB_LINEAR_F32:       yf[m][n] = acc (f32; the lm head's logits of decoded rows);
  *   SPB_LINEAR_QKV_ROPE:  W = [Wq; Wk; Wv] (n = (hq + 2 hkv) head_dim); the
  *     three column ranges go to q [m][hq*d], k [m][hkv*d], v [m][hkv*d], q
  *     and k rotated by pos[r] with rope_table (spb_rope_table; positions
@@ -339,7 +340,8 @@ spb_status spb_rmsnorm(const spb_rmsnorm_args *args, void *stream);
  * k % 64 == 0, n % 8 == 0, m * k * 2 and n * k * 2 below 4 GiB; every
  * tensor is device memory, 16-byte aligned, caller-owned.  gemm_event_begin /
  * gemm_event_end: optional hipEvent_t handles recorded around the kernel. */
-enum { SPB_LINEAR_BF16 = 0, SPB_LINEAR_RESIDUAL = 1, SPB_LINEAR_SILU_GATE = 2, SPB_LINEAR_QKV_ROPE = 3 };
+enum { SPB_LINEAR_BF16 = 0, SPB_LINEAR_RESIDUAL = 1, SPB_LINEAR_SILU_GATE = 2, SPB_LINEAR_QKV_ROPE = 3,
+       SPB_LINEAR_F32 = 4 };
 typedef struct {
   const void *x;
   const void *w;
@@ -348,6 +350,7 @@ typedef struct {
   int32_t mode;
   void *y;
   float *resid;
+  float *yf;
   void *q, *k_out, *v;
   int32_t hq, hkv, head_dim;
   const int32_t *pos;
@@ -356,6 +359,116 @@ typedef struct {
   void *gemm_event_begin, *gemm_event_end;
 } spb_linear_args;
 spb_status spb_linear(const spb_linear_args *args, void *stream);
+
+/* --------------------------------------------------------- extraction slots
+ * A slot ({*} text, {n} a number, {$} an amount) is decoded from the same
+ * read, with its answers' probabilities [PyPI "spinf-serve 0.1.1", "What it
+ * does": Extraction and generation]; the slots of many inputs are decoded
+ * together [PyPI "Speed and scale"].  The search is a beam search of width B:
+ * step 0 takes the k best allowed tokens after the slot question's template
+ * (its scored last row), every later step feeds each live beam's last token
+ * through the decoder stack (spb_gather_rows, the layer calls with
+ * spb_decode_attention in place of branch attention, the lm head as
+ * spb_linear SPB_LINEAR_F32) and spb_topk_lse, and spb_beam_step keeps the B
+ * best candidates: score (sum of the tokens' vocab-wide log-probabilities)
+ * descending, then the earlier beam, then the smaller token id; finished
+ * beams (the stop token chosen) stay candidates with their scores.  A step's
+ * rows are slot-major: row r = slot * B + beam; the decode K/V cache of a
+ * layer holds the rows of depth j (1-based) at rows (j - 1) * R + r. */
+
+/* The slot question's template row and its prefix in the pass: the key rows
+ * that row attends to (itself included), as runs (first pass row, count) in
+ * attention order.  logical_branch: as in spb_plan_branches. */
+enum { SPB_MAX_SLOT_RANGES = 16, SPB_MAX_TOPK = 16, SPB_MAX_BEAMS = 16 };
+typedef struct {
+  int32_t pass;
+  int32_t row;
+  int32_t position;
+  int32_t n_ranges;
+  int32_t ranges[SPB_MAX_SLOT_RANGES][2];
+} spb_slot_info;
+spb_status spb_plan_slot(const spb_plan *plan, int32_t logical_branch, spb_slot_info *out);
+
+/* dst[r] = src[idx[r]] for r < rows (bf16 rows of dim; dst as f32 or bf16,
+ * exactly one non-NULL), idx clamped into [0, n_src); with pos non-NULL also
+ * pos[r] = pos_base[r / per] + pos_add (the positions of a decode step's rows). */
+typedef struct {
+  const void *src;
+  int32_t n_src;
+  const int32_t *idx;
+  int64_t rows;
+  int32_t dim;
+  float *dst_f32;
+  void *dst_bf16;
+  int32_t *pos;
+  const int32_t *pos_base;
+  int32_t per, pos_add;
+} spb_gather_args;
+spb_status spb_gather_rows(const spb_gather_args *args, void *stream);
+
+/* Per row of f32 logits [rows][vocab]: lse = log sum exp over the whole
+ * vocabulary (a fixed-order reduction), and the k (<= 16) best tokens the
+ * row's mask allows (the row's stop token always allowed) in the order
+ * logit descending, then smaller id, as ids [rows][k] and lp = logit - lse;
+ * -1 / -inf when fewer are allowed.  masks: [n_masks][ceil(vocab / 32)]
+ * bit sets, mask_of_row[r] in [-1, n_masks) (-1: every token); both may be
+ * NULL (every token); stop_of_row may be NULL. */
+typedef struct {
+  const float *logits;
+  int64_t rows;
+  int32_t vocab, k;
+  const uint32_t *masks;
+  int32_t n_masks;
+  const int32_t *mask_of_row;
+  const int32_t *stop_of_row;
+  int32_t *ids;
+  float *lp;
+  float *lse;
+} spb_topk_args;
+spb_status spb_topk_lse(const spb_topk_args *args, void *stream);
+
+/* Attention of a decode step's rows (q [rows][hq][d], after RoPE): row r of
+ * slot s = r / beams attends to its slot's prefix ranges (spb_plan_slot) in
+ * the pass's K/V of this layer (k_pass, v_pass [n_pass_rows][hkv][d]), then
+ * to its n_path ancestors path[r][0 .. n_path) in the decode cache (k_dec,
+ * v_dec [t_cap * rows][hkv][d]), then to itself at decode row
+ * n_path * rows + r.  o [rows][hq][d] bf16.  Scores, softmax and P.V in f32.
+ * ranges [n_slots][16][2] and n_ranges [n_slots] are device copies of
+ * spb_plan_slot's; row indices are clamped into the caches. */
+typedef struct {
+  const void *q;
+  const void *k_pass, *v_pass;
+  int32_t n_pass_rows;
+  const void *k_dec, *v_dec;
+  void *o;
+  int32_t rows, beams, hq, hkv, head_dim;
+  const int32_t *ranges, *n_ranges;
+  const int32_t *path;
+  int32_t t_cap, n_path;
+  float softmax_scale;
+} spb_decode_attn_args;
+spb_status spb_decode_attention(const spb_decode_attn_args *args, void *stream);
+
+/* One beam-search step for n_slots slots of `beams` beams (<= 16).  step 0:
+ * ids / lp [n_slots][k] are the candidates after each slot's template row;
+ * step >= 1: [n_slots * beams][k] after each beam's fed row.  State, device
+ * arrays per beam (slot-major): tok [t_cap] (decoded tokens, -1 past len),
+ * len, fin (1: finished), score (sum of lp), path [t_cap] (decode-cache rows
+ * of the fed tokens), and per slot nb (live beam count); *_in is read (not at
+ * step 0), *_out written.  feed[r]: the token row r feeds at the next step
+ * (the stop token for a finished beam). */
+typedef struct {
+  int32_t n_slots, beams, k, t_cap, step;
+  const int32_t *stop;
+  const int32_t *ids;
+  const float *lp;
+  const int32_t *tok_in, *len_in, *fin_in, *path_in, *nb_in;
+  const float *score_in;
+  int32_t *tok_out, *len_out, *fin_out, *path_out, *nb_out;
+  float *score_out;
+  int32_t *feed;
+} spb_beam_args;
+spb_status spb_beam_step(const spb_beam_args *args, void *stream);
 
 #ifdef __cplusplus
 }

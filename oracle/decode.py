@@ -44,14 +44,19 @@ class Beam:
 
 
 def beam_search(next_lp: Callable[[tuple], np.ndarray], B: int, T: int, stop: int,
-                allowed: Optional[Sequence[int]] = None) -> List[Beam]:
+                allowed: Optional[Sequence[int]] = None, margins: Optional[list] = None) -> List[Beam]:
     """next_lp(tokens) -> float64 [V] log-probabilities of the next token after
-    the slot's prefix followed by ``tokens``."""
+    the slot's prefix followed by ``tokens``.  ``margins``, if given, receives
+    per step the score gap between the last kept and the first dropped
+    candidate (how close the step was to a different choice)."""
     first = next_lp(())
     V = first.shape[0]
     cand_ids = np.arange(V) if allowed is None else np.unique(np.r_[np.asarray(allowed, np.int64), stop])
     # step 0: the template's own next-token distribution
-    order = sorted(cand_ids.tolist(), key=lambda x: (-first[x], x))[:B]
+    ranked = sorted(cand_ids.tolist(), key=lambda x: (-first[x], x))
+    order = ranked[:B]
+    if margins is not None and len(ranked) > B:
+        margins.append(float(first[ranked[B - 1]] - first[ranked[B]]))
     beams = [Beam((x,), float(first[x]), x == stop) for x in order]
     for _ in range(1, T):
         if all(b.finished for b in beams):
@@ -65,6 +70,8 @@ def beam_search(next_lp: Callable[[tuple], np.ndarray], B: int, T: int, stop: in
             for x in cand_ids.tolist():
                 cands.append((b.lp + float(lp[x]), bi, x, None))
         cands.sort(key=lambda c: (-c[0], c[1], c[2]))
+        if margins is not None and len(cands) > B:
+            margins.append(cands[B - 1][0] - cands[B][0])
         nxt = []
         for score, bi, x, kept in cands[:B]:
             if kept is not None:

@@ -20,14 +20,16 @@ __all__ = [
     "score_options_batch",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
     "HEAD_F32OUT", "HEAD_BF16", "HEAD_FP32",
-    "LINEAR_BF16", "LINEAR_RESIDUAL", "LINEAR_SILU_GATE", "LINEAR_QKV_ROPE", "rope_table", "PreparedNorm",
+    "LINEAR_BF16", "LINEAR_RESIDUAL", "LINEAR_SILU_GATE", "LINEAR_QKV_ROPE", "LINEAR_F32", "rope_table",
+    "PreparedNorm", "gather_rows", "topk_lse", "decode_attention", "beam_step",
     "PreparedLinear", "rmsnorm", "linear",
     "EXPORTED_SYMBOLS",
 ]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 HEAD_F32OUT, HEAD_BF16, HEAD_FP32 = 0, 1, 2  # lm-head output kinds
-LINEAR_BF16, LINEAR_RESIDUAL, LINEAR_SILU_GATE, LINEAR_QKV_ROPE = 0, 1, 2, 3  # linear-layer epilogues
+LINEAR_BF16, LINEAR_RESIDUAL, LINEAR_SILU_GATE, LINEAR_QKV_ROPE, LINEAR_F32 = 0, 1, 2, 3, 4  # linear epilogues
+MAX_SLOT_RANGES, MAX_TOPK, MAX_BEAMS = 16, 16, 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libspb.so")
 
@@ -38,6 +40,7 @@ EXPORTED_SYMBOLS = [
     "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
     "spb_score_batch_workspace_bytes", "spb_score_options_batch",
     "spb_score_finalize", "spb_plan_positions", "spb_rope_table", "spb_rmsnorm", "spb_linear",
+    "spb_plan_slot", "spb_gather_rows", "spb_topk_lse", "spb_decode_attention", "spb_beam_step",
 ]
 
 
@@ -99,10 +102,48 @@ class _NormArgs(ctypes.Structure):
 class _LinearArgs(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("m", ctypes.c_int64), ("n", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("mode", ctypes.c_int32), ("y", ctypes.c_void_p), ("resid", ctypes.c_void_p),
+                ("yf", ctypes.c_void_p),
                 ("q", ctypes.c_void_p), ("k_out", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("pos", ctypes.c_void_p), ("rope_table", ctypes.c_void_p), ("n_pos", ctypes.c_int32),
                 ("gemm_event_begin", ctypes.c_void_p), ("gemm_event_end", ctypes.c_void_p)]
+
+
+class _SlotInfo(ctypes.Structure):
+    _fields_ = [("pass_", ctypes.c_int32), ("row", ctypes.c_int32), ("position", ctypes.c_int32),
+                ("n_ranges", ctypes.c_int32), ("ranges", (ctypes.c_int32 * 2) * 16)]
+
+
+class _GatherArgs(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("n_src", ctypes.c_int32), ("idx", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("dim", ctypes.c_int32), ("dst_f32", ctypes.c_void_p),
+                ("dst_bf16", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("pos_base", ctypes.c_void_p),
+                ("per", ctypes.c_int32), ("pos_add", ctypes.c_int32)]
+
+
+class _TopkArgs(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("rows", ctypes.c_int64), ("vocab", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("masks", ctypes.c_void_p), ("n_masks", ctypes.c_int32),
+                ("mask_of_row", ctypes.c_void_p), ("stop_of_row", ctypes.c_void_p), ("ids", ctypes.c_void_p),
+                ("lp", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+class _DecodeAttnArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_pass", ctypes.c_void_p), ("v_pass", ctypes.c_void_p),
+                ("n_pass_rows", ctypes.c_int32), ("k_dec", ctypes.c_void_p), ("v_dec", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("rows", ctypes.c_int32), ("beams", ctypes.c_int32), ("hq", ctypes.c_int32),
+                ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ranges", ctypes.c_void_p),
+                ("n_ranges", ctypes.c_void_p), ("path", ctypes.c_void_p), ("t_cap", ctypes.c_int32),
+                ("n_path", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class _BeamArgs(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("beams", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("t_cap", ctypes.c_int32), ("step", ctypes.c_int32), ("stop", ctypes.c_void_p),
+                ("ids", ctypes.c_void_p), ("lp", ctypes.c_void_p)] + \
+               [(n, ctypes.c_void_p) for n in ("tok_in", "len_in", "fin_in", "path_in", "nb_in", "score_in",
+                                               "tok_out", "len_out", "fin_out", "path_out", "nb_out",
+                                               "score_out", "feed")]
 
 
 _lib = None
@@ -147,6 +188,11 @@ def lib() -> ctypes.CDLL:
         L.spb_rope_table.argtypes = [_f32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
         L.spb_rmsnorm.argtypes = [ctypes.POINTER(_NormArgs), ctypes.c_void_p]
         L.spb_linear.argtypes = [ctypes.POINTER(_LinearArgs), ctypes.c_void_p]
+        L.spb_plan_slot.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(_SlotInfo)]
+        L.spb_gather_rows.argtypes = [ctypes.POINTER(_GatherArgs), ctypes.c_void_p]
+        L.spb_topk_lse.argtypes = [ctypes.POINTER(_TopkArgs), ctypes.c_void_p]
+        L.spb_decode_attention.argtypes = [ctypes.POINTER(_DecodeAttnArgs), ctypes.c_void_p]
+        L.spb_beam_step.argtypes = [ctypes.POINTER(_BeamArgs), ctypes.c_void_p]
         for name in EXPORTED_SYMBOLS:
             if name not in ("spb_last_error", "spb_fingerprint", "spb_pack_opts_default", "spb_plan_free"):
                 getattr(L, name).restype = ctypes.c_int32
@@ -212,6 +258,13 @@ class Plan:
         out = np.empty(self.info(pass_)["n_tokens"], np.int32)
         _check(lib().spb_plan_positions(self._h, pass_, _ptr(out, _i32p)))
         return out
+
+    def slot(self, logical_branch: int) -> dict:
+        """A slot question's template row and its prefix key runs in the pass."""
+        s = _SlotInfo()
+        _check(lib().spb_plan_slot(self._h, int(logical_branch), ctypes.byref(s)))
+        return {"pass": s.pass_, "row": s.row, "position": s.position,
+                "ranges": [(s.ranges[i][0], s.ranges[i][1]) for i in range(s.n_ranges)]}
 
     def branches(self, pass_: int):
         inf = self.info(pass_)
@@ -500,7 +553,7 @@ class PreparedLinear:
     [m, n]); LINEAR_QKV_ROPE: q, k_out, v, heads, pos (int32 [m] device),
     rope (float32 [n_pos, d/2, 2] device)."""
 
-    def __init__(self, x, w, mode: int, y=None, resid=None, q=None, k_out=None, v=None, hq: int = 0, hkv: int = 0,
+    def __init__(self, x, w, mode: int, y=None, resid=None, yf=None, q=None, k_out=None, v=None, hq: int = 0, hkv: int = 0,
                  head_dim: int = 0, pos=None, rope=None):
         import torch
         A = _LinearArgs()
@@ -519,6 +572,9 @@ class PreparedLinear:
         if resid is not None:
             A.resid = _dev(resid, "resid", torch.float32)
             keep.append(resid)
+        if yf is not None:
+            A.yf = _dev(yf, "yf", torch.float32)
+            keep.append(yf)
         if q is not None:
             A.q, A.k_out, A.v = (_dev(t, n, torch.bfloat16) for t, n in ((q, "q"), (k_out, "k"), (v, "v")))
             A.hq, A.hkv, A.head_dim = int(hq), int(hkv), int(head_dim)
@@ -549,3 +605,81 @@ def rmsnorm(x, gain, out, eps: float = 1e-6, stream=None):
 
 def linear(x, w, mode: int, stream=None, **kw):
     PreparedLinear(x, w, mode, **kw)(stream)
+
+
+# ---------------------------------------------------------------- slot decoding
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+class PreparedCall:
+    """A decode-step call with its argument struct marshalled once."""
+
+    def __init__(self, fn_name: str, args, keep):
+        self.fn = getattr(lib(), fn_name)
+        self.args = args
+        self._keep = keep
+
+    def __call__(self, stream=None):
+        _check(self.fn(ctypes.byref(self.args), ctypes.c_void_p(_stream_handle(stream))))
+
+
+def gather_rows(src, idx, rows: int, dst_f32=None, dst_bf16=None, pos=None, pos_base=None, per: int = 1,
+                pos_add: int = 0) -> PreparedCall:
+    import torch
+    A = _GatherArgs()
+    A.src = _dev(src, "src", torch.bfloat16)
+    A.n_src = int(src.shape[0])
+    A.idx = _dev(idx, "idx", torch.int32)
+    A.rows = int(rows)
+    A.dim = int(src.shape[1])
+    A.dst_f32, A.dst_bf16, A.pos, A.pos_base = _p(dst_f32), _p(dst_bf16), _p(pos), _p(pos_base)
+    A.per, A.pos_add = int(per), int(pos_add)
+    return PreparedCall("spb_gather_rows", A, (src, idx, dst_f32, dst_bf16, pos, pos_base))
+
+
+def topk_lse(logits, k: int, ids, lp, lse, masks=None, mask_of_row=None, stop_of_row=None) -> PreparedCall:
+    import torch
+    A = _TopkArgs()
+    A.logits = _dev(logits, "logits", torch.float32)
+    A.rows, A.vocab, A.k = int(logits.shape[0]), int(logits.shape[1]), int(k)
+    A.masks = _p(masks)
+    A.n_masks = 0 if masks is None else int(masks.shape[0])
+    A.mask_of_row, A.stop_of_row = _p(mask_of_row), _p(stop_of_row)
+    A.ids, A.lp, A.lse = _dev(ids, "ids", torch.int32), _dev(lp, "lp", torch.float32), _dev(lse, "lse", torch.float32)
+    return PreparedCall("spb_topk_lse", A, (logits, ids, lp, lse, masks, mask_of_row, stop_of_row))
+
+
+def decode_attention(q, k_pass, v_pass, k_dec, v_dec, o, beams: int, ranges, n_ranges, path, n_path: int,
+                     softmax_scale: float = 0.0) -> PreparedCall:
+    """q / o [rows, hq, d]; k_pass / v_pass [n_pass_rows, hkv, d]; k_dec / v_dec
+    [t_cap * rows, hkv, d]; ranges [n_slots, 16, 2], n_ranges [n_slots], path
+    [rows, t_cap] int32 device tensors."""
+    import torch
+    A = _DecodeAttnArgs()
+    A.q = _dev(q, "q", torch.bfloat16)
+    A.k_pass, A.v_pass = _dev(k_pass, "k_pass", torch.bfloat16), _dev(v_pass, "v_pass", torch.bfloat16)
+    A.n_pass_rows = int(k_pass.shape[0])
+    A.k_dec, A.v_dec = _dev(k_dec, "k_dec", torch.bfloat16), _dev(v_dec, "v_dec", torch.bfloat16)
+    A.o = _dev(o, "o", torch.bfloat16)
+    A.rows, A.beams = int(q.shape[0]), int(beams)
+    A.hq, A.hkv, A.head_dim = int(q.shape[1]), int(k_pass.shape[1]), int(q.shape[2])
+    A.ranges, A.n_ranges, A.path = (_dev(ranges, "ranges", torch.int32), _dev(n_ranges, "n_ranges", torch.int32),
+                                    _dev(path, "path", torch.int32))
+    A.t_cap, A.n_path = int(path.shape[1]), int(n_path)
+    A.softmax_scale = float(softmax_scale)
+    return PreparedCall("spb_decode_attention", A, (q, k_pass, v_pass, k_dec, v_dec, o, ranges, n_ranges, path))
+
+
+def beam_step(n_slots: int, beams: int, k: int, t_cap: int, step: int, stop, ids, lp, state_in, state_out,
+              feed) -> PreparedCall:
+    """state_*: dict of device tensors tok [n_slots*beams, t_cap], len, fin,
+    path [n_slots*beams, t_cap], nb [n_slots] (int32) and score (float32)."""
+    A = _BeamArgs()
+    A.n_slots, A.beams, A.k, A.t_cap, A.step = int(n_slots), int(beams), int(k), int(t_cap), int(step)
+    A.stop, A.ids, A.lp, A.feed = _p(stop), _p(ids), _p(lp), _p(feed)
+    for n in ("tok", "len", "fin", "path", "nb", "score"):
+        setattr(A, n + "_in", _p(state_in[n]) if state_in is not None else None)
+        setattr(A, n + "_out", _p(state_out[n]))
+    return PreparedCall("spb_beam_step", A, (stop, ids, lp, state_in, state_out, feed))

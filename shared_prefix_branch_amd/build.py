@@ -3,7 +3,7 @@
     python -m shared_prefix_branch_amd.build
 
 One shared library: the host planner and C ABI (spb_host.cpp) and the
-kernel sources (attention, lm head, decoder-stack layers).  Packed-FP32 instruction selection is switched off for the GPU
+kernel sources (attention, lm head, decoder-stack layers, slot decoding).  Packed-FP32 instruction selection is switched off for the GPU
 code (-packed-fp32-ops).
 """
 from __future__ import annotations
@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspb.so")
-SOURCES = ["spb_host.cpp", "spb_attention.hip", "spb_score.hip", "spb_layer.hip"]
+SOURCES = ["spb_host.cpp", "spb_attention.hip", "spb_score.hip", "spb_layer.hip", "spb_decode.hip"]
 ARCH = "gfx950"
 
 

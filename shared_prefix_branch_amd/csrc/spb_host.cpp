@@ -1078,19 +1078,14 @@ spb_status spb_plan_inputs(const spb_plan *plan, int64_t *row_off, int32_t *floo
   return ok();
 }
 
-spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int32_t *keys, int32_t cap,
-                            int32_t *n_keys) {
-  spb_status st = check_pass(plan, pass);
-  if (st != SPB_OK) return st;
-  const PassPlan &P = plan->passes[pass];
-  if (row < 0 || row >= (int32_t)P.rows.size()) return fail(SPB_ERR_ARG, "row %d outside the pass", row);
-  if (!n_keys || (cap > 0 && !keys)) return fail(SPB_ERR_ARG, "NULL argument");
+}  // extern "C"
+
+namespace {
+// The pass rows a row attends to, in attention order (content, stems root
+// first, own branch), from the same metadata and rule the kernels use.
+template <typename Emit>
+void visible_keys(const PassPlan &P, int row, Emit emit) {
   const SpbRow &r = P.rows[row];
-  int n = 0;
-  auto emit = [&](int y) {
-    if (n < cap) keys[n] = y;
-    ++n;
-  };
   for (int j = 0; j < r.cvis; ++j) emit(r.seg + j);
   // stems on the row's path, root first: all their tokens, the row's own stem
   // causally
@@ -1110,8 +1105,54 @@ spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int
     for (int ep = 0; ep < E; ++ep)
       if (branch_visible(r, ep)) emit(r.br + ep);
   }
+}
+}  // namespace
+
+extern "C" {
+
+spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int32_t *keys, int32_t cap,
+                            int32_t *n_keys) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  const PassPlan &P = plan->passes[pass];
+  if (row < 0 || row >= (int32_t)P.rows.size()) return fail(SPB_ERR_ARG, "row %d outside the pass", row);
+  if (!n_keys || (cap > 0 && !keys)) return fail(SPB_ERR_ARG, "NULL argument");
+  int n = 0;
+  visible_keys(P, row, [&](int y) {
+    if (n < cap) keys[n] = y;
+    ++n;
+  });
   *n_keys = n;
   if (n > cap) return fail(SPB_ERR_SIZE, "%d keys exceed cap %d", n, cap);
+  return ok();
+}
+
+spb_status spb_plan_slot(const spb_plan *plan, int32_t logical_branch, spb_slot_info *out) {
+  if (!plan || !out) return fail(SPB_ERR_ARG, "NULL argument");
+  if (logical_branch < 0 || logical_branch >= (int32_t)plan->lb_pass.size())
+    return fail(SPB_ERR_ARG, "logical branch %d outside [0, %zu)", logical_branch, plan->lb_pass.size());
+  spb_slot_info s{};
+  s.pass = plan->lb_pass[logical_branch];
+  const PassPlan &P = plan->passes[s.pass];
+  const SpbBranch &b = P.branches[plan->lb_slot[logical_branch]];
+  s.row = b.start + b.L - 1;
+  s.position = P.pos[s.row];
+  bool over = false;
+  int prev = -2;
+  visible_keys(P, s.row, [&](int y) {
+    if (y == prev + 1 && s.n_ranges > 0) {
+      s.ranges[s.n_ranges - 1][1]++;
+    } else if (s.n_ranges < SPB_MAX_SLOT_RANGES) {
+      s.ranges[s.n_ranges][0] = y;
+      s.ranges[s.n_ranges][1] = 1;
+      s.n_ranges++;
+    } else {
+      over = true;
+    }
+    prev = y;
+  });
+  if (over) return fail(SPB_ERR_LIMIT, "slot prefix needs more than %d key ranges", SPB_MAX_SLOT_RANGES);
+  *out = s;
   return ok();
 }
 
@@ -1442,7 +1483,7 @@ spb_status spb_rmsnorm(const spb_rmsnorm_args *a, void *stream) {
 
 spb_status spb_linear(const spb_linear_args *a, void *stream) {
   if (!a) return fail(SPB_ERR_ARG, "args is NULL");
-  if (a->mode < SPB_LINEAR_BF16 || a->mode > SPB_LINEAR_QKV_ROPE) return fail(SPB_ERR_ARG, "mode %d", a->mode);
+  if (a->mode < SPB_LINEAR_BF16 || a->mode > SPB_LINEAR_F32) return fail(SPB_ERR_ARG, "mode %d", a->mode);
   if (a->m < 0 || a->m > 0x7FFFFFFF) return fail(SPB_ERR_ARG, "m %lld", (long long)a->m);
   if (a->k < 64 || a->k % 64) return fail(SPB_ERR_ARG, "k %d must be a positive multiple of 64", a->k);
   if (a->n < 8 || a->n % 8) return fail(SPB_ERR_ARG, "n %d must be a positive multiple of 8", a->n);
@@ -1471,6 +1512,10 @@ spb_status spb_linear(const spb_linear_args *a, void *stream) {
       if (!a->resid || misaligned16(a->resid)) return fail(SPB_ERR_ARG, "resid must be non-NULL and 16-byte aligned");
       L.resid = a->resid;
       break;
+    case SPB_LINEAR_F32:
+      if (!a->yf || misaligned16(a->yf)) return fail(SPB_ERR_ARG, "yf must be non-NULL and 16-byte aligned");
+      L.yf = a->yf;
+      break;
     case SPB_LINEAR_QKV_ROPE:
       if (a->head_dim != 64 && a->head_dim != 128) return fail(SPB_ERR_DTYPE, "head_dim %d not in {64, 128}", a->head_dim);
       if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv) return fail(SPB_ERR_ARG, "hq %d, hkv %d", a->hq, a->hkv);
@@ -1495,6 +1540,124 @@ spb_status spb_linear(const spb_linear_args *a, void *stream) {
   L.ev_end = a->gemm_event_end;
   int e = launch_linear(L, stream);
   if (e) return fail(SPB_ERR_HIP, "linear launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_gather_rows(const spb_gather_args *a, void *stream) {
+  if (!a) return fail(SPB_ERR_ARG, "args is NULL");
+  if (a->rows < 0 || a->dim < 1 || a->n_src < 1) return fail(SPB_ERR_ARG, "rows, dim or n_src");
+  if (a->rows == 0) return ok();
+  if (!a->src || !a->idx || (!a->dst_f32) == (!a->dst_bf16)) return fail(SPB_ERR_ARG, "src, idx and one dst");
+  if (a->pos && (!a->pos_base || a->per < 1)) return fail(SPB_ERR_ARG, "pos needs pos_base and per >= 1");
+  GatherLaunch L{};
+  L.src = (const uint16_t *)a->src;
+  L.idx = a->idx;
+  L.rows = a->rows;
+  L.n_src = a->n_src;
+  L.dim = a->dim;
+  L.dst_f32 = a->dst_f32;
+  L.dst_bf16 = (uint16_t *)a->dst_bf16;
+  L.pos = a->pos;
+  L.pos_base = a->pos_base;
+  L.per = a->per;
+  L.pos_add = a->pos_add;
+  int e = launch_gather_rows(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "gather launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_topk_lse(const spb_topk_args *a, void *stream) {
+  if (!a) return fail(SPB_ERR_ARG, "args is NULL");
+  if (a->rows < 0 || a->rows > 0x7FFFFFFF || a->vocab < 1 || a->k < 1 || a->k > kMaxTopK)
+    return fail(SPB_ERR_ARG, "rows %lld, vocab %d, k %d (1..%d)", (long long)a->rows, a->vocab, a->k, kMaxTopK);
+  if (a->rows == 0) return ok();
+  if (!a->logits || !a->ids || !a->lp || !a->lse) return fail(SPB_ERR_ARG, "NULL tensor");
+  if (a->mask_of_row && (!a->masks || a->n_masks < 1))
+    return fail(SPB_ERR_ARG, "mask_of_row needs masks");
+  TopkLaunch L{a->logits, (long long)a->rows, a->vocab, a->k, a->masks, a->mask_of_row, a->stop_of_row,
+               a->ids, a->lp, a->lse};
+  int e = launch_topk_lse(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "top-k launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_decode_attention(const spb_decode_attn_args *a, void *stream) {
+  if (!a) return fail(SPB_ERR_ARG, "args is NULL");
+  if (a->head_dim != 64 && a->head_dim != 128) return fail(SPB_ERR_DTYPE, "head_dim %d not in {64, 128}", a->head_dim);
+  if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv) return fail(SPB_ERR_DTYPE, "hq %d, hkv %d", a->hq, a->hkv);
+  const int g = a->hq / a->hkv;
+  if (g != 1 && g != 2 && g != 4) return fail(SPB_ERR_DTYPE, "hq / hkv = %d not in {1, 2, 4}", g);
+  if (a->rows < 0 || a->beams < 1 || a->beams > kMaxBeams || a->rows % a->beams)
+    return fail(SPB_ERR_ARG, "rows %d must be a multiple of beams %d (1..%d)", a->rows, a->beams, kMaxBeams);
+  if (a->t_cap < 1 || a->n_path < 0 || a->n_path >= a->t_cap || a->n_pass_rows < 1)
+    return fail(SPB_ERR_ARG, "t_cap %d, n_path %d, n_pass_rows %d", a->t_cap, a->n_path, a->n_pass_rows);
+  if (a->rows == 0) return ok();
+  if ((int64_t)a->t_cap * a->rows > 0x7FFFFFFF) return fail(SPB_ERR_LIMIT, "decode cache too large");
+  if (!a->q || !a->k_pass || !a->v_pass || !a->k_dec || !a->v_dec || !a->o || !a->ranges || !a->n_ranges ||
+      !a->path)
+    return fail(SPB_ERR_ARG, "NULL tensor");
+  if (misaligned16(a->k_pass) || misaligned16(a->k_dec)) return fail(SPB_ERR_ARG, "K caches must be 16-byte aligned");
+  DecodeAttnLaunch L{};
+  L.q = (const uint16_t *)a->q;
+  L.kp = (const uint16_t *)a->k_pass;
+  L.vp = (const uint16_t *)a->v_pass;
+  L.kd = (const uint16_t *)a->k_dec;
+  L.vd = (const uint16_t *)a->v_dec;
+  L.o = (uint16_t *)a->o;
+  L.R = a->rows;
+  L.beams = a->beams;
+  L.hq = a->hq;
+  L.hkv = a->hkv;
+  L.head_dim = a->head_dim;
+  L.ranges = a->ranges;
+  L.n_ranges = a->n_ranges;
+  L.path = a->path;
+  L.t_cap = a->t_cap;
+  L.n_path = a->n_path;
+  L.n_pass_rows = a->n_pass_rows;
+  L.n_dec_rows = a->t_cap * a->rows;
+  L.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)a->head_dim);
+  int e = launch_decode_attention(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "decode attention launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_beam_step(const spb_beam_args *a, void *stream) {
+  if (!a) return fail(SPB_ERR_ARG, "args is NULL");
+  if (a->n_slots < 0 || a->beams < 1 || a->beams > kMaxBeams || a->k < 1 || a->k > kMaxTopK || a->t_cap < 1 ||
+      a->step < 0 || a->step >= a->t_cap)
+    return fail(SPB_ERR_ARG, "n_slots %d, beams %d, k %d, t_cap %d, step %d", a->n_slots, a->beams, a->k, a->t_cap,
+                a->step);
+  if (a->n_slots == 0) return ok();
+  if (!a->stop || !a->ids || !a->lp || !a->tok_out || !a->len_out || !a->fin_out || !a->path_out || !a->nb_out ||
+      !a->score_out || !a->feed)
+    return fail(SPB_ERR_ARG, "NULL tensor");
+  if (a->step > 0 && (!a->tok_in || !a->len_in || !a->fin_in || !a->path_in || !a->nb_in || !a->score_in))
+    return fail(SPB_ERR_ARG, "steps after the first need the previous state");
+  BeamLaunch L{};
+  L.n_slots = a->n_slots;
+  L.beams = a->beams;
+  L.k = a->k;
+  L.t_cap = a->t_cap;
+  L.step = a->step;
+  L.stop = a->stop;
+  L.ids = a->ids;
+  L.lp = a->lp;
+  L.tok_in = a->tok_in;
+  L.len_in = a->len_in;
+  L.fin_in = a->fin_in;
+  L.path_in = a->path_in;
+  L.nb_in = a->nb_in;
+  L.score_in = a->score_in;
+  L.tok_out = a->tok_out;
+  L.len_out = a->len_out;
+  L.fin_out = a->fin_out;
+  L.path_out = a->path_out;
+  L.nb_out = a->nb_out;
+  L.score_out = a->score_out;
+  L.feed = a->feed;
+  int e = launch_beam_step(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "beam step launch: %s", hip_error_string(e));
   return ok();
 }
 

@@ -91,6 +91,7 @@ struct LinearLaunch {
   int m, n, k;
   int mode;
   uint16_t *y;             // BF16: [m][n]; SILU_GATE: [m][n/2]
+  float *yf;               // F32: [m][n]
   float *resid;            // RESIDUAL: [m][n] f32, added to in place
   uint16_t *q, *kk, *v;    // QKV_ROPE: [m][hq*d], [m][hkv*d], [m][hkv*d]
   int hq, hkv, head_dim;
@@ -101,6 +102,67 @@ struct LinearLaunch {
 };
 
 int launch_rmsnorm(const NormLaunch &a, void *stream);
+
+// Slot decoding kernels (spb_decode.hip).
+constexpr int kMaxTopK = 16;       // candidates per row
+constexpr int kMaxBeams = 16;      // beams per slot
+constexpr int kMaxSlotRanges = 16; // key ranges of a slot's prefix
+
+struct TopkLaunch {
+  const float *z;            // [rows][vocab] logits
+  long long rows;
+  int vocab, k;
+  const uint32_t *masks;     // [n_masks][ceil(vocab/32)] allowed-token bits, or NULL
+  const int32_t *mask_of_row;// [rows] mask index, -1 all tokens (NULL: all rows all tokens)
+  const int32_t *stop_of_row;// [rows] a token always allowed (NULL: none)
+  int32_t *ids;              // [rows][k]
+  float *lp;                 // [rows][k] z - LSE
+  float *lse;                // [rows]
+};
+
+struct DecodeAttnLaunch {
+  const uint16_t *q;         // [R][hq][d] bf16
+  const uint16_t *kp, *vp;   // pass cache of the layer: [n_pass_rows][hkv][d]
+  const uint16_t *kd, *vd;   // decode cache of the layer: [t_cap * R][hkv][d]
+  uint16_t *o;               // [R][hq][d]
+  int R, beams, hq, hkv, head_dim;
+  const int32_t *ranges;     // [n_slots][kMaxSlotRanges][2] (first pass row, count)
+  const int32_t *n_ranges;   // [n_slots]
+  const int32_t *path;       // [R][t_cap] decode-cache rows of the ancestors
+  int t_cap, n_path;         // ancestors per row this step; own row = n_path * R + r
+  int n_pass_rows, n_dec_rows;  // bounds the kernel clamps row indices to
+  float scale;
+};
+
+struct BeamLaunch {
+  int n_slots, beams, k, t_cap, step, stop_any;
+  const int32_t *stop;       // [n_slots]
+  const int32_t *ids;        // [rows][k] candidates (rows: n_slots at step 0, else n_slots * beams)
+  const float *lp;
+  const int32_t *tok_in, *len_in, *fin_in, *path_in, *nb_in;   // state before the step
+  const float *score_in;
+  int32_t *tok_out, *len_out, *fin_out, *path_out, *nb_out;    // state after
+  float *score_out;
+  int32_t *feed;             // [n_slots * beams] token each beam feeds next
+};
+
+struct GatherLaunch {
+  const uint16_t *src;       // [*][dim] bf16
+  const int32_t *idx;        // [rows], clamped into [0, n_src)
+  long long rows;
+  int n_src;
+  int dim;
+  float *dst_f32;            // one of the two
+  uint16_t *dst_bf16;
+  int32_t *pos;              // optional: pos[r] = pos_base[r / per] + pos_add
+  const int32_t *pos_base;
+  int per, pos_add;
+};
+
+int launch_topk_lse(const TopkLaunch &a, void *stream);
+int launch_decode_attention(const DecodeAttnLaunch &a, void *stream);
+int launch_beam_step(const BeamLaunch &a, void *stream);
+int launch_gather_rows(const GatherLaunch &a, void *stream);
 int launch_linear(const LinearLaunch &a, void *stream);
 
 int launch_attention(const AttnLaunch &a, void *stream);

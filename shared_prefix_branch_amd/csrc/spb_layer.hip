@@ -22,7 +22,8 @@
 //                interleaved in blocks of 32 rows (gate block, then up block)
 //     QKV_ROPE   q, k, v = split(x [Wq; Wk; Wv]^T), q and k rotated at the
 //                row's position (pairs (2i, 2i+1), angle pos * theta_i, from
-//                a (cos, sin) table), each rounded once to bf16.
+//                a (cos, sin) table), each rounded once to bf16
+//     F32        y = x W^T in f32 (the lm head's logits for decoded rows)
 #define SPB_HD __host__ __device__
 #include "spb_meta.h"
 #include "spb_launch.h"
@@ -172,7 +173,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinParams P) {
       const float4 a0 = *(const float4 *)(st + tl * PITCH + c8 * 8);
       const float4 a1 = *(const float4 *)(st + tl * PITCH + c8 * 8 + 4);
       float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      if constexpr (MODE == SPB_LINEAR_RESIDUAL) {
+      if constexpr (MODE == SPB_LINEAR_F32) {
+        float4 *yf = (float4 *)(p.yf + (size_t)m * p.n + f);
+        yf[0] = a0;
+        yf[1] = a1;
+      } else if constexpr (MODE == SPB_LINEAR_RESIDUAL) {
         float4 *r = (float4 *)(p.resid + (size_t)m * p.n + f);
         float4 r0 = r[0], r1 = r[1];
         r0.x += bf2f(f2bf(v[0])); r0.y += bf2f(f2bf(v[1])); r0.z += bf2f(f2bf(v[2])); r0.w += bf2f(f2bf(v[3]));
@@ -250,6 +255,7 @@ int launch_linear(const LinearLaunch &a, void *stream) {
     case SPB_LINEAR_RESIDUAL: return launch_linear_mode<SPB_LINEAR_RESIDUAL>(a, s);
     case SPB_LINEAR_SILU_GATE: return launch_linear_mode<SPB_LINEAR_SILU_GATE>(a, s);
     case SPB_LINEAR_QKV_ROPE: return launch_linear_mode<SPB_LINEAR_QKV_ROPE>(a, s);
+    case SPB_LINEAR_F32: return launch_linear_mode<SPB_LINEAR_F32>(a, s);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -32,11 +32,11 @@ __all__ = [
     "Problem", "Dims", "Workload", "CONFIGS", "make_workload", "make_problem",
     "count_trie_nodes", "logical_inputs", "seed_for", "STREAM_INPUT",
     "STREAM_FLOOR", "STREAM_LM_HEAD", "STREAM_CALIB", "STREAM_HIDDEN",
-    "ModelDims", "model_weights", "embed_block",
+    "ModelDims", "model_weights", "embed_block", "embed_table",
 ]
 
 STREAM_INPUT, STREAM_FLOOR, STREAM_LM_HEAD, STREAM_CALIB, STREAM_HIDDEN = 0, 1, 2, 3, 4
-STREAM_MODEL, STREAM_EMBED = 5, 6
+STREAM_MODEL, STREAM_EMBED, STREAM_TOKEN_EMBED = 5, 6, 7
 
 
 @dataclasses.dataclass
@@ -491,3 +491,11 @@ def embed_block(wl: Workload, md: ModelDims, which: tuple, device="cpu"):
     g = torch.Generator(device=device)
     g.manual_seed(seed_for(wl.cfg_seed, STREAM_EMBED, ident if stream == STREAM_INPUT else 10_000_000 + ident))
     return torch.randn((n, md.hidden), generator=g, device=device)
+
+
+def embed_table(md: ModelDims, vocab: int, seed: int, device="cpu"):
+    """Embedding rows of decoded tokens: E [vocab, H] ~ N(0, 1), cast to bf16."""
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(seed, STREAM_TOKEN_EMBED, 0))
+    return torch.randn((vocab, md.hidden), generator=g, device=device).to(torch.bfloat16)

@@ -1,0 +1,179 @@
+"""GPU parity of searched slot decoding through the C ABI: the vocab-wide
+top-k / LSE kernel and the beam step against what the oracle fixes, then
+whole slot decodes (decoder stack, decode attention, head, beam search)
+against the oracle's beam search, and slots decoded alone against slots
+decoded together, bit for bit."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_helpers import say
+from tests.test_gpu_stack import StackCase, _stack_case
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 0.1    # an oracle step closer than this to another choice is a near-tie
+TOL_LP = 2e-2   # |lp_gpu - lp_oracle| <= TOL_LP * |lp_oracle|, as for option scoring
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import shared_prefix_branch_amd as spb
+    spb.lib()
+
+
+def test_topk_lse_against_definition():
+    import torch
+    import shared_prefix_branch_amd as spb
+    say("case: top-k + lse rows=37 vocab=5000 k=7, masks")
+    rng = np.random.default_rng(1)
+    R, V, K = 37, 5000, 7
+    z = rng.normal(size=(R, V)).astype(np.float32) * 3
+    masks = np.zeros((2, (V + 31) // 32), np.uint32)
+    allowed0 = rng.choice(V, size=40, replace=False)
+    for x in allowed0:
+        masks[0, x >> 5] |= np.uint32(1 << (x & 31))
+    masks[1, 0] = np.uint32(0b1010)  # tokens 1 and 3 only
+    mrow = rng.integers(-1, 2, size=R).astype(np.int32)
+    stop = rng.integers(0, V, size=R).astype(np.int32)
+    dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    ids = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    lp = torch.empty((R, K), dtype=torch.float32, device="cuda")
+    lse = torch.empty(R, dtype=torch.float32, device="cuda")
+    spb.topk_lse(dev(z), K, ids, lp, lse, masks=dev(masks.view(np.int32)), mask_of_row=dev(mrow),
+                 stop_of_row=dev(stop))()
+    torch.cuda.synchronize()
+    ids, lp, lse = ids.cpu().numpy(), lp.cpu().numpy(), lse.cpu().numpy()
+    for r in range(R):
+        zz = z[r].astype(np.float64)
+        ref_lse = zz.max() + math.log(np.exp(zz - zz.max()).sum())
+        assert abs(lse[r] - ref_lse) <= 1e-5 * abs(ref_lse) + 1e-5
+        if mrow[r] < 0:
+            cand = np.arange(V)
+        elif mrow[r] == 0:
+            cand = np.unique(np.r_[allowed0, stop[r]])
+        else:
+            cand = np.unique([1, 3, stop[r]])
+        order = sorted(cand.tolist(), key=lambda x: (-z[r, x], x))[:K]
+        got = [int(x) for x in ids[r] if x >= 0]
+        assert got == order, r
+        assert np.allclose(lp[r, :len(order)], z[r, order] - ref_lse, atol=1e-4)
+        assert (ids[r, len(order):] == -1).all()
+
+
+def test_beam_step_exact_ties_by_hand():
+    # the oracle's hand-worked example: token 0 -> -1, 1 -> -2, stop 2 -> -3
+    import torch
+    import shared_prefix_branch_amd as spb
+    say("case: beam step, exact ties")
+    S, B, K, T = 1, 3, 3, 4
+    i32 = dict(dtype=torch.int32, device="cuda")
+    st = [dict(tok=torch.empty((S * B, T), **i32), len=torch.empty(S * B, **i32), fin=torch.empty(S * B, **i32),
+               path=torch.empty((S * B, T), **i32), nb=torch.empty(S, **i32),
+               score=torch.empty(S * B, dtype=torch.float32, device="cuda")) for _ in range(2)]
+    feed = torch.empty(S * B, **i32)
+    stop = torch.tensor([2], **i32)
+    ids0 = torch.tensor([[0, 1, 2]], **i32)
+    lp0 = torch.tensor([[-1.0, -2.0, -3.0]], device="cuda")
+    spb.beam_step(S, B, K, T, 0, stop, ids0, lp0, None, st[0], feed)()
+    ids1 = ids0.repeat(B, 1).contiguous()
+    lp1 = lp0.repeat(B, 1).contiguous()
+    spb.beam_step(S, B, K, T, 1, stop, ids1, lp1, st[0], st[1], feed)()
+    torch.cuda.synchronize()
+    s0, s1 = ({k: v.cpu().numpy() for k, v in s.items()} for s in st)
+    assert s0["tok"][:, 0].tolist() == [0, 1, 2] and s0["fin"].tolist() == [0, 0, 1]
+    assert s1["score"].tolist() == [-2.0, -3.0, -3.0]
+    assert [tuple(s1["tok"][b, :s1["len"][b]]) for b in range(B)] == [(0, 0), (0, 1), (1, 0)]
+    # each new beam's path holds its parent's depth-1 row: row (1 - 1) * R + parent
+    assert s1["path"][:, 0].tolist() == [0, 0, 1]
+    assert feed.cpu().tolist() == [0, 1, 0] and int(s1["nb"][0]) == 3
+
+
+def _slot_setup(seed, md_name, n_slots, kinds):
+    """A stacked read with some content branches decoded as slots."""
+    import torch
+    wl, md = _stack_case("shared" if seed % 2 else "random", md_name, 16384, seed)
+    prob = wl.problem
+    V = wl.dims.vocab
+    rng = np.random.default_rng(seed)
+    nb = len(prob.branch_q)
+    lbs = sorted(rng.choice(nb, size=min(n_slots, nb), replace=False).tolist())
+    digits = np.arange(10, 20)
+    masks = np.zeros((1, (V + 31) // 32), np.uint32)
+    for x in digits:
+        masks[0, x >> 5] |= np.uint32(1 << (x & 31))
+    slots = []
+    for j, lb in enumerate(lbs):
+        kind = kinds[j % len(kinds)]
+        slots.append(dict(branch=lb, stop=int(rng.integers(20, V)), mask=0 if kind == "n" else -1))
+    return wl, md, slots, masks, digits
+
+
+def _run_slots(wl, md, slots, masks, budget, inputs=None, B=4, T=5, seed=31, case_cache=None):
+    import torch
+    from shared_prefix_branch_amd.stack import ForwardJob, SlotDecoder
+    case = StackCase(wl, md, budget, inputs=inputs, seed=seed, cache=case_cache, peaked=True)
+    W = (synth.lm_head(wl).float() * 10).to(torch.bfloat16).cuda()  # decisive next-token distributions
+    E = synth.embed_table(md, wl.dims.vocab, seed).cuda()
+    case.job = ForwardJob(case.plan, md, case.layers, case.g_final, wl.dims.vocab, device="cuda", keep_kv=True)
+    case.job.load(case.provider)
+    case.job.run(W)
+    dec = SlotDecoder(case.job, E, W, slots, B, T, masks=torch.from_numpy(masks.view(np.int32)).cuda())
+    dec.run()
+    torch.cuda.synchronize()
+    return case, dec.results(), W.cpu(), E.cpu()
+
+
+@pytest.mark.parametrize("seed,md_name,budget", [(71, "small", 16384), (72, "small_d128", 16384),
+                                                 (71, "small", 150)])
+def test_slots_against_oracle_beam_search(seed, md_name, budget):
+    from oracle import decode as OD, forward as OF, tree as OT
+    from oracle.numerics import to_f64
+    wl, md, slots, masks, digits = _slot_setup(seed, md_name, 5, ["*", "n"])
+    say(f"case: slots seed={seed} {md_name} budget={budget} ({len(slots)} slots, B=4, T=5)")
+    case, res, W, E = _run_slots(wl, md, slots, masks, budget)
+    m = OF.Model.from_synth(md, case.layers, case.g_final)
+    lay = OT.build_layout(case.prob, floors=True)
+    Wf, Ef = to_f64(W), to_f64(E)
+    # logical branch -> (input number, branch object)
+    lbs = [(n, b) for n, li in enumerate(lay.inputs) for b in li.branches]
+    exact = 0
+    for s, got in zip(slots, res):
+        n, b = lbs[s["branch"]]
+        li = lay.inputs[n]
+        x0 = to_f64(case.block(case.ids[n]))
+        path = np.asarray(OT.root_path(lay, b.last_row)) - li.first_row
+        f = OD.model_next_lp(m, x0[path], Ef, Wf)
+        allowed = digits.tolist() if s["mask"] == 0 else None
+        margins = []
+        ref = OD.beam_search(f, 4, 5, s["stop"], allowed, margins)
+        # every answer is a valid candidate with the oracle's score for that sequence
+        for g in got:
+            toks = g["tokens"]
+            if allowed is not None:
+                assert set(toks) <= set(allowed) | {s["stop"]}
+            want = sum(f(toks[:i])[toks[i]] for i in range(len(toks)))
+            assert abs(g["lp"] - want) <= TOL_LP * abs(want), (toks, g["lp"], want)
+            assert g["finished"] == (toks[-1] == s["stop"])
+        if min(margins, default=1.0) > MARGIN:
+            assert [g["tokens"] for g in got] == [r.tokens for r in ref]
+            exact += 1
+    say(f"  {exact} of {len(slots)} slots compared answer for answer (the rest had near-ties)")
+    assert exact >= 1
+
+
+def test_slots_alone_and_together_bit_identical():
+    wl, md, slots, masks, _ = _slot_setup(73, "small", 6, ["*", "n"])
+    say("case: slots together vs alone")
+    cache = {}
+    _, together, _, _ = _run_slots(wl, md, slots, masks, 16384, case_cache=cache)
+    for j in (0, len(slots) - 1):
+        _, alone, _, _ = _run_slots(wl, md, [slots[j]], masks, 16384, case_cache=cache)
+        a, t = alone[0], together[j]
+        assert [g["tokens"] for g in a] == [g["tokens"] for g in t]
+        assert [np.float32(g["lp"]).view(np.uint32) for g in a] == [np.float32(g["lp"]).view(np.uint32) for g in t]

@@ -77,3 +77,54 @@ def test_layer_entry_points_validate_before_any_hip_call():
     assert L.spb_linear(ctypes.byref(A), None) == -2           # x over 4 GiB
     A.m = 0
     assert L.spb_linear(ctypes.byref(A), None) == 0            # nothing to do
+
+
+@pytest.mark.parametrize("budget", [16384, 150])
+def test_slot_prefix_runs_equal_the_root_path(budget):
+    prob = synth.make_problem("random_shared", 71, vocab=1000, n_inputs=3, n_questions=6, min_content=0,
+                              max_content=120, max_lead=40, tail_vocab=3, max_options=3, max_option_tokens=3)
+    plan = spb.pack_pass(prob, token_budget=budget)
+    lay = OT.build_layout(prob, floors=True)
+    lbs = [b for li in lay.inputs for b in li.branches]
+    pos = OF.positions(lay)
+    for lb, b in enumerate(lbs):
+        s = plan.slot(lb)
+        lr, _ = plan.rows(s["pass"])
+        assert lr[s["row"]] == b.last_row
+        assert s["position"] == pos[b.last_row]
+        keys = [y for first, n in s["ranges"] for y in range(first, first + n)]
+        assert keys == plan.visible(s["pass"], s["row"])
+        assert sorted(lr[keys].tolist()) == sorted(OT.root_path(lay, b.last_row))
+    with pytest.raises(spb.SpbError):
+        plan.slot(len(lbs))
+
+
+def test_decode_entry_points_validate_before_any_hip_call():
+    L = spb.lib()
+    T = spb._TopkArgs()
+    T.logits = T.ids = T.lp = T.lse = 256
+    T.rows, T.vocab, T.k = 4, 100, 17
+    assert L.spb_topk_lse(ctypes.byref(T), None) == -1         # k > 16
+    T.k, T.mask_of_row = 4, 256
+    assert L.spb_topk_lse(ctypes.byref(T), None) == -1         # mask_of_row without masks
+    D = spb._DecodeAttnArgs()
+    D.q = D.k_pass = D.v_pass = D.k_dec = D.v_dec = D.o = D.ranges = D.n_ranges = D.path = 256
+    D.rows, D.beams, D.hq, D.hkv, D.head_dim, D.t_cap, D.n_path, D.n_pass_rows = 8, 4, 4, 2, 128, 5, 5, 10
+    assert L.spb_decode_attention(ctypes.byref(D), None) == -1  # n_path >= t_cap
+    D.n_path, D.rows = 2, 6
+    assert L.spb_decode_attention(ctypes.byref(D), None) == -1  # rows % beams
+    D.rows, D.hq = 8, 24
+    assert L.spb_decode_attention(ctypes.byref(D), None) == -3  # hq / hkv = 12
+    Bm = spb._BeamArgs()
+    Bm.n_slots, Bm.beams, Bm.k, Bm.t_cap, Bm.step = 2, 17, 4, 5, 0
+    assert L.spb_beam_step(ctypes.byref(Bm), None) == -1        # beams > 16
+    Bm.beams, Bm.step = 4, 5
+    assert L.spb_beam_step(ctypes.byref(Bm), None) == -1        # step >= t_cap
+    Bm.step = 1
+    Bm.stop = Bm.ids = Bm.lp = Bm.tok_out = Bm.len_out = Bm.fin_out = Bm.path_out = Bm.nb_out = 256
+    Bm.score_out = Bm.feed = 256
+    assert L.spb_beam_step(ctypes.byref(Bm), None) == -1        # later steps need the previous state
+    G = spb._GatherArgs()
+    G.src = G.idx = G.dst_f32 = G.dst_bf16 = 256
+    G.rows, G.dim, G.n_src = 4, 8, 10
+    assert L.spb_gather_rows(ctypes.byref(G), None) == -1       # two destinations
