@@ -14,8 +14,14 @@ from tests.test_gpu_stack import StackCase, _stack_case
 
 pytestmark = pytest.mark.gpu
 
-MARGIN = 0.1    # an oracle step closer than this to another choice is a near-tie
+# The GPU's answer scores sit within 0.1 of the oracle's (observed <= 0.09:
+# bf16 hidden rows into a head whose logits span about +-10, over up to four
+# tokens).  An oracle step whose kept and dropped candidates are more than
+# twice that apart cannot turn out differently on the GPU; closer steps are
+# near-ties, where several answer lists are correct.
+MARGIN = 0.2
 TOL_LP = 2e-2   # |lp_gpu - lp_oracle| <= TOL_LP * |lp_oracle|, as for option scoring
+TOL_RANK = 0.25  # rank by rank, GPU and oracle answer scores agree even across near-ties
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -134,15 +140,17 @@ def _run_slots(wl, md, slots, masks, budget, inputs=None, B=4, T=5, seed=31, cas
 def test_slots_against_oracle_beam_search(seed, md_name, budget):
     from oracle import decode as OD, forward as OF, tree as OT
     from oracle.numerics import to_f64
-    wl, md, slots, masks, digits = _slot_setup(seed, md_name, 5, ["*", "n"])
-    say(f"case: slots seed={seed} {md_name} budget={budget} ({len(slots)} slots, B=4, T=5)")
-    case, res, W, E = _run_slots(wl, md, slots, masks, budget)
+    wl, md, slots, masks, digits = _slot_setup(seed, md_name, 12, ["*", "n", "n"])
+    B, T = 3, 4
+    say(f"case: slots seed={seed} {md_name} budget={budget} ({len(slots)} slots, B={B}, T={T})")
+    case, res, W, E = _run_slots(wl, md, slots, masks, budget, B=B, T=T)
     m = OF.Model.from_synth(md, case.layers, case.g_final)
     lay = OT.build_layout(case.prob, floors=True)
     Wf, Ef = to_f64(W), to_f64(E)
     # logical branch -> (input number, branch object)
     lbs = [(n, b) for n, li in enumerate(lay.inputs) for b in li.branches]
     exact = 0
+    worst, gaps = 0.0, []
     for s, got in zip(slots, res):
         n, b = lbs[s["branch"]]
         li = lay.inputs[n]
@@ -151,20 +159,26 @@ def test_slots_against_oracle_beam_search(seed, md_name, budget):
         f = OD.model_next_lp(m, x0[path], Ef, Wf)
         allowed = digits.tolist() if s["mask"] == 0 else None
         margins = []
-        ref = OD.beam_search(f, 4, 5, s["stop"], allowed, margins)
+        ref = OD.beam_search(f, B, T, s["stop"], allowed, margins)
+        assert len(got) == len(ref)
+        for g, r in zip(got, ref):
+            assert abs(g["lp"] - r.lp) <= TOL_RANK
         # every answer is a valid candidate with the oracle's score for that sequence
         for g in got:
             toks = g["tokens"]
             if allowed is not None:
                 assert set(toks) <= set(allowed) | {s["stop"]}
             want = sum(f(toks[:i])[toks[i]] for i in range(len(toks)))
+            worst = max(worst, abs(g["lp"] - want))
             assert abs(g["lp"] - want) <= TOL_LP * abs(want), (toks, g["lp"], want)
             assert g["finished"] == (toks[-1] == s["stop"])
+        gaps.append(min(margins, default=1.0))
         if min(margins, default=1.0) > MARGIN:
             assert [g["tokens"] for g in got] == [r.tokens for r in ref]
             exact += 1
-    say(f"  {exact} of {len(slots)} slots compared answer for answer (the rest had near-ties)")
-    assert exact >= 1
+    say(f"  {exact} of {len(slots)} slots compared answer for answer (the rest had near-ties); "
+        f"max |lp error| {worst:.2e}; smallest oracle gap per slot {[round(x, 4) for x in gaps]}")
+    assert exact >= 2
 
 
 def test_slots_alone_and_together_bit_identical():
