@@ -64,6 +64,11 @@ def parse():
     ap.add_argument("--layers", type=int, default=0,
                     help="decoder layers in front of the head (synthetic weights, news model dims); "
                          "0: attention alone with given hidden states")
+    ap.add_argument("--slots", type=int, default=0,
+                    help="with --layers: after the timed steps, decode this many extraction slots (the first "
+                         "question of each of the first contents) by beam search and time them")
+    ap.add_argument("--beams", type=int, default=4)
+    ap.add_argument("--slot-tokens", type=int, default=8)
     ap.add_argument("--no-template-sharing", action="store_true",
                     help="drop the template token ids, so questions share no template prefix")
     ap.add_argument("--cpu-sample-inputs", type=int, default=0,
@@ -169,7 +174,7 @@ def main():
                                  hkv=d.hkv, head_dim=d.head_dim)
         layers_w, g_final = synth.model_weights(md, wl.cfg_seed, device=dev)
         job = ForwardJob(plan, md, layers_w, g_final, d.vocab, device=dev, batch_head=batch_head,
-                         lm_head_kind=head_kind)
+                         lm_head_kind=head_kind, keep_kv=args.slots > 0)
         job.load(lambda n: synth.embed_block(wl, md, ids[n], device=dev))
         del layers_w
     else:
@@ -341,6 +346,8 @@ def main():
                              "unmasked_pairs": int(info["unmasked_pairs"]),
                              "note": "inside the decoder stack: stack.forward_ms covers every layer of each pass"}
 
+    if args.slots > 0 and md is not None:
+        line["slots"] = time_slots(job, wl, md, W, prob, args, ms_step, tokens)
     if not args.no_cpu_baseline:
         if md is not None:
             line["cpu_baseline"] = cpu_baseline_stack(wl, md, W)
@@ -442,6 +449,36 @@ def cpu_baseline(wl, W, scales, n_inputs):
             "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{n_inputs} contents x {len(wl.problem.q_len)} questions + {len(ids) - n_inputs} floors "
                       f"= {lay.n_rows} tokens, {qn} questions; float64 NumPy, BLAS threads {cores}"}
+
+
+def time_slots(job, wl, md, W, prob, args, ms_step, tokens):
+    """Decodes ``args.slots`` {*} slots (the first question of each of the
+    first contents, full vocabulary) on the last step's read, timed with HIP
+    events over ``args.steps`` repeats."""
+    import torch
+    import synth
+    from shared_prefix_branch_amd.stack import SlotDecoder
+    n = min(args.slots, prob.n_inputs)
+    E = synth.embed_table(md, wl.dims.vocab, wl.cfg_seed, device="cuda")
+    slots = [dict(branch=int(prob.branch_off[i]), stop=1) for i in range(n)]
+    dec = SlotDecoder(job, E, W, slots, args.beams, args.slot_tokens)
+    stream = torch.cuda.current_stream()
+    dec.run(stream)  # warm-up
+    torch.cuda.synchronize()
+    b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.record(stream)
+    for _ in range(args.steps):
+        dec.run(stream)
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = b.elapsed_time(e) / args.steps
+    res = dec.results()
+    per_slot = ms / n
+    per_token = ms_step / tokens  # GPU-and-host time of one packed scoring token in the step
+    return {"slots": n, "beams": args.beams, "max_tokens": args.slot_tokens, "ms": round(ms, 4),
+            "ms_per_slot": round(per_slot, 4), "scoring_token_equivalents_per_slot": round(per_slot / per_token, 1),
+            "decode_steps": args.slot_tokens, "rows_per_step": n * args.beams,
+            "example": {"tokens": list(res[0][0]["tokens"]), "lp": round(res[0][0]["lp"], 4)}}
 
 
 def cpu_baseline_stack(wl, md, W):

@@ -424,7 +424,10 @@ typedef struct {
   int32_t *ids;
   float *lp;
   float *lse;
+  void *workspace; /* device, spb_topk_workspace_bytes, 16-byte aligned */
+  size_t workspace_bytes;
 } spb_topk_args;
+spb_status spb_topk_workspace_bytes(int64_t rows, int32_t vocab, size_t *out);
 spb_status spb_topk_lse(const spb_topk_args *args, void *stream);
 
 /* Attention of a decode step's rows (q [rows][hq][d], after RoPE): row r of

@@ -21,7 +21,7 @@ __all__ = [
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
     "HEAD_F32OUT", "HEAD_BF16", "HEAD_FP32",
     "LINEAR_BF16", "LINEAR_RESIDUAL", "LINEAR_SILU_GATE", "LINEAR_QKV_ROPE", "LINEAR_F32", "rope_table",
-    "PreparedNorm", "gather_rows", "topk_lse", "decode_attention", "beam_step",
+    "PreparedNorm", "gather_rows", "topk_lse", "topk_workspace_bytes", "decode_attention", "beam_step",
     "PreparedLinear", "rmsnorm", "linear",
     "EXPORTED_SYMBOLS",
 ]
@@ -40,7 +40,8 @@ EXPORTED_SYMBOLS = [
     "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
     "spb_score_batch_workspace_bytes", "spb_score_options_batch",
     "spb_score_finalize", "spb_plan_positions", "spb_rope_table", "spb_rmsnorm", "spb_linear",
-    "spb_plan_slot", "spb_gather_rows", "spb_topk_lse", "spb_decode_attention", "spb_beam_step",
+    "spb_plan_slot", "spb_gather_rows", "spb_topk_workspace_bytes", "spb_topk_lse", "spb_decode_attention",
+    "spb_beam_step",
 ]
 
 
@@ -125,7 +126,8 @@ class _TopkArgs(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("rows", ctypes.c_int64), ("vocab", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("masks", ctypes.c_void_p), ("n_masks", ctypes.c_int32),
                 ("mask_of_row", ctypes.c_void_p), ("stop_of_row", ctypes.c_void_p), ("ids", ctypes.c_void_p),
-                ("lp", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+                ("lp", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _DecodeAttnArgs(ctypes.Structure):
@@ -191,6 +193,7 @@ def lib() -> ctypes.CDLL:
         L.spb_plan_slot.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(_SlotInfo)]
         L.spb_gather_rows.argtypes = [ctypes.POINTER(_GatherArgs), ctypes.c_void_p]
         L.spb_topk_lse.argtypes = [ctypes.POINTER(_TopkArgs), ctypes.c_void_p]
+        L.spb_topk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_decode_attention.argtypes = [ctypes.POINTER(_DecodeAttnArgs), ctypes.c_void_p]
         L.spb_beam_step.argtypes = [ctypes.POINTER(_BeamArgs), ctypes.c_void_p]
         for name in EXPORTED_SYMBOLS:
@@ -639,8 +642,19 @@ def gather_rows(src, idx, rows: int, dst_f32=None, dst_bf16=None, pos=None, pos_
     return PreparedCall("spb_gather_rows", A, (src, idx, dst_f32, dst_bf16, pos, pos_base))
 
 
-def topk_lse(logits, k: int, ids, lp, lse, masks=None, mask_of_row=None, stop_of_row=None) -> PreparedCall:
+def topk_workspace_bytes(rows: int, vocab: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().spb_topk_workspace_bytes(int(rows), int(vocab), ctypes.byref(n)))
+    return int(n.value)
+
+
+def topk_lse(logits, k: int, ids, lp, lse, masks=None, mask_of_row=None, stop_of_row=None,
+             workspace=None) -> PreparedCall:
+    """workspace: a device uint8 tensor of topk_workspace_bytes (allocated here if None)."""
     import torch
+    if workspace is None:
+        workspace = torch.empty(max(16, topk_workspace_bytes(logits.shape[0], logits.shape[1])), dtype=torch.uint8,
+                                device=logits.device)
     A = _TopkArgs()
     A.logits = _dev(logits, "logits", torch.float32)
     A.rows, A.vocab, A.k = int(logits.shape[0]), int(logits.shape[1]), int(k)
@@ -648,7 +662,9 @@ def topk_lse(logits, k: int, ids, lp, lse, masks=None, mask_of_row=None, stop_of
     A.n_masks = 0 if masks is None else int(masks.shape[0])
     A.mask_of_row, A.stop_of_row = _p(mask_of_row), _p(stop_of_row)
     A.ids, A.lp, A.lse = _dev(ids, "ids", torch.int32), _dev(lp, "lp", torch.float32), _dev(lse, "lse", torch.float32)
-    return PreparedCall("spb_topk_lse", A, (logits, ids, lp, lse, masks, mask_of_row, stop_of_row))
+    A.workspace = workspace.data_ptr()
+    A.workspace_bytes = workspace.numel() * workspace.element_size()
+    return PreparedCall("spb_topk_lse", A, (logits, ids, lp, lse, masks, mask_of_row, stop_of_row, workspace))
 
 
 def decode_attention(q, k_pass, v_pass, k_dec, v_dec, o, beams: int, ranges, n_ranges, path, n_path: int,

@@ -13,8 +13,8 @@
 //   decode_attention_kernel each new row over its slot's prefix in the pass's
 //                           KV cache, then its own beam's decoded rows
 //   (lm head)               linear kernel, f32 logits
-//   topk_lse_kernel         per row: LSE over the vocabulary and the k best
-//                           allowed tokens
+//   topk_part_kernel,       per row: LSE over the vocabulary and the k best
+//   topk_merge_kernel       allowed tokens (8192-entry parts, merged in order)
 //   beam_step_kernel        per slot: the B best candidates, the new beams
 //
 // Every choice is taken in a total order (score, then beam, then token id),
@@ -68,56 +68,36 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherLaunch a) {
 // ------------------------------------------------------------ top-k + LSE
 
 constexpr int kTopkThreads = 256;
+constexpr int kTopkSpan = 8192;  // vocabulary entries per work group of the first kernel
 
-// One work group per row.  Thread t walks elements t, t + 256, ... keeping a
-// running (max, sum of exp) and its own best kMaxTopK allowed tokens; the 256
-// partials are merged pairwise in a fixed tree.
-__global__ __launch_bounds__(kTopkThreads) void topk_lse_kernel(TopkLaunch a) {
-  const long long row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float *z = a.z + (size_t)row * a.vocab;
-  const int mi = a.mask_of_row ? a.mask_of_row[row] : -1;
-  const uint32_t *mask = (a.masks && mi >= 0) ? a.masks + (size_t)mi * ((a.vocab + 31) / 32) : nullptr;
-  const int stop = a.stop_of_row ? a.stop_of_row[row] : -1;
+// Merges two (max, sum of exp) partials.
+__device__ inline void lse_merge(float &m, float &s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  s = (m == kNegInf ? 0.f : s * __expf(m - mn)) + (m2 == kNegInf ? 0.f : s2 * __expf(m2 - mn));
+  m = mn;
+}
 
-  float m = kNegInf, s = 0.f;
-  Cand best[kMaxTopK];
+// Inserts c into the sorted list L (best first) if it belongs there.
+__device__ __attribute__((always_inline)) inline void topk_insert(Cand (&L)[kMaxTopK], const Cand &c) {
+  if (!better(c, L[kMaxTopK - 1])) return;
+  L[kMaxTopK - 1] = c;
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) best[j] = Cand{kNegInf, 0x7FFFFFFF};
-  for (int i = tid; i < a.vocab; i += kTopkThreads) {
-    const float v = z[i];
-    if (v > m) {
-      s = s * __expf(m - v) + 1.f;
-      m = v;
-    } else {
-      s += __expf(v - m);
+  for (int j = kMaxTopK - 1; j > 0; --j)
+    if (better(L[j], L[j - 1])) {
+      const Cand t = L[j];
+      L[j] = L[j - 1];
+      L[j - 1] = t;
     }
-    const bool ok = !mask || i == stop || ((mask[i >> 5] >> (i & 31)) & 1u);
-    const Cand c{v, i};
-    if (ok && better(c, best[kMaxTopK - 1])) {
-      best[kMaxTopK - 1] = c;
-#pragma unroll
-      for (int j = kMaxTopK - 1; j > 0; --j)
-        if (better(best[j], best[j - 1])) {
-          const Cand t = best[j];
-          best[j] = best[j - 1];
-          best[j - 1] = t;
-        }
-    }
-  }
-  __shared__ float sm[kTopkThreads], ss[kTopkThreads];
-  __shared__ Cand sl[kTopkThreads][kMaxTopK];
-  sm[tid] = m;
-  ss[tid] = s;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) sl[tid][j] = best[j];
-  __syncthreads();
+}
+
+// Tree merge of the work group's 256 partials (fixed pairs), result in slot 0.
+__device__ inline void topk_tree(float *sm, float *ss, Cand (*sl)[kMaxTopK], int tid) {
   for (int w = kTopkThreads / 2; w >= 1; w >>= 1) {
     if (tid < w) {
-      const float m1 = sm[tid], m2 = sm[tid + w];
-      const float mn = fmaxf(m1, m2);
-      ss[tid] = (m1 == kNegInf ? 0.f : ss[tid] * __expf(m1 - mn)) + (m2 == kNegInf ? 0.f : ss[tid + w] * __expf(m2 - mn));
-      sm[tid] = mn;
+      float m = sm[tid], s = ss[tid];
+      lse_merge(m, s, sm[tid + w], ss[tid + w]);
+      sm[tid] = m;
+      ss[tid] = s;
       Cand out[kMaxTopK];
       int i1 = 0, i2 = 0;
 #pragma unroll
@@ -136,14 +116,91 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lse_kernel(TopkLaunch a) {
     }
     __syncthreads();
   }
-  if (tid == 0) {
-    const float lse = sm[0] + __logf(ss[0]);
-    a.lse[row] = lse;
-    for (int j = 0; j < a.k; ++j) {
-      const Cand c = sl[0][j];
-      a.ids[row * a.k + j] = c.v == kNegInf ? -1 : c.id;
-      a.lp[row * a.k + j] = c.v == kNegInf ? kNegInf : c.v - lse;
+}
+
+struct TopkPart {  // one work group's partial of one row
+  float m, s;
+  Cand best[kMaxTopK];
+};
+
+// First kernel: work group (row, part) covers vocabulary entries
+// part*8192 .. +8192; each thread reads 8 entries per round (two 16-byte
+// loads in flight) and keeps a running (max, sum of exp) and its best
+// kMaxTopK allowed tokens.
+__global__ __launch_bounds__(kTopkThreads) void topk_part_kernel(TopkLaunch a, TopkPart *parts, int n_parts) {
+  const long long row = blockIdx.x / n_parts;
+  const int part = blockIdx.x % n_parts;
+  const int tid = threadIdx.x;
+  const float *z = a.z + (size_t)row * a.vocab;
+  const int mi = a.mask_of_row ? a.mask_of_row[row] : -1;
+  const uint32_t *mask = (a.masks && mi >= 0) ? a.masks + (size_t)mi * ((a.vocab + 31) / 32) : nullptr;
+  const int stop = a.stop_of_row ? a.stop_of_row[row] : -1;
+  const int lo = part * kTopkSpan, hi = min(lo + kTopkSpan, a.vocab);
+  float m = kNegInf, s = 0.f;
+  Cand best[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) best[j] = Cand{kNegInf, 0x7FFFFFFF};
+  auto take = [&](int i, float v) {
+    if (v > m) {
+      s = s * __expf(m - v) + 1.f;
+      m = v;
+    } else {
+      s += __expf(v - m);
     }
+    const bool ok = !mask || i == stop || ((mask[i >> 5] >> (i & 31)) & 1u);
+    if (ok) topk_insert(best, Cand{v, i});
+  };
+  const bool vec = (a.vocab & 3) == 0;  // rows 16-byte aligned
+  for (int i0 = lo + tid * 8; i0 < hi; i0 += kTopkThreads * 8) {
+    if (vec && i0 + 8 <= hi) {
+      const float4 u0 = *(const float4 *)(z + i0), u1 = *(const float4 *)(z + i0 + 4);
+      const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) take(i0 + j, v[j]);
+    } else {
+      for (int j = 0; j < 8 && i0 + j < hi; ++j) take(i0 + j, z[i0 + j]);
+    }
+  }
+  __shared__ float sm[kTopkThreads], ss[kTopkThreads];
+  __shared__ Cand sl[kTopkThreads][kMaxTopK];
+  sm[tid] = m;
+  ss[tid] = s;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) sl[tid][j] = best[j];
+  __syncthreads();
+  topk_tree(sm, ss, sl, tid);
+  if (tid == 0) {
+    TopkPart &P = parts[blockIdx.x];
+    P.m = sm[0];
+    P.s = ss[0];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) P.best[j] = sl[0][j];
+  }
+}
+
+// Second kernel: one wave per row merges the row's parts in part order.
+__global__ __launch_bounds__(64) void topk_merge_kernel(TopkLaunch a, const TopkPart *parts, int n_parts) {
+  const long long row = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const TopkPart *P = parts + row * n_parts;
+  float m = P[0].m, s = P[0].s;
+  Cand best[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) best[j] = P[0].best[j];
+  for (int q = 1; q < n_parts; ++q) {
+    lse_merge(m, s, P[q].m, P[q].s);
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const Cand c = P[q].best[j];
+      if (!better(c, best[kMaxTopK - 1])) break;  // the part's list is sorted
+      topk_insert(best, c);
+    }
+  }
+  const float lse = m + __logf(s);
+  a.lse[row] = lse;
+  for (int j = 0; j < a.k; ++j) {
+    const Cand c = best[j];
+    a.ids[row * a.k + j] = c.v == kNegInf ? -1 : c.id;
+    a.lp[row * a.k + j] = c.v == kNegInf ? kNegInf : c.v - lse;
   }
 }
 
@@ -152,16 +209,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lse_kernel(TopkLaunch a) {
 // One wave per (decoded row, KV head), the G = hq / hkv query heads of the
 // group together.  Keys: the slot's prefix ranges in the pass cache, then
 // the row's ancestors in the decode cache, then the row itself.  Lane j
-// scores key j of each 64-key chunk (q . k in f32); the online softmax's max
-// and sum run over a fixed butterfly; for P.V lane l owns dimensions
-// l * D / 64 .. of every head.
+// scores key j of each 64-key chunk (q . k in f32, its key row read with all
+// 16-byte loads in flight); the online softmax's max and sum run over a fixed
+// butterfly; the chunk's V rows are staged in LDS, and for P.V lane l owns
+// dimensions l * D / 64 .. of every head.
 template <int D, int G>
 __global__ __launch_bounds__(64) void decode_attention_kernel(DecodeAttnLaunch a) {
   constexpr int DL = D / 64;  // dimensions per lane in P.V
+  constexpr int PR = D / 8;   // 16-byte pieces per key row
   const int r = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
   const int lane = threadIdx.x;
   const int slot = r / a.beams;
   __shared__ float qs[G][D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[64][D];  // the chunk's V rows
   for (int i = lane; i < G * D; i += 64) {
     const int h = i / D, dd = i % D;
     qs[h][dd] = bf2f(a.q[((size_t)r * a.hq + g * G + h) * D + dd]);
@@ -181,22 +241,23 @@ __global__ __launch_bounds__(64) void decode_attention_kernel(DecodeAttnLaunch a
   for (int i = 0; i < nr; ++i) total += max(rg[2 * i + 1], 0);
   const int n_keys = total + a.n_path + 1;
   const size_t kstride = (size_t)a.hkv * D;
-  // key index -> row pointer (pass cache, then decode cache)
-  auto key_row = [&](int kidx, bool v) -> const uint16_t * {
+  // key index -> row offset in its cache (pass cache, then decode cache)
+  auto key_at = [&](int kidx, bool &dec) -> size_t {
     if (kidx < total) {
       int i = 0;
       while (i < nr - 1 && kidx >= max(rg[2 * i + 1], 0)) {
         kidx -= max(rg[2 * i + 1], 0);
         ++i;
       }
-      const int prow = min(max(rg[2 * i] + kidx, 0), a.n_pass_rows - 1);
-      return (v ? a.vp : a.kp) + (size_t)prow * kstride + (size_t)g * D;
+      dec = false;
+      return (size_t)min(max(rg[2 * i] + kidx, 0), a.n_pass_rows - 1) * kstride + (size_t)g * D;
     }
     kidx -= total;
     const int own = a.n_path * a.R + r;
     int crow = kidx < a.n_path ? a.path[(size_t)r * a.t_cap + kidx] : own;
     if (crow < 0 || crow >= a.n_dec_rows) crow = own;  // a finished beam's unused row
-    return (v ? a.vd : a.kd) + (size_t)crow * kstride + (size_t)g * D;
+    dec = true;
+    return (size_t)crow * kstride + (size_t)g * D;
   };
   for (int c0 = 0; c0 < n_keys; c0 += 64) {
     const int kidx = c0 + lane;
@@ -204,25 +265,50 @@ __global__ __launch_bounds__(64) void decode_attention_kernel(DecodeAttnLaunch a
 #pragma unroll
     for (int h = 0; h < G; ++h) sc[h] = kNegInf;
     if (kidx < n_keys) {
-      const uint16_t *kr = key_row(kidx, false);
+      bool dec;
+      const size_t off = key_at(kidx, dec);
+      const uint16_t *kr = (dec ? a.kd : a.kp) + off;
+      uint4 u[PR];
+#pragma unroll
+      for (int pc = 0; pc < PR; ++pc) u[pc] = *(const uint4 *)(kr + pc * 8);
       float acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h] = 0.f;
-      for (int dd = 0; dd < D; dd += 8) {
-        const uint4 u = *(const uint4 *)(kr + dd);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int pc = 0; pc < PR; ++pc) {
+        const uint32_t w[4] = {u[pc].x, u[pc].y, u[pc].z, u[pc].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float k0 = bf2f(w[e] & 0xFFFFu), k1 = bf2f(w[e] >> 16);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            acc[h] = __builtin_fmaf(qs[h][dd + 2 * e], k0, acc[h]);
-            acc[h] = __builtin_fmaf(qs[h][dd + 2 * e + 1], k1, acc[h]);
+            acc[h] = __builtin_fmaf(qs[h][pc * 8 + 2 * e], k0, acc[h]);
+            acc[h] = __builtin_fmaf(qs[h][pc * 8 + 2 * e + 1], k1, acc[h]);
           }
         }
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[h] = acc[h] * a.scale;
+    }
+    // the chunk's V rows into LDS: piece p of the chunk is row p / PR, 16 bytes p % PR
+    const int nk = n_keys - c0 < 64 ? n_keys - c0 : 64;
+    {
+      uint4 vv[PR];
+#pragma unroll
+      for (int i = 0; i < PR; ++i) {
+        const int pcs = lane + 64 * i, kr = pcs / PR, pc = pcs % PR;
+        vv[i] = uint4{0u, 0u, 0u, 0u};
+        if (kr < nk) {
+          bool dec;
+          const size_t off = key_at(c0 + kr, dec);
+          vv[i] = *(const uint4 *)((dec ? a.vd : a.vp) + off + pc * 8);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PR; ++i) {
+        const int pcs = lane + 64 * i;
+        *(uint4 *)&vs[pcs / PR][(pcs % PR) * 8] = vv[i];
+      }
     }
     float p[G];
 #pragma unroll
@@ -241,19 +327,19 @@ __global__ __launch_bounds__(64) void decode_attention_kernel(DecodeAttnLaunch a
       for (int j = 0; j < DL; ++j) o[h][j] *= alpha;
       m[h] = mn;
     }
-    const int nk = n_keys - c0 < 64 ? n_keys - c0 : 64;
+    __syncthreads();  // V rows in LDS
     for (int j = 0; j < nk; ++j) {
-      const uint16_t *vr = key_row(c0 + j, true);
-      float vv[DL];
+      float vf[DL];
 #pragma unroll
-      for (int e = 0; e < DL; ++e) vv[e] = bf2f(vr[lane * DL + e]);
+      for (int e = 0; e < DL; ++e) vf[e] = bf2f(vs[j][lane * DL + e]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float pj = __shfl(p[h], j);
 #pragma unroll
-        for (int e = 0; e < DL; ++e) o[h][e] = __builtin_fmaf(pj, vv[e], o[h][e]);
+        for (int e = 0; e < DL; ++e) o[h][e] = __builtin_fmaf(pj, vf[e], o[h][e]);
       }
     }
+    __syncthreads();  // before the next chunk overwrites vs
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -400,10 +486,22 @@ int launch_gather_rows(const GatherLaunch &a, void *stream) {
   return (int)hipGetLastError();
 }
 
+size_t topk_workspace_bytes(long long rows, int vocab) {
+  const int n_parts = (vocab + kTopkSpan - 1) / kTopkSpan;
+  return (size_t)rows * n_parts * sizeof(TopkPart);
+}
+
 int launch_topk_lse(const TopkLaunch &a, void *stream) {
   if (a.rows == 0) return 0;
-  if (a.rows > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_lse_kernel, dim3((unsigned)a.rows), dim3(kTopkThreads), 0, (hipStream_t)stream, a);
+  const int n_parts = (a.vocab + kTopkSpan - 1) / kTopkSpan;
+  const long long blocks = a.rows * n_parts;
+  if (blocks > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  TopkPart *parts = (TopkPart *)a.workspace;
+  hipLaunchKernelGGL(topk_part_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, (hipStream_t)stream, a, parts,
+                     n_parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.rows), dim3(64), 0, (hipStream_t)stream, a, parts, n_parts);
   return (int)hipGetLastError();
 }
 

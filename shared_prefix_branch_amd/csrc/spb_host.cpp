@@ -1566,6 +1566,12 @@ spb_status spb_gather_rows(const spb_gather_args *a, void *stream) {
   return ok();
 }
 
+spb_status spb_topk_workspace_bytes(int64_t rows, int32_t vocab, size_t *out) {
+  if (!out || rows < 0 || vocab < 1) return fail(SPB_ERR_ARG, "rows %lld, vocab %d", (long long)rows, vocab);
+  *out = topk_workspace_bytes(rows, vocab);
+  return ok();
+}
+
 spb_status spb_topk_lse(const spb_topk_args *a, void *stream) {
   if (!a) return fail(SPB_ERR_ARG, "args is NULL");
   if (a->rows < 0 || a->rows > 0x7FFFFFFF || a->vocab < 1 || a->k < 1 || a->k > kMaxTopK)
@@ -1574,8 +1580,11 @@ spb_status spb_topk_lse(const spb_topk_args *a, void *stream) {
   if (!a->logits || !a->ids || !a->lp || !a->lse) return fail(SPB_ERR_ARG, "NULL tensor");
   if (a->mask_of_row && (!a->masks || a->n_masks < 1))
     return fail(SPB_ERR_ARG, "mask_of_row needs masks");
+  const size_t need = topk_workspace_bytes(a->rows, a->vocab);
+  if (!a->workspace || a->workspace_bytes < need || misaligned16(a->workspace))
+    return fail(SPB_ERR_SIZE, "top-k needs a 16-byte aligned workspace of %zu bytes", need);
   TopkLaunch L{a->logits, (long long)a->rows, a->vocab, a->k, a->masks, a->mask_of_row, a->stop_of_row,
-               a->ids, a->lp, a->lse};
+               a->ids, a->lp, a->lse, a->workspace};
   int e = launch_topk_lse(L, stream);
   if (e) return fail(SPB_ERR_HIP, "top-k launch: %s", hip_error_string(e));
   return ok();

@@ -118,7 +118,9 @@ struct TopkLaunch {
   int32_t *ids;              // [rows][k]
   float *lp;                 // [rows][k] z - LSE
   float *lse;                // [rows]
+  void *workspace;           // topk_workspace_bytes(rows, vocab)
 };
+size_t topk_workspace_bytes(long long rows, int vocab);
 
 struct DecodeAttnLaunch {
   const uint16_t *q;         // [R][hq][d] bf16

@@ -77,8 +77,11 @@ class ForwardJob(Job):
         buf.act = t.empty((n, md.ffn), dtype=t.bfloat16, device=self.device)
         buf.kv = [(buf.k, buf.v)]
         if self.keep_kv:
-            for _ in range(1, md.layers):
-                buf.kv.append((t.empty_like(buf.k), t.empty_like(buf.v)))
+            # every layer's K/V, all passes in one buffer per layer (slot decoding
+            # reads the prefixes of every pass's slots from it in one launch)
+            o, rows = self.kv_off[k], buf.k.shape[0]
+            buf.kv = [(K[o:o + rows], V[o:o + rows]) for K, V in self.kv_global]
+            buf.k, buf.v = buf.kv[0]
         pos = self.plan.positions(k)
         if pos.size and int(pos.max()) >= self.n_pos:
             raise ValueError(f"positions up to {int(pos.max())} need n_pos > {self.n_pos}")
@@ -105,8 +108,15 @@ class ForwardJob(Job):
             buf.x0.index_copy_(0, t.from_numpy(sel).to(self.device), x0.index_select(0, t.from_numpy(off[sel]).to(self.device)))
 
     def load(self, provider):
-        super().load(provider)
+        t = self.torch
         md = self.md
+        if self.keep_kv:
+            rows = [max(1, self.plan.info(k)["n_tokens"]) for k in range(self.plan.n_passes)]
+            self.kv_off = np.r_[0, np.cumsum(rows)].astype(np.int64).tolist()
+            shape = (self.kv_off[-1], md.hkv, md.head_dim)
+            self.kv_global = [(t.empty(shape, dtype=t.bfloat16, device=self.device),
+                               t.empty(shape, dtype=t.bfloat16, device=self.device)) for _ in range(md.layers)]
+        super().load(provider)
         self._ops = []
         for k, buf in enumerate(self.passes):
             n = buf.n_tokens
@@ -163,8 +173,8 @@ class ForwardJob(Job):
 
 class SlotDecoder:
     """Searched decoding of slot questions on the read a ``ForwardJob``
-    (built with ``keep_kv=True``) has run: per pass, the B beams of all its
-    slots advance together, one decode step per token (see spb_decode.hip).
+    (built with ``keep_kv=True``) has run: the B beams of every slot, of every
+    pass, advance together, one decode step per token (see spb_decode.hip).
 
     slots: per slot a dict(branch=logical branch id, stop=token, mask=row of
     ``masks`` or -1 for the whole vocabulary); embed: bf16 [V, H] embedding
@@ -175,122 +185,120 @@ class SlotDecoder:
                  masks=None):
         import torch
         t = torch
+        if not job.keep_kv:
+            raise ValueError("slot decoding needs a ForwardJob built with keep_kv=True")
         self.job, self.embed, self.W = job, embed, lm_head
         self.B, self.T, self.k = int(beams), int(max_tokens), int(beams)
         self.masks = masks
         md, dev = job.md, job.device
-        self.by_pass = {}
+        items = []
         for i, s in enumerate(slots):
-            info = job.plan.slot(s["branch"])
-            self.by_pass.setdefault(info["pass"], []).append((i, s, info))
-        self.n_slots = len(slots)
-        self._runs = []
+            items.append((i, s, job.plan.slot(s["branch"])))
+        items.sort(key=lambda it: (it[2]["pass"], it[0]))  # slots grouped by pass
+        self.items = items
+        S = len(items)
+        R = S * self.B
         V = lm_head.shape[0]
-        for k, items in sorted(self.by_pass.items()):
-            S = len(items)
-            R = S * self.B
-            buf = job.passes[k]
-            i32 = dict(dtype=t.int32, device=dev)
-            rng = np.zeros((S, MAX_SLOT_RANGES, 2), np.int32)
-            nrg = np.zeros(S, np.int32)
-            for j, (_, s, info) in enumerate(items):
-                nrg[j] = len(info["ranges"])
-                rng[j, :nrg[j]] = np.asarray(info["ranges"], np.int32)
-            run = dict(
-                pass_=k, items=items, S=S, R=R,
-                ranges=t.from_numpy(rng).to(dev), n_ranges=t.from_numpy(nrg).to(dev),
-                slot_rows=t.tensor([info["row"] for _, _, info in items], **i32),
-                slot_pos=t.tensor([info["position"] for _, _, info in items], **i32),
-                stop=t.tensor([s["stop"] for _, s, _ in items], **i32),
-                mask0=t.tensor([s.get("mask", -1) for _, s, _ in items], **i32),
-                stop_r=t.tensor([s["stop"] for _, s, _ in items for _ in range(self.B)], **i32),
-                mask_r=t.tensor([s.get("mask", -1) for _, s, _ in items for _ in range(self.B)], **i32),
-                h0=t.empty((S, md.hidden), dtype=t.bfloat16, device=dev),
-                z0=t.empty((S, V), dtype=t.float32, device=dev),
-                ids0=t.empty((S, self.k), **i32), lp0=t.empty((S, self.k), dtype=t.float32, device=dev),
-                lse0=t.empty(S, dtype=t.float32, device=dev),
-                x=t.empty((R, md.hidden), dtype=t.float32, device=dev),
-                h=t.empty((R, md.hidden), dtype=t.bfloat16, device=dev),
-                q=t.empty((R, md.hq, md.head_dim), dtype=t.bfloat16, device=dev),
-                o=t.empty((R, md.hq, md.head_dim), dtype=t.bfloat16, device=dev),
-                act=t.empty((R, md.ffn), dtype=t.bfloat16, device=dev),
-                hid=t.empty((R, md.hidden), dtype=t.bfloat16, device=dev),
-                z=t.empty((R, V), dtype=t.float32, device=dev),
-                ids=t.empty((R, self.k), **i32), lp=t.empty((R, self.k), dtype=t.float32, device=dev),
-                lse=t.empty(R, dtype=t.float32, device=dev),
-                pos=t.empty(R, **i32), feed=t.empty(R, **i32),
-                kdec=[t.empty((self.T * R, md.hkv, md.head_dim), dtype=t.bfloat16, device=dev)
-                      for _ in range(md.layers)],
-                vdec=[t.empty((self.T * R, md.hkv, md.head_dim), dtype=t.bfloat16, device=dev)
-                      for _ in range(md.layers)],
-                state=[dict(tok=t.empty((R, self.T), **i32), len=t.empty(R, **i32), fin=t.empty(R, **i32),
-                            path=t.empty((R, self.T), **i32), nb=t.empty(S, **i32),
-                            score=t.empty(R, dtype=t.float32, device=dev)) for _ in range(2)])
-            self._runs.append(run)
-            self._prepare(run, buf)
+        i32 = dict(dtype=t.int32, device=dev)
+        rng = np.zeros((S, MAX_SLOT_RANGES, 2), np.int32)
+        nrg = np.zeros(S, np.int32)
+        for j, (_, s, info) in enumerate(items):
+            nrg[j] = len(info["ranges"])
+            rng[j, :nrg[j]] = np.asarray(info["ranges"], np.int32)
+            rng[j, :nrg[j], 0] += job.kv_off[info["pass"]]
+        self.S, self.R = S, R
+        f32 = dict(dtype=t.float32, device=dev)
+        bf = dict(dtype=t.bfloat16, device=dev)
+        self.buf = dict(
+            ranges=t.from_numpy(rng).to(dev), n_ranges=t.from_numpy(nrg).to(dev),
+            slot_pos=t.tensor([info["position"] for _, _, info in items], **i32),
+            stop=t.tensor([s["stop"] for _, s, _ in items], **i32),
+            mask0=t.tensor([s.get("mask", -1) for _, s, _ in items], **i32),
+            stop_r=t.tensor([s["stop"] for _, s, _ in items for _ in range(self.B)], **i32),
+            mask_r=t.tensor([s.get("mask", -1) for _, s, _ in items for _ in range(self.B)], **i32),
+            h0=t.empty((S, md.hidden), **bf), z0=t.empty((S, V), **f32),
+            ids0=t.empty((S, self.k), **i32), lp0=t.empty((S, self.k), **f32), lse0=t.empty(S, **f32),
+            x=t.empty((R, md.hidden), **f32), h=t.empty((R, md.hidden), **bf),
+            q=t.empty((R, md.hq, md.head_dim), **bf), o=t.empty((R, md.hq, md.head_dim), **bf),
+            act=t.empty((R, md.ffn), **bf), hid=t.empty((R, md.hidden), **bf), z=t.empty((R, V), **f32),
+            ids=t.empty((R, self.k), **i32), lp=t.empty((R, self.k), **f32), lse=t.empty(R, **f32),
+            pos=t.empty(R, **i32), feed=t.empty(R, **i32),
+            kdec=[t.empty((self.T * R, md.hkv, md.head_dim), **bf) for _ in range(md.layers)],
+            vdec=[t.empty((self.T * R, md.hkv, md.head_dim), **bf) for _ in range(md.layers)],
+            state=[dict(tok=t.empty((R, self.T), **i32), len=t.empty(R, **i32), fin=t.empty(R, **i32),
+                        path=t.empty((R, self.T), **i32), nb=t.empty(S, **i32), score=t.empty(R, **f32))
+                   for _ in range(2)])
+        self._prepare()
 
-    def _prepare(self, run, buf):
-        """Marshals every call of the run once (step 0 and steps 1 .. T-1)."""
-        job, md = self.job, self.job.md
-        S, R, B = run["S"], run["R"], self.B
-        ops0 = [gather_rows(buf.hidden, run["slot_rows"], S, dst_bf16=run["h0"]),
-                PreparedLinear(run["h0"], self.W, LINEAR_F32, yf=run["z0"]),
-                topk_lse(run["z0"], self.k, run["ids0"], run["lp0"], run["lse0"], masks=self.masks,
-                         mask_of_row=run["mask0"] if self.masks is not None else None, stop_of_row=run["stop"]),
-                beam_step(S, B, self.k, self.T, 0, run["stop"], run["ids0"], run["lp0"], None, run["state"][0],
-                          run["feed"])]
+    def _prepare(self):
+        """Marshals every call once: step 0 and steps 1 .. T-1."""
+        job, md, b = self.job, self.job.md, self.buf
+        S, R, B = self.S, self.R, self.B
+        ops0 = []
+        j = 0
+        while j < S:  # the slots' template rows, pass by pass, into h0
+            k = self.items[j][2]["pass"]
+            j1 = j
+            while j1 < S and self.items[j1][2]["pass"] == k:
+                j1 += 1
+            rows = self.job.torch.tensor([self.items[x][2]["row"] for x in range(j, j1)], dtype=self.job.torch.int32,
+                                         device=job.device)
+            ops0.append(gather_rows(job.passes[k].hidden, rows, j1 - j, dst_bf16=b["h0"][j:j1]))
+            j = j1
+        masked = self.masks is not None
+        ops0 += [PreparedLinear(b["h0"], self.W, LINEAR_F32, yf=b["z0"]),
+                 topk_lse(b["z0"], self.k, b["ids0"], b["lp0"], b["lse0"], masks=self.masks,
+                          mask_of_row=b["mask0"] if masked else None, stop_of_row=b["stop"]),
+                 beam_step(S, B, self.k, self.T, 0, b["stop"], b["ids0"], b["lp0"], None, b["state"][0], b["feed"])]
         steps = []
         for st in range(1, self.T):
-            cur, nxt = run["state"][(st - 1) % 2], run["state"][st % 2]
-            ops = [gather_rows(self.embed, run["feed"], R, dst_f32=run["x"], pos=run["pos"], pos_base=run["slot_pos"],
+            cur, nxt = b["state"][(st - 1) % 2], b["state"][st % 2]
+            ops = [gather_rows(self.embed, b["feed"], R, dst_f32=b["x"], pos=b["pos"], pos_base=b["slot_pos"],
                                per=B, pos_add=st)]
             for li, W in enumerate(job.W):
-                kp, vp = buf.kv[li % len(buf.kv)]
-                kd = run["kdec"][li][(st - 1) * R:st * R]
-                vd = run["vdec"][li][(st - 1) * R:st * R]
-                ops.append(PreparedNorm(run["x"], W["g_attn"], run["h"], md.eps))
-                ops.append(PreparedLinear(run["h"], W["wqkv"], LINEAR_QKV_ROPE, q=run["q"], k_out=kd, v=vd,
-                                          hq=md.hq, hkv=md.hkv, head_dim=md.head_dim, pos=run["pos"], rope=job.rope))
-                ops.append(decode_attention(run["q"], kp, vp, run["kdec"][li], run["vdec"][li], run["o"], B,
-                                            run["ranges"], run["n_ranges"], cur["path"], st - 1))
-                ops.append(PreparedLinear(run["o"].reshape(R, -1), W["wo"], LINEAR_RESIDUAL, resid=run["x"]))
-                ops.append(PreparedNorm(run["x"], W["g_mlp"], run["h"], md.eps))
-                ops.append(PreparedLinear(run["h"], W["wgu"], LINEAR_SILU_GATE, y=run["act"]))
-                ops.append(PreparedLinear(run["act"], W["wd"], LINEAR_RESIDUAL, resid=run["x"]))
-            ops.append(PreparedNorm(run["x"], job.g_final, run["hid"], md.eps))
-            ops.append(PreparedLinear(run["hid"], self.W, LINEAR_F32, yf=run["z"]))
-            ops.append(topk_lse(run["z"], self.k, run["ids"], run["lp"], run["lse"], masks=self.masks,
-                                mask_of_row=run["mask_r"] if self.masks is not None else None,
-                                stop_of_row=run["stop_r"]))
-            ops.append(beam_step(S, B, self.k, self.T, st, run["stop"], run["ids"], run["lp"], cur, nxt, run["feed"]))
+                kp, vp = job.kv_global[li]
+                kd = b["kdec"][li][(st - 1) * R:st * R]
+                vd = b["vdec"][li][(st - 1) * R:st * R]
+                ops.append(PreparedNorm(b["x"], W["g_attn"], b["h"], md.eps))
+                ops.append(PreparedLinear(b["h"], W["wqkv"], LINEAR_QKV_ROPE, q=b["q"], k_out=kd, v=vd,
+                                          hq=md.hq, hkv=md.hkv, head_dim=md.head_dim, pos=b["pos"], rope=job.rope))
+                ops.append(decode_attention(b["q"], kp, vp, b["kdec"][li], b["vdec"][li], b["o"], B,
+                                            b["ranges"], b["n_ranges"], cur["path"], st - 1))
+                ops.append(PreparedLinear(b["o"].reshape(R, -1), W["wo"], LINEAR_RESIDUAL, resid=b["x"]))
+                ops.append(PreparedNorm(b["x"], W["g_mlp"], b["h"], md.eps))
+                ops.append(PreparedLinear(b["h"], W["wgu"], LINEAR_SILU_GATE, y=b["act"]))
+                ops.append(PreparedLinear(b["act"], W["wd"], LINEAR_RESIDUAL, resid=b["x"]))
+            ops.append(PreparedNorm(b["x"], job.g_final, b["hid"], md.eps))
+            ops.append(PreparedLinear(b["hid"], self.W, LINEAR_F32, yf=b["z"]))
+            ops.append(topk_lse(b["z"], self.k, b["ids"], b["lp"], b["lse"], masks=self.masks,
+                                mask_of_row=b["mask_r"] if masked else None, stop_of_row=b["stop_r"]))
+            ops.append(beam_step(S, B, self.k, self.T, st, b["stop"], b["ids"], b["lp"], cur, nxt, b["feed"]))
             steps.append(ops)
-        run["ops0"], run["steps"] = ops0, steps
+        self._ops0, self._steps = ops0, steps
 
     def run(self, stream=None):
-        """Enqueues every pass's decoding (after the job's run on the same stream)."""
-        for run in self._runs:
-            for op in run["ops0"]:
+        """Enqueues the decoding of every slot (after the job's run on the same stream)."""
+        for op in self._ops0:
+            op(stream)
+        for ops in self._steps:
+            for op in ops:
                 op(stream)
-            for ops in run["steps"]:
-                for op in ops:
-                    op(stream)
 
     def results(self) -> List[List[dict]]:
         """Per slot (in the order given): its beams, best first, as dicts
         tokens / lp / finished (host; waits for the device)."""
-        out = [None] * self.n_slots
-        for run in self._runs:
-            st = run["state"][(self.T - 1) % 2]
-            tok = st["tok"].cpu().numpy()
-            ln = st["len"].cpu().numpy()
-            fin = st["fin"].cpu().numpy()
-            sc = st["score"].cpu().numpy()
-            nb = st["nb"].cpu().numpy()
-            for j, (i, s, info) in enumerate(run["items"]):
-                beams = []
-                for b in range(int(nb[j])):
-                    r = j * self.B + b
-                    beams.append(dict(tokens=tuple(int(x) for x in tok[r, :ln[r]]), lp=float(sc[r]),
-                                      finished=bool(fin[r])))
-                out[i] = beams
+        st = self.buf["state"][(self.T - 1) % 2]
+        tok = st["tok"].cpu().numpy()
+        ln = st["len"].cpu().numpy()
+        fin = st["fin"].cpu().numpy()
+        sc = st["score"].cpu().numpy()
+        nb = st["nb"].cpu().numpy()
+        out = [None] * len(self.items)
+        for j, (i, s, info) in enumerate(self.items):
+            beams = []
+            for bb in range(int(nb[j])):
+                r = j * self.B + bb
+                beams.append(dict(tokens=tuple(int(x) for x in tok[r, :ln[r]]), lp=float(sc[r]),
+                                  finished=bool(fin[r])))
+            out[i] = beams
         return out

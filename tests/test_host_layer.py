@@ -107,6 +107,10 @@ def test_decode_entry_points_validate_before_any_hip_call():
     assert L.spb_topk_lse(ctypes.byref(T), None) == -1         # k > 16
     T.k, T.mask_of_row = 4, 256
     assert L.spb_topk_lse(ctypes.byref(T), None) == -1         # mask_of_row without masks
+    T.mask_of_row = None
+    T.workspace, T.workspace_bytes = 256, 8
+    assert L.spb_topk_lse(ctypes.byref(T), None) == -4         # workspace too small
+    assert spb.topk_workspace_bytes(4, 100) > 0
     D = spb._DecodeAttnArgs()
     D.q = D.k_pass = D.v_pass = D.k_dec = D.v_dec = D.o = D.ranges = D.n_ranges = D.path = 256
     D.rows, D.beams, D.hq, D.hkv, D.head_dim, D.t_cap, D.n_path, D.n_pass_rows = 8, 4, 4, 2, 128, 5, 5, 10
