@@ -50,7 +50,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # lm-head ridge in scored rows per W stream: the head does M flop per W byte
 HEAD_RIDGE_ROWS = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # 312.5
 HERE = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCES = ("shared_prefix_branch_amd/csrc/spb_score.hip", "shared_prefix_branch_amd/csrc/spb_launch.h")
+# the files that define the lm-head kernel and its tiling
+GEMM_SOURCES = ("shared_prefix_branch_amd/csrc/spb_score.hip", "shared_prefix_branch_amd/csrc/spb_gemm.h",
+                "shared_prefix_branch_amd/csrc/spb_dev.h", "shared_prefix_branch_amd/csrc/spb_head_layout.h")
 TRAFFIC_SUMMARY = "profiles/head_lse_kernel_news_traffic.md"
 
 

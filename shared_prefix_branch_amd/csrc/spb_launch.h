@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "spb_head_layout.h"
+
 namespace spb {
 
 struct AttnLaunch {
@@ -37,20 +39,6 @@ struct ScoreLaunch {
   int kind;                 // lm-head output kind (SPB_HEAD_*)
 };
 
-inline int n_vocab_slices(int vocab) { return (vocab + 255) / 256; }
-// bf16 planes of a gathered hidden row: three (hi, mid, lo) for the fp32 head
-inline int head_planes(int kind) { return kind == 2 ? 3 : 1; }
-
-// Scored rows per lm-head work group: n_chunks chunks of 32*mb rows (mb in
-// 1..8), the fewest chunks of at most 256 rows, each as small as possible.
-inline void head_m_layout(int M, int *n_chunks, int *mb) {
-  int n = (M + 255) / 256;
-  if (n < 1) n = 1;
-  int per = (M + n - 1) / n;
-  int b = (per + 31) / 32;
-  *n_chunks = n;
-  *mb = b < 1 ? 1 : (b > 8 ? 8 : b);
-}
 
 // Several passes' scored rows through one lm-head stream: pass i's rows
 // occupy combined rows m_off[i] .. +n_scored and its targets combined
