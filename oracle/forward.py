@@ -29,6 +29,15 @@ and after the last layer the head reads rmsnorm(x) * g_final.
     own prompt -- the pages' "the same answers" as running each question on
     its own [PyPI "Speed and scale"].
 
+fp8 linears (the pages' checkpoints are calibrated static fp8 [man page
+"spinf-serve", DESCRIPTION: fp8s]; reading: every linear layer of the stack
+quantizes its weight and its input per tensor with static scales,
+q8(t, s) = round_to_e4m3(t / s) * s, and multiplies the quantized values
+exactly; the fused q/k/v and gate/up weights share one scale each;
+attention and the lm head keep their bf16 inputs):
+
+    y = q8(x, s_x) q8(W, s_w)^T
+
 Form (i)  ``forward_input``: the model run over ordinary sequences: the
           content; content + template for each branch (keeping the template
           rows); the root path of each trie node (keeping its last row).
@@ -44,7 +53,7 @@ from typing import Iterable, List, Optional
 import numpy as np
 
 from .attention import causal_attention_tail, dense_mask
-from .numerics import to_f64
+from .numerics import round_to_e4m3, to_f64
 from .tree import Layout, LInput, root_path
 
 
@@ -59,11 +68,28 @@ class Model:
     eps: float
     layers: List[dict]
     g_final: np.ndarray
+    # per layer, with fp8 linears: weight scales s_qkv, s_o, s_gu, s_d and
+    # input scales x_qkv, x_o, x_gu, x_d; None: exact linears
+    fp8: Optional[List[dict]] = None
 
     @staticmethod
-    def from_synth(md, layers, g_final) -> "Model":
+    def from_synth(md, layers, g_final, fp8_scales=None) -> "Model":
         return Model(md.hidden, md.hq, md.hkv, md.head_dim, float(md.rope_base), float(md.eps),
-                     [{k: to_f64(v) for k, v in L.items()} for L in layers], to_f64(g_final))
+                     [{k: to_f64(v) for k, v in L.items()} for L in layers], to_f64(g_final),
+                     None if fp8_scales is None else [dict(s) for s in fp8_scales])
+
+
+def q8(t: np.ndarray, s: float) -> np.ndarray:
+    """Per-tensor e4m3 quantization with scale s, as float64 values."""
+    return round_to_e4m3(np.asarray(t, np.float64) / s) * s
+
+
+def _lin(m: Model, li: int, x: np.ndarray, w: np.ndarray, kind: str) -> np.ndarray:
+    """x W^T, with the layer's fp8 quantization of both when the model has it."""
+    if m.fp8 is None:
+        return x @ w.T
+    f = m.fp8[li]
+    return q8(x, f["x_" + kind]) @ q8(w, f["s_" + kind]).T
 
 
 def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
@@ -89,18 +115,25 @@ def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return out
 
 
-def _qkv(m: Model, L: dict, x: np.ndarray, pos: np.ndarray):
+def _qkv(m: Model, li: int, x: np.ndarray, pos: np.ndarray):
+    L = m.layers[li]
     n = x.shape[0]
     h = rms_norm(x, L["g_attn"], m.eps)
-    q = (h @ L["wq"].T).reshape(n, m.hq, m.head_dim)
-    k = (h @ L["wk"].T).reshape(n, m.hkv, m.head_dim)
-    v = (h @ L["wv"].T).reshape(n, m.hkv, m.head_dim)
+    w = np.concatenate([L["wq"], L["wk"], L["wv"]], axis=0)  # one fused linear
+    y = _lin(m, li, h, w, "qkv")
+    qd, kd = m.hq * m.head_dim, m.hkv * m.head_dim
+    q = y[:, :qd].reshape(n, m.hq, m.head_dim)
+    k = y[:, qd:qd + kd].reshape(n, m.hkv, m.head_dim)
+    v = y[:, qd + kd:].reshape(n, m.hkv, m.head_dim)
     return rope(q, pos, m.rope_base), rope(k, pos, m.rope_base), v
 
 
-def _mlp(m: Model, L: dict, x: np.ndarray) -> np.ndarray:
+def _mlp(m: Model, li: int, x: np.ndarray) -> np.ndarray:
+    L = m.layers[li]
     h = rms_norm(x, L["g_mlp"], m.eps)
-    return (silu(h @ L["wg"].T) * (h @ L["wu"].T)) @ L["wd"].T
+    F = L["wg"].shape[0]
+    gu = _lin(m, li, h, np.concatenate([L["wg"], L["wu"]], axis=0), "gu")  # one fused linear
+    return _lin(m, li, silu(gu[:, :F]) * gu[:, F:], L["wd"], "d")
 
 
 def decoder_sequence(m: Model, x0: np.ndarray) -> np.ndarray:
@@ -110,11 +143,11 @@ def decoder_sequence(m: Model, x0: np.ndarray) -> np.ndarray:
     n = x.shape[0]
     pos = np.arange(n)
     scale = 1.0 / math.sqrt(m.head_dim)
-    for L in m.layers:
-        q, k, v = _qkv(m, L, x, pos)
+    for li, L in enumerate(m.layers):
+        q, k, v = _qkv(m, li, x, pos)
         att = causal_attention_tail(q, k, v, scale).reshape(n, m.hq * m.head_dim)
-        x = x + att @ L["wo"].T
-        x = x + _mlp(m, L, x)
+        x = x + _lin(m, li, att, L["wo"], "o")
+        x = x + _mlp(m, li, x)
     return rms_norm(x, m.g_final, m.eps)
 
 
@@ -154,8 +187,8 @@ def forward_dense(m: Model, layout: Layout, x0: np.ndarray) -> np.ndarray:
     mask = dense_mask(layout)
     scale = 1.0 / math.sqrt(m.head_dim)
     g = m.hq // m.hkv
-    for L in m.layers:
-        q, k, v = _qkv(m, L, x, pos)
+    for li, L in enumerate(m.layers):
+        q, k, v = _qkv(m, li, x, pos)
         att = np.empty((n, m.hq, m.head_dim))
         for h in range(m.hq):
             s = (q[:, h, :] @ k[:, h // g, :].T) * scale
@@ -163,6 +196,6 @@ def forward_dense(m: Model, layout: Layout, x0: np.ndarray) -> np.ndarray:
             s = s - s.max(axis=1, keepdims=True)
             p = np.exp(s)
             att[:, h, :] = (p / p.sum(axis=1, keepdims=True)) @ v[:, h // g, :]
-        x = x + att.reshape(n, -1) @ L["wo"].T
-        x = x + _mlp(m, L, x)
+        x = x + _lin(m, li, att.reshape(n, -1), L["wo"], "o")
+        x = x + _mlp(m, li, x)
     return rms_norm(x, m.g_final, m.eps)

@@ -78,3 +78,16 @@ def round_to_bf16(x) -> np.ndarray:
     y = np.where(tiny, np.rint(x * 2.0 ** 133) * 2.0 ** -133, y)
     big = np.abs(y) > (2 - 2.0 ** -7) * 2.0 ** 127
     return np.where(big, np.copysign(np.inf, x), y)
+
+
+def round_to_e4m3(x) -> np.ndarray:
+    """The OCP e4m3fn value nearest to each float64 (ties to the even
+    significand), saturated to +-448, as float64.  e4m3 keeps 4 significant
+    bits: normal values 1.fff * 2**e for e in -6 .. 8 (largest 1.75 * 2**8 =
+    448), subnormal spacing 2**-9 below 2**-6."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m 2**e, 0.5 <= |m| < 1
+    y = np.ldexp(np.rint(np.ldexp(m, 4)), e - 4)
+    tiny = np.abs(x) < 2.0 ** -6
+    y = np.where(tiny, np.rint(x * 2.0 ** 9) * 2.0 ** -9, y)
+    return np.clip(y, -448.0, 448.0)

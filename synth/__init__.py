@@ -32,7 +32,7 @@ __all__ = [
     "Problem", "Dims", "Workload", "CONFIGS", "make_workload", "make_problem",
     "count_trie_nodes", "logical_inputs", "seed_for", "STREAM_INPUT",
     "STREAM_FLOOR", "STREAM_LM_HEAD", "STREAM_CALIB", "STREAM_HIDDEN",
-    "ModelDims", "model_weights", "embed_block", "embed_table",
+    "ModelDims", "model_weights", "embed_block", "embed_table", "stack_fp8_scales",
 ]
 
 STREAM_INPUT, STREAM_FLOOR, STREAM_LM_HEAD, STREAM_CALIB, STREAM_HIDDEN = 0, 1, 2, 3, 4
@@ -499,3 +499,24 @@ def embed_table(md: ModelDims, vocab: int, seed: int, device="cpu"):
     g = torch.Generator(device=device)
     g.manual_seed(seed_for(seed, STREAM_TOKEN_EMBED, 0))
     return torch.randn((vocab, md.hidden), generator=g, device=device).to(torch.bfloat16)
+
+
+# static input scales of the fp8 linears: rmsnorm outputs (gains up to 1.5,
+# tails to about 5 sigma), attention outputs (convex mixes of v rows) and the
+# gated MLP product (heavier tails); values beyond saturate at +-448 * s
+FP8_INPUT_AMAX = {"qkv": 8.0, "o": 4.0, "gu": 8.0, "d": 16.0}
+
+
+def stack_fp8_scales(layers):
+    """Per layer the static e4m3 scales of the fp8 linears: s_* = amax(W) / 448
+    over each (fused) weight, x_* = FP8_INPUT_AMAX / 448 for its input."""
+    torch = _torch()
+    out = []
+    for L in layers:
+        def amax(*ws):
+            return max(float(w.float().abs().max()) for w in ws)
+        s = dict(s_qkv=amax(L["wq"], L["wk"], L["wv"]) / 448.0, s_o=amax(L["wo"]) / 448.0,
+                 s_gu=amax(L["wg"], L["wu"]) / 448.0, s_d=amax(L["wd"]) / 448.0)
+        s.update({"x_" + k: v / 448.0 for k, v in FP8_INPUT_AMAX.items()})
+        out.append(s)
+    return out

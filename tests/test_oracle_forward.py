@@ -218,3 +218,69 @@ def test_question_rows_equal_the_question_asked_alone():
         list(range(b.node_row0 - lo, b.node_row0 - lo + len(b.trie.prefixes)))
     got = OF.forward_input(m, la, la.inputs[0], x0[lo:hi][rows])
     assert np.allclose(got, full[rows], atol=1e-12)
+
+
+def test_round_to_e4m3_against_the_table_and_torch():
+    from oracle import numerics as ON
+    grid = np.unique(ON.E4M3_TABLE[~np.isnan(ON.E4M3_TABLE)])
+    # every representable value maps to itself
+    assert np.array_equal(ON.round_to_e4m3(grid), grid)
+    # midpoints between neighbours go to the neighbour with the even code
+    pos = grid[grid >= 0]
+    mids = (pos[:-1] + pos[1:]) / 2
+    codes = {float(v): b for b, v in enumerate(ON.E4M3_TABLE) if b < 128 and not np.isnan(v)}
+    for lo, hi, mid in zip(pos[:-1], pos[1:], mids):
+        want = lo if codes[float(lo)] % 2 == 0 else hi
+        assert ON.round_to_e4m3(mid) == want
+    assert ON.round_to_e4m3(1000.0) == 448.0 and ON.round_to_e4m3(-470.0) == -448.0
+    # torch's cast (saturated first) on random values across the range
+    x = np.random.default_rng(0).normal(size=20000) * np.exp2(np.random.default_rng(1).uniform(-12, 10, 20000))
+    ref = torch.from_numpy(np.clip(x, -448, 448)).float().to(torch.float8_e4m3fn).double().numpy()
+    xf = x.astype(np.float32).astype(np.float64)  # torch rounds the f32 value
+    assert np.array_equal(ON.round_to_e4m3(np.clip(xf, -448, 448)), ref)
+
+
+def test_fp8_linears_quantize_weights_and_inputs_per_tensor():
+    # q8 by hand: 1.0625 / 1 is the midpoint of 1 and 1.125 -> 1 (even code);
+    # with scale 2, 3.3 -> 1.65 -> 1.625 -> 3.25
+    assert OF.q8(np.array([1.0625]), 1.0)[0] == 1.0
+    assert OF.q8(np.array([3.3]), 2.0)[0] == 3.25
+    assert OF.q8(np.array([5000.0]), 1.0)[0] == 448.0
+    # a linear whose weight and input already sit on the scaled e4m3 grid is exact
+    m = _model(seed=3)
+    rng = np.random.default_rng(4)
+    sx, sw = 0.5, 0.01
+    x = OF.q8(rng.normal(size=(5, 32)), sx)
+    w = OF.q8(rng.normal(size=(16, 32)) * 0.1, sw)
+    m.fp8 = [dict(x_o=sx, s_o=sw)] * 2
+    assert np.array_equal(OF._lin(m, 0, x, w, "o"), x @ w.T)
+    # off the grid, both operands are rounded: the product moves
+    x2, w2 = rng.normal(size=(5, 32)), rng.normal(size=(16, 32)) * 0.1
+    y = OF._lin(m, 0, x2, w2, "o")
+    assert not np.allclose(y, x2 @ w2.T, atol=1e-6)
+    assert np.allclose(y, OF.q8(x2, sx) @ OF.q8(w2, sw).T, atol=1e-12)
+
+
+def _fp8_scales(m, sx=(8 / 448, 4 / 448, 8 / 448, 16 / 448)):
+    out = []
+    for L in m.layers:
+        out.append(dict(s_qkv=np.abs(np.concatenate([L["wq"], L["wk"], L["wv"]])).max() / 448,
+                        s_o=np.abs(L["wo"]).max() / 448, s_gu=np.abs(np.concatenate([L["wg"], L["wu"]])).max() / 448,
+                        s_d=np.abs(L["wd"]).max() / 448, x_qkv=sx[0], x_o=sx[1], x_gu=sx[2], x_d=sx[3]))
+    return out
+
+
+def test_fp8_stack_per_sequence_equals_dense_and_stays_near_exact():
+    prob = synth.make_problem("random_shared", 13, vocab=16, n_inputs=2, n_questions=5, max_content=6,
+                              max_lead=4, tail_vocab=3, max_options=3, max_option_tokens=3)
+    m = _model(seed=13)
+    lay, x0 = _layout_and_x0(prob, 13)
+    exact = OF.forward_dense(m, lay, x0)
+    m.fp8 = _fp8_scales(m)
+    dense = OF.forward_dense(m, lay, x0)
+    for li in lay.inputs:
+        lo = li.first_row
+        hi = lo + int((lay.row_input == lay.row_input[lo]).sum())
+        assert np.allclose(OF.forward_input(m, lay, li, x0[lo:hi]), dense[lo:hi], atol=1e-10)
+    rel = np.linalg.norm(dense - exact, axis=1) / np.linalg.norm(exact, axis=1)
+    assert 0 < rel.max() < 0.2   # e4m3 keeps 4 significant bits
