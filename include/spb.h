@@ -357,8 +357,27 @@ typedef struct {
   const float *rope_table;
   int32_t n_pos;
   void *gemm_event_begin, *gemm_event_end;
+  /* fp8 = 1: x and W are OCP e4m3 bytes (spb_quantize_e4m3) with per-tensor
+   * scales, multiplied on v_mfma_scale_f32_32x32x64_f8f6f4, acc scaled by
+   * scale_x * scale_w before the epilogue; k % 128 == 0.  0: bf16 operands. */
+  int32_t fp8;
+  float scale_x, scale_w;
 } spb_linear_args;
 spb_status spb_linear(const spb_linear_args *args, void *stream);
+
+/* dst[i] = e4m3(src[i] / scale) for i < n: the nearest OCP e4m3fn value (ties
+ * to the even significand), saturated to +-448 -- the per-tensor static
+ * quantization of the pages' fp8s checkpoints [man page "spinf-serve",
+ * DESCRIPTION].  src: f32 or bf16 (src_dtype SPB_F32 / SPB_BF16), dst: bytes;
+ * device memory, 16-byte aligned (src) and 8-byte aligned (dst). */
+typedef struct {
+  const void *src;
+  int32_t src_dtype;
+  void *dst;
+  int64_t n;
+  float scale;
+} spb_quantize_args;
+spb_status spb_quantize_e4m3(const spb_quantize_args *args, void *stream);
 
 /* --------------------------------------------------------- extraction slots
  * A slot ({*} text, {n} a number, {$} an amount) is decoded from the same

@@ -22,6 +22,7 @@ __all__ = [
     "HEAD_F32OUT", "HEAD_BF16", "HEAD_FP32",
     "LINEAR_BF16", "LINEAR_RESIDUAL", "LINEAR_SILU_GATE", "LINEAR_QKV_ROPE", "LINEAR_F32", "rope_table",
     "PreparedNorm", "gather_rows", "topk_lse", "topk_workspace_bytes", "decode_attention", "beam_step",
+    "quantize_e4m3",
     "PreparedLinear", "rmsnorm", "linear",
     "EXPORTED_SYMBOLS",
 ]
@@ -41,7 +42,7 @@ EXPORTED_SYMBOLS = [
     "spb_score_batch_workspace_bytes", "spb_score_options_batch",
     "spb_score_finalize", "spb_plan_positions", "spb_rope_table", "spb_rmsnorm", "spb_linear",
     "spb_plan_slot", "spb_gather_rows", "spb_topk_workspace_bytes", "spb_topk_lse", "spb_decode_attention",
-    "spb_beam_step",
+    "spb_beam_step", "spb_quantize_e4m3",
 ]
 
 
@@ -107,7 +108,13 @@ class _LinearArgs(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k_out", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("pos", ctypes.c_void_p), ("rope_table", ctypes.c_void_p), ("n_pos", ctypes.c_int32),
-                ("gemm_event_begin", ctypes.c_void_p), ("gemm_event_end", ctypes.c_void_p)]
+                ("gemm_event_begin", ctypes.c_void_p), ("gemm_event_end", ctypes.c_void_p),
+                ("fp8", ctypes.c_int32), ("scale_x", ctypes.c_float), ("scale_w", ctypes.c_float)]
+
+
+class _QuantArgs(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("src_dtype", ctypes.c_int32), ("dst", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("scale", ctypes.c_float)]
 
 
 class _SlotInfo(ctypes.Structure):
@@ -191,6 +198,7 @@ def lib() -> ctypes.CDLL:
         L.spb_rmsnorm.argtypes = [ctypes.POINTER(_NormArgs), ctypes.c_void_p]
         L.spb_linear.argtypes = [ctypes.POINTER(_LinearArgs), ctypes.c_void_p]
         L.spb_plan_slot.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(_SlotInfo)]
+        L.spb_quantize_e4m3.argtypes = [ctypes.POINTER(_QuantArgs), ctypes.c_void_p]
         L.spb_gather_rows.argtypes = [ctypes.POINTER(_GatherArgs), ctypes.c_void_p]
         L.spb_topk_lse.argtypes = [ctypes.POINTER(_TopkArgs), ctypes.c_void_p]
         L.spb_topk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
@@ -557,11 +565,15 @@ class PreparedLinear:
     rope (float32 [n_pos, d/2, 2] device)."""
 
     def __init__(self, x, w, mode: int, y=None, resid=None, yf=None, q=None, k_out=None, v=None, hq: int = 0, hkv: int = 0,
-                 head_dim: int = 0, pos=None, rope=None):
+                 head_dim: int = 0, pos=None, rope=None, fp8_scales=None):
+        """fp8_scales: (s_x, s_w) with x and w e4m3 bytes (uint8), else bf16 operands."""
         import torch
         A = _LinearArgs()
-        A.x = _dev(x, "x", torch.bfloat16)
-        A.w = _dev(w, "w", torch.bfloat16)
+        op_dt = torch.uint8 if fp8_scales is not None else torch.bfloat16
+        A.x = _dev(x, "x", op_dt)
+        A.w = _dev(w, "w", op_dt)
+        if fp8_scales is not None:
+            A.fp8, A.scale_x, A.scale_w = 1, float(fp8_scales[0]), float(fp8_scales[1])
         A.m = int(x.shape[0])
         A.n = int(w.shape[0])
         A.k = int(x.shape[1])
@@ -699,3 +711,17 @@ def beam_step(n_slots: int, beams: int, k: int, t_cap: int, step: int, stop, ids
         setattr(A, n + "_in", _p(state_in[n]) if state_in is not None else None)
         setattr(A, n + "_out", _p(state_out[n]))
     return PreparedCall("spb_beam_step", A, (stop, ids, lp, state_in, state_out, feed))
+
+
+def quantize_e4m3(src, dst, scale: float) -> PreparedCall:
+    """dst (uint8, same number of elements) = e4m3(src / scale); src f32 or bf16."""
+    import torch
+    A = _QuantArgs()
+    A.src = src.data_ptr()
+    A.src_dtype = F32 if src.dtype == torch.float32 else BF16
+    A.dst = _dev(dst, "dst", torch.uint8)
+    A.n = int(src.numel())
+    if int(dst.numel()) != A.n:
+        raise SpbError(-1, "src and dst sizes differ")
+    A.scale = float(scale)
+    return PreparedCall("spb_quantize_e4m3", A, (src, dst))

@@ -1,0 +1,133 @@
+// spb_gemm8.h -- the K loop of spb_gemm.h on OCP e4m3 operands (gfx950).
+//
+// Same tile, rings, swizzle and copy schedule as the bf16 loop: a stage is
+// still one 128-byte line per tile row, now 128 K elements, and each stage is
+// two K steps of v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, f32
+// accumulation, scale operands neutral).  Lane (qi, half) of a K step holds
+// the 32 bytes 32 * half .. +32 of its row's 64-element step, i.e. the
+// 16-byte chunks 4 ks + 2 half and 4 ks + 2 half + 1 of the stage.  The K
+// order of every result element is fixed, as in the bf16 loop.
+#pragma once
+
+#include "spb_gemm.h"
+
+namespace spb {
+namespace gemm {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kKT8 = 128;  // e4m3 K elements per stage (128-byte rows)
+
+template <int MB>
+struct Frags8 {
+  i32x8 a[2];
+  i32x8 b[MB];
+};
+
+__device__ __attribute__((always_inline)) inline i32x8 frag8(const u32x4 *T, int row, int c) {
+  const u32x4 u0 = T[swz(row, c)], u1 = T[swz(row, c + 1)];
+  return i32x8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+}
+
+template <int MB>
+__device__ __attribute__((always_inline)) inline void frags8(Frags8<MB> &f, const u32x4 *Wb, const u32x4 *Hb, int ks,
+                                                             int wave, int qi, int half) {
+  const int c = ks * 4 + half * 2;
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb) f.a[vb] = frag8(Wb, wave * 64 + vb * 32 + qi, c);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) f.b[mb] = frag8(Hb, mb * 32 + qi, c);
+}
+
+template <int MB>
+__device__ __attribute__((always_inline)) inline void mfma8(f32x16 (&acc)[2][MB], const Frags8<MB> &f) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+      acc[vb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0, 0, 0, 0);
+}
+
+// Byte offsets of the tile copies for 1-byte elements (see tile_offsets).
+template <int MB, typename WRow, typename XRow>
+__device__ __attribute__((always_inline)) inline void tile_offsets8(uint32_t (&woff)[8], uint32_t (&hoff)[MB],
+                                                                    WRow w_row, XRow x_row, int ldw, int ldx,
+                                                                    int wave, int lane) {
+  const int dr = lane >> 3;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = wave * 64 + i * 8 + dr;
+    const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    woff[i] = (uint32_t)w_row(r) * (uint32_t)ldw + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = (wave * MB + i) * 8 + dr;
+    const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    hoff[i] = (uint32_t)x_row(r) * (uint32_t)ldx + c * 16;
+  }
+}
+
+// acc += W tile . X tile^T over S stages of 128 e4m3 K elements; ends with
+// every copy landed and the LDS ring free.
+template <int MB>
+__device__ __attribute__((always_inline)) inline void k_loop8(f32x16 (&acc)[2][MB], char *lds, const uint8_t *W,
+                                                              const uint8_t *X, const uint32_t (&woff)[8],
+                                                              const uint32_t (&hoff)[MB], int S, int wave, int qi,
+                                                              int half) {
+  using T = Tile<MB>;
+  char *const wring = lds;
+  char *const hring = lds + T::RW * T::WBYTES;
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  auto issue_w = [&](int stage, int sl) {
+    const uint32_t kb = (uint32_t)stage * 128;
+    const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
+#pragma unroll
+    for (int i = 0; i < T::NW; ++i)
+      dma16(W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 8) * 128));
+  };
+  auto issue_h = [&](int stage, int sl) {
+    const uint32_t kb = (uint32_t)stage * 128;
+    const uint32_t s0 = lds0 + T::RW * T::WBYTES + (uint32_t)sl * T::HBYTES;
+#pragma unroll
+    for (int i = 0; i < T::NH; ++i)
+      dma16(X, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
+  };
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x16{0.f};
+
+  const int last = S - 1;
+  // the copy schedule of k_loop: trip s issues X(s+1) then W(s+2)
+  issue_h(0, 0);
+  issue_w(0, 0);
+  issue_w(min(1, last), 1);
+  wait_vmcnt<T::NW>();
+  lds_barrier();
+  int sw = 0, sh = 0;
+  for (int s = 0; s < S; ++s) {
+    const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
+    const u32x4 *Hb = (const u32x4 *)(hring + sh * T::HBYTES);
+    Frags8<MB> f0, f1;
+    frags8<MB>(f0, Wb, Hb, 0, wave, qi, half);
+    const int sw2 = sw == 0 ? 2 : sw - 1;
+    issue_h(min(s + 1, last), sh ^ 1);
+    issue_w(min(s + 2, last), sw2);
+    frags8<MB>(f1, Wb, Hb, 1, wave, qi, half);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma8<MB>(acc, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma8<MB>(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<T::NW>();
+    lds_barrier();
+    sw = sw == 2 ? 0 : sw + 1;
+    sh ^= 1;
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+}
+
+}  // namespace gemm
+}  // namespace spb

@@ -1486,8 +1486,12 @@ spb_status spb_linear(const spb_linear_args *a, void *stream) {
   if (a->mode < SPB_LINEAR_BF16 || a->mode > SPB_LINEAR_F32) return fail(SPB_ERR_ARG, "mode %d", a->mode);
   if (a->m < 0 || a->m > 0x7FFFFFFF) return fail(SPB_ERR_ARG, "m %lld", (long long)a->m);
   if (a->k < 64 || a->k % 64) return fail(SPB_ERR_ARG, "k %d must be a positive multiple of 64", a->k);
+  if (a->fp8 && a->k % 128) return fail(SPB_ERR_ARG, "fp8 k %d must be a multiple of 128", a->k);
+  if (a->fp8 && (!(a->scale_x > 0.f) || !(a->scale_w > 0.f) || !std::isfinite(a->scale_x * a->scale_w)))
+    return fail(SPB_ERR_ARG, "fp8 scales must be finite and > 0");
   if (a->n < 8 || a->n % 8) return fail(SPB_ERR_ARG, "n %d must be a positive multiple of 8", a->n);
-  if ((uint64_t)a->m * (uint64_t)a->k * 2u >= (1ull << 32) || (uint64_t)a->n * (uint64_t)a->k * 2u >= (1ull << 32))
+  const uint64_t es = a->fp8 ? 1u : 2u;  // bytes per operand element
+  if ((uint64_t)a->m * (uint64_t)a->k * es >= (1ull << 32) || (uint64_t)a->n * (uint64_t)a->k * es >= (1ull << 32))
     return fail(SPB_ERR_LIMIT, "x (%lld x %d) and W (%d x %d) must each stay under 4 GiB", (long long)a->m, a->k,
                 a->n, a->k);
   if (a->m == 0) return ok();
@@ -1538,8 +1542,31 @@ spb_status spb_linear(const spb_linear_args *a, void *stream) {
   }
   L.ev_begin = a->gemm_event_begin;
   L.ev_end = a->gemm_event_end;
+  L.fp8 = a->fp8 ? 1 : 0;
+  L.scale = a->fp8 ? a->scale_x * a->scale_w : 1.f;
   int e = launch_linear(L, stream);
   if (e) return fail(SPB_ERR_HIP, "linear launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_quantize_e4m3(const spb_quantize_args *a, void *stream) {
+  if (!a) return fail(SPB_ERR_ARG, "args is NULL");
+  if (a->n < 0) return fail(SPB_ERR_ARG, "n %lld", (long long)a->n);
+  if (a->src_dtype != SPB_F32 && a->src_dtype != SPB_BF16) return fail(SPB_ERR_DTYPE, "src_dtype %d", a->src_dtype);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale)) return fail(SPB_ERR_ARG, "scale must be finite and > 0");
+  if (a->n == 0) return ok();
+  if (!a->src || !a->dst || misaligned16(a->src) || (uintptr_t)a->dst % 8)
+    return fail(SPB_ERR_ARG, "src (16-byte aligned) and dst (8-byte aligned) required");
+  QuantLaunch L{};
+  if (a->src_dtype == SPB_F32)
+    L.src_f32 = (const float *)a->src;
+  else
+    L.src_bf16 = (const uint16_t *)a->src;
+  L.dst = (uint8_t *)a->dst;
+  L.n = a->n;
+  L.inv_scale = 1.0f / a->scale;
+  int e = launch_quantize_e4m3(L, stream);
+  if (e) return fail(SPB_ERR_HIP, "quantize launch: %s", hip_error_string(e));
   return ok();
 }
 

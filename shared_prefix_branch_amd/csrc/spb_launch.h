@@ -87,7 +87,18 @@ struct LinearLaunch {
   const float *rope;       // QKV_ROPE: [n_pos][d/2] (cos, sin) pairs
   int n_pos;
   void *ev_begin, *ev_end; // optional hipEvent_t around the kernel
+  int fp8;                 // x and w are e4m3 bytes; the products are scaled by `scale`
+  float scale;             // s_x * s_w
 };
+
+struct QuantLaunch {       // dst = e4m3(src * inv_scale)
+  const float *src_f32;    // one of the two
+  const uint16_t *src_bf16;
+  uint8_t *dst;
+  long long n;
+  float inv_scale;
+};
+int launch_quantize_e4m3(const QuantLaunch &a, void *stream);
 
 int launch_rmsnorm(const NormLaunch &a, void *stream);
 

@@ -29,6 +29,7 @@
 #include "spb_launch.h"
 #include "spb_dev.h"
 #include "spb_gemm.h"
+#include "spb_gemm8.h"
 #include "../../include/spb.h"
 
 #include <hip/hip_runtime.h>
@@ -98,7 +99,7 @@ struct LinParams {
 // XCD (work groups are dealt round-robin to the XCDs, block b to XCD b % 8).
 // So every XCD gets the same number of tiles, and the 32 work groups an XCD
 // runs at once cover 8 token chunks x 4 W tiles, sharing both through its L2.
-template <int MODE>
+template <int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinParams P) {
   using T = gemm::Tile<kMB>;
   constexpr int TM = T::TM;
@@ -121,11 +122,22 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinParams P) {
   const int m0 = mchunk * TM;
 
   uint32_t woff[8], hoff[kMB];
-  gemm::tile_offsets<kMB>(
-      woff, hoff, [&](int r) { return w0 + r < p.n ? w0 + r : p.n - 1; },
-      [&](int r) { return m0 + r < p.m ? m0 + r : p.m - 1; }, p.k, p.k, wave, lane);
   f32x16 acc[2][kMB];
-  gemm::k_loop<kMB>(acc, lds, p.w, p.x, woff, hoff, p.k / kKT, p.k / kKT, wave, qi, half);
+  auto w_row = [&](int r) { return w0 + r < p.n ? w0 + r : p.n - 1; };
+  auto x_row = [&](int r) { return m0 + r < p.m ? m0 + r : p.m - 1; };
+  if constexpr (FP8) {
+    // e4m3 operands; the products are scaled back by s_x * s_w
+    gemm::tile_offsets8<kMB>(woff, hoff, w_row, x_row, p.k, p.k, wave, lane);
+    gemm::k_loop8<kMB>(acc, lds, (const uint8_t *)p.w, (const uint8_t *)p.x, woff, hoff, p.k / gemm::kKT8, wave, qi,
+                       half);
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) acc[vb][mb] *= p.scale;
+  } else {
+    gemm::tile_offsets<kMB>(woff, hoff, w_row, x_row, p.k, p.k, wave, lane);
+    gemm::k_loop<kMB>(acc, lds, p.w, p.x, woff, hoff, p.k / kKT, p.k / kKT, wave, qi, half);
+  }
 
   // ---- epilogue: f32 staging of up to 128 tokens at a time, [token][feature]
   constexpr bool GLU = MODE == SPB_LINEAR_SILU_GATE;
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_kernel(LinParams P) {
   }
 }
 
-template <int MODE>
+template <int MODE, bool FP8>
 int launch_linear_mode(const LinearLaunch &a, hipStream_t s) {
   LinParams P;
   P.a = a;
@@ -230,7 +242,7 @@ int launch_linear_mode(const LinearLaunch &a, hipStream_t s) {
     hipError_t e = hipEventRecord((hipEvent_t)a.ev_begin, s);
     if (e != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL((linear_kernel<MODE>), dim3((unsigned)blocks), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL((linear_kernel<MODE, FP8>), dim3((unsigned)blocks), dim3(kThreads), 0, s, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (a.ev_end) return (int)hipEventRecord((hipEvent_t)a.ev_end, s);
@@ -247,17 +259,91 @@ int launch_rmsnorm(const NormLaunch &a, void *stream) {
   return (int)hipGetLastError();
 }
 
+namespace {
+
+template <bool FP8>
+int launch_linear_t(const LinearLaunch &a, hipStream_t s) {
+  switch (a.mode) {
+    case SPB_LINEAR_BF16: return launch_linear_mode<SPB_LINEAR_BF16, FP8>(a, s);
+    case SPB_LINEAR_RESIDUAL: return launch_linear_mode<SPB_LINEAR_RESIDUAL, FP8>(a, s);
+    case SPB_LINEAR_SILU_GATE: return launch_linear_mode<SPB_LINEAR_SILU_GATE, FP8>(a, s);
+    case SPB_LINEAR_QKV_ROPE: return launch_linear_mode<SPB_LINEAR_QKV_ROPE, FP8>(a, s);
+    case SPB_LINEAR_F32: return launch_linear_mode<SPB_LINEAR_F32, FP8>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------- e4m3 quantize
+
+// OCP e4m3fn code of v (finite): the nearest value, ties to the even
+// significand, saturated to +-448.
+__device__ inline uint32_t f32_to_e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  const float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9 (8 steps reach 2^-6, code 8)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    int e;
+    const float m = frexpf(a, &e);        // a = m 2^e, 0.5 <= m < 1
+    float q = __builtin_rintf(m * 16.0f);  // 8 .. 16: 1.fff with 3 fraction bits
+    int E = e - 1;
+    if (q == 16.0f) {
+      q = 8.0f;
+      ++E;
+    }
+    code = ((uint32_t)(E + 7) << 3) | ((uint32_t)q - 8u);
+  }
+  return sign | code;
+}
+
+// dst[i] = e4m3(src[i] * inv_scale), 8 elements per thread.
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(QuantLaunch a) {
+  const long long i0 = ((long long)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= a.n) return;
+  if (i0 + 8 <= a.n) {
+    float v[8];
+    if (a.src_f32) {
+      const float4 u0 = *(const float4 *)(a.src_f32 + i0), u1 = *(const float4 *)(a.src_f32 + i0 + 4);
+      v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w; v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+    } else {
+      const u32x4 u = *(const u32x4 *)(a.src_bf16 + i0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf2f(w[j] & 0xFFFFu);
+        v[2 * j + 1] = bf2f(w[j] >> 16);
+      }
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= f32_to_e4m3(v[j] * a.inv_scale) << (8 * j);
+      hi |= f32_to_e4m3(v[4 + j] * a.inv_scale) << (8 * j);
+    }
+    *(u32x2 *)(a.dst + i0) = u32x2{lo, hi};
+  } else {
+    for (long long i = i0; i < a.n; ++i) {
+      const float v = a.src_f32 ? a.src_f32[i] : bf2f(a.src_bf16[i]);
+      a.dst[i] = (uint8_t)f32_to_e4m3(v * a.inv_scale);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_quantize_e4m3(const QuantLaunch &a, void *stream) {
+  if (a.n == 0) return 0;
+  const long long blocks = (a.n + 2047) / 2048;
+  if (blocks > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
 int launch_linear(const LinearLaunch &a, void *stream) {
   if (a.m == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
-  switch (a.mode) {
-    case SPB_LINEAR_BF16: return launch_linear_mode<SPB_LINEAR_BF16>(a, s);
-    case SPB_LINEAR_RESIDUAL: return launch_linear_mode<SPB_LINEAR_RESIDUAL>(a, s);
-    case SPB_LINEAR_SILU_GATE: return launch_linear_mode<SPB_LINEAR_SILU_GATE>(a, s);
-    case SPB_LINEAR_QKV_ROPE: return launch_linear_mode<SPB_LINEAR_QKV_ROPE>(a, s);
-    case SPB_LINEAR_F32: return launch_linear_mode<SPB_LINEAR_F32>(a, s);
-  }
-  return (int)hipErrorInvalidValue;
+  return a.fp8 ? launch_linear_t<true>(a, s) : launch_linear_t<false>(a, s);
 }
 
 }  // namespace spb

@@ -15,8 +15,11 @@ metadata upload:
                 x += a Wd^T                                    spb_linear (RESIDUAL)
     hidden = rmsnorm(x) * g_final                               spb_rmsnorm
 
-then the lm head and the floor join as for ``Job``.  Every step runs in
-libspb; this module only lays out buffers and orders the calls.
+then the lm head and the floor join as for ``Job``.  With ``fp8_scales``
+the four linears run on e4m3 operands: the weights are quantized once at
+load, each input right before its linear (spb_quantize_e4m3), with static
+per-tensor scales.  Every step runs in libspb; this module only lays out
+buffers and orders the calls.
 """
 from __future__ import annotations
 
@@ -25,9 +28,16 @@ from typing import List, Optional
 import numpy as np
 
 from . import (LINEAR_F32, LINEAR_QKV_ROPE, LINEAR_RESIDUAL, LINEAR_SILU_GATE, MAX_SLOT_RANGES, Plan,
-               PreparedAttention, PreparedLinear, PreparedNorm, beam_step, decode_attention, gather_rows, rope_table,
-               topk_lse)
+               PreparedAttention, PreparedLinear, PreparedNorm, beam_step, decode_attention, gather_rows,
+               quantize_e4m3, rope_table, topk_lse)
 from .driver import Job, PassBuffers
+
+
+class _Quant:
+    """An e4m3 quantization step of ForwardJob's op list (marshalled once)."""
+
+    def __init__(self, src, dst, scale):
+        self.call = quantize_e4m3(src, dst, scale)
 
 
 def gate_up_rows(wg, wu):
@@ -47,7 +57,8 @@ class ForwardJob(Job):
     rotary table covers (content + template + option depth)."""
 
     def __init__(self, plan: Plan, md, layers: List[dict], g_final, vocab: int, device="cuda",
-                 batch_head: bool = False, lm_head_kind: int = 0, n_pos: int = 8192, keep_kv: bool = False):
+                 batch_head: bool = False, lm_head_kind: int = 0, n_pos: int = 8192, keep_kv: bool = False,
+                 fp8_scales: Optional[List[dict]] = None):
         import torch
         super().__init__(plan, md.hq, md.hkv, md.head_dim, md.hidden, vocab, torch.bfloat16, torch.bfloat16,
                          torch.bfloat16, device=device, batch_head=batch_head, lm_head_kind=lm_head_kind)
@@ -61,6 +72,15 @@ class ForwardJob(Job):
                 wd=L["wd"].to(device).contiguous(),
                 g_attn=L["g_attn"].to(device).contiguous(), g_mlp=L["g_mlp"].to(device).contiguous()))
         self.g_final = g_final.to(device).contiguous()
+        self.fp8 = fp8_scales
+        if fp8_scales is not None:
+            # weights to e4m3 once, with their per-tensor scales
+            for W, s in zip(self.W, fp8_scales):
+                for name, key in (("wqkv", "qkv"), ("wo", "o"), ("wgu", "gu"), ("wd", "d")):
+                    q = torch.empty(W[name].shape, dtype=torch.uint8, device=device)
+                    quantize_e4m3(W[name], q, s["s_" + key])()
+                    W[name + "8"] = q
+                torch.cuda.synchronize()
         self.rope = torch.from_numpy(rope_table(n_pos, md.head_dim, md.rope_base)).to(device)
         self.n_pos = int(n_pos)
         self.lin_marks = None  # optional: per pass, per layer, 4 (begin, end) event pairs
@@ -75,6 +95,10 @@ class ForwardJob(Job):
         buf.x = t.empty((n, md.hidden), dtype=t.float32, device=self.device)
         buf.h = t.empty((n, md.hidden), dtype=t.bfloat16, device=self.device)
         buf.act = t.empty((n, md.ffn), dtype=t.bfloat16, device=self.device)
+        if self.fp8 is not None:  # e4m3 copies of the linears' inputs
+            buf.h8 = t.empty((n, md.hidden), dtype=t.uint8, device=self.device)
+            buf.o8 = t.empty((n, md.hq * md.head_dim), dtype=t.uint8, device=self.device)
+            buf.a8 = t.empty((n, md.ffn), dtype=t.uint8, device=self.device)
         buf.kv = [(buf.k, buf.v)]
         if self.keep_kv:
             # every layer's K/V, all passes in one buffer per layer (slot decoding
@@ -126,17 +150,37 @@ class ForwardJob(Job):
                 o2 = buf.o.reshape(buf.o.shape[0], -1)[:n]
                 for li, W in enumerate(self.W):
                     kk, vv = buf.kv[li % len(buf.kv)]
+                    lin_in = self._lin_inputs(buf, li, n, ops)
                     ops.append(PreparedNorm(x, W["g_attn"], h, md.eps))
-                    ops.append(PreparedLinear(h, W["wqkv"], LINEAR_QKV_ROPE, q=buf.q[:n], k_out=kk[:n],
+                    xin, wq, sc = lin_in("qkv", h, W)
+                    ops.append(PreparedLinear(xin, wq, LINEAR_QKV_ROPE, q=buf.q[:n], k_out=kk[:n],
                                               v=vv[:n], hq=md.hq, hkv=md.hkv, head_dim=md.head_dim,
-                                              pos=buf.pos[:n], rope=self.rope))
+                                              pos=buf.pos[:n], rope=self.rope, fp8_scales=sc))
                     ops.append(PreparedAttention(k, buf.meta, buf.q, kk, vv, buf.o))
-                    ops.append(PreparedLinear(o2, W["wo"], LINEAR_RESIDUAL, resid=x))
+                    xin, wq, sc = lin_in("o", o2, W)
+                    ops.append(PreparedLinear(xin, wq, LINEAR_RESIDUAL, resid=x, fp8_scales=sc))
                     ops.append(PreparedNorm(x, W["g_mlp"], h, md.eps))
-                    ops.append(PreparedLinear(h, W["wgu"], LINEAR_SILU_GATE, y=buf.act[:n]))
-                    ops.append(PreparedLinear(buf.act[:n], W["wd"], LINEAR_RESIDUAL, resid=x))
+                    xin, wq, sc = lin_in("gu", h, W)
+                    ops.append(PreparedLinear(xin, wq, LINEAR_SILU_GATE, y=buf.act[:n], fp8_scales=sc))
+                    xin, wq, sc = lin_in("d", buf.act[:n], W)
+                    ops.append(PreparedLinear(xin, wq, LINEAR_RESIDUAL, resid=x, fp8_scales=sc))
                 ops.append(PreparedNorm(x, self.g_final, buf.hidden[:n], md.eps))
             self._ops.append(ops)
+
+    def _lin_inputs(self, buf, li: int, n: int, ops: list):
+        """For a linear of layer li: (its input operand, its weight, fp8 scales
+        or None); with fp8 it first appends the quantization of the input."""
+        names = {"qkv": "wqkv", "o": "wo", "gu": "wgu", "d": "wd"}
+        dst = {"qkv": "h8", "o": "o8", "gu": "h8", "d": "a8"}
+
+        def f(kind, x, W):
+            if self.fp8 is None:
+                return x, W[names[kind]], None
+            s = self.fp8[li]
+            xq = getattr(buf, dst[kind])[:n]
+            ops.append(_Quant(x, xq, s["x_" + kind]))
+            return xq, W[names[kind] + "8"], (s["x_" + kind], s["s_" + kind])
+        return f
 
     def _forward(self, k: int, plan: Plan, stream):
         buf = self.passes[k]
@@ -149,6 +193,8 @@ class ForwardJob(Job):
         for op in self._ops[k]:
             if isinstance(op, PreparedAttention):
                 op(plan, stream)
+            elif isinstance(op, _Quant):
+                op.call(stream)
             elif isinstance(op, PreparedLinear):
                 op(stream, None if marks is None else marks[li])
                 li += 1
@@ -187,6 +233,8 @@ class SlotDecoder:
         t = torch
         if not job.keep_kv:
             raise ValueError("slot decoding needs a ForwardJob built with keep_kv=True")
+        if job.fp8 is not None:
+            raise ValueError("slot decoding runs the bf16 stack")
         self.job, self.embed, self.W = job, embed, lm_head
         self.B, self.T, self.k = int(beams), int(max_tokens), int(beams)
         self.masks = masks

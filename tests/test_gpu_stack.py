@@ -131,10 +131,11 @@ def test_rmsnorm():
 class StackCase(Case):
     """A Case whose hidden states come from the decoder stack."""
 
-    def __init__(self, wl, md, budget, inputs=None, seed=31, **kw):
+    def __init__(self, wl, md, budget, inputs=None, seed=31, fp8=False, **kw):
         super().__init__(wl, budget, inputs=inputs, **kw)
         self.md = md
         self.layers, self.g_final = synth.model_weights(md, seed)
+        self.fp8 = synth.stack_fp8_scales(self.layers) if fp8 else None
 
     def block(self, ident):
         if ident not in self._blocks:
@@ -144,7 +145,8 @@ class StackCase(Case):
     def run(self, W):
         from shared_prefix_branch_amd.stack import ForwardJob
         t = self.torch
-        self.job = ForwardJob(self.plan, self.md, self.layers, self.g_final, self.dims.vocab, device=self.device)
+        self.job = ForwardJob(self.plan, self.md, self.layers, self.g_final, self.dims.vocab, device=self.device,
+                              fp8_scales=self.fp8)
         self.job.load(self.provider)
         self.job.run(W)
         t.cuda.synchronize()
@@ -154,7 +156,7 @@ class StackCase(Case):
     def oracle(self):
         from oracle import forward as OF, tree as OT
         from oracle.numerics import to_f64
-        m = OF.Model.from_synth(self.md, self.layers, self.g_final)
+        m = OF.Model.from_synth(self.md, self.layers, self.g_final, self.fp8)
         lay = OT.build_layout(self.prob, floors=self.floors)
         hid = {}
         for n, li in enumerate(lay.inputs):
@@ -239,3 +241,92 @@ def test_stack_packed_spilled_and_alone_bit_identical():
     alone = StackCase(wl, md, 16384, inputs=[1], cache=cache)
     alone.run(W)
     _same(P[1], by_input(alone)[1], "input 1 alone")
+
+
+def test_quantize_e4m3_codes_equal_the_oracle_rounding():
+    import torch
+    import shared_prefix_branch_amd as spb
+    from oracle import numerics as ON
+    say("case: e4m3 quantize, f32 and bf16 inputs, power-of-two scale")
+    rng = np.random.default_rng(3)
+    x = (rng.normal(size=4099) * np.exp2(rng.uniform(-12, 12, 4099))).astype(np.float32)
+    for src in (torch.from_numpy(x), torch.from_numpy(x).to(torch.bfloat16)):
+        q = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+        spb.quantize_e4m3(src.cuda(), q, 0.125)()
+        torch.cuda.synchronize()
+        got = ON.e4m3_bytes_to_f64(q.cpu().numpy())
+        want = ON.round_to_e4m3(ON.to_f64(src) / 0.125)
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "residual"])
+def test_linear_fp8_against_oracle(mode):
+    import torch
+    import shared_prefix_branch_amd as spb
+    from oracle import forward as OF
+    from oracle.numerics import to_f64
+    say(f"case: fp8 linear ({mode}) m=300 n=392 k=256")
+    rng = np.random.default_rng(11)
+    m, n, k = 300, 392, 256
+    x, w = _bf16(rng, (m, k)), _bf16(rng, (n, k), 1 / math.sqrt(k))
+    sx, sw = float(x.float().abs().max()) / 448, float(w.float().abs().max()) / 448
+    x8 = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    w8 = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+    spb.quantize_e4m3(x.cuda(), x8, sx)()
+    spb.quantize_e4m3(w.cuda(), w8, sw)()
+    ref = OF.q8(to_f64(x), sx) @ OF.q8(to_f64(w), sw).T
+    if mode == "bf16":
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        spb.linear(x8, w8, spb.LINEAR_BF16, y=y, fp8_scales=(sx, sw))
+        torch.cuda.synchronize()
+        got = to_f64(y)
+    else:
+        r = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+        spb.linear(x8, w8, spb.LINEAR_RESIDUAL, resid=r, fp8_scales=(sx, sw))
+        torch.cuda.synchronize()
+        got = r.cpu().double().numpy()
+    assert _rel_rows(got, ref) <= TOL_OP
+
+
+TOL_FP8 = 1e-1  # the fp8 tolerance for hidden rows and scores
+
+
+def test_stack_fp8_parity_and_bit_identity():
+    from oracle import scoring as OS
+    wl, md = _stack_case("shared", "small_d128", 16384, 63)
+    W, Wh = lm_head(wl)
+    say("case: fp8 stack, shared templates, packed and spilled")
+    cache = {}
+    packed = StackCase(wl, md, 16384, fp8=True, cache=cache)
+    packed.run(W)
+    lay, hid = packed.oracle()
+    got = packed.job.hidden_by_logical_row(list(hid))
+    worst = max(_rel_rows(got[r][0][None], ref[None]) for r, ref in hid.items())
+    assert worst <= TOL_FP8, f"hidden rel err {worst}"
+    sc = OS.score_branches(lay, lambda rows: np.stack([hid[r] for r in rows]), Wh)
+    OS.join_floors(lay, sc)
+    err = {"lp": 0.0, "p": 0.0}
+    res = packed.branch_results()
+    for key, s in sc.items():
+        if lay.inputs[key[0]].kind != "input":
+            continue
+        lp, p = res[key][0], res[key][1]
+        err["lp"] = max(err["lp"], float(np.max(np.abs(lp - s.lp) / np.abs(s.lp))))
+        err["p"] = max(err["p"], float(np.max(np.abs(p - s.p))))
+    assert err["lp"] <= TOL_FP8 and err["p"] <= TOL_FP8, err
+    say(f"  hidden rel err {worst:.2e}; scores {err}")
+    spilled = StackCase(wl, md, 135, inputs=[1, 2, 0], fp8=True, cache=cache)
+    assert spilled.plan.info()["n_tokens"] > packed.plan.info()["n_tokens"]  # content and stems re-staged
+    spilled.run(W)
+    rows = list(hid)
+    a = packed.job.hidden_by_logical_row(rows)
+    b = spilled.job.hidden_by_logical_row(rows)
+    # the spilled case numbers logical rows in its own input order: compare by input
+    la = packed.plan.inputs()[0]
+    lb = spilled.plan.inputs()[0]
+    for pos_b, i in enumerate([1, 2, 0]):
+        n_rows = int(la[i + 1] - la[i])
+        for r in range(n_rows):
+            xa = a[int(la[i]) + r][0]
+            xb = b[int(lb[pos_b]) + r][0]
+            assert np.array_equal(xa.view(np.uint32), xb.view(np.uint32)), (i, r)

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     hdr = open(os.path.join(ROOT, "include", "spb.h")).read()
-    declared = set(re.findall(r"\b(spb_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(spb_[a-z_0-9]+)\s*\(", hdr))
     assert declared == set(spb.EXPORTED_SYMBOLS)
     L = spb.lib()
     for name in sorted(declared):
