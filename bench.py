@@ -47,6 +47,7 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # lm-head ridge in scored rows per W stream: the head does M flop per W byte
 HEAD_RIDGE_ROWS = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # 312.5
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +67,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=0,
                     help="decoder layers in front of the head (synthetic weights, news model dims); "
                          "0: attention alone with given hidden states")
+    ap.add_argument("--fp8", action="store_true",
+                    help="with --layers: the linears on e4m3 operands (static per-tensor scales)")
     ap.add_argument("--slots", type=int, default=0,
                     help="with --layers: after the timed steps, decode this many extraction slots (the first "
                          "question of each of the first contents) by beam search and time them")
@@ -175,8 +178,9 @@ def main():
         md = dataclasses.replace(synth.MODEL_CONFIGS["news"], layers=args.layers, hidden=d.hidden, hq=d.hq,
                                  hkv=d.hkv, head_dim=d.head_dim)
         layers_w, g_final = synth.model_weights(md, wl.cfg_seed, device=dev)
+        fp8_scales = synth.stack_fp8_scales(layers_w) if args.fp8 else None
         job = ForwardJob(plan, md, layers_w, g_final, d.vocab, device=dev, batch_head=batch_head,
-                         lm_head_kind=head_kind, keep_kv=args.slots > 0)
+                         lm_head_kind=head_kind, keep_kv=args.slots > 0, fp8_scales=fp8_scales)
         job.load(lambda n: synth.embed_block(wl, md, ids[n], device=dev))
         del layers_w
     else:
@@ -285,10 +289,11 @@ def main():
             ms_k = float(lin_ms[:, sel].sum())
             per_kind[name] = {"n": n_, "k": k_, "ms": round(ms_k, 4),
                               "tflops": round(float(lin_flops[:, sel].sum()) / (ms_k * 1e-3) / 1e12, 2)}
-        stack = {"layers": md.layers, "hidden": md.hidden, "ffn": md.ffn,
+        peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
+        stack = {"layers": md.layers, "hidden": md.hidden, "ffn": md.ffn, "linear_dtype": "e4m3" if args.fp8 else "bf16",
                  "forward_ms": round(float(att_ms.sum()), 4),
                  "linear": {"ms": round(float(lin_ms.sum()), 4), "tflops": round(lin_tf, 2),
-                            "frac": round(lin_tf / PEAK_BF16_TFLOPS, 4), "launches_per_step": int(n_pass * n_lin),
+                            "frac": round(lin_tf / peak, 4), "launches_per_step": int(n_pass * n_lin),
                             "per_kind": per_kind}}
     if args.workload != "news":
         traffic, traffic_src = None, "counters taken on news only"
@@ -313,8 +318,8 @@ def main():
 
     if stack is not None:
         # the linear layers dominate the step: their GEMM kernel is the roofline
-        roof = {"bound": "mfma", "achieved": round(lin_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(lin_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        roof = {"bound": "mfma", "achieved": round(lin_tf, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(lin_tf / peak, 4), "traffic": None,
                 "traffic_source": "counters not taken for the linear kernel",
                 "kernel": "linear_kernel (decoder-stack GEMMs with fused epilogues, spb_linear)",
                 "per_launch": {"ms_mean": round(float(lin_ms.mean()), 4),
@@ -348,7 +353,7 @@ def main():
                              "unmasked_pairs": int(info["unmasked_pairs"]),
                              "note": "inside the decoder stack: stack.forward_ms covers every layer of each pass"}
 
-    if args.slots > 0 and md is not None:
+    if args.slots > 0 and md is not None and not args.fp8:
         line["slots"] = time_slots(job, wl, md, W, prob, args, ms_step, tokens)
     if not args.no_cpu_baseline:
         if md is not None:
