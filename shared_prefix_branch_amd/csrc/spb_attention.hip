@@ -659,7 +659,7 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
 
   __syncthreads();  // chunk list in LDS
   issue(0);
-  wait_vmcnt<0>();
+  wait_all_loads();  // chunk 0, the row and the Q fragments
   lds_barrier();
   if (nch > 1) issue(1);
 

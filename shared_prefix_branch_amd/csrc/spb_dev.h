@@ -30,6 +30,14 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// vmcnt(0) issued through the compiler's own builtin, so its wait-count
+// tracking knows that every load it issued so far has landed.  The copies
+// above are invisible to that tracking; without this, a register loaded
+// before a copy loop is waited for at its first use inside the loop, with an
+// s_waitcnt vmcnt(0) that runs on every trip and so also waits for the
+// copies of later stages.  (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
+__device__ inline void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Barrier for an LDS hand-off that leaves outstanding global loads in flight.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 

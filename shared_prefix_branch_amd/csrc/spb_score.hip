@@ -177,28 +177,30 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   f32x16 acc[2][MB];
   gemm::k_loop<MB>(acc, lds, p.W, p.hg, woff, hoff, p.Hrow / kKT, p.SW, wave, qi, half);
   float (*red)[TM][2] = (float (*)[TM][2])lds;  // [4][TM][2], reusing the ring
-  if (p.round_bf16) {
-#pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[vb][mb][r] = bf2f(f2bf(acc[vb][mb][r]));
-  }
 
   // epilogue.  Lane holds column m = m0 + mb*32 + qi; register r of block vb
   // holds vocabulary row v0 + wave*64 + vb*32 + (r/4)*8 + half*4 + r%4.
   const int vw0 = v0 + wave * 64;
   const int nvalid = p.V - vw0;  // rows past the vocabulary (last slice only) are excluded
+  // one 32-row block at a time, so only its two accumulators leave the
+  // accumulation registers at once
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
+    f32x16 z[2] = {acc[0][mb], acc[1][mb]};
+    asm volatile("" : "+v"(z[0]), "+v"(z[1]));  // the copy out of acc happens here, not at the loop exit
+    if (p.round_bf16) {
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[vb][r] = bf2f(f2bf(z[vb][r]));
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        mx = fmaxf(mx, vr < nvalid ? acc[vb][mb][r] : kNegInf);
+        mx = fmaxf(mx, vr < nvalid ? z[vb][r] : kNegInf);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     float se = 0.f;
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          se += vr < nvalid ? __expf(acc[vb][mb][r] - mx) : 0.f;
+          se += vr < nvalid ? __expf(z[vb][r] - mx) : 0.f;
         }
     }
     se = se + __shfl_xor(se, 32);
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) val = (vb == vbt && r == rt) ? acc[vb][mb][r] : val;
+          for (int r = 0; r < 16; ++r) val = (vb == vbt && r == rt) ? z[vb][r] : val;
         p.tz[t] = val;
       }
     }
