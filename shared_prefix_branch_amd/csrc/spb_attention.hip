@@ -594,35 +594,6 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
   const bool active = local < it.nrows;
   const int x = it.row0 + local;
 
-  load_chunk_list(p, it, chunks, tid, C::NT);
-  const SpbRow row = load_row(p, x, active);
-  QFrag<D, IN> qf[HPW];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) load_q<D, IN>(qf[j], p, x, h0 + j, active, half);
-
-  // fragment offsets in the swizzled layout
-  FragOffsets<D, IN> fo;
-#pragma unroll
-  for (int t = 0; t < QFrag<D, IN>::STEPS; ++t)
-    fo.k[t][0] = qi * C::ROWB + (((2 * t + half) ^ swz_k<C::ROWB>(qi)) << 4);
-  {
-    const int g = qi >> 4, l16 = lane & 15;
-    const int rr = half * 4 + (l16 >> 2);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int cv = 2 * g + ((l16 & 3) >> 1) + 4 * db;
-      fo.v[db] = rr * C::ROWB + ((cv ^ swz_v<C::ROWB>(rr)) << 4) + (l16 & 1) * 8;
-    }
-  }
-
-  RowState st[HPW];
-  f32x16 o[HPW][D / 32];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    st[j] = RowState{kNegInf, 0.f};
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[j][db] = f32x16{0.f};
-  }
   const uint32_t k_lds = lds_addr(&Ks[0][0]), v_lds = lds_addr(&Vs[0][0]);
 
   // Copies chunk i (64 or 32 key rows; rows past the pass repeat its last
@@ -657,8 +628,45 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
     }
   };
 
+  // An item's content chunk 0 starts at its content start, so its copy needs
+  // no chunk list: it goes out first, ahead of the list, row and Q loads.
+  const bool early = it.ncc > 0;
+  if (early) {
+#pragma unroll
+    for (int qq = 0; qq < C::Q64; ++qq) copy_rows(it.seg, 0u, qq);
+  }
+
+  load_chunk_list(p, it, chunks, tid, C::NT);
+  const SpbRow row = load_row(p, x, active);
+  QFrag<D, IN> qf[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) load_q<D, IN>(qf[j], p, x, h0 + j, active, half);
+
+  // fragment offsets in the swizzled layout
+  FragOffsets<D, IN> fo;
+#pragma unroll
+  for (int t = 0; t < QFrag<D, IN>::STEPS; ++t)
+    fo.k[t][0] = qi * C::ROWB + (((2 * t + half) ^ swz_k<C::ROWB>(qi)) << 4);
+  {
+    const int g = qi >> 4, l16 = lane & 15;
+    const int rr = half * 4 + (l16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int cv = 2 * g + ((l16 & 3) >> 1) + 4 * db;
+      fo.v[db] = rr * C::ROWB + ((cv ^ swz_v<C::ROWB>(rr)) << 4) + (l16 & 1) * 8;
+    }
+  }
+
+  RowState st[HPW];
+  f32x16 o[HPW][D / 32];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    st[j] = RowState{kNegInf, 0.f};
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[j][db] = f32x16{0.f};
+  }
   __syncthreads();  // chunk list in LDS
-  issue(0);
+  if (!early) issue(0);
   wait_all_loads();  // chunk 0, the row and the Q fragments
   lds_barrier();
   if (nch > 1) issue(1);
