@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--head-batch", action="store_true",
                     help="one lm-head launch for all passes of the step (spb_score_options_batch) "
                          "instead of one per pass")
+    ap.add_argument("--head-rows", type=int, default=768,
+                    help="group consecutive passes into one lm-head launch while their scored rows total at "
+                         "most this many (0: one launch per pass); 768 = three row chunks of 256 per "
+                         "vocabulary slice, the most that share W lines in one XCD's L2 well")
     ap.add_argument("--lm-head", default="f32out", choices=["f32out", "bf16", "fp32"],
                     help="lm-head output kind (f32out is the default of the engine the pages describe)")
     ap.add_argument("--head-sweep", default="",
@@ -180,12 +184,13 @@ def main():
         layers_w, g_final = synth.model_weights(md, wl.cfg_seed, device=dev)
         fp8_scales = synth.stack_fp8_scales(layers_w) if args.fp8 else None
         job = ForwardJob(plan, md, layers_w, g_final, d.vocab, device=dev, batch_head=batch_head,
-                         lm_head_kind=head_kind, keep_kv=args.slots > 0, fp8_scales=fp8_scales)
+                         lm_head_kind=head_kind, keep_kv=args.slots > 0, fp8_scales=fp8_scales,
+                         head_rows=args.head_rows)
         job.load(lambda n: synth.embed_block(wl, md, ids[n], device=dev))
         del layers_w
     else:
         job = Job(plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv_dt, out_dt, hid_dt, device=dev,
-                  scales=scales, batch_head=batch_head, lm_head_kind=head_kind)
+                  scales=scales, batch_head=batch_head, lm_head_kind=head_kind, head_rows=args.head_rows)
         job.load(provider)
     W = synth.lm_head(wl, device=dev)
     torch.cuda.synchronize()
@@ -250,7 +255,8 @@ def main():
         job.lin_marks = None
 
     att_ms = np.zeros(n_pass)
-    n_head = 1 if batch_head else n_pass   # lm-head launches per step
+    groups = job.head_groups
+    n_head = len(groups)   # lm-head launches per step
     head_ms = np.zeros(n_head)
     for ms in marks:
         for k, mk in enumerate(ms):
@@ -259,9 +265,7 @@ def main():
                 head_ms[k] += mk[2].elapsed_time(mk[3]) / args.steps
     pair_flops = 4.0 * d.head_dim * d.hq
     att_flops = np.array([plan.info(k)["unmasked_pairs"] * pair_flops for k in range(n_pass)])
-    M = np.array([plan.info(k)["n_scored_rows"] for k in range(n_pass)], dtype=np.float64)
-    if batch_head:
-        M = np.array([M.sum()])
+    M = np.array([sum(plan.info(k)["n_scored_rows"] for k in g) for g in groups], dtype=np.float64)
     head_flops = 2.0 * d.hidden * d.vocab * M
     w_bytes = 2.0 * d.hidden * d.vocab
     head_bytes = w_bytes + M * d.hidden * 2.0
@@ -301,6 +305,8 @@ def main():
         traffic, traffic_src = None, "counters taken for the f32out lm head only"
     else:
         traffic, traffic_src = measured_traffic("batched" if batch_head else "per_pass")
+        if args.head_rows > 0 and not batch_head and n_head != n_pass:
+            traffic, traffic_src = None, "counters taken per pass and for one launch per step only"
     if head_bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(head_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(head_tflops / PEAK_BF16_TFLOPS, 4)}

@@ -15,9 +15,12 @@ write their option scores into one device buffer, copied back in one transfer
 at the end of the run; results are double-buffered, so a caller may enqueue
 run i+1 before it joins run i and the GPU never waits on the host.
 
-With ``batch_head`` the scored rows of all passes go through one lm-head
-launch after the passes' attention (W streamed once per run instead of once
-per pass); the scores are bit-identical to the per-pass head.
+Head groups: by default each pass has its own lm-head launch.  With
+``head_rows`` > 0, consecutive passes whose scored rows total at most
+``head_rows`` share one launch, made after the last of them has run its
+attention, so W streams once per group instead of once per pass (a pass with
+more rows than that is a group of its own); ``batch_head`` puts every pass in
+one group.  The scores are bit-identical to the per-pass head.
 """
 from __future__ import annotations
 
@@ -54,7 +57,7 @@ class Job:
 
     def __init__(self, plan: Plan, hq: int, hkv: int, head_dim: int, hidden_dim: int, vocab: int,
                  qkv_dtype, out_dtype, hidden_dtype, device="cuda", scales=(1.0, 1.0, 1.0),
-                 batch_head: bool = False, lm_head_kind: int = 0):
+                 batch_head: bool = False, lm_head_kind: int = 0, head_rows: int = 0):
         import torch
         self.torch = torch
         self.plan = plan
@@ -75,9 +78,33 @@ class Job:
         self._attn: List = []
         self._score: List = []
         self.batch_head = bool(batch_head)
+        self.head_rows = int(head_rows)
         self.lm_head_kind = int(lm_head_kind)
         if self.batch_head and plan.n_passes > 64:
             raise ValueError("batch_head covers at most 64 passes")
+        self.grouped = self.batch_head or self.head_rows > 0
+        self.head_groups = self._group_passes(plan)
+
+    def _group_passes(self, plan: Plan) -> List[List[int]]:
+        """The passes of each lm-head launch, in pass order."""
+        n = plan.n_passes
+        if self.batch_head:
+            return [list(range(n))]
+        if self.head_rows <= 0:
+            return [[k] for k in range(n)]
+        groups: List[List[int]] = []
+        cur: List[int] = []
+        rows = 0
+        for k in range(n):
+            m = plan.info(k)["n_scored_rows"]
+            if cur and (rows + m > self.head_rows or len(cur) == 64):  # 64: the batch call's pass limit
+                groups.append(cur)
+                cur, rows = [], 0
+            cur.append(k)
+            rows += m
+        if cur:
+            groups.append(cur)
+        return groups
 
     # -- buffers ---------------------------------------------------------------
     def _result_sizes(self):
@@ -93,7 +120,7 @@ class Job:
         n = max(1, inf["n_tokens"])
         dev = self.device
         meta = t.empty(inf["meta_bytes"], dtype=t.uint8, device=dev)
-        ws_bytes = 256 if self.batch_head else max(256, score_workspace_bytes(self.plan, k, self.V, self.H,
+        ws_bytes = 256 if self.grouped else max(256, score_workspace_bytes(self.plan, k, self.V, self.H,
                                                                               self.lm_head_kind))
         ws = t.empty(ws_bytes, dtype=t.uint8, device=dev)
         return PassBuffers(
@@ -153,20 +180,20 @@ class Job:
             self.passes.append(buf)
         self._attn = [PreparedAttention(k, b.meta, b.q, b.k, b.v, b.o, scales=self.scales)
                       for k, b in enumerate(self.passes)]
-        if self.batch_head:
-            nb = score_batch_workspace_bytes(self.plan, list(range(self.plan.n_passes)), self.V, self.H,
-                                             self.lm_head_kind)
+        if self.grouped:
+            # one workspace for every group: their launches run in order on one stream
+            nb = max(score_batch_workspace_bytes(self.plan, g, self.V, self.H, self.lm_head_kind)
+                     for g in self.head_groups)
             self.batch_ws = t.empty(max(256, nb), dtype=t.uint8, device=self.device)
         self._pass_done = [None] * len(self.passes)
 
     def _prepare_head(self, lm_head):
         if self._head is not lm_head:
-            if self.batch_head:
-                ks = list(range(len(self.passes)))
-                self._score = [PreparedScoreBatch(ks, [b.meta for b in self.passes], [b.hidden for b in self.passes],
-                                                  lm_head, self.batch_ws, [b.slots[r] for b in self.passes],
-                                                  self.lm_head_kind)
-                               for r in range(2)]
+            if self.grouped:
+                P = self.passes
+                self._score = [[PreparedScoreBatch(g, [P[k].meta for k in g], [P[k].hidden for k in g], lm_head,
+                                                   self.batch_ws, [P[k].slots[r] for k in g], self.lm_head_kind)
+                                for r in range(2)] for g in self.head_groups]
             else:
                 self._score = [[PreparedScore(k, b.meta, b.hidden, lm_head, b.workspace, *b.slots[r],
                                               lm_head_kind=self.lm_head_kind)
@@ -217,7 +244,8 @@ class Job:
         metadata); None stages the job's plan now.  ``marks``, if given, holds
         per pass four created events: recorded on ``stream`` around the
         attention kernel (0, 1) and, by the library, around the lm-head GEMM
-        kernel (2, 3)."""
+        kernel (2, 3); with head groups, events 2, 3 of entry g time the
+        launch of group g."""
         t = self.torch
         stream = stream if stream is not None else t.cuda.current_stream()
         if staged is None:
@@ -229,6 +257,7 @@ class Job:
         if self._slot_done[r] is not None:
             self._slot_done[r].synchronize()  # its previous copy back has landed
         uploaded = self._upload(which, stream)
+        gi = 0
         for k, buf in enumerate(self.passes):
             stream.wait_event(uploaded[k])
             mk = None if marks is None else marks[k]
@@ -238,19 +267,22 @@ class Job:
                 self._forward(k, plan, stream)
             if mk is not None:
                 mk[1].record(stream)
-            if scoring and not self.batch_head:
-                self._score[k][r](plan, stream, None if mk is None else (mk[2], mk[3]))
-            if not self.batch_head:
+            if not self.grouped:
+                if scoring:
+                    self._score[k][r](plan, stream, None if mk is None else (mk[2], mk[3]))
                 done = t.cuda.Event()
                 done.record(stream)
                 self._pass_done[k] = done
+            elif k == self.head_groups[gi][-1]:
+                if scoring:
+                    mg = None if marks is None else marks[gi]
+                    self._score[gi][r](plan, stream, None if mg is None else (mg[2], mg[3]))
+                done = t.cuda.Event()
+                done.record(stream)
+                for kk in self.head_groups[gi]:
+                    self._pass_done[kk] = done
+                gi += 1
             buf.lp, buf.p, buf.residual = buf.slots[r]
-        if self.batch_head:
-            if scoring:
-                self._score[r](plan, stream, None if marks is None else (marks[0][2], marks[0][3]))
-            done = t.cuda.Event()
-            done.record(stream)
-            self._pass_done = [done] * len(self.passes)
         with t.cuda.stream(stream):
             self.results_host[r].copy_(self.results[r], non_blocking=True)
         ev = t.cuda.Event()

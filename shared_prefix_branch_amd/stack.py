@@ -58,10 +58,11 @@ class ForwardJob(Job):
 
     def __init__(self, plan: Plan, md, layers: List[dict], g_final, vocab: int, device="cuda",
                  batch_head: bool = False, lm_head_kind: int = 0, n_pos: int = 8192, keep_kv: bool = False,
-                 fp8_scales: Optional[List[dict]] = None):
+                 fp8_scales: Optional[List[dict]] = None, head_rows: int = 0):
         import torch
         super().__init__(plan, md.hq, md.hkv, md.head_dim, md.hidden, vocab, torch.bfloat16, torch.bfloat16,
-                         torch.bfloat16, device=device, batch_head=batch_head, lm_head_kind=lm_head_kind)
+                         torch.bfloat16, device=device, batch_head=batch_head, lm_head_kind=lm_head_kind,
+                         head_rows=head_rows)
         self.md = md
         self.W = []
         for L in layers:

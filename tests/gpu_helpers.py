@@ -30,7 +30,7 @@ class Case:
     def __init__(self, wl: synth.Workload, budget: int, inputs: Optional[Sequence[int]] = None,
                  floors: bool = True, peaked: bool = False, device: str = "cuda", gen_device: str = "cuda",
                  chained: bool = False, cache: Optional[dict] = None, batch_head: bool = False,
-                 lm_head_kind: int = 0):
+                 lm_head_kind: int = 0, head_rows: int = 0):
         import torch
         self.torch = torch
         self.wl = wl
@@ -50,6 +50,7 @@ class Case:
         self.scales = synth.fp8_scales(wl) if wl.dims.dtype == "fp8" else (1.0, 1.0, 1.0)
         self._blocks: Dict[tuple, tuple] = {} if cache is None else cache  # activations by identity
         self.batch_head = batch_head
+        self.head_rows = head_rows
         self.lm_head_kind = lm_head_kind
 
     # -- inputs --------------------------------------------------------------
@@ -74,7 +75,7 @@ class Case:
         hid = t.float32 if d.dtype == "f32" else t.bfloat16
         self.job = Job(self.plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv, out, hid,
                        device=self.device, scales=self.scales, batch_head=self.batch_head,
-                       lm_head_kind=self.lm_head_kind)
+                       lm_head_kind=self.lm_head_kind, head_rows=self.head_rows)
         self.job.load(self.provider)
         self.job.run(W)
         t.cuda.synchronize()

@@ -438,3 +438,32 @@ def test_repacking_gives_identical_metadata():
     blobs(other)
     assert blobs(news) == first
     assert blobs(other) == blobs(other)
+
+
+def test_head_groups_rule():
+    """Head groups (driver): consecutive passes while their scored rows total
+    at most the cap, at most 64 per launch; a pass above the cap alone; no cap
+    means one launch per pass; batch_head one launch for all."""
+    from shared_prefix_branch_amd.driver import Job
+    pr = synth.make_problem("random", 31, vocab=4096, n_inputs=12, n_questions=5, min_content=5,
+                            max_content=60, max_len=8, max_options=4, max_option_tokens=3)
+    plan = spb.pack_pass(pr, token_budget=110)
+    m = [plan.info(k)["n_scored_rows"] for k in range(plan.n_passes)]
+    assert m == [21, 16, 13, 21, 6, 23, 25, 11, 26, 14]
+
+    def groups(**kw):
+        return Job(plan, 8, 4, 128, 256, 4096, None, None, None, device="cpu", **kw).head_groups
+
+    assert groups() == [[k] for k in range(10)]
+    assert groups(batch_head=True) == [list(range(10))]
+    assert groups(head_rows=40) == [[0, 1], [2, 3, 4], [5], [6, 7], [8, 9]]  # 37, 40, 23, 36, 40
+    assert groups(head_rows=30) == [[0], [1, 2], [3, 4], [5], [6], [7], [8], [9]]  # 29 and 27 fit
+    assert groups(head_rows=20) == [[k] for k in range(10)]  # no two neighbours fit
+    assert groups(head_rows=10 ** 6) == [list(range(10))]
+    # the 64-pass limit of one batched launch
+    pr = synth.make_problem("random", 5, vocab=4096, n_inputs=70, n_questions=1, min_content=5,
+                            max_content=8, max_len=4, max_options=2, max_option_tokens=1)
+    plan = spb.pack_pass(pr, token_budget=12, floors=False)
+    assert plan.n_passes == 70
+    g = groups(head_rows=10 ** 6)
+    assert [len(x) for x in g] == [64, plan.n_passes - 64]
