@@ -90,6 +90,49 @@ __device__ __attribute__((always_inline)) inline void mfma(f32x16 (&acc)[2][MB],
       acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0);
 }
 
+// Piece j (0..MB+1) of a K step's fragments: the wave's W blocks, then the
+// X blocks.
+template <int MB>
+__device__ __attribute__((always_inline)) inline void frag_piece(Frags<MB> &f, const u32x4 *Wb, const u32x4 *Hb,
+                                                                 int ks, int j, int wave, int qi, int half) {
+  if (j < 2) {
+    u32x4 u = Wb[swz(wave * 64 + j * 32 + qi, ks * 2 + half)];
+    f.a[j] = *(bf16x8_t *)&u;
+  } else {
+    u32x4 u = Hb[swz((j - 2) * 32 + qi, ks * 2 + half)];
+    f.b[j - 2] = *(bf16x8_t *)&u;
+  }
+}
+
+// One K step, scheduled by hand: its 2 MB MFMAs in the order of mfma(), and
+// after MFMA j, piece j of the next step's fragments (when READ; pieces past
+// the last MFMA follow it) and tile copies c0 + j*CPS .. +CPS (those below
+// c1).  One MFMA, one read and a copy
+// per slot keep the MFMA pipe fed while the LDS and memory queues take the
+// rest; a burst of either would hold up MFMA issue.
+template <int MB, bool READ, int CPS, typename Copy>
+__device__ __attribute__((always_inline)) inline void k_step(f32x16 (&acc)[2][MB], const Frags<MB> &fc,
+                                                             Frags<MB> &fn, const u32x4 *Wb, const u32x4 *Hb,
+                                                             int ks_next, int wave, int qi, int half, Copy copy,
+                                                             int c0, int c1) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb) {
+      const int j = mb * 2 + vb;
+      acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[vb], fc.b[mb], acc[vb][mb], 0, 0, 0);
+      if (READ && j < 2 + MB) frag_piece<MB>(fn, Wb, Hb, ks_next, j, wave, qi, half);
+#pragma unroll
+      for (int c = c0 + j * CPS; c < c0 + (j + 1) * CPS; ++c)
+        if (c < c1) copy(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  // MB = 1: three pieces, two MFMAs
+#pragma unroll
+  for (int j = 2 * MB; j < 2 + MB; ++j)
+    if (READ) frag_piece<MB>(fn, Wb, Hb, ks_next, j, wave, qi, half);
+}
+
 // Per-lane global byte offsets of the tile copies: one DMA instruction moves
 // 8 rows x 128 bytes, lane t filling LDS position t%8 of row r8 + t/8, which
 // swz() maps to chunk (t%8) ^ ((r/2)%8).  w_row(r) / x_row(r) give the global
@@ -127,6 +170,19 @@ __device__ __attribute__((always_inline)) inline void k_loop(f32x16 (&acc)[2][MB
   char *const wring = lds;
   char *const hring = lds + T::RW * T::WBYTES;
   const uint32_t lds0 = lds_addr(&lds[0]);
+  auto copy_w = [&](int i, int stage, int sl) {  // W copy i (0..7) of a stage
+    int ws = stage;
+    if (ws >= SW) ws -= SW;
+    if (ws >= SW) ws -= SW;
+    const uint32_t kb = (uint32_t)ws * kKT * 2;
+    const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
+    dma16(W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 8) * 128));
+  };
+  auto copy_h = [&](int i, int stage, int sl) {  // X copy i (0..MB-1) of a stage
+    const uint32_t kb = (uint32_t)stage * kKT * 2;
+    const uint32_t s0 = lds0 + T::RW * T::WBYTES + (uint32_t)sl * T::HBYTES;
+    dma16(X, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
+  };
   auto issue_w = [&](int stage, int sl) {
     int ws = stage;  // stage within the sweep of W (stage < 3 SW)
     if (ws >= SW) ws -= SW;
@@ -160,33 +216,41 @@ __device__ __attribute__((always_inline)) inline void k_loop(f32x16 (&acc)[2][MB
   wait_vmcnt<T::NW>();  // X(0), W(0) landed (this wave's copies)
   lds_barrier();
 
+  // the stage's copies, X(s+1) first (the stage-end wait relies on it), spread
+  // over the slots of its first two K steps
+  constexpr int NC = T::NH + T::NW;
+  constexpr int CPS = (NC + 4 * MB - 1) / (4 * MB);
+  constexpr int C0 = 2 * MB * CPS;  // copies of step 0
+  // The stage hand-off (copies landed, barrier) comes before the last K
+  // step, whose MFMAs carry the reads of the next stage's first fragments, so
+  // no stage starts by waiting on LDS.  The barrier follows every read of
+  // stage s (its lgkmcnt(0)), so trip s+1's copies may overwrite its slots.
+  // After the last stage those reads fetch landed copies of the last stage,
+  // unused.
+  Frags<MB> f0, f1;
+  frags<MB>(f0, (const u32x4 *)wring, (const u32x4 *)hring, 0, wave, qi, half);
   int sw = 0, sh = 0;  // ring slots of stage s
   for (int s = 0; s < S; ++s) {
     const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
     const u32x4 *Hb = (const u32x4 *)(hring + sh * T::HBYTES);
-    Frags<MB> f0, f1;
-    frags<MB>(f0, Wb, Hb, 0, wave, qi, half);
     const int sw2 = sw == 0 ? 2 : sw - 1;  // slot of stage s + 2 (= s - 1 mod 3)
-    issue_h(min(s + 1, last), sh ^ 1);
-    issue_w(min(s + 2, last), sw2);
-    frags<MB>(f1, Wb, Hb, 1, wave, qi, half);
+    const int sx = min(s + 1, last), sx2 = min(s + 2, last);
+    auto copy = [&](int c) {
+      if (c < T::NH)
+        copy_h(c, sx, sh ^ 1);
+      else
+        copy_w(c - T::NH, sx2, sw2);
+    };
     __builtin_amdgcn_sched_barrier(0);
-    mfma<MB>(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    frags<MB>(f0, Wb, Hb, 2, wave, qi, half);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma<MB>(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    frags<MB>(f1, Wb, Hb, 3, wave, qi, half);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma<MB>(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma<MB>(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
+    k_step<MB, true, CPS>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy, 0, NC);
+    k_step<MB, true, CPS>(acc, f1, f0, Wb, Hb, 2, wave, qi, half, copy, C0, NC);
+    k_step<MB, true, 0>(acc, f0, f1, Wb, Hb, 3, wave, qi, half, copy, 0, 0);
     wait_vmcnt<T::NW>();  // X(s+1) and W(s+1) landed
     lds_barrier();
     sw = sw == 2 ? 0 : sw + 1;
     sh ^= 1;
+    k_step<MB, true, 0>(acc, f1, f0, (const u32x4 *)(wring + sw * T::WBYTES), (const u32x4 *)(hring + sh * T::HBYTES),
+                        0, wave, qi, half, copy, 0, 0);
   }
   wait_vmcnt<0>();  // no copy may land after the ring is reused or released
   lds_barrier();

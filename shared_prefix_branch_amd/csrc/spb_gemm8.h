@@ -1,6 +1,6 @@
 // spb_gemm8.h -- the K loop of spb_gemm.h on OCP e4m3 operands (gfx950).
 //
-// Same tile, rings, swizzle and copy schedule as the bf16 loop: a stage is
+// Same tile, rings, swizzle and copies as the bf16 loop: a stage is
 // still one 128-byte line per tile row, now 128 K elements, and each stage is
 // two K steps of v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, f32
 // accumulation, scale operands neutral).  Lane (qi, half) of a K step holds
@@ -48,6 +48,39 @@ __device__ __attribute__((always_inline)) inline void mfma8(f32x16 (&acc)[2][MB]
       acc[vb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0, 0, 0, 0);
 }
 
+// A K step scheduled by hand, as k_step: after MFMA j, piece j of the next
+// step's fragments (two 16-byte reads) when READ, and copies c0 + j*CPS ..
+// +CPS below c1.
+template <int MB, bool READ, int CPS, typename Copy>
+__device__ __attribute__((always_inline)) inline void k_step8(f32x16 (&acc)[2][MB], const Frags8<MB> &fc,
+                                                              Frags8<MB> &fn, const u32x4 *Wb, const u32x4 *Hb,
+                                                              int ks_next, int wave, int qi, int half, Copy copy,
+                                                              int c0, int c1) {
+  const int c = ks_next * 4 + half * 2;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb) {
+      const int j = mb * 2 + vb;
+      acc[vb][mb] =
+          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[vb], fc.b[mb], acc[vb][mb], 0, 0, 0, 0, 0, 0);
+      if (READ && j < 2 + MB) {
+        if (j < 2)
+          fn.a[j] = frag8(Wb, wave * 64 + j * 32 + qi, c);
+        else
+          fn.b[j - 2] = frag8(Hb, (j - 2) * 32 + qi, c);
+      }
+#pragma unroll
+      for (int k = c0 + j * CPS; k < c0 + (j + 1) * CPS; ++k)
+        if (k < c1) copy(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  // MB = 1: three pieces, two MFMAs
+#pragma unroll
+  for (int j = 2 * MB; j < 2 + MB; ++j)
+    if (READ) fn.b[j - 2] = frag8(Hb, (j - 2) * 32 + qi, c);
+}
+
 // Byte offsets of the tile copies for 1-byte elements (see tile_offsets).
 template <int MB, typename WRow, typename XRow>
 __device__ __attribute__((always_inline)) inline void tile_offsets8(uint32_t (&woff)[8], uint32_t (&hoff)[MB],
@@ -79,6 +112,14 @@ __device__ __attribute__((always_inline)) inline void k_loop8(f32x16 (&acc)[2][M
   char *const wring = lds;
   char *const hring = lds + T::RW * T::WBYTES;
   const uint32_t lds0 = lds_addr(&lds[0]);
+  auto copy_w = [&](int i, int stage, int sl) {
+    const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
+    dma16(W, woff[i] + (uint32_t)stage * 128, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 8) * 128));
+  };
+  auto copy_h = [&](int i, int stage, int sl) {
+    const uint32_t s0 = lds0 + T::RW * T::WBYTES + (uint32_t)sl * T::HBYTES;
+    dma16(X, hoff[i] + (uint32_t)stage * 128, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
+  };
   auto issue_w = [&](int stage, int sl) {
     const uint32_t kb = (uint32_t)stage * 128;
     const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
@@ -105,6 +146,10 @@ __device__ __attribute__((always_inline)) inline void k_loop8(f32x16 (&acc)[2][M
   issue_w(min(1, last), 1);
   wait_vmcnt<T::NW>();
   lds_barrier();
+  // per stage: X(s+1) then W(s+2) copied one per slot of the first K step,
+  // whose MFMAs also carry the second step's fragment reads
+  constexpr int NC = T::NH + T::NW;
+  constexpr int CPS = (NC + 2 * MB - 1) / (2 * MB);
   int sw = 0, sh = 0;
   for (int s = 0; s < S; ++s) {
     const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
@@ -112,14 +157,16 @@ __device__ __attribute__((always_inline)) inline void k_loop8(f32x16 (&acc)[2][M
     Frags8<MB> f0, f1;
     frags8<MB>(f0, Wb, Hb, 0, wave, qi, half);
     const int sw2 = sw == 0 ? 2 : sw - 1;
-    issue_h(min(s + 1, last), sh ^ 1);
-    issue_w(min(s + 2, last), sw2);
-    frags8<MB>(f1, Wb, Hb, 1, wave, qi, half);
+    const int sx = min(s + 1, last), sx2 = min(s + 2, last);
+    auto copy = [&](int c) {
+      if (c < T::NH)
+        copy_h(c, sx, sh ^ 1);
+      else
+        copy_w(c - T::NH, sx2, sw2);
+    };
     __builtin_amdgcn_sched_barrier(0);
-    mfma8<MB>(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma8<MB>(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
+    k_step8<MB, true, CPS>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy, 0, NC);
+    k_step8<MB, false, 0>(acc, f1, f0, Wb, Hb, 0, wave, qi, half, copy, 0, 0);
     wait_vmcnt<T::NW>();
     lds_barrier();
     sw = sw == 2 ? 0 : sw + 1;
