@@ -216,11 +216,13 @@ __device__ __attribute__((always_inline)) inline void k_loop(f32x16 (&acc)[2][MB
   wait_vmcnt<T::NW>();  // X(0), W(0) landed (this wave's copies)
   lds_barrier();
 
-  // the stage's copies, X(s+1) first (the stage-end wait relies on it), spread
-  // over the slots of its first two K steps
+  // The stage's copies: X(s+1), which every wave reads and which must land by
+  // this stage's barrier, alone over the slots of the first K step; then
+  // W(s+2), two stages ahead, over the second (the stage-end wait relies on X
+  // going first).
   constexpr int NC = T::NH + T::NW;
-  constexpr int CPS = (NC + 4 * MB - 1) / (4 * MB);
-  constexpr int C0 = 2 * MB * CPS;  // copies of step 0
+  constexpr int CPSX = (T::NH + 2 * MB - 1) / (2 * MB);
+  constexpr int CPSW = (T::NW + 2 * MB - 1) / (2 * MB);
   // The stage hand-off (copies landed, barrier) comes before the last K
   // step, whose MFMAs carry the reads of the next stage's first fragments, so
   // no stage starts by waiting on LDS.  The barrier follows every read of
@@ -242,8 +244,8 @@ __device__ __attribute__((always_inline)) inline void k_loop(f32x16 (&acc)[2][MB
         copy_w(c - T::NH, sx2, sw2);
     };
     __builtin_amdgcn_sched_barrier(0);
-    k_step<MB, true, CPS>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy, 0, NC);
-    k_step<MB, true, CPS>(acc, f1, f0, Wb, Hb, 2, wave, qi, half, copy, C0, NC);
+    k_step<MB, true, CPSX>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy, 0, T::NH);
+    k_step<MB, true, CPSW>(acc, f1, f0, Wb, Hb, 2, wave, qi, half, copy, T::NH, NC);
     k_step<MB, true, 0>(acc, f0, f1, Wb, Hb, 3, wave, qi, half, copy, 0, 0);
     wait_vmcnt<T::NW>();  // X(s+1) and W(s+1) landed
     lds_barrier();

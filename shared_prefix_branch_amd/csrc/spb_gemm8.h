@@ -146,10 +146,11 @@ __device__ __attribute__((always_inline)) inline void k_loop8(f32x16 (&acc)[2][M
   issue_w(min(1, last), 1);
   wait_vmcnt<T::NW>();
   lds_barrier();
-  // per stage: X(s+1) then W(s+2) copied one per slot of the first K step,
-  // whose MFMAs also carry the second step's fragment reads
+  // per stage: X(s+1) over the slots of the first K step, whose MFMAs also
+  // carry the second step's fragment reads, then W(s+2) over the second
   constexpr int NC = T::NH + T::NW;
-  constexpr int CPS = (NC + 2 * MB - 1) / (2 * MB);
+  constexpr int CPSX = (T::NH + 2 * MB - 1) / (2 * MB);
+  constexpr int CPSW = (T::NW + 2 * MB - 1) / (2 * MB);
   int sw = 0, sh = 0;
   for (int s = 0; s < S; ++s) {
     const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
@@ -165,8 +166,8 @@ __device__ __attribute__((always_inline)) inline void k_loop8(f32x16 (&acc)[2][M
         copy_w(c - T::NH, sx2, sw2);
     };
     __builtin_amdgcn_sched_barrier(0);
-    k_step8<MB, true, CPS>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy, 0, NC);
-    k_step8<MB, false, 0>(acc, f1, f0, Wb, Hb, 0, wave, qi, half, copy, 0, 0);
+    k_step8<MB, true, CPSX>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy, 0, T::NH);
+    k_step8<MB, false, CPSW>(acc, f1, f0, Wb, Hb, 0, wave, qi, half, copy, T::NH, NC);
     wait_vmcnt<T::NW>();
     lds_barrier();
     sw = sw == 2 ? 0 : sw + 1;
