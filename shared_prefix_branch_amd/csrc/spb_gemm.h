@@ -10,8 +10,10 @@
 // copied global -> LDS into ring slot j % 3 two stages ahead of use (each wave
 // copies the 64 rows only it reads); its X tile into slot j % 2 one stage
 // ahead.  Both are XOR-swizzled so fragment reads are free of bank conflicts.
-// Within a stage the fragments of K step t+1 are read while step t
-// multiplies.
+// The loop is scheduled by hand (k_step): each MFMA of K step t is followed
+// by one LDS read of step t+1's fragments and, in a stage's first two steps,
+// one tile copy (X copies in the first, W copies in the second), so no queue
+// takes a burst that holds up MFMA issue.
 //
 // Accumulator layout: acc[vb][mb] register r of lane (qi, half) holds
 // W row w*64 + vb*32 + (r/4)*8 + half*4 + r%4 against X row mb*32 + qi.
@@ -79,15 +81,6 @@ __device__ __attribute__((always_inline)) inline void frags(Frags<MB> &f, const 
     u32x4 u = Hb[swz(mb * 32 + qi, ks * 2 + half)];
     f.b[mb] = *(bf16x8_t *)&u;
   }
-}
-
-template <int MB>
-__device__ __attribute__((always_inline)) inline void mfma(f32x16 (&acc)[2][MB], const Frags<MB> &f) {
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-      acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0);
 }
 
 // Piece j (0..MB+1) of a K step's fragments: the wave's W blocks, then the
@@ -184,21 +177,12 @@ __device__ __attribute__((always_inline)) inline void k_loop(f32x16 (&acc)[2][MB
     dma16(X, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
   };
   auto issue_w = [&](int stage, int sl) {
-    int ws = stage;  // stage within the sweep of W (stage < 3 SW)
-    if (ws >= SW) ws -= SW;
-    if (ws >= SW) ws -= SW;
-    const uint32_t kb = (uint32_t)ws * kKT * 2;
-    const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
 #pragma unroll
-    for (int i = 0; i < T::NW; ++i)
-      dma16(W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 8) * 128));
+    for (int i = 0; i < T::NW; ++i) copy_w(i, stage, sl);
   };
   auto issue_h = [&](int stage, int sl) {
-    const uint32_t kb = (uint32_t)stage * kKT * 2;
-    const uint32_t s0 = lds0 + T::RW * T::WBYTES + (uint32_t)sl * T::HBYTES;
 #pragma unroll
-    for (int i = 0; i < T::NH; ++i)
-      dma16(X, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
+    for (int i = 0; i < T::NH; ++i) copy_h(i, stage, sl);
   };
 
 #pragma unroll

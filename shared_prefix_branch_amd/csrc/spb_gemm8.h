@@ -39,15 +39,6 @@ __device__ __attribute__((always_inline)) inline void frags8(Frags8<MB> &f, cons
   for (int mb = 0; mb < MB; ++mb) f.b[mb] = frag8(Hb, mb * 32 + qi, c);
 }
 
-template <int MB>
-__device__ __attribute__((always_inline)) inline void mfma8(f32x16 (&acc)[2][MB], const Frags8<MB> &f) {
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-      acc[vb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[vb], f.b[mb], acc[vb][mb], 0, 0, 0, 0, 0, 0);
-}
-
 // A K step scheduled by hand, as k_step: after MFMA j, piece j of the next
 // step's fragments (two 16-byte reads) when READ, and copies c0 + j*CPS ..
 // +CPS below c1.
@@ -121,18 +112,12 @@ __device__ __attribute__((always_inline)) inline void k_loop8(f32x16 (&acc)[2][M
     dma16(X, hoff[i] + (uint32_t)stage * 128, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
   };
   auto issue_w = [&](int stage, int sl) {
-    const uint32_t kb = (uint32_t)stage * 128;
-    const uint32_t s0 = lds0 + (uint32_t)sl * T::WBYTES;
 #pragma unroll
-    for (int i = 0; i < T::NW; ++i)
-      dma16(W, woff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * 64 + i * 8) * 128));
+    for (int i = 0; i < T::NW; ++i) copy_w(i, stage, sl);
   };
   auto issue_h = [&](int stage, int sl) {
-    const uint32_t kb = (uint32_t)stage * 128;
-    const uint32_t s0 = lds0 + T::RW * T::WBYTES + (uint32_t)sl * T::HBYTES;
 #pragma unroll
-    for (int i = 0; i < T::NH; ++i)
-      dma16(X, hoff[i] + kb, __builtin_amdgcn_readfirstlane(s0 + (wave * T::NH + i) * 8 * 128));
+    for (int i = 0; i < T::NH; ++i) copy_h(i, stage, sl);
   };
 #pragma unroll
   for (int vb = 0; vb < 2; ++vb)
