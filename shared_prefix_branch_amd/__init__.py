@@ -422,6 +422,21 @@ class PreparedScore:
         self.pass_ = pass_
         self.meta = ctypes.c_void_p(d_meta.data_ptr())
         self.fn = lib().spb_score_options
+        self.out_sizes = (lp.numel(), p.numel(), residual.numel())
+        self.meta_bytes = d_meta.numel() * d_meta.element_size()
+        self._checked = None  # the plan whose pass shapes were last checked
+
+    def check_plan(self, plan: Plan):
+        """The outputs and the metadata buffer must hold the plan's pass:
+        the library takes raw pointers and cannot see their sizes."""
+        if self._checked is plan:
+            return
+        inf = plan.info(self.pass_)
+        need = (inf["n_options"], inf["n_options"], inf["n_branches"])
+        if any(have < n for have, n in zip(self.out_sizes, need)) or self.meta_bytes < inf["meta_bytes"]:
+            raise SpbError(-4, f"pass {self.pass_}: outputs hold {self.out_sizes} and metadata "
+                               f"{self.meta_bytes} bytes; the plan needs {need} and {inf['meta_bytes']}")
+        self._checked = plan
 
     def __call__(self, plan: Plan, stream=None, gemm_events=None):
         S = self.args
@@ -432,6 +447,7 @@ class PreparedScore:
             S.gemm_event_begin, S.gemm_event_end = gemm_events[0].cuda_event, gemm_events[1].cuda_event
         else:
             S.gemm_event_begin = S.gemm_event_end = None
+        self.check_plan(plan)
         _check(self.fn(plan.handle, self.pass_, self.meta, ctypes.byref(S), ctypes.c_void_p(_stream_handle(stream))))
 
 
@@ -467,10 +483,12 @@ class PreparedScoreBatch:
         self.passes = np.ascontiguousarray(passes, dtype=np.int32)
         self.metas = (ctypes.c_void_p * n)(*[m.data_ptr() for m in d_metas])
         self.args = (_ScoreArgs * n)()
+        self.each = []
         for i in range(n):
             one = PreparedScore(int(passes[i]), d_metas[i], hiddens[i], lm_head, workspace, *outs[i],
                                 lm_head_kind=lm_head_kind)
             self.args[i] = one.args
+            self.each.append(one)
         self.workspace = ctypes.c_void_p(workspace.data_ptr())
         self.workspace_bytes = workspace.numel() * workspace.element_size()
         self.fn = lib().spb_score_options_batch
@@ -484,6 +502,8 @@ class PreparedScoreBatch:
             A.gemm_event_begin, A.gemm_event_end = gemm_events[0].cuda_event, gemm_events[1].cuda_event
         else:
             A.gemm_event_begin = A.gemm_event_end = None
+        for one in self.each:
+            one.check_plan(plan)
         _check(self.fn(plan.handle, len(self.passes), _ptr(self.passes, _i32p), self.metas, self.args,
                        self.workspace, self.workspace_bytes, ctypes.c_void_p(_stream_handle(stream))))
 

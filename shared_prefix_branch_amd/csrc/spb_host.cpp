@@ -821,6 +821,20 @@ size_t score_batch_workspace_layout(int m_tot, int t_tot, int vocab, int hidden_
 
 const SpbMetaHeader &header(const PassPlan &P) { return *reinterpret_cast<const SpbMetaHeader *>(P.blob.data()); }
 
+// Limits of the attention kernel's metadata fields: stem index below bit 20
+// of a chunk's info word (below the stem flag), DFS numbers below 2^24, and
+// at most kMaxTileChunks key chunks in one work item's list.
+spb_status check_attention_limits(const PassPlan &P, int pass) {
+  if (P.stems.size() >= (1u << 20) || P.stem_base >= (1 << 24))
+    return fail(SPB_ERR_LIMIT, "pass %d holds %zu shared template stems, too many", pass, P.stems.size());
+  for (int g = 0; g < 3; ++g)
+    for (const SpbItem &it : P.items[g])
+      if (it.cost > kMaxTileChunks)
+        return fail(SPB_ERR_LIMIT, "pass %d: an attention tile needs %d key chunks, more than %d", pass, it.cost,
+                    kMaxTileChunks);
+  return ok();
+}
+
 spb_status check_pass(const spb_plan *plan, int32_t pass) {
   if (!plan) return fail(SPB_ERR_ARG, "plan is NULL");
   if (pass < 0 || pass >= (int32_t)plan->passes.size())
@@ -995,6 +1009,10 @@ spb_status spb_pack_pass(const spb_problem *P, const spb_pack_opts *opts, spb_pl
     PassPlan &pp = pk.passes[k];
     build_tiles(pp, pk.pass_groups[k], pk.pass_group_seg[k]);
     build_items(pp);
+    // what the attention kernel can run is decided here, so that a plan it
+    // would refuse is never handed out (raised limits, e.g. a long content)
+    spb_status lim = check_attention_limits(pp, (int)k);
+    if (lim != SPB_OK) return lim;
     build_scoring(pp, Q);
     build_blob(pp, (int)k);
   }
@@ -1205,14 +1223,8 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
     return fail(SPB_ERR_LIMIT, "a bf16 pass's K/V (%d tokens x %d heads x %d) must stay under 4 GiB", h.n_tokens, a->hkv,
                 a->head_dim);
   if (h.n_tiles == 0) return ok();
-  // stem chunk fields: stem index below bit 20 of the info word (below the
-  // stem flag), DFS numbers below 2^24
-  if (P.stems.size() >= (1u << 20) || P.stem_base >= (1 << 24))
-    return fail(SPB_ERR_LIMIT, "a pass holds %zu shared template stems, too many", P.stems.size());
-  for (int g = 0; g < 3; ++g)
-    for (const SpbItem &it : P.items[g])
-      if (it.cost > kMaxTileChunks)
-        return fail(SPB_ERR_LIMIT, "an attention tile needs %d key chunks, more than %d", it.cost, kMaxTileChunks);
+  st = check_attention_limits(P, pass);  // also checked when the plan was packed
+  if (st != SPB_OK) return st;
   AttnLaunch L{};
   L.q = a->q; L.k = a->k; L.v = a->v; L.o = a->o;
   L.in_dtype = a->in_dtype; L.out_dtype = a->out_dtype;

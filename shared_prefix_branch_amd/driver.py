@@ -29,7 +29,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from . import (Plan, PreparedAttention, PreparedScore, PreparedScoreBatch, score_batch_workspace_bytes,
+from . import (Plan, PreparedAttention, PreparedScore, PreparedScoreBatch, SpbError, score_batch_workspace_bytes,
                score_finalize, score_workspace_bytes)
 
 
@@ -84,6 +84,7 @@ class Job:
             raise ValueError("batch_head covers at most 64 passes")
         self.grouped = self.batch_head or self.head_rows > 0
         self.head_groups = self._group_passes(plan)
+        self._shapes = [tuple(plan.info(k)[f] for f in self._SHAPE_FIELDS) for k in range(plan.n_passes)]
 
     def _group_passes(self, plan: Plan) -> List[List[int]]:
         """The passes of each lm-head launch, in pass order."""
@@ -207,12 +208,29 @@ class Job:
         plan must have this job's pass shapes.  Returns the token ``run``
         takes."""
         plan = self.plan if plan is None else plan
+        self.check_shapes(plan)
         self._set ^= 1
         if self._set_done[self._set] is not None:
             self._set_done[self._set].synchronize()  # its previous upload has left the buffers
         for k in range(plan.n_passes):
             plan.meta_copy(k, self.meta_host[self._set][k])
         return plan, self._set
+
+    _SHAPE_FIELDS = ("n_tokens", "n_options", "n_branches", "n_scored_rows", "meta_bytes")
+
+    def check_shapes(self, plan: Plan):
+        """Raises SpbError unless ``plan`` has the pass shapes this job's
+        buffers were sized for (rows, options, branches, scored rows and
+        metadata bytes of every pass)."""
+        if plan is self.plan:  # the job's own plan, or one staged (and checked) before
+            return
+        if plan.n_passes != len(self._shapes):
+            raise SpbError(-4, f"the plan has {plan.n_passes} passes, this job {len(self._shapes)}")
+        for k in range(plan.n_passes):
+            got = tuple(plan.info(k)[f] for f in self._SHAPE_FIELDS)
+            if got != self._shapes[k]:
+                raise SpbError(-4, f"pass {k}: the plan's {dict(zip(self._SHAPE_FIELDS, got))} differ from this "
+                                   f"job's {dict(zip(self._SHAPE_FIELDS, self._shapes[k]))}")
 
     def _upload(self, which: int, stream):
         """Uploads pinned set ``which`` on the copy stream, pass k after the

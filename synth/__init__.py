@@ -301,6 +301,19 @@ def make_problem(name: str, cfg_seed: int, **over) -> Problem:
             k = int(rng.integers(1, nq + 1))
             asks.append(sorted(int(q) for q in rng.choice(nq, size=k, replace=False)))
         return _assemble(cl, asks, [len(x) for x in templates], q_opts, V, templates)
+    if name == "long":
+        # inputs at the request limits: one content of max_content tokens (the
+        # man page's default limit is 4,096), one of 1,000-2,000 and one of at
+        # most 64; templates of 100 to max_query tokens (limit 256), so a
+        # branch spans several 32-key chunks; multi-token labels
+        V = over.get("vocab", 1000)
+        nq = over.get("n_questions", 8)
+        q_len = rng.integers(100, over.get("max_query", 256) + 1, size=nq)
+        q_opts = [_label_options(rng, int(rng.integers(2, 5)), 3, V) for _ in range(nq)]
+        cl = [over.get("max_content", 4096), int(rng.integers(1000, 2001)), int(rng.integers(0, 65))]
+        asks = [sorted(int(q) for q in rng.choice(nq, size=int(rng.integers(3, nq + 1)), replace=False))
+                for _ in cl]
+        return _assemble(cl, asks, q_len, q_opts, V)
     if name == "random":
         # small random problems for oracle self-tests and packer tests
         V = over.get("vocab", 64)
@@ -358,11 +371,36 @@ def input_ident(which: tuple):
     return (STREAM_INPUT, idx) if kind == "input" else (STREAM_FLOOR, idx)
 
 
-def activation_block(wl: Workload, which: tuple, device="cpu", peaked: bool = False):
+# "sharp" query/key draws for parity tests that must be able to fail on the
+# score arithmetic: Q, K ~ N(0, 1), so q.k / sqrt(d) has a standard deviation
+# near 1 (the metric draws divide both by sqrt(d) again, which leaves scores
+# of std 1/d and a softmax that is almost a plain average), and a few planted
+# key rows scaled by SHARP_PLANT, whose scores (std about SHARP_PLANT) often
+# rise far above the maximum of the chunks before them.  Planted rows: inside
+# the content, the rows whose index is SHARP_CONTENT_AT mod SHARP_CONTENT_EVERY
+# (so never in the first 64-key chunk); after the content, the rows whose
+# offset from the content end is SHARP_TAIL_AT mod SHARP_TAIL_EVERY (inside a
+# template's first chunk of 32 keys, and again in every later one).
+SHARP_PLANT = 6.0
+SHARP_CONTENT_AT, SHARP_CONTENT_EVERY = 100, 128
+SHARP_TAIL_AT, SHARP_TAIL_EVERY = 7, 32
+
+
+def sharp_plant_rows(content: int, n_rows: int) -> np.ndarray:
+    """Boolean mask over a logical input's rows: the planted key rows."""
+    r = np.arange(n_rows)
+    tail = r - content
+    return np.where(r < content, r % SHARP_CONTENT_EVERY == SHARP_CONTENT_AT,
+                    tail % SHARP_TAIL_EVERY == SHARP_TAIL_AT)
+
+
+def activation_block(wl: Workload, which: tuple, device="cpu", peaked: bool = False, sharp: bool = False):
     """Q, K, V [rows, H*, d] (float32, before any dtype cast) and hidden [rows, H]
     for every logical row of one logical input, drawn from its own seed.
 
     Q, K, V ~ N(0,1)/sqrt(d); hidden ~ N(0,1)/sqrt(H) (``peaked``: N(0,1)).
+    ``sharp``: Q, K ~ N(0,1) with planted key rows (see SHARP_PLANT); V and
+    hidden as above.  The same seed draws the same normals in every mode.
     """
     torch = _torch()
     stream, ident = input_ident(which)
@@ -371,9 +409,14 @@ def activation_block(wl: Workload, which: tuple, device="cpu", peaked: bool = Fa
     g = torch.Generator(device=device)
     g.manual_seed(seed_for(wl.cfg_seed, stream, ident))
     s = 1.0 / np.sqrt(d.head_dim)
-    q = torch.randn((n, d.hq, d.head_dim), generator=g, device=device) * s
-    k = torch.randn((n, d.hkv, d.head_dim), generator=g, device=device) * s
+    sqk = 1.0 if sharp else s
+    q = torch.randn((n, d.hq, d.head_dim), generator=g, device=device) * sqk
+    k = torch.randn((n, d.hkv, d.head_dim), generator=g, device=device) * sqk
     v = torch.randn((n, d.hkv, d.head_dim), generator=g, device=device) * s
+    if sharp:
+        c = int(wl.problem.content_len[ident]) if which[0] == "input" else 0
+        plant = torch.from_numpy(sharp_plant_rows(c, n)).to(device)
+        k[plant] *= SHARP_PLANT
     g2 = torch.Generator(device=device)
     g2.manual_seed(seed_for(wl.cfg_seed, STREAM_HIDDEN, ident if stream == STREAM_INPUT else 10_000_000 + ident))
     h = torch.randn((n, d.hidden), generator=g2, device=device)
@@ -396,17 +439,22 @@ def lm_head(wl: Workload, device="cpu", dtype=None):
     return w.to(dtype if dtype is not None else torch.bfloat16)
 
 
-def fp8_scales(wl: Workload, calib_tokens: int = 4096):
+def fp8_scales(wl: Workload, calib_tokens: int = 4096, sharp: bool = False):
     """Per-tensor e4m3 scales s = amax / 448 for Q, K, V from a separate seeded
-    calibration draw of the same distribution (static calibration)."""
+    calibration draw of the same distribution (static calibration); ``sharp``
+    calibrates on the sharp draws, planted key rows included (the calibration
+    tokens read as one content)."""
     torch = _torch()
     d = wl.dims
     g = torch.Generator()
     g.manual_seed(seed_for(wl.cfg_seed, STREAM_CALIB, 0))
     s = 1.0 / np.sqrt(d.head_dim)
-    q = torch.randn((calib_tokens, d.hq, d.head_dim), generator=g) * s
-    k = torch.randn((calib_tokens, d.hkv, d.head_dim), generator=g) * s
+    sqk = 1.0 if sharp else s
+    q = torch.randn((calib_tokens, d.hq, d.head_dim), generator=g) * sqk
+    k = torch.randn((calib_tokens, d.hkv, d.head_dim), generator=g) * sqk
     v = torch.randn((calib_tokens, d.hkv, d.head_dim), generator=g) * s
+    if sharp:
+        k[torch.from_numpy(sharp_plant_rows(calib_tokens, calib_tokens))] *= SHARP_PLANT
     return tuple(float(t.abs().max()) / 448.0 for t in (q, k, v))
 
 

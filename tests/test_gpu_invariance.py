@@ -56,28 +56,40 @@ def _random_wl(dtype="bf16"):
     return wl
 
 
-def test_packed_equals_alone_random_multitoken():
-    wl = _random_wl()
+SHARP = pytest.mark.parametrize("sharp", [False, True], ids=["metric", "sharp"])
+
+
+@SHARP
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_packed_equals_alone_random_multitoken(dtype, sharp):
+    # sharp: planted keys whose scores rise far above their chunk's running
+    # maximum, so rows rescale mid-way; the bits must still not depend on the
+    # packing
+    wl = _random_wl(dtype)
     W, _ = lm_head(wl)
-    say("case: random multi-token problem, packed vs alone")
-    packed = Case(wl, 16384, peaked=True)
+    say(f"case: random multi-token problem, packed vs alone, dtype={dtype} sharp={sharp}")
+    packed = Case(wl, 16384, peaked=True, sharp=sharp)
     packed.run(W)
     P = _by_input(packed)
     for i in range(wl.problem.n_inputs):
-        alone = Case(wl, 16384, inputs=[i], peaked=True)
+        alone = Case(wl, 16384, inputs=[i], peaked=True, sharp=sharp)
         alone.run(W)
         _same(P[i], _by_input(alone)[i], f"input {i} alone")
 
 
-def test_orders_and_budgets_bit_identical_fp8():
+@SHARP
+def test_orders_and_budgets_bit_identical_fp8(sharp):
     wl = synth.make_workload("fp8", n_inputs=24)
     W, _ = lm_head(wl)
-    say("case: fp8, 3 orders x 3 budgets + alone; the third order's passes share lm-head launches (head groups)")
+    cache = {}
+    say(f"case: fp8, 3 orders x 3 budgets + alone; the third order's passes share lm-head launches "
+        f"(head groups); sharp={sharp}")
     ref = None
     for seed in (101, 102, 103):
         order = np.random.default_rng(seed).permutation(wl.problem.n_inputs).tolist()
         for budget in (8192, 16384, 32768):
-            c = Case(wl, budget, inputs=order, head_rows=768 if seed == 103 else 0)
+            c = Case(wl, budget, inputs=order, head_rows=768 if seed == 103 else 0, peaked=sharp, sharp=sharp,
+                     cache=cache)
             c.run(W)
             got = _by_input(c)
             say(f"  order seed {seed} budget {budget}: {c.plan.n_passes} passes, "
@@ -88,21 +100,22 @@ def test_orders_and_budgets_bit_identical_fp8():
                 for i in ref:
                     _same(ref[i], got[i], f"input {i} order {seed} budget {budget}")
     for i in (0, 5, 17):
-        c = Case(wl, 16384, inputs=[i])
+        c = Case(wl, 16384, inputs=[i], peaked=sharp, sharp=sharp, cache=cache)
         c.run(W)
         _same(ref[i], _by_input(c)[i], f"input {i} alone")
 
 
-def test_spilled_input_matches_alone_extreme_shape():
+@SHARP
+def test_spilled_input_matches_alone_extreme_shape(sharp):
     # inputs larger than a pass: content re-staged per pass, same bits as alone
     wl = synth.make_workload("extreme", n_inputs=3, n_questions=300, content=700, hidden=128, vocab=4096)
     W, _ = lm_head(wl)
-    say("case: extreme shape (scaled), spill at budget 2048")
-    packed = Case(wl, 2048)
+    say(f"case: extreme shape (scaled), spill at budget 2048, sharp={sharp}")
+    packed = Case(wl, 2048, peaked=sharp, sharp=sharp)
     packed.run(W)
     assert packed.plan.n_passes > 3
     P = _by_input(packed)
-    alone = Case(wl, 16384, inputs=[1])
+    alone = Case(wl, 16384, inputs=[1], peaked=sharp, sharp=sharp)
     alone.run(W)
     _same(P[1], _by_input(alone)[1], "input 1 unspilled alone")
 

@@ -49,18 +49,20 @@ def test_grid_templates_parity():
             f"attention rel err {ea:.2e}; scores {es}")
 
 
+@pytest.mark.parametrize("sharp", [False, True], ids=["metric", "sharp"])
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 8, 2, 64), ("bf16", 4, 4, 128), ("f32", 4, 2, 128),
                                              ("fp8", 8, 2, 128)])
-def test_random_shared_templates_parity(dtype, hq, hkv, d):
+def test_random_shared_templates_parity(dtype, hq, hkv, d, sharp):
     # long shared lead-ins (stems over several 32-key chunks), empty contents,
-    # inputs whose questions share nothing, spills at a small budget
+    # inputs whose questions share nothing, spills at a small budget; sharp:
+    # planted keys in the stems and branch chunks, with the comparison's guard
     wl = _shared_wl(dtype, hq, hkv, d)
     W, Wh = lm_head(wl)
     for budget in (16384, 180):
-        say(f"case: random shared templates dtype={dtype} hq={hq} hkv={hkv} d={d} budget {budget}")
-        case = Case(wl, budget, peaked=True)
+        say(f"case: random shared templates dtype={dtype} hq={hq} hkv={hkv} d={d} budget {budget} sharp={sharp}")
+        case = Case(wl, budget, peaked=True, sharp=sharp)
         case.run(W)
-        ea = check_attention(case)
+        ea = check_attention(case, guard=sharp)
         es = check_scores(case, oracle_scores(case, Wh))
         say(f"  passes {case.plan.n_passes} attention rel err {ea:.2e}; scores {es}")
 

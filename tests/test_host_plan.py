@@ -174,6 +174,19 @@ def test_budget_too_small_and_processed_limit():
     assert e.value.code == -2
 
 
+def test_unrunnable_attention_item_rejected_when_packed():
+    # a raised content limit can make one attention work item's key-chunk list
+    # longer than the kernel runs (320 chunks: 64-key content chunks plus
+    # branch chunks); the packer refuses such a plan instead of handing out one
+    # that fails after staging
+    ok = spb.pack_pass(_prob(content_len=[20000]), token_budget=32768, max_content_tokens=30000)
+    assert ok.n_passes == 1
+    with pytest.raises(spb.SpbError) as e:
+        spb.pack_pass(_prob(content_len=[20500]), token_budget=32768, max_content_tokens=30000)
+    assert e.value.code == -2
+    assert "key chunks" in spb.lib().spb_last_error().decode()
+
+
 def test_kernel_entry_points_validate_before_any_hip_call():
     plan = spb.pack_pass(_prob())
     L = spb.lib()
@@ -467,3 +480,33 @@ def test_head_groups_rule():
     assert plan.n_passes == 70
     g = groups(head_rows=10 ** 6)
     assert [len(x) for x in g] == [64, plan.n_passes - 64]
+
+
+def test_job_and_scoring_refuse_plans_of_other_shapes():
+    # buffers are sized from the plan a job was made for: a re-packed plan
+    # with more rows, options or branches in a pass is refused on the host
+    # instead of writing past the device buffers
+    import torch
+    from shared_prefix_branch_amd.driver import Job
+    wl = synth.make_workload("fp8", n_inputs=6, hidden=128, vocab=1000)
+    plan = spb.pack_pass(wl.problem, token_budget=8192)
+    same = spb.pack_pass(wl.problem, token_budget=8192)
+    other = spb.pack_pass(wl.problem.subset([0, 1, 2, 3, 4]), token_budget=8192)
+    job = Job(plan, 8, 2, 128, 128, 1000, torch.uint8, torch.bfloat16, torch.bfloat16, device="cpu")
+    job.check_shapes(same)
+    with pytest.raises(spb.SpbError) as e:
+        job.check_shapes(other)
+    assert e.value.code == -4
+    inf = plan.info(0)
+    meta = torch.empty(inf["meta_bytes"], dtype=torch.uint8)
+    hid = torch.empty((inf["n_tokens"], 128), dtype=torch.bfloat16)
+    W = torch.empty((1000, 128), dtype=torch.bfloat16)
+    ws = torch.empty(256, dtype=torch.uint8)
+    lp, p = torch.empty(inf["n_options"]), torch.empty(inf["n_options"])
+    res = torch.empty(inf["n_branches"])
+    sc = spb.PreparedScore(0, meta, hid, W, ws, lp, p, res)
+    sc.check_plan(same)
+    small = spb.PreparedScore(0, meta, hid, W, ws, lp[:-1], p, res)
+    with pytest.raises(spb.SpbError) as e:
+        small.check_plan(plan)
+    assert e.value.code == -4
