@@ -1,6 +1,11 @@
 """Benchmark of the packed scoring pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload news] [--layers L] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload moderation] [--layers L] [--no-cpu-baseline]
+
+The default workload is the moderation shape (300 contents x 106 questions of
+2-5 multi-token labels, 61 passes of 16,384 tokens), the largest of the
+configurations that fits one GPU; news, news2, extreme, fp8, tiny and grid are
+the others.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 pack the batch into token-budget passes (host C++), and per pass upload the
@@ -14,9 +19,15 @@ timing starts.
 Prints one JSON line: whole-job packed tokens/s as `value`, plus scored
 questions/s, per-kernel timings from HIP events recorded on the launch stream
 inside the timed steps, the roofline of the dominant kernel (the lm-head GEMM)
-and the oracle timed on the host cores as `cpu_baseline`.  The roofline's
-`traffic` is the kernel's HBM bytes per launch from the committed counter
-summary in profiles/ (null when the kernel source has changed since).
+and the oracle timed on the host cores as `cpu_baseline`.  Each lm-head launch
+is placed against its own bound (HBM at most 312 scored rows per W stream,
+MFMA above); `roofline` aggregates the launches of the bound that takes most
+of the head's time, never mixing the two, and `per_launch` lists every
+launch's bound and fraction.  Attention reports its MFMA utilisation on
+unmasked pairs against the peak of its input dtype (e4m3 Q.K^T with bf16 P.V:
+the mixed peak) and its HBM rate against algorithmic bytes.  `traffic` is the
+kernel's HBM bytes per launch from the committed counter summary for the
+workload in profiles/ (null when the kernel source has changed since).
 
 With --layers L the hidden states are not given: each pass first runs L
 decoder layers (synthetic bf16 weights, the news attention shape with a 4x
@@ -48,13 +59,19 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+# e4m3 attention: Q.K^T (half the flops) on the fp8 MFMA, P.V on the bf16 one
+PEAK_ATT_FP8_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)   # 3,333
 # lm-head ridge in scored rows per W stream: the head does M flop per W byte
 HEAD_RIDGE_ROWS = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # 312.5
 HERE = os.path.dirname(os.path.abspath(__file__))
-# the files that define the lm-head kernel and its tiling
-GEMM_SOURCES = ("shared_prefix_branch_amd/csrc/spb_score.hip", "shared_prefix_branch_amd/csrc/spb_gemm.h",
-                "shared_prefix_branch_amd/csrc/spb_dev.h", "shared_prefix_branch_amd/csrc/spb_head_layout.h")
-TRAFFIC_SUMMARY = "profiles/head_lse_kernel_news_traffic.md"
+# the files that define each kernel (a counter summary holds while they match)
+KERNEL_SOURCES = {
+    "head_lse_kernel": ("shared_prefix_branch_amd/csrc/spb_score.hip", "shared_prefix_branch_amd/csrc/spb_gemm.h",
+                        "shared_prefix_branch_amd/csrc/spb_dev.h", "shared_prefix_branch_amd/csrc/spb_head_layout.h"),
+    "branch_attention": ("shared_prefix_branch_amd/csrc/spb_attention.hip", "shared_prefix_branch_amd/csrc/spb_dev.h",
+                         "shared_prefix_branch_amd/csrc/spb_meta.h"),
+}
+DEFAULT_CPU_SAMPLE = {"moderation": 20, "fp8": 40}   # contents in the oracle's sample (else all)
 
 
 def parse():
@@ -62,7 +79,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="news")
+    ap.add_argument("--workload", default="moderation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0,
                     help="decoder layers in front of the head (synthetic weights, news model dims); "
@@ -77,7 +94,8 @@ def parse():
     ap.add_argument("--no-template-sharing", action="store_true",
                     help="drop the template token ids, so questions share no template prefix")
     ap.add_argument("--cpu-sample-inputs", type=int, default=0,
-                    help="contents in the oracle's sample (0: all of the workload's)")
+                    help="contents in the oracle's sample (0: the workload's default, all of them for news, "
+                         "tiny and extreme, 20 for moderation, 40 for fp8)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--head-batch", action="store_true",
                     help="one lm-head launch for all passes of the step (spb_score_options_batch) "
@@ -93,29 +111,30 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_source_hash() -> str:
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(HERE, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(mode: str):
-    """HBM bytes per lm-head GEMM launch (mode "batched": one launch for all
-    passes of the step; "per_pass") from the committed counter summary, or
-    None when it is missing or was taken on other kernel sources."""
-    path = os.path.join(HERE, TRAFFIC_SUMMARY)
+def measured_traffic(kernel: str, workload: str, mode: str = "per_launch"):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from the committed
+    counter summary profiles/<kernel>_<workload>_traffic.md, or None when it
+    is missing or was taken on other kernel sources."""
+    rel = f"profiles/{kernel}_{workload}_traffic.md"
+    path = os.path.join(HERE, rel)
     if not os.path.exists(path):
-        return None, "no counter summary"
+        return None, f"no counter summary for {workload}"
     text = open(path).read()
     m_src = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     m_val = re.search(r"hbm_bytes_per_launch\[" + mode + r"\]:\s*([0-9.eE+]+)", text)
     if not (m_src and m_val):
         return None, "counter summary unreadable"
-    if m_src.group(1) != gemm_source_hash():
+    if m_src.group(1) != source_hash(kernel):
         return None, "kernel changed since the counters were taken"
-    return float(m_val.group(1)), TRAFFIC_SUMMARY
+    return float(m_val.group(1)), rel
 
 
 def copy_calibration():
@@ -265,14 +284,31 @@ def main():
                 head_ms[k] += mk[2].elapsed_time(mk[3]) / args.steps
     pair_flops = 4.0 * d.head_dim * d.hq
     att_flops = np.array([plan.info(k)["unmasked_pairs"] * pair_flops for k in range(n_pass)])
+    # attention's algorithmic bytes: Q, K, V read once, O written once
+    b_in = {"bf16": 2, "fp8": 1, "f32": 4}[d.dtype]
+    b_out = 4 if d.dtype == "f32" else 2
+    att_bytes_tok = (d.hq + 2 * d.hkv) * d.head_dim * b_in + d.hq * d.head_dim * b_out
+    att_bytes = np.array([plan.info(k)["n_tokens"] * att_bytes_tok for k in range(n_pass)], dtype=np.float64)
+    att_peak = PEAK_ATT_FP8_TFLOPS if d.dtype == "fp8" else PEAK_BF16_TFLOPS
+    att_ridge = att_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    att_tflops = att_flops.sum() / (att_ms.sum() * 1e-3) / 1e12
+    att_gbs = att_bytes.sum() / (att_ms.sum() * 1e-3) / 1e9
+    att_ai = att_flops.sum() / att_bytes.sum()
+    att_bound = "mfma" if att_ai > att_ridge else "hbm"
     M = np.array([sum(plan.info(k)["n_scored_rows"] for k in g) for g in groups], dtype=np.float64)
     head_flops = 2.0 * d.hidden * d.vocab * M
     w_bytes = 2.0 * d.hidden * d.vocab
     head_bytes = w_bytes + M * d.hidden * 2.0
-    att_tflops = att_flops.sum() / (att_ms.sum() * 1e-3) / 1e12
     head_tflops = head_flops.sum() / (head_ms.sum() * 1e-3) / 1e12
     head_gbs = head_bytes.sum() / (head_ms.sum() * 1e-3) / 1e9
-    head_bound = "mfma" if M.mean() > HEAD_RIDGE_ROWS else "hbm"
+    # each launch against its own bound; the roofline aggregates the launches
+    # of the bound holding most of the head's time
+    bounds = np.where(M > HEAD_RIDGE_ROWS, "mfma", "hbm")
+    fracs = np.where(bounds == "mfma", head_flops / (head_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     head_bytes / (head_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+    t_mfma = float(head_ms[bounds == "mfma"].sum())
+    head_bound = "mfma" if t_mfma >= 0.5 * float(head_ms.sum()) else "hbm"
+    sel = bounds == head_bound
     stack = None
     if n_lin:
         # linear launches: (n, k) per kind; m = the pass's tokens
@@ -289,38 +325,45 @@ def main():
         lin_tf = lin_flops.sum() / (lin_ms.sum() * 1e-3) / 1e12
         per_kind = {}
         for j4, (name, n_, k_) in enumerate(kinds):
-            sel = [j for j in range(n_lin) if j % 4 == j4]
-            ms_k = float(lin_ms[:, sel].sum())
+            js = [j for j in range(n_lin) if j % 4 == j4]
+            ms_k = float(lin_ms[:, js].sum())
             per_kind[name] = {"n": n_, "k": k_, "ms": round(ms_k, 4),
-                              "tflops": round(float(lin_flops[:, sel].sum()) / (ms_k * 1e-3) / 1e12, 2)}
+                              "tflops": round(float(lin_flops[:, js].sum()) / (ms_k * 1e-3) / 1e12, 2)}
         peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
         stack = {"layers": md.layers, "hidden": md.hidden, "ffn": md.ffn, "linear_dtype": "e4m3" if args.fp8 else "bf16",
                  "forward_ms": round(float(att_ms.sum()), 4),
                  "linear": {"ms": round(float(lin_ms.sum()), 4), "tflops": round(lin_tf, 2),
                             "frac": round(lin_tf / peak, 4), "launches_per_step": int(n_pass * n_lin),
                             "per_kind": per_kind}}
-    if args.workload != "news":
-        traffic, traffic_src = None, "counters taken on news only"
-    elif head_kind != 0:
+    kernel_name = "head_lse_kernel"
+    if head_kind != 0:
         traffic, traffic_src = None, "counters taken for the f32out lm head only"
+    elif batch_head or (args.head_rows > 0 and n_head != n_pass):
+        traffic, traffic_src = None, "counters taken with one lm-head launch per pass only"
     else:
-        traffic, traffic_src = measured_traffic("batched" if batch_head else "per_pass")
-        if args.head_rows > 0 and not batch_head and n_head != n_pass:
-            traffic, traffic_src = None, "counters taken per pass and for one launch per step only"
+        traffic, traffic_src = measured_traffic(kernel_name, args.workload)
     if head_bound == "mfma":
-        roof = {"bound": "mfma", "achieved": round(head_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(head_tflops / PEAK_BF16_TFLOPS, 4)}
+        ach = float(head_flops[sel].sum() / (head_ms[sel].sum() * 1e-3) / 1e12)
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
     else:
-        roof = {"bound": "hbm", "achieved": round(head_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(head_gbs / PEAK_HBM_GBS, 4)}
+        ach = float(head_bytes[sel].sum() / (head_ms[sel].sum() * 1e-3) / 1e9)
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["traffic_source"] = traffic_src
+    roof["algorithmic_bytes_per_launch"] = round(float(head_bytes.mean()))
     roof["kernel"] = "head_lse_kernel (lm-head GEMM with fused log-sum-exp, in spb_score_options)"
+    roof["launches"] = f"{int(sel.sum())} of {n_head} lm-head launches per step are {head_bound}-bound; " \
+                       f"achieved is over those"
     # the fp32 head runs three bf16 products per logit term (hi, mid, lo planes of h)
     roof["mfma_products_per_term"] = 3 if head_kind == 2 else 1
+    roof["time_weighted_frac"] = round(float((fracs * head_ms).sum() / head_ms.sum()), 4)
     roof["per_launch"] = {"ms": [round(x, 4) for x in head_ms], "scored_rows": M.astype(int).tolist(),
+                          "bound": bounds.tolist(), "frac": [round(float(x), 4) for x in fracs],
                           "flops_per_scored_row": 2 * d.hidden * d.vocab,
                           "algorithmic_bytes": [int(x) for x in head_bytes]}
+    att_traffic, att_traffic_src = measured_traffic("branch_attention", args.workload)
 
     if stack is not None:
         # the linear layers dominate the step: their GEMM kernel is the roofline
@@ -346,7 +389,14 @@ def main():
                    "template_sharing": prob.tmpl_tok is not None, "decoder_layers": args.layers},
         "questions_per_s": round(questions / (ms_step * 1e-3), 1),
         "attention": {"ms": round(float(att_ms.sum()), 4), "tflops": round(att_tflops, 2),
-                      "mfma_util": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+                      "mfma_util": round(att_tflops / att_peak, 4), "mfma_peak": round(att_peak, 1),
+                      "gbs": round(att_gbs, 1), "hbm_frac": round(att_gbs / PEAK_HBM_GBS, 4),
+                      "arithmetic_intensity": round(att_ai, 1), "bound": att_bound,
+                      "roofline_frac": round((att_tflops / att_peak) if att_bound == "mfma"
+                                             else (att_gbs / PEAK_HBM_GBS), 4),
+                      "algorithmic_bytes_per_launch": round(float(att_bytes.mean())),
+                      "traffic": None if att_traffic is None else round(att_traffic),
+                      "traffic_source": att_traffic_src,
                       "unmasked_pairs": int(info["unmasked_pairs"])},
         "head": {"ms": round(float(head_ms.sum()), 4), "tflops": round(head_tflops, 2), "gbs": round(head_gbs, 1),
                  "scored_rows": int(M.sum())},
@@ -365,7 +415,8 @@ def main():
         if md is not None:
             line["cpu_baseline"] = cpu_baseline_stack(wl, md, W)
         else:
-            n_cpu = args.cpu_sample_inputs if args.cpu_sample_inputs > 0 else prob.n_inputs
+            n_cpu = args.cpu_sample_inputs if args.cpu_sample_inputs > 0 else \
+                DEFAULT_CPU_SAMPLE.get(args.workload, prob.n_inputs)
             line["cpu_baseline"] = cpu_baseline(wl, W, scales, min(n_cpu, prob.n_inputs))
     print(json.dumps(line), flush=True)
 
