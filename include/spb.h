@@ -56,6 +56,15 @@ enum {
 
 typedef enum { SPB_F32 = 0, SPB_BF16 = 1, SPB_FP8_E4M3 = 2 /* OCP e4m3fn */ } spb_dtype;
 
+/* The message of the last failed spb_* call on the calling thread: what went
+ * wrong, with the offending index or size (e.g. "question 3: template of 300
+ * tokens exceeds max_query_tokens 256").  The pages name the engine's error
+ * envelopes without giving their contents [PyPI "Status": the response and
+ * error envelopes]; this string is what such an envelope's message would
+ * carry, and the negative spb_status its kind.  Returns "" when the last
+ * spb_* call on this thread succeeded (or none was made).  The pointer is
+ * library-owned, thread-local and valid until the next spb_* call on the same
+ * thread; never NULL. */
 const char *spb_last_error(void);
 /* Build id, tile constants and numerics-contract version.  Two results are
  * bit-comparable when their fingerprints are equal (PyPI "What it does":
@@ -118,6 +127,9 @@ typedef struct {
   int64_t max_processed_tokens;  /* default 2000000 (all passes, re-staged content, floors) */
 } spb_pack_opts;
 
+/* Fills *opts (caller-owned) with the defaults: a 16,384-token budget [man
+ * PARAMETERS --token-budget], floors on [article, the floor paragraph], and the
+ * man page's request limits [man PARAMETERS].  A NULL opts is ignored. */
 void spb_pack_opts_default(spb_pack_opts *opts);
 
 typedef struct spb_plan spb_plan; /* opaque, library-owned */
@@ -145,33 +157,76 @@ typedef struct {
  * Cites [PyPI "What it does": Throughput; man PARAMETERS --token-budget,
  * --max-tokens and the request limits; man CAVEATS]. */
 spb_status spb_pack_pass(const spb_problem *problem, const spb_pack_opts *opts, spb_plan **out);
+/* Releases a plan made by spb_pack_pass (NULL is accepted and ignored).  The
+ * pages name no such step: the plan is this library's own handle.  Device
+ * memory the caller filled from the plan (uploaded metadata) stays the
+ * caller's; after the call the plan must not be used. */
 void spb_plan_free(spb_plan *plan);
+/* The number of passes the plan packs its inputs into (*n >= 1).  The pages
+ * count passes for the news set ("packs the 24 articles into two 16k-token
+ * passes" [PyPI "Speed and scale"]) and add packed tokens and engine
+ * internals to a response on request [man PARAMETERS --debug]; this is that
+ * count.  SPB_ERR_ARG for a NULL plan or n. */
 spb_status spb_plan_num_passes(const spb_plan *plan, int32_t *n);
-spb_status spb_plan_info(const spb_plan *plan, int32_t pass, spb_pass_info *out); /* pass -1: totals */
-/* logical_row[n_tokens]: the logical row placed at each pass row.
- * scored_row[n_scored_rows]: pass rows read by the lm head, in scoring order.
- * Either pointer may be NULL.  Host buffers, caller-owned. */
+/* Sizes of pass `pass` (0 .. n_passes-1), or with pass = -1 the sums over
+ * all passes (meta_bytes then is the largest pass's): the packed tokens and
+ * engine internals a debug response shows [man PARAMETERS --debug], and every
+ * size a caller needs to allocate the pass's device buffers (n_tokens rows of
+ * Q/K/V/O and hidden states, meta_bytes of metadata, n_options and n_branches
+ * score outputs).  n_passes, n_content_branches, n_content_options and
+ * n_logical_inputs are plan totals in every call.  *out is caller-owned host
+ * memory.  SPB_ERR_ARG for a NULL argument or a pass out of range. */
+spb_status spb_plan_info(const spb_plan *plan, int32_t pass, spb_pass_info *out);
+/* The placement map of one pass [PyPI "Layout": packer.py packs; man
+ * PARAMETERS --debug: packed tokens]: logical_row[n_tokens] receives the
+ * logical row (numbered as above) placed at each pass row; a re-staged
+ * content row appears in every pass that holds it.  scored_row[n_scored_rows]
+ * receives the pass rows read by the lm head, in scoring order.  Either
+ * pointer may be NULL (that array is skipped).  Host buffers, caller-owned,
+ * sized from spb_plan_info.  SPB_ERR_ARG for a NULL plan or a pass out of
+ * range; nothing is written then. */
 spb_status spb_plan_rows(const spb_plan *plan, int32_t pass, int64_t *logical_row, int32_t *scored_row);
-/* Per placed branch of the pass: its logical branch (content branches numbered
- * in input / CSR order, then floor branches in ascending question id) and its
- * first option slot.  Either pointer may be NULL. */
+/* Per placed branch of the pass (every question is a branch of its input's
+ * read [PyPI "What it does": Many questions, one read]): its logical branch
+ * (content branches numbered in input / CSR order, then floor branches in
+ * ascending question id) and its first option slot in the pass's lp / p
+ * outputs.  Host arrays of n_branches, caller-owned; either pointer may be
+ * NULL.  SPB_ERR_ARG for a NULL plan or a pass out of range. */
 spb_status spb_plan_branches(const spb_plan *plan, int32_t pass, int32_t *logical_branch, int32_t *opt_first);
-/* Logical inputs in row-numbering order (inputs, then floor inputs):
- * row_off[n_logical_inputs + 1] is the first logical row of each;
- * floor_question[n_logical_inputs] is the question of a floor input, -1 for
- * a content input.  Either pointer may be NULL. */
+/* Logical inputs in row-numbering order (inputs, then floor inputs, one per
+ * asked question [article, the floor paragraph]): row_off[n_logical_inputs +
+ * 1] is the first logical row of each; floor_question[n_logical_inputs] is the
+ * question of a floor input, -1 for a content input.  The numbering is this
+ * library's addressing of activations; the pages have none.  Host arrays,
+ * caller-owned; either pointer may be NULL.  SPB_ERR_ARG for a NULL plan. */
 spb_status spb_plan_inputs(const spb_plan *plan, int64_t *row_off, int32_t *floor_question);
-/* Host debugging aid: the pass rows that pass row `row` attends to, read from
- * the same metadata and visibility rule the kernel uses. */
+/* Host debugging aid: the pass rows that pass row `row` attends to (its own
+ * content and the causal prefix of its own branch [PyPI "What it does": Many
+ * questions, one read]), read from the same metadata and visibility rule the
+ * kernel uses, in key order.  keys[cap] is caller-owned; *n_keys receives the
+ * count.  SPB_ERR_ARG for a NULL argument or a pass or row out of range,
+ * SPB_ERR_SIZE when more than cap keys are visible. */
 spb_status spb_plan_visible(const spb_plan *plan, int32_t pass, int32_t row, int32_t *keys, int32_t cap,
                             int32_t *n_keys);
-/* Copies the pass's device metadata (meta_bytes) from host to d_meta on the
- * stream.  d_meta: device memory, 256-byte aligned, caller-owned. */
+/* Enqueues the host-to-device copy of the pass's metadata (meta_bytes bytes:
+ * row, tile, work-item, chunk, branch and scoring tables, the layout
+ * branch_attention and score_options read) into d_meta on `stream` (a
+ * hipStream_t; NULL = the null stream).  The pages name no upload step: it is
+ * the host-to-device half of one packed forward [PyPI "Layout": packer.py,
+ * scorer.py].  d_meta: device memory of at least `bytes` >= meta_bytes,
+ * 256-byte aligned, caller-owned; it must stay untouched until the copy and
+ * every kernel reading it have run.  The host side is read from the plan,
+ * which must outlive the copy.  Checks run first and enqueue nothing on
+ * failure: SPB_ERR_ARG (NULL plan or d_meta, pass out of range, misaligned
+ * d_meta), SPB_ERR_SIZE (bytes < meta_bytes); SPB_ERR_HIP if the runtime
+ * refuses the copy. */
 spb_status spb_plan_upload(const spb_plan *plan, int32_t pass, void *d_meta, size_t bytes, void *stream);
 /* Host-to-host copy of the same metadata bytes into caller memory (bytes >=
  * meta_bytes), e.g. pinned memory from which the caller uploads the pass
  * asynchronously on a copy stream, overlapping the previous pass's kernels.
- * The device layout is identical to what spb_plan_upload writes. */
+ * The device layout is identical to what spb_plan_upload writes.  No passage
+ * of the pages: a staging variant of the upload.  SPB_ERR_ARG (NULL argument,
+ * pass out of range), SPB_ERR_SIZE (bytes < meta_bytes); nothing written then. */
 spb_status spb_plan_meta_copy(const spb_plan *plan, int32_t pass, void *host_dst, size_t bytes);
 
 /* ------------------------------------------------------------------ attention

@@ -32,7 +32,9 @@ HEAD_F32OUT, HEAD_BF16, HEAD_FP32 = 0, 1, 2  # lm-head output kinds
 LINEAR_BF16, LINEAR_RESIDUAL, LINEAR_SILU_GATE, LINEAR_QKV_ROPE, LINEAR_F32 = 0, 1, 2, 3, 4  # linear epilogues
 MAX_SLOT_RANGES, MAX_TOPK, MAX_BEAMS = 16, 16, 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libspb.so")
+# SPB_LIBRARY names another build of the same C ABI (the host-only sanitizer
+# build used by the host tests); by default the gfx950 library built in-tree.
+library_path = os.environ.get("SPB_LIBRARY") or os.path.join(_HERE, "libspb.so")
 
 EXPORTED_SYMBOLS = [
     "spb_last_error", "spb_fingerprint", "spb_pack_opts_default", "spb_pack_pass", "spb_plan_free",

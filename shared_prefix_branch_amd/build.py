@@ -47,5 +47,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The host-only sanitizer build: the planner, plan accessors and validations
+# of spb_host.cpp under AddressSanitizer and UndefinedBehaviorSanitizer, built
+# by g++ (no GPU code; the kernel launchers are spb_host_nogpu.cpp, which
+# refuse every launch).  Loaded in place of libspb.so through SPB_LIBRARY by
+# the host tests, in a process started with the ASan runtime preloaded.
+SAN_LIB = os.path.join(HERE, "_build", "libspb_host_san.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_host_sanitized() -> str:
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    tmp = SAN_LIB + ".tmp"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROCM, "include"), "-I", os.path.join(HERE, "..", "include"),
+           os.path.join(CSRC, "spb_host.cpp"), os.path.join(CSRC, "spb_host_nogpu.cpp"),
+           "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed ({r.returncode}):\n{r.stdout}{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -41,10 +41,6 @@ __device__ inline uint32_t f2bf(float f) {  // round to nearest even (finite inp
 }
 
 // (value, id) with the order: larger value first, then smaller id.
-struct Cand {
-  float v;
-  int id;
-};
 __device__ inline bool better(const Cand &a, const Cand &b) { return a.v > b.v || (a.v == b.v && a.id < b.id); }
 
 // ------------------------------------------------------------ row gather
@@ -68,7 +64,6 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherLaunch a) {
 // ------------------------------------------------------------ top-k + LSE
 
 constexpr int kTopkThreads = 256;
-constexpr int kTopkSpan = 8192;  // vocabulary entries per work group of the first kernel
 
 // Merges two (max, sum of exp) partials.
 __device__ inline void lse_merge(float &m, float &s, float m2, float s2) {
@@ -117,11 +112,6 @@ __device__ inline void topk_tree(float *sm, float *ss, Cand (*sl)[kMaxTopK], int
     __syncthreads();
   }
 }
-
-struct TopkPart {  // one work group's partial of one row
-  float m, s;
-  Cand best[kMaxTopK];
-};
 
 // First kernel: work group (row, part) covers vocabulary entries
 // part*8192 .. +8192; each thread reads 8 entries per round (two 16-byte
@@ -484,11 +474,6 @@ int launch_gather_rows(const GatherLaunch &a, void *stream) {
   if (blocks > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
-}
-
-size_t topk_workspace_bytes(long long rows, int vocab) {
-  const int n_parts = (vocab + kTopkSpan - 1) / kTopkSpan;
-  return (size_t)rows * n_parts * sizeof(TopkPart);
 }
 
 int launch_topk_lse(const TopkLaunch &a, void *stream) {

@@ -119,7 +119,21 @@ struct TopkLaunch {
   float *lse;                // [rows]
   void *workspace;           // topk_workspace_bytes(rows, vocab)
 };
-size_t topk_workspace_bytes(long long rows, int vocab);
+// The top-k workspace: one partial per (row, vocabulary span of kTopkSpan
+// entries), each a running (max, sum of exp) and its best kMaxTopK candidates.
+constexpr int kTopkSpan = 8192;  // vocabulary entries per work group of the first kernel
+struct Cand {
+  float v;
+  int id;
+};
+struct TopkPart {  // one work group's partial of one row
+  float m, s;
+  Cand best[kMaxTopK];
+};
+inline size_t topk_workspace_bytes(long long rows, int vocab) {
+  const int n_parts = (vocab + kTopkSpan - 1) / kTopkSpan;
+  return (size_t)rows * n_parts * sizeof(TopkPart);
+}
 
 struct DecodeAttnLaunch {
   const uint16_t *q;         // [R][hq][d] bf16
