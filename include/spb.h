@@ -309,6 +309,25 @@ spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t
 spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *args,
                              void *stream);
 
+/* spb_score_options for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, with the workspace
+ * taken from a library-owned device array of 64 MiB per GPU instead of
+ * args->workspace (which is ignored, as is workspace_bytes).  The array is
+ * in the library's code object: each GPU the library runs on holds its own
+ * copy until the process ends; its address is looked up once per device, on
+ * the first call with that device current.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array and finds the last call's
+ * contents there (the kernels write every byte they read, so nothing needs
+ * clearing): calls that overlap on one GPU, on different streams or threads,
+ * race and corrupt each other's results; serialise them.  A pass whose
+ * workspace (spb_score_workspace_bytes) exceeds 64 MiB is refused with
+ * SPB_ERR_SIZE before anything is enqueued: about 4,200 scored rows at
+ * vocabulary 262,144 and hidden 3,840 with f32out or bf16 output, 2,100 with
+ * fp32.  Otherwise the arguments, checks and errors are spb_score_options'. */
+spb_status spb_score_options_noalloc(const spb_plan *plan, int32_t pass, const void *d_meta,
+                                     const spb_score_args *args, void *stream);
+
 /* Several passes' scored rows through ONE lm-head stream: W is read once for
  * the whole batch instead of once per pass (for passes whose scored rows alone
  * leave the head HBM-bound, this moves the head toward its MFMA roofline).

@@ -16,6 +16,7 @@ import numpy as np
 
 __all__ = [
     "SpbError", "lib", "library_path", "fingerprint", "Plan", "pack_pass", "branch_attention",
+    "score_options_noalloc",
     "PreparedAttention", "PreparedScore", "PreparedScoreBatch", "score_batch_workspace_bytes",
     "score_options_batch",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
@@ -41,6 +42,7 @@ EXPORTED_SYMBOLS = [
     "spb_plan_num_passes", "spb_plan_info", "spb_plan_rows", "spb_plan_branches", "spb_plan_inputs",
     "spb_plan_visible",
     "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
+    "spb_score_options_noalloc",
     "spb_score_batch_workspace_bytes", "spb_score_options_batch",
     "spb_score_finalize", "spb_plan_positions", "spb_rope_table", "spb_rmsnorm", "spb_linear",
     "spb_plan_slot", "spb_gather_rows", "spb_topk_workspace_bytes", "spb_topk_lse", "spb_decode_attention",
@@ -188,6 +190,7 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_options.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.POINTER(_ScoreArgs), ctypes.c_void_p]
+        L.spb_score_options_noalloc.argtypes = L.spb_score_options.argtypes
         L.spb_score_batch_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_options_batch.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.POINTER(ctypes.c_void_p),
@@ -396,7 +399,9 @@ def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int, l
 
 
 class PreparedScore:
-    """spb_score_options with its arguments marshalled once."""
+    """spb_score_options with its arguments marshalled once.  workspace=None:
+    spb_score_options_noalloc, whose workspace is the library's own per-GPU
+    scratch (calls on one GPU must not overlap)."""
 
     def __init__(self, pass_: int, d_meta, hidden, lm_head, workspace, lp, p, residual, lm_head_kind: int = 0):
         import torch
@@ -414,8 +419,9 @@ class PreparedScore:
             raise SpbError(-1, "lm_head and hidden disagree on the hidden size")
         S.lm_head = lm_head.data_ptr()
         S.vocab = int(lm_head.shape[0])
-        S.workspace = workspace.data_ptr()
-        S.workspace_bytes = workspace.numel() * workspace.element_size()
+        if workspace is not None:
+            S.workspace = workspace.data_ptr()
+            S.workspace_bytes = workspace.numel() * workspace.element_size()
         S.lp = ctypes.cast(ctypes.c_void_p(lp.data_ptr()), _f32p)
         S.p = ctypes.cast(ctypes.c_void_p(p.data_ptr()), _f32p)
         S.residual = ctypes.cast(ctypes.c_void_p(residual.data_ptr()), _f32p)
@@ -423,7 +429,7 @@ class PreparedScore:
         self.args = S
         self.pass_ = pass_
         self.meta = ctypes.c_void_p(d_meta.data_ptr())
-        self.fn = lib().spb_score_options
+        self.fn = lib().spb_score_options if workspace is not None else lib().spb_score_options_noalloc
         self.out_sizes = (lp.numel(), p.numel(), residual.numel())
         self.meta_bytes = d_meta.numel() * d_meta.element_size()
         self._checked = None  # the plan whose pass shapes were last checked
@@ -462,6 +468,14 @@ def score_options(plan: Plan, pass_: int, d_meta, hidden, lm_head, workspace, lp
     HEAD_BF16 or HEAD_FP32."""
     PreparedScore(pass_, d_meta, hidden, lm_head, workspace, lp, p, residual, lm_head_kind)(plan, stream,
                                                                                                gemm_events)
+
+
+def score_options_noalloc(plan: Plan, pass_: int, d_meta, hidden, lm_head, lp, p, residual, stream=None,
+                          gemm_events=None, lm_head_kind: int = 0):
+    """score_options without a workspace argument: spb_score_options_noalloc
+    (no device allocation; the library's per-GPU scratch; calls on one GPU
+    must not overlap)."""
+    PreparedScore(pass_, d_meta, hidden, lm_head, None, lp, p, residual, lm_head_kind)(plan, stream, gemm_events)
 
 
 def score_batch_workspace_bytes(plan: Plan, passes: Sequence[int], vocab: int, hidden_dim: int,

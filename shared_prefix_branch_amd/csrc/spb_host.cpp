@@ -1259,8 +1259,13 @@ spb_status spb_score_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t
   return ok();
 }
 
-spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *a,
-                             void *stream) {
+namespace {
+
+// spb_score_options' checks and launches; own_scratch: the workspace is the
+// library's allocation-free scratch of the current device instead of the
+// caller's a->workspace.
+spb_status score_options_at(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *a,
+                            void *stream, bool own_scratch) {
   spb_status st = check_pass(plan, pass);
   if (st != SPB_OK) return st;
   if (!a || !d_meta) return fail(SPB_ERR_ARG, "NULL argument");
@@ -1277,11 +1282,26 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   if (a->lm_head_kind < SPB_HEAD_F32OUT || a->lm_head_kind > SPB_HEAD_FP32)
     return fail(SPB_ERR_ARG, "lm_head_kind %d outside 0..2", a->lm_head_kind);
   const size_t need = score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, a->lm_head_kind, nullptr);
-  if (a->workspace_bytes < need) return fail(SPB_ERR_SIZE, "workspace needs %zu bytes, got %zu", need, a->workspace_bytes);
-  if (h.n_scored > 0 && (!a->hidden || !a->lm_head || !a->workspace || !a->lp || !a->p || !a->residual))
+  if (own_scratch) {
+    if (need > kScoreScratchBytes)
+      return fail(SPB_ERR_SIZE, "the pass's head workspace needs %zu bytes, more than the %zu bytes of the "
+                  "allocation-free scratch (%d scored rows)", need, kScoreScratchBytes, h.n_scored);
+  } else if (a->workspace_bytes < need) {
+    return fail(SPB_ERR_SIZE, "workspace needs %zu bytes, got %zu", need, a->workspace_bytes);
+  }
+  if (h.n_scored > 0 && (!a->hidden || !a->lm_head || (!own_scratch && !a->workspace) || !a->lp || !a->p ||
+                         !a->residual))
     return fail(SPB_ERR_ARG, "NULL tensor");
-  if ((uintptr_t)d_meta % 256 || (uintptr_t)a->workspace % 256) return fail(SPB_ERR_ARG, "d_meta and workspace must be 256-byte aligned");
+  if ((uintptr_t)d_meta % 256 || (!own_scratch && (uintptr_t)a->workspace % 256))
+    return fail(SPB_ERR_ARG, "d_meta and workspace must be 256-byte aligned");
   if (h.n_scored == 0) return ok();
+  char *ws = (char *)a->workspace;
+  if (own_scratch) {
+    void *scr = nullptr;
+    int e = score_scratch(&scr);
+    if (e) return fail(SPB_ERR_HIP, "allocation-free scratch: %s", hip_error_string(e));
+    ws = (char *)scr;
+  }
   ScoreLaunch L{};
   L.hidden = a->hidden; L.h_dtype = a->h_dtype; L.hidden_dim = a->hidden_dim;
   L.lm_head = a->lm_head; L.vocab = a->vocab;
@@ -1296,7 +1316,6 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   L.step_row = base + h.off_step_row;
   size_t off[4];
   score_workspace_layout(h.n_scored, h.n_targets, a->vocab, a->hidden_dim, a->lm_head_kind, off);
-  char *ws = (char *)a->workspace;
   L.part = (float *)(ws + off[0]);
   L.tz = (float *)(ws + off[1]);
   L.lse = (float *)(ws + off[2]);
@@ -1307,6 +1326,18 @@ spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_m
   int e = launch_score(L, stream);
   if (e) return fail(SPB_ERR_HIP, "score launch: %s", hip_error_string(e));
   return ok();
+}
+
+}  // namespace
+
+spb_status spb_score_options(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_score_args *a,
+                             void *stream) {
+  return score_options_at(plan, pass, d_meta, a, stream, false);
+}
+
+spb_status spb_score_options_noalloc(const spb_plan *plan, int32_t pass, const void *d_meta,
+                                     const spb_score_args *a, void *stream) {
+  return score_options_at(plan, pass, d_meta, a, stream, true);
 }
 
 namespace {

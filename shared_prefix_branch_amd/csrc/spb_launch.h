@@ -182,6 +182,11 @@ int launch_linear(const LinearLaunch &a, void *stream);
 
 int launch_attention(const AttnLaunch &a, void *stream);
 int launch_score(const ScoreLaunch &a, void *stream);
+// The allocation-free head's workspace: a device array of this many bytes per
+// GPU; score_scratch gives the current device's address of it (taken once per
+// device), or returns a hipError_t value.
+constexpr size_t kScoreScratchBytes = size_t(64) << 20;
+int score_scratch(void **out);
 int launch_score_batch(const ScoreBatchLaunch &a, void *stream);
 const char *hip_error_string(int err);
 

@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace spb {
 namespace {
 
@@ -478,6 +480,36 @@ int launch_score_batch(const ScoreBatchLaunch &a, void *stream) {
     e = launch_finalize(f, P.n_branches, s);
     if (e) return e;
   }
+  return 0;
+}
+
+// ------------------------------------------------------ allocation-free head
+// The workspace of spb_score_options_noalloc: one file-scope device array per
+// GPU (each device that loads the library holds its own copy until the
+// process ends).  Host code never passes the array's name to a kernel or a
+// copy: in host code it is a host-side stand-in.  Its device address is taken
+// once per device, with that device current, and kept.
+namespace {
+__device__ __align__(256) unsigned char scratch[kScoreScratchBytes];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kScratchDevices] = {};
+}  // namespace
+
+int score_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kScratchDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!ptr || (uintptr_t)ptr % 256) return (int)hipErrorInvalidSymbol;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
   return 0;
 }
 

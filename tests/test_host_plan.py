@@ -510,3 +510,28 @@ def test_job_and_scoring_refuse_plans_of_other_shapes():
     with pytest.raises(spb.SpbError) as e:
         small.check_plan(plan)
     assert e.value.code == -4
+
+
+def test_noalloc_head_refuses_a_pass_beyond_its_scratch():
+    # the allocation-free head has 64 MiB of scratch per GPU: a pass whose
+    # head workspace is larger is refused on the host, before any HIP call,
+    # with SPB_ERR_SIZE (host tensors stand in for the device buffers: the
+    # call returns before it reads them)
+    import torch
+    H, V, M = 4096, 262144, 2200
+    prob = synth.Problem(np.array([0], np.int32), np.array([0, M], np.int32), np.arange(M, dtype=np.int32),
+                         np.ones(M, np.int32), np.arange(0, 2 * M + 1, 2, dtype=np.int32),
+                         np.arange(2 * M + 1, dtype=np.int32), (np.arange(2 * M) * 97 % V).astype(np.int32), V)
+    plan = spb.pack_pass(prob, floors=False)
+    assert spb.score_workspace_bytes(plan, 0, V, H, spb.HEAD_FP32) > 64 << 20
+    assert spb.score_workspace_bytes(plan, 0, V, H, spb.HEAD_F32OUT) < 64 << 20
+    inf = plan.info(0)
+    meta = torch.empty(inf["meta_bytes"] + 256, dtype=torch.uint8)
+    meta = meta[(-meta.data_ptr()) % 256:][:inf["meta_bytes"]]
+    hid = torch.empty((inf["n_tokens"], H), dtype=torch.bfloat16)
+    W = torch.empty((1, H), dtype=torch.bfloat16).expand(V, H)
+    outs = (torch.empty(inf["n_options"]), torch.empty(inf["n_options"]), torch.empty(inf["n_branches"]))
+    with pytest.raises(spb.SpbError) as e:
+        spb.score_options_noalloc(plan, 0, meta, hid, W, *outs, stream=0, lm_head_kind=spb.HEAD_FP32)
+    assert e.value.code == -4
+    assert "allocation-free scratch" in spb.lib().spb_last_error().decode()
