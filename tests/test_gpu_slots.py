@@ -14,14 +14,28 @@ from tests.test_gpu_stack import StackCase, _stack_case
 
 pytestmark = pytest.mark.gpu
 
-# The GPU's answer scores sit within 0.1 of the oracle's (observed <= 0.09:
-# bf16 hidden rows into a head whose logits span about +-10, over up to four
-# tokens).  An oracle step whose kept and dropped candidates are more than
-# twice that apart cannot turn out differently on the GPU; closer steps are
-# near-ties, where several answer lists are correct.
-MARGIN = 0.2
+# Where two candidates of an oracle beam step score closer than the GPU's
+# error, both answer lists are correct.  The error, a priori: each op of a
+# decoder layer rounds its output to bf16 once (RNE: uniform in +-2^-9
+# relative, rms 2^-9/sqrt(3)); five such roundings per layer feed the final
+# hidden row, plus the head's own bf16 input, and independent roundings add in
+# quadrature, so the hidden row's rms relative error is
+#   eps = sqrt(5 L + 1) * 2^-9 / sqrt(3).
+# A logit z_v = W_v . h then errs by about sigma_W * eps * |h| (W's entries of
+# std sigma_W, |h| about sqrt(H) * rms(g_final) after the final rmsnorm); a
+# step's log-probability z_t - LSE by sqrt(2) times that, a T-token score by
+# sqrt(T) times more, and the difference of two candidates' scores by sqrt(2)
+# again.  Six standard deviations of that difference is the margin beyond
+# which an oracle step cannot turn out differently on the GPU.
+def slot_margin(W, g_final, layers: int, T: int) -> float:
+    sigma_w = float(np.std(np.asarray(W, np.float64)))
+    h_norm = math.sqrt(W.shape[1]) * float(np.sqrt(np.mean(np.asarray(g_final, np.float64) ** 2)))
+    eps = math.sqrt(5 * layers + 1) * 2.0 ** -9 / math.sqrt(3.0)
+    return 6.0 * math.sqrt(2.0) * math.sqrt(T) * math.sqrt(2.0) * sigma_w * eps * h_norm
+
+
 TOL_LP = 2e-2   # |lp_gpu - lp_oracle| <= TOL_LP * |lp_oracle|, as for option scoring
-TOL_RANK = 0.25  # rank by rank, GPU and oracle answer scores agree even across near-ties
+TOL_RANK = 0.25  # rank by rank, GPU and oracle answer scores agree where no step had a near-tie
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -100,10 +114,10 @@ def test_beam_step_exact_ties_by_hand():
     assert feed.cpu().tolist() == [0, 1, 0] and int(s1["nb"][0]) == 3
 
 
-def _slot_setup(seed, md_name, n_slots, kinds):
+def _slot_setup(seed, md_name, n_slots, kinds, n_inputs=3):
     """A stacked read with some content branches decoded as slots."""
     import torch
-    wl, md = _stack_case("shared" if seed % 2 else "random", md_name, 16384, seed)
+    wl, md = _stack_case("shared" if seed % 2 else "random", md_name, 16384, seed, n_inputs=n_inputs)
     prob = wl.problem
     V = wl.dims.vocab
     rng = np.random.default_rng(seed)
@@ -140,13 +154,14 @@ def _run_slots(wl, md, slots, masks, budget, inputs=None, B=4, T=5, seed=31, cas
 def test_slots_against_oracle_beam_search(seed, md_name, budget):
     from oracle import decode as OD, forward as OF, tree as OT
     from oracle.numerics import to_f64
-    wl, md, slots, masks, digits = _slot_setup(seed, md_name, 12, ["*", "n", "n"])
+    wl, md, slots, masks, digits = _slot_setup(seed, md_name, 32, ["*", "n", "n"], n_inputs=10)
     B, T = 3, 4
     say(f"case: slots seed={seed} {md_name} budget={budget} ({len(slots)} slots, B={B}, T={T})")
     case, res, W, E = _run_slots(wl, md, slots, masks, budget, B=B, T=T)
     m = OF.Model.from_synth(md, case.layers, case.g_final)
     lay = OT.build_layout(case.prob, floors=True)
     Wf, Ef = to_f64(W), to_f64(E)
+    MARGIN = slot_margin(Wf, to_f64(case.g_final), md.layers, T)
     # logical branch -> (input number, branch object)
     lbs = [(n, b) for n, li in enumerate(lay.inputs) for b in li.branches]
     exact = 0
@@ -161,8 +176,6 @@ def test_slots_against_oracle_beam_search(seed, md_name, budget):
         margins = []
         ref = OD.beam_search(f, B, T, s["stop"], allowed, margins)
         assert len(got) == len(ref)
-        for g, r in zip(got, ref):
-            assert abs(g["lp"] - r.lp) <= TOL_RANK
         # every answer is a valid candidate with the oracle's score for that sequence
         for g in got:
             toks = g["tokens"]
@@ -174,11 +187,16 @@ def test_slots_against_oracle_beam_search(seed, md_name, budget):
             assert g["finished"] == (toks[-1] == s["stop"])
         gaps.append(min(margins, default=1.0))
         if min(margins, default=1.0) > MARGIN:
+            # no near-tie on the oracle's path: the same answers, rank by rank
+            # the same scores; with a near-tie the two searches may keep
+            # different beams from then on, each a correct beam search
             assert [g["tokens"] for g in got] == [r.tokens for r in ref]
+            for g, r in zip(got, ref):
+                assert abs(g["lp"] - r.lp) <= TOL_RANK
             exact += 1
-    say(f"  {exact} of {len(slots)} slots compared answer for answer (the rest had near-ties); "
-        f"max |lp error| {worst:.2e}; smallest oracle gap per slot {[round(x, 4) for x in gaps]}")
-    assert exact >= 2
+    say(f"  margin {MARGIN:.3f}: {exact} of {len(slots)} slots compared answer for answer (the rest had "
+        f"near-ties); max |lp error| {worst:.2e}; smallest oracle gap per slot {[round(x, 4) for x in gaps]}")
+    assert exact >= 4
 
 
 def test_slots_alone_and_together_bit_identical():

@@ -168,15 +168,15 @@ class StackCase(Case):
         return lay, hid
 
 
-def _stack_case(kind, md_name, budget, seed, **over):
+def _stack_case(kind, md_name, budget, seed, n_inputs=3, **over):
     md = synth.MODEL_CONFIGS[md_name]
     wl = synth.make_workload("grid", hq=md.hq, hkv=md.hkv, head_dim=md.head_dim, hidden=md.hidden, vocab=1000,
                              dtype="bf16")
     if kind == "random":
-        wl.problem = synth.make_problem("random", seed, vocab=1000, n_inputs=3, n_questions=4, min_content=20,
+        wl.problem = synth.make_problem("random", seed, vocab=1000, n_inputs=n_inputs, n_questions=4, min_content=20,
                                         max_content=140, max_len=12, max_options=4, max_option_tokens=3)
     else:
-        wl.problem = synth.make_problem("random_shared", seed, vocab=1000, n_inputs=3, n_questions=6,
+        wl.problem = synth.make_problem("random_shared", seed, vocab=1000, n_inputs=n_inputs, n_questions=6,
                                         min_content=0, max_content=120, max_lead=40, tail_vocab=3, max_options=3,
                                         max_option_tokens=3)
     wl.inputs = synth.logical_inputs(wl.problem, True)
