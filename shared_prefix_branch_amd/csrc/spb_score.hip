@@ -261,11 +261,10 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
 }
 
 struct FinParams {
-  int n_slices;
   const SpbBranch *branches;
   const int32_t *opt_step_off, *step_slot, *step_row;
-  const float *part, *tz;
-  float *lse, *lp, *p, *residual;
+  const float *tz, *lse;
+  float *lp, *p, *residual;
 };
 
 __device__ inline void merge(float &M, float &S, float m2, float s2) {
@@ -276,24 +275,44 @@ __device__ inline void merge(float &M, float &S, float m2, float s2) {
   S = a + b;
 }
 
+struct LseParams {
+  int n_slices, M;
+  const float *part;  // [M][n_slices] (max, sum of exp) pairs
+  float *lse;         // [M]
+};
+
+// LSE of every scored row, one wave per row: each lane merges slices lane,
+// lane + 64, ... in increasing order (its loads issued eight at a time ahead
+// of the merges), then a butterfly whose pairwise merges are commutative, so
+// every lane agrees and the order is fixed.
+__global__ __launch_bounds__(256) void lse_kernel(LseParams a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;
+  const int lane = threadIdx.x & 63;
+  const float2 *pp = (const float2 *)(a.part + (size_t)row * a.n_slices * 2);
+  float M = kNegInf, S = 0.f;
+  for (int i0 = lane; i0 < a.n_slices; i0 += 64 * 8) {
+    float2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j;
+      v[j] = i < a.n_slices ? pp[i] : make_float2(kNegInf, 0.f);  // (-inf, 0) merges as nothing
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) merge(M, S, v[j].x, v[j].y);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float m2 = __shfl_xor(M, off), s2 = __shfl_xor(S, off);
+    merge(M, S, m2, s2);
+  }
+  if (lane == 0) a.lse[row] = M + __logf(S);
+}
+
+// One wave per branch, after lse_kernel: option chains and renormalisation.
 __global__ __launch_bounds__(64) void finalize_kernel(FinParams f) {
   const SpbBranch br = f.branches[blockIdx.x];
   const int lane = threadIdx.x;
-  // LSE of each scored row of the branch: slices in order per lane, then a
-  // butterfly whose pairwise merges are commutative, so every lane agrees
-  for (int s = br.scored0; s < br.scored0 + br.n_scored; ++s) {
-    float M = kNegInf, S = 0.f;
-    const float *pp = f.part + (size_t)s * f.n_slices * 2;
-    for (int i = lane; i < f.n_slices; i += 64) merge(M, S, pp[2 * i], pp[2 * i + 1]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float m2 = __shfl_xor(M, off), s2 = __shfl_xor(S, off);
-      merge(M, S, m2, s2);
-    }
-    if (lane == 0) f.lse[s] = M + __logf(S);
-  }
-  __threadfence_block();
-  __syncthreads();
   // option log-probabilities: chain rule in token order
   float mx = kNegInf;
   for (int o = lane; o < br.n_opt; o += 64) {
@@ -362,6 +381,13 @@ int launch_head(const HeadParams &p0, int mb, void *ev_begin, void *ev_end, hipS
   return 0;
 }
 
+int launch_lse(int n_slices, int M, const float *part, float *lse, hipStream_t s) {
+  if (M <= 0) return 0;
+  LseParams a{n_slices, M, part, lse};
+  hipLaunchKernelGGL(lse_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+
 int launch_finalize(const FinParams &f, int n_branches, hipStream_t s) {
   if (n_branches <= 0) return 0;
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)n_branches), dim3(64), 0, s, f);
@@ -405,17 +431,17 @@ int launch_score(const ScoreLaunch &a, void *stream) {
   if (e) return e;
 
   FinParams f;
-  f.n_slices = p.n_slices;
   f.branches = (const SpbBranch *)a.branches;
   f.opt_step_off = (const int32_t *)a.opt_step_off;
   f.step_slot = (const int32_t *)a.step_slot;
   f.step_row = (const int32_t *)a.step_row;
-  f.part = a.part;
   f.tz = a.tz;
   f.lse = a.lse;
   f.lp = a.lp;
   f.p = a.p;
   f.residual = a.residual;
+  e = launch_lse(p.n_slices, a.n_scored, a.part, a.lse, s);
+  if (e) return e;
   return launch_finalize(f, a.n_branches, s);
 }
 
@@ -463,15 +489,15 @@ int launch_score_batch(const ScoreBatchLaunch &a, void *stream) {
   p.tz = a.tz;
   e = launch_head(p, mb, a.ev_begin, a.ev_end, s);
   if (e) return e;
+  e = launch_lse(p.n_slices, a.m_tot, a.part, a.lse, s);  // the passes' rows lie back to back
+  if (e) return e;
   for (int i = 0; i < a.n; ++i) {
     const ScoreLaunch &P = a.pass[i];
     FinParams f;
-    f.n_slices = p.n_slices;
     f.branches = (const SpbBranch *)P.branches;
     f.opt_step_off = (const int32_t *)P.opt_step_off;
     f.step_slot = (const int32_t *)P.step_slot;
     f.step_row = (const int32_t *)P.step_row;
-    f.part = a.part + (size_t)a.m_off[i] * p.n_slices * 2;
     f.tz = a.tz + a.t_off[i];
     f.lse = a.lse + a.m_off[i];
     f.lp = P.lp;
