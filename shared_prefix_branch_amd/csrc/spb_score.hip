@@ -178,12 +178,30 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
       p.Hrow, wave, lane);
   f32x16 acc[2][MB];
   gemm::k_loop<MB>(acc, lds, p.W, p.hg, woff, hoff, p.Hrow / kKT, p.SW, wave, qi, half);
-  float (*red)[TM][2] = (float (*)[TM][2])lds;  // [4][TM][2], reusing the ring
 
-  // epilogue.  Lane holds column m = m0 + mb*32 + qi; register r of block vb
-  // holds vocabulary row v0 + wave*64 + vb*32 + (r/4)*8 + half*4 + r%4.
+  // epilogue; the ring is free.  LDS: the four waves' (max, sum) per row,
+  // then the group's target CSR (offsets relative to its first target) and,
+  // when they fit, its target tokens, staged in one round trip so the
+  // capture below waits on LDS, not on a global load per target.
+  float (*red)[TM][2] = (float (*)[TM][2])lds;  // [4][TM][2]
+  int *s_off = (int *)(lds + 4 * TM * 2 * 4);   // [TM + 1]
+  int *s_tok = s_off + TM + 1;
+  constexpr int kTokCap = (T::LDS - 4 * TM * 2 * 4) / 4 - (TM + 1);
+  static_assert(kTokCap >= 4 * TM, "room for several targets per row");
+  const int tb = p.tgt_off[m0 < p.M ? m0 : p.M];
+  const int te = p.tgt_off[m0 + TM < p.M ? m0 + TM : p.M];
+  const bool staged = te - tb <= kTokCap;
+  for (int i = tid; i <= TM; i += kThreads) s_off[i] = p.tgt_off[m0 + i < p.M ? m0 + i : p.M] - tb;
+  if (staged)
+    for (int i = tid; i < te - tb; i += kThreads) s_tok[i] = p.tgt_tok[tb + i];
+  __syncthreads();
+
+  // Lane holds column m = m0 + mb*32 + qi; register r of block vb holds
+  // vocabulary row v0 + wave*64 + vb*32 + (r/4)*8 + half*4 + r%4.
   const int vw0 = v0 + wave * 64;
-  const int nvalid = p.V - vw0;  // rows past the vocabulary (last slice only) are excluded
+  const int nvalid = p.V - vw0;      // rows past the vocabulary (last slice only) are excluded
+  const bool full = nvalid >= 64;    // uniform: every strip but the vocabulary's tail
+  constexpr float kL2e = 1.44269504088896340736f;
   // one 32-row block at a time, so only its two accumulators leave the
   // accumulation registers at once
 #pragma unroll
@@ -197,23 +215,39 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
         for (int r = 0; r < 16; ++r) z[vb][r] = bf2f(f2bf(z[vb][r]));
     }
     float mx = kNegInf;
+    if (full) {
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
+      for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        mx = fmaxf(mx, vr < nvalid ? z[vb][r] : kNegInf);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float se = 0.f;
-    if (mx != kNegInf) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, z[vb][r]);
+    } else {
 #pragma unroll
       for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          se += vr < nvalid ? __expf(z[vb][r] - mx) : 0.f;
+          mx = fmaxf(mx, vr < nvalid ? z[vb][r] : kNegInf);
         }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float se = 0.f;
+    if (mx != kNegInf) {
+      // exp(z - mx) as 2^(z log2e - mx log2e): one fma and one v_exp_f32
+      const float nm = -mx * kL2e;
+      if (full) {
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) se += __builtin_amdgcn_exp2f(__builtin_fmaf(z[vb][r], kL2e, nm));
+      } else {
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+            se += vr < nvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[vb][r], kL2e, nm)) : 0.f;
+          }
+      }
     }
     se = se + __shfl_xor(se, 32);
     const int ml = mb * 32 + qi;
@@ -224,9 +258,9 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
     // capture the logits of the tokens this row predicts
     const int m = m0 + ml;
     if (m < p.M) {
-      const int t0 = p.tgt_off[m], t1 = p.tgt_off[m + 1];
+      const int t0 = s_off[ml], t1 = s_off[ml + 1];
       for (int t = t0; t < t1; ++t) {
-        const int rel = p.tgt_tok[t] - vw0;
+        const int rel = (staged ? s_tok[t] : p.tgt_tok[tb + t]) - vw0;
         if (rel < 0 || rel >= 64) continue;
         const int rr = rel & 31;
         if (((rr >> 2) & 1) != half) continue;
@@ -236,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
         for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) val = (vb == vbt && r == rt) ? z[vb][r] : val;
-        p.tz[t] = val;
+        p.tz[tb + t] = val;
       }
     }
   }
