@@ -245,7 +245,13 @@ spb_status spb_plan_meta_copy(const spb_plan *plan, int32_t pass, void *host_dst
  * out_dtype: SPB_F32 or SPB_BF16.  head_dim 64 or 128; hq % hkv == 0 and
  * hq / hkv in {1, 2, 4}.  softmax_scale <= 0 selects 1/sqrt(head_dim).
  * SPB_BF16 passes need n_tokens * hkv * head_dim * 2 < 4 GiB (SPB_ERR_LIMIT).
- * d_meta: the upload of (plan, pass). */
+ * d_meta: the upload of (plan, pass).
+ * workspace (SPB_FP8_E4M3 only; ignored otherwise): NULL, or device memory of
+ * spb_attention_workspace_bytes, 256-byte aligned, caller-owned, not shared
+ * with a call in flight.  With it, V is first widened to bf16 there (exact:
+ * every e4m3 value is a bf16 value) and K/V chunks reach LDS by asynchronous
+ * copies; without it they pass through registers.  The two give the same
+ * bits: same MFMAs in the same order.  SPB_ERR_SIZE if it is too small. */
 typedef struct {
   const void *q, *k, *v;
   void *o;
@@ -254,7 +260,15 @@ typedef struct {
   float softmax_scale;
   float s_q, s_k, s_v;
   int64_t rows; /* rows of q/k/v/o buffers, >= n_tokens */
+  void *workspace;
+  size_t workspace_bytes;
 } spb_attn_args;
+
+/* Workspace bytes spb_branch_attention can use for this pass and input
+ * dtype: n_tokens * hkv * head_dim * 2 for SPB_FP8_E4M3 (V widened to bf16),
+ * 0 otherwise.  SPB_ERR_ARG for a pass out of range or hkv / head_dim < 1. */
+spb_status spb_attention_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t in_dtype, int32_t hkv,
+                                         int32_t head_dim, size_t *out);
 
 spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_attn_args *args,
                                 void *stream);

@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "SpbError", "lib", "library_path", "fingerprint", "Plan", "pack_pass", "branch_attention",
-    "score_options_noalloc",
+    "score_options_noalloc", "attention_workspace_bytes",
     "PreparedAttention", "PreparedScore", "PreparedScoreBatch", "score_batch_workspace_bytes",
     "score_options_batch",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = [
     "spb_plan_num_passes", "spb_plan_info", "spb_plan_rows", "spb_plan_branches", "spb_plan_inputs",
     "spb_plan_visible",
     "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
-    "spb_score_options_noalloc",
+    "spb_score_options_noalloc", "spb_attention_workspace_bytes",
     "spb_score_batch_workspace_bytes", "spb_score_options_batch",
     "spb_score_finalize", "spb_plan_positions", "spb_rope_table", "spb_rmsnorm", "spb_linear",
     "spb_plan_slot", "spb_gather_rows", "spb_topk_workspace_bytes", "spb_topk_lse", "spb_decode_attention",
@@ -88,7 +88,7 @@ class _AttnArgs(ctypes.Structure):
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("hq", ctypes.c_int32),
                 ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("s_q", ctypes.c_float), ("s_k", ctypes.c_float), ("s_v", ctypes.c_float),
-                ("rows", ctypes.c_int64)]
+                ("rows", ctypes.c_int64), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _ScoreArgs(ctypes.Structure):
@@ -186,6 +186,8 @@ def lib() -> ctypes.CDLL:
         L.spb_plan_meta_copy.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]
         L.spb_branch_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.POINTER(_AttnArgs), ctypes.c_void_p]
+        L.spb_attention_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_options.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
@@ -359,7 +361,7 @@ class PreparedAttention:
     with a plan (same pass shapes) and a stream only enqueues the kernel."""
 
     def __init__(self, pass_: int, d_meta, q, k, v, o, softmax_scale: float = 0.0,
-                 scales: Sequence[float] = (1.0, 1.0, 1.0)):
+                 scales: Sequence[float] = (1.0, 1.0, 1.0), workspace=None):
         for t in (q, k, v, o):
             if not t.is_contiguous():
                 raise SpbError(-1, "tensors must be contiguous")
@@ -375,6 +377,9 @@ class PreparedAttention:
         A.softmax_scale = float(softmax_scale)
         A.s_q, A.s_k, A.s_v = (float(s) for s in scales)
         A.rows = int(min(q.shape[0], k.shape[0], v.shape[0], o.shape[0]))
+        if workspace is not None:  # e4m3 inputs: V widened there, K/V copied asynchronously
+            A.workspace = workspace.data_ptr()
+            A.workspace_bytes = workspace.numel() * workspace.element_size()
         self.args = A
         self.pass_ = pass_
         self.meta = ctypes.c_void_p(d_meta.data_ptr())
@@ -386,9 +391,17 @@ class PreparedAttention:
 
 
 def branch_attention(plan: Plan, pass_: int, d_meta, q, k, v, o, softmax_scale: float = 0.0,
-                     scales: Sequence[float] = (1.0, 1.0, 1.0), stream=None):
-    """q [rows, hq, d], k/v [rows, hkv, d], o [rows, hq, d]: contiguous device tensors."""
-    PreparedAttention(pass_, d_meta, q, k, v, o, softmax_scale, scales)(plan, stream)
+                     scales: Sequence[float] = (1.0, 1.0, 1.0), stream=None, workspace=None):
+    """q [rows, hq, d], k/v [rows, hkv, d], o [rows, hq, d]: contiguous device tensors.
+    workspace: for e4m3 inputs, a uint8 device buffer of attention_workspace_bytes (or None)."""
+    PreparedAttention(pass_, d_meta, q, k, v, o, softmax_scale, scales, workspace)(plan, stream)
+
+
+def attention_workspace_bytes(plan: Plan, pass_: int, in_dtype: int, hkv: int, head_dim: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().spb_attention_workspace_bytes(plan.handle, pass_, int(in_dtype), int(hkv), int(head_dim),
+                                               ctypes.byref(n)))
+    return int(n.value)
 
 
 def score_workspace_bytes(plan: Plan, pass_: int, vocab: int, hidden_dim: int, lm_head_kind: int = 0) -> int:

@@ -326,9 +326,8 @@ __device__ __attribute__((always_inline)) inline void qk_chunk(const char *Kb, c
 }
 
 // V^T operands of k-step ks (keys 16 ks .. 16 ks + 16 of the chunk)
-template <int D, int ROWB>
-__device__ __attribute__((always_inline)) inline void read_v_step(const char *Vb, const FragOffsets<D, SPB_BF16> &fo,
-                                                                  int ks, VStep<D> &f) {
+template <int D, int ROWB, typename FO>
+__device__ __attribute__((always_inline)) inline void read_v_step(const char *Vb, const FO &fo, int ks, VStep<D> &f) {
   const char *vstep = Vb + 16 * ks * ROWB;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -342,8 +341,8 @@ __device__ __attribute__((always_inline)) inline void read_v_step(const char *Vb
   }
 }
 
-template <int D, int HPW, int ROWB>
-__device__ __attribute__((always_inline)) inline void pv_chunk(const char *Vb, const FragOffsets<D, SPB_BF16> &fo,
+template <int D, int HPW, int ROWB, typename FO>
+__device__ __attribute__((always_inline)) inline void pv_chunk(const char *Vb, const FO &fo,
                                                                const uint32_t (&pk)[HPW][2][8],
                                                                f32x16 (&o)[HPW][D / 32], bool two,
                                                                const VStep<D> &first) {
@@ -534,9 +533,70 @@ __device__ __attribute__((always_inline)) inline void walk_chunks(const int4 *ch
   }
 }
 
+// S^T of one chunk for e4m3 K and Q on the fp8 MFMA (32x32x64), K in
+// 16-byte-swizzled LDS rows of ROWB bytes: block 0, then block 1 when `two`,
+// each over the 64-element K steps in order -- the same MFMAs in the same
+// order as qk_block, so the same bits.
+template <int D, int HPW, int ROWB>
+__device__ __attribute__((always_inline)) inline void qk_chunk_fp8(const char *Kb,
+                                                                   const FragOffsets<D, SPB_FP8_E4M3> &fo,
+                                                                   const QFrag<D, SPB_FP8_E4M3> (&qf)[HPW],
+                                                                   f32x16 (&s0)[HPW], f32x16 (&s1)[HPW], bool two) {
+  constexpr int STEPS = QFrag<D, SPB_FP8_E4M3>::STEPS;
+  u32x4 a[2][STEPS][2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    if (blk == 1 && !two) break;
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      a[blk][t][0] = *(const u32x4 *)(Kb + blk * 32 * ROWB + fo.k[t][0]);
+      a[blk][t][1] = *(const u32x4 *)(Kb + blk * 32 * ROWB + fo.k[t][1]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) s0[j] = f32x16{0.f};
+  if (two) {
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) s1[j] = f32x16{0.f};
+  }
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    if (blk == 1 && !two) break;
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      const u32x4 a0 = a[blk][t][0], a1 = a[blk][t][1];
+      const i32x8 k8 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        if (blk == 0)
+          s0[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k8, qf[j].f[t], s0[j], 0, 0, 0, 0, 0, 0);
+        else
+          s1[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k8, qf[j].f[t], s1[j], 0, 0, 0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// e4m3 V -> bf16 V (exact), 16 elements per thread, for the fp8 dma kernel.
+__global__ __launch_bounds__(256) void widen_v_kernel(const unsigned char *v8, uint32_t *v16, long long n16) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 w = ((const u32x4 *)v8)[i];
+  uint32_t out[8];
+  const uint32_t src[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    out[2 * q] = e4m3_to_bf(src[q] & 0xFFu) | (e4m3_to_bf((src[q] >> 8) & 0xFFu) << 16);
+    out[2 * q + 1] = e4m3_to_bf((src[q] >> 16) & 0xFFu) | (e4m3_to_bf(src[q] >> 24) << 16);
+  }
+  u32x4 *dst = (u32x4 *)v16 + 2 * i;
+  dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+  dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+}
+
 // ------------------------------------------------------- bf16: dma kernel
 
-template <int D, int G, int HPW_, int RG_>
+template <int D, int G, int HPW_, int RG_, int IN_ = SPB_BF16>
 struct DmaCfg {
   static constexpr int HPW = HPW_;            // query heads per wave
   static constexpr int HG = G / HPW;          // waves per 32-row group
@@ -544,9 +604,14 @@ struct DmaCfg {
   static constexpr int NW = RG * HG;          // waves
   static constexpr int NT = 64 * NW;
   static constexpr int GRAN = RG == 1 ? 0 : RG == 2 ? 1 : 2;  // work items of 32 << GRAN rows
-  static constexpr int ROWB = 2 * D;          // bytes per K or V row
-  static constexpr int BUF = 64 * ROWB;       // one chunk of K (or V)
+  static constexpr bool FP8 = IN_ == SPB_FP8_E4M3;  // e4m3 K (fp8 MFMA for S), bf16 V (widened beforehand)
+  static constexpr int ROWB_K = FP8 ? D : 2 * D;    // bytes per K row in LDS
+  static constexpr int ROWB = 2 * D;                // bytes per V row (and per K row for bf16)
+  static constexpr int BUFK = 64 * ROWB_K;          // one chunk of K
+  static constexpr int BUF = 64 * ROWB;             // one chunk of V
   // copies per wave per tensor for a 64-key and a 32-key chunk
+  static constexpr int QK64 = 64 * ROWB_K / 1024 / NW;
+  static constexpr int QK32 = 32 * ROWB_K / 1024 / NW;
   static constexpr int Q64 = 64 * ROWB / 1024 / NW;
   static constexpr int Q32 = 32 * ROWB / 1024 / NW;
   // work groups per CU the registers are budgeted for: two (at most 256 per
@@ -554,6 +619,8 @@ struct DmaCfg {
   static constexpr int MINWG = HPW == 1 ? 2 : 1;
   static_assert(G % HPW == 0 && (RG == 1 || RG == 2 || RG == 4), "work item shape");
   static_assert(Q32 >= 1 && Q32 * NW * 1024 == 32 * ROWB, "a 32-key chunk must give every wave whole copies");
+  static_assert(QK32 >= 1 && QK32 * NW * 1024 == 32 * ROWB_K, "a 32-key chunk must give every wave whole copies");
+  static_assert(!FP8 || D == 128, "e4m3 inputs need head_dim 128");
 };
 
 // LDS row swizzles (16-byte chunk c of row r lives at chunk c ^ f(r)).  K: a
@@ -570,13 +637,12 @@ __device__ inline int swz_v(int r) { return ROWB == 256 ? 4 * (r & 3) : 4 * ((r 
 // chunks of the branches meeting its rows) is taken from the item table.  K
 // and V of the chunks are copied global -> LDS into a two-slot ring, the copy
 // of chunk i + 1 running while chunk i is computed.
-template <int D, int G, int HPW_, int RG_, int OUT>
-__global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, RG_>::MINWG)) void branch_attention_dma(
-    AttnParams p) {
-  using C = DmaCfg<D, G, HPW_, RG_>;
+template <int D, int G, int HPW_, int RG_, int OUT, int IN = SPB_BF16>
+__global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_, IN>::NT), (DmaCfg<D, G, HPW_, RG_, IN>::MINWG)) void
+branch_attention_dma(AttnParams p) {
+  using C = DmaCfg<D, G, HPW_, RG_, IN>;
   constexpr int HPW = C::HPW;
-  constexpr int IN = SPB_BF16;
-  __shared__ __attribute__((aligned(1024))) char Ks[2][C::BUF];
+  __shared__ __attribute__((aligned(1024))) char Ks[2][C::BUFK];
   __shared__ __attribute__((aligned(1024))) char Vs[2][C::BUF];
   __shared__ int4 chunks[kMaxChunks];
 
@@ -602,39 +668,48 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
   // lane t fills row r0 + qq*RSTEP at 16-byte position pos, where r0 and pos
   // do not depend on qq, and neither does the row swizzle (RSTEP is a
   // multiple of its period), so only the source row changes per copy.
+  // (For e4m3 K, whose rows are half as long, K has its own row step and
+  // lane positions; copy qq of K moves its own 1,024 bytes the same way.)
   constexpr int RSTEP = C::NW * 1024 / C::ROWB;
-  static_assert(RSTEP % 16 == 0, "copy rounds must keep the swizzle phase");
+  constexpr int RSTEPK = C::NW * 1024 / C::ROWB_K;
+  static_assert(RSTEP % 16 == 0 && RSTEPK % 16 == 0, "copy rounds must keep the swizzle phase");
   const int r0 = (wave * 1024 + lane * 16) / C::ROWB;
   const int pos = ((lane * 16) % C::ROWB) >> 4;
-  const uint32_t kofs = (uint32_t)(kvh * C::ROWB + ((pos ^ swz_k<C::ROWB>(r0)) << 4));
+  const int r0k = (wave * 1024 + lane * 16) / C::ROWB_K;
+  const int posk = ((lane * 16) % C::ROWB_K) >> 4;
+  const uint32_t kofs = (uint32_t)(kvh * C::ROWB_K + ((posk ^ swz_k<C::ROWB_K>(r0k)) << 4));
   const uint32_t vofs = (uint32_t)(kvh * C::ROWB + ((pos ^ swz_v<C::ROWB>(r0)) << 4));
   const uint32_t ystride = (uint32_t)(p.hkv * C::ROWB);
-  auto copy_rows = [&](int key0, uint32_t slot, int qq) {
-    const int y = min(key0 + r0 + qq * RSTEP, p.n_tokens - 1);
-    const uint32_t rowoff = (uint32_t)y * ystride;
-    const uint32_t dst = slot + (uint32_t)(qq * C::NW + wave) * 1024;
-    dma16(p.k, rowoff + kofs, k_lds + dst);
-    dma16(p.v, rowoff + vofs, v_lds + dst);
+  const uint32_t ystridek = (uint32_t)(p.hkv * C::ROWB_K);
+  auto copy_k = [&](int key0, int slot, int qq) {
+    const int y = min(key0 + r0k + qq * RSTEPK, p.n_tokens - 1);
+    dma16(p.k, (uint32_t)y * ystridek + kofs, k_lds + (uint32_t)slot * C::BUFK + (uint32_t)(qq * C::NW + wave) * 1024);
   };
-  auto issue = [&](int i) {
-    const int2 ch = int2{chunks[i].x, chunks[i].y};
-    const uint32_t slot = (uint32_t)(i & 1) * C::BUF;
-    if (ch.y < 0) {
+  auto copy_v = [&](int key0, int slot, int qq) {
+    const int y = min(key0 + r0 + qq * RSTEP, p.n_tokens - 1);
+    dma16(p.v, (uint32_t)y * ystride + vofs, v_lds + (uint32_t)slot * C::BUF + (uint32_t)(qq * C::NW + wave) * 1024);
+  };
+  auto copy_chunk = [&](int key0, int slot, bool content) {
+    if (content) {
 #pragma unroll
-      for (int qq = 0; qq < C::Q64; ++qq) copy_rows(ch.x, slot, qq);
+      for (int qq = 0; qq < C::Q64; ++qq) {
+        if (qq < C::QK64) copy_k(key0, slot, qq);
+        copy_v(key0, slot, qq);
+      }
     } else {
 #pragma unroll
-      for (int qq = 0; qq < C::Q32; ++qq) copy_rows(ch.x, slot, qq);
+      for (int qq = 0; qq < C::Q32; ++qq) {
+        if (qq < C::QK32) copy_k(key0, slot, qq);
+        copy_v(key0, slot, qq);
+      }
     }
   };
+  auto issue = [&](int i) { copy_chunk(chunks[i].x, i & 1, chunks[i].y < 0); };
 
   // An item's content chunk 0 starts at its content start, so its copy needs
   // no chunk list: it goes out first, ahead of the list, row and Q loads.
   const bool early = it.ncc > 0;
-  if (early) {
-#pragma unroll
-    for (int qq = 0; qq < C::Q64; ++qq) copy_rows(it.seg, 0u, qq);
-  }
+  if (early) copy_chunk(it.seg, 0, true);
 
   load_chunk_list(p, it, chunks, tid, C::NT);
   const SpbRow row = load_row(p, x, active);
@@ -645,8 +720,14 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
   // fragment offsets in the swizzled layout
   FragOffsets<D, IN> fo;
 #pragma unroll
-  for (int t = 0; t < QFrag<D, IN>::STEPS; ++t)
-    fo.k[t][0] = qi * C::ROWB + (((2 * t + half) ^ swz_k<C::ROWB>(qi)) << 4);
+  for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
+    if constexpr (C::FP8) {  // 64 elements per step: 16-byte chunks 4t + 2half, +1
+      fo.k[t][0] = qi * C::ROWB_K + (((4 * t + 2 * half) ^ swz_k<C::ROWB_K>(qi)) << 4);
+      fo.k[t][1] = qi * C::ROWB_K + (((4 * t + 2 * half + 1) ^ swz_k<C::ROWB_K>(qi)) << 4);
+    } else {
+      fo.k[t][0] = qi * C::ROWB + (((2 * t + half) ^ swz_k<C::ROWB>(qi)) << 4);
+    }
+  }
   {
     const int g = qi >> 4, l16 = lane & 15;
     const int rr = half * 4 + (l16 >> 2);
@@ -675,7 +756,10 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_>::NT), (DmaCfg<D, G, HPW_, 
     const char *Kb = Ks[slot];
     const char *Vb = Vs[slot];
     f32x16 s0[HPW], s1[HPW];
-    qk_chunk<D, HPW, C::ROWB>(Kb, fo, qf, s0, s1, two);
+    if constexpr (C::FP8)
+      qk_chunk_fp8<D, HPW, C::ROWB_K>(Kb, fo, qf, s0, s1, two);
+    else
+      qk_chunk<D, HPW, C::ROWB>(Kb, fo, qf, s0, s1, two);
     if (masked) {
       if (anc) {
 #pragma unroll
@@ -948,19 +1032,31 @@ struct DmaShape {  // four waves per work group
   static constexpr int RG = 4 / (G / HPW);
 };
 
-template <int D, int G, int OUT>
+template <int D, int G, int OUT, int IN = SPB_BF16>
 int launch_dma(const AttnLaunch &a, hipStream_t s) {
   using Sh = DmaShape<D, G>;
-  using C = DmaCfg<D, G, Sh::HPW, Sh::RG>;
+  using C = DmaCfg<D, G, Sh::HPW, Sh::RG, IN>;
   const long long work = (long long)a.n_items[C::GRAN] * a.hkv;
   if (work > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
-  if (work == 0) return 0;
   // the copies address K/V with 32-bit byte offsets
   if ((long long)a.n_tokens * a.hkv * C::ROWB > 0xFFFFFFFFll) return (int)hipErrorInvalidValue;
   AttnParams p = make_params(a);
+  if constexpr (C::FP8) {
+    // V widened to bf16 into the workspace first (every row of the pass)
+    const long long n16 = (long long)a.n_tokens * a.hkv * D / 16;
+    if (n16 > 0) {
+      hipLaunchKernelGGL(widen_v_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                         (const unsigned char *)a.v, (uint32_t *)a.v_wide, n16);
+      const int e = (int)hipGetLastError();
+      if (e) return e;
+    }
+    p.v = a.v_wide;
+  }
+  if (work == 0) return 0;
   p.items = (const SpbItem *)a.items[C::GRAN];
   p.n_work = (int)work;
-  hipLaunchKernelGGL((branch_attention_dma<D, G, Sh::HPW, Sh::RG, OUT>), dim3((unsigned)work), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((branch_attention_dma<D, G, Sh::HPW, Sh::RG, OUT, IN>), dim3((unsigned)work), dim3(C::NT), 0, s,
+                     p);
   return (int)hipGetLastError();
 }
 
@@ -984,9 +1080,13 @@ int launch_dtypes(const AttnLaunch &a, hipStream_t s) {
   if (a.in_dtype == SPB_F32)
     return a.out_dtype == SPB_F32 ? launch_staged<D, G, SPB_F32, SPB_F32>(a, s)
                                   : launch_staged<D, G, SPB_F32, SPB_BF16>(a, s);
-  if constexpr (D == 128)
+  if constexpr (D == 128) {
+    if (a.v_wide)
+      return a.out_dtype == SPB_F32 ? launch_dma<D, G, SPB_F32, SPB_FP8_E4M3>(a, s)
+                                    : launch_dma<D, G, SPB_BF16, SPB_FP8_E4M3>(a, s);
     return a.out_dtype == SPB_F32 ? launch_staged<D, G, SPB_FP8_E4M3, SPB_F32>(a, s)
                                   : launch_staged<D, G, SPB_FP8_E4M3, SPB_BF16>(a, s);
+  }
   return (int)hipErrorInvalidValue;
 }
 

@@ -1222,6 +1222,18 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
   if (a->in_dtype == SPB_BF16 && (uint64_t)h.n_tokens * (uint64_t)a->hkv * (uint64_t)a->head_dim * 2u > 0xFFFFFFFFull)
     return fail(SPB_ERR_LIMIT, "a bf16 pass's K/V (%d tokens x %d heads x %d) must stay under 4 GiB", h.n_tokens, a->hkv,
                 a->head_dim);
+  const bool wide = a->in_dtype == SPB_FP8_E4M3 && a->workspace;
+  if (wide) {
+    const uint64_t need = (uint64_t)h.n_tokens * (uint64_t)a->hkv * (uint64_t)a->head_dim * 2u;
+    if (a->workspace_bytes < need)
+      return fail(SPB_ERR_SIZE, "attention workspace needs %llu bytes, got %zu", (unsigned long long)need,
+                  a->workspace_bytes);
+    if ((uintptr_t)a->workspace % 256) return fail(SPB_ERR_ARG, "workspace must be 256-byte aligned");
+    if ((uintptr_t)a->v % 16) return fail(SPB_ERR_ARG, "v must be 16-byte aligned");
+    if (need > 0xFFFFFFFFull)
+      return fail(SPB_ERR_LIMIT, "a pass's widened V (%d tokens x %d heads x %d) must stay under 4 GiB", h.n_tokens,
+                  a->hkv, a->head_dim);
+  }
   if (h.n_tiles == 0) return ok();
   st = check_attention_limits(P, pass);  // also checked when the plan was packed
   if (st != SPB_OK) return st;
@@ -1242,8 +1254,20 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
     L.n_items[g] = h.n_items[g];
   }
   L.bchunks = base + h.off_bchunks;
+  L.v_wide = wide ? a->workspace : nullptr;
   int e = launch_attention(L, stream);
   if (e) return fail(SPB_ERR_HIP, "branch attention launch: %s", hip_error_string(e));
+  return ok();
+}
+
+spb_status spb_attention_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t in_dtype, int32_t hkv,
+                                         int32_t head_dim, size_t *out) {
+  spb_status st = check_pass(plan, pass);
+  if (st != SPB_OK) return st;
+  if (!out) return fail(SPB_ERR_ARG, "NULL argument");
+  if (hkv < 1 || head_dim < 1) return fail(SPB_ERR_ARG, "hkv %d and head_dim %d must be >= 1", hkv, head_dim);
+  const SpbMetaHeader &h = header(plan->passes[pass]);
+  *out = in_dtype == SPB_FP8_E4M3 ? (size_t)h.n_tokens * (size_t)hkv * (size_t)head_dim * 2u : 0;
   return ok();
 }
 

@@ -21,6 +21,7 @@ struct AttnLaunch {
   const void *rows, *tiles, *branches;  // device pointers into the metadata blob
   const void *items[3], *bchunks;       // work items at 32, 64, 128 rows; their branch chunks
   int n_items[3];
+  void *v_wide;              // e4m3 inputs: bf16 copy of V (n_tokens x hkv x d), or NULL
 };
 
 struct ScoreLaunch {

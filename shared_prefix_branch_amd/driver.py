@@ -57,7 +57,7 @@ class Job:
 
     def __init__(self, plan: Plan, hq: int, hkv: int, head_dim: int, hidden_dim: int, vocab: int,
                  qkv_dtype, out_dtype, hidden_dtype, device="cuda", scales=(1.0, 1.0, 1.0),
-                 batch_head: bool = False, lm_head_kind: int = 0, head_rows: int = 0):
+                 batch_head: bool = False, lm_head_kind: int = 0, head_rows: int = 0, fp8_dma: bool = True):
         import torch
         self.torch = torch
         self.plan = plan
@@ -80,6 +80,9 @@ class Job:
         self.batch_head = bool(batch_head)
         self.head_rows = int(head_rows)
         self.lm_head_kind = int(lm_head_kind)
+        # e4m3 inputs: attention widens V into a workspace and copies K/V
+        # asynchronously (fp8_dma), else it stages them through registers
+        self.fp8_dma = bool(fp8_dma)
         if self.batch_head and plan.n_passes > 64:
             raise ValueError("batch_head covers at most 64 passes")
         self.grouped = self.batch_head or self.head_rows > 0
@@ -179,7 +182,14 @@ class Job:
             off += 2 * no + nb
             self.fill(k, buf, provider, cache)
             self.passes.append(buf)
-        self._attn = [PreparedAttention(k, b.meta, b.q, b.k, b.v, b.o, scales=self.scales)
+        # one attention workspace serves every pass: their kernels run in order on one stream
+        self.att_ws = None
+        if self.fp8_dma and self.qkv_dtype in (t.uint8, getattr(t, "float8_e4m3fn", t.uint8)):
+            from . import FP8_E4M3, attention_workspace_bytes
+            nb = max(attention_workspace_bytes(self.plan, k, FP8_E4M3, self.hkv, self.d)
+                     for k in range(self.plan.n_passes))
+            self.att_ws = t.empty(max(256, nb), dtype=t.uint8, device=self.device)
+        self._attn = [PreparedAttention(k, b.meta, b.q, b.k, b.v, b.o, scales=self.scales, workspace=self.att_ws)
                       for k, b in enumerate(self.passes)]
         if self.grouped:
             # one workspace for every group: their launches run in order on one stream

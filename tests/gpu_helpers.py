@@ -39,7 +39,7 @@ class Case:
     def __init__(self, wl: synth.Workload, budget: int, inputs: Optional[Sequence[int]] = None,
                  floors: bool = True, peaked: bool = False, device: str = "cuda", gen_device: str = "cuda",
                  chained: bool = False, cache: Optional[dict] = None, batch_head: bool = False,
-                 lm_head_kind: int = 0, head_rows: int = 0, sharp: bool = False):
+                 lm_head_kind: int = 0, head_rows: int = 0, sharp: bool = False, fp8_dma: bool = True):
         import torch
         self.torch = torch
         self.wl = wl
@@ -62,6 +62,7 @@ class Case:
         self.batch_head = batch_head
         self.head_rows = head_rows
         self.lm_head_kind = lm_head_kind
+        self.fp8_dma = fp8_dma
 
     # -- inputs --------------------------------------------------------------
     def block(self, ident):
@@ -86,7 +87,7 @@ class Case:
         hid = t.float32 if d.dtype == "f32" else t.bfloat16
         self.job = Job(self.plan, d.hq, d.hkv, d.head_dim, d.hidden, d.vocab, qkv, out, hid,
                        device=self.device, scales=self.scales, batch_head=self.batch_head,
-                       lm_head_kind=self.lm_head_kind, head_rows=self.head_rows)
+                       lm_head_kind=self.lm_head_kind, head_rows=self.head_rows, fp8_dma=self.fp8_dma)
         self.job.load(self.provider)
         self.job.run(W)
         t.cuda.synchronize()

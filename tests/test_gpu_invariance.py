@@ -133,3 +133,26 @@ def test_run_to_run_deterministic():
     B = _by_input(a)
     for i in A:
         _same(A[i], B[i], f"input {i} second run")
+
+
+@SHARP
+def test_fp8_async_copy_kernel_equals_register_staged(sharp):
+    # e4m3 attention two ways: V widened to bf16 in a workspace with K/V
+    # copied asynchronously into LDS, or K/V staged through registers.  Same
+    # MFMAs in the same order per row, so the same bits, across spilling
+    # passes of 8,192 tokens; scores follow.
+    wl = synth.make_workload("fp8", n_inputs=30)
+    W, _ = lm_head(wl)
+    cache = {}
+    say(f"case: fp8 attention, async-copy kernel vs register-staged kernel, sharp={sharp}")
+    a = Case(wl, 8192, peaked=sharp, sharp=sharp, cache=cache, fp8_dma=True)
+    a.run(W)
+    assert a.job.att_ws is not None
+    A = _by_input(a)
+    a.job = None
+    b = Case(wl, 8192, peaked=sharp, sharp=sharp, cache=cache, fp8_dma=False)
+    b.run(W)
+    assert b.job.att_ws is None
+    B = _by_input(b)
+    for i in A:
+        _same(A[i], B[i], f"input {i}: async-copy vs staged")

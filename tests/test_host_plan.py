@@ -236,6 +236,30 @@ def test_lm_head_kind_workspace():
         spb.score_batch_workspace_bytes(plan, [0], 1000, 256, -1)
 
 
+def test_attention_workspace_size_and_checks():
+    # e4m3 attention may take a workspace of n_tokens * hkv * d * 2 bytes
+    # (V widened to bf16); other dtypes need none.  A short or misaligned one
+    # is refused on the host before any HIP call.
+    plan = spb.pack_pass(_prob())
+    n = plan.info(0)["n_tokens"]
+    assert spb.attention_workspace_bytes(plan, 0, spb.FP8_E4M3, 2, 128) == n * 2 * 128 * 2
+    assert spb.attention_workspace_bytes(plan, 0, spb.BF16, 2, 128) == 0
+    with pytest.raises(spb.SpbError):
+        spb.attention_workspace_bytes(plan, 3, spb.FP8_E4M3, 2, 128)
+    L = spb.lib()
+    A = spb._AttnArgs()
+    A.q = A.k = A.v = A.o = 256
+    A.in_dtype, A.out_dtype, A.hq, A.hkv, A.head_dim, A.rows = spb.FP8_E4M3, spb.BF16, 4, 2, 128, 1 << 20
+    A.s_q = A.s_k = A.s_v = 1.0
+    A.workspace = 4096
+    A.workspace_bytes = n * 2 * 128 * 2 - 1
+    meta = ctypes.c_void_p(4096)
+    assert L.spb_branch_attention(plan.handle, 0, meta, ctypes.byref(A), None) == -4
+    A.workspace_bytes += 1
+    A.workspace = 4096 + 64
+    assert L.spb_branch_attention(plan.handle, 0, meta, ctypes.byref(A), None) == -1
+
+
 def test_upload_rejects_small_or_misaligned_buffers():
     plan = spb.pack_pass(_prob())
     L = spb.lib()
