@@ -39,6 +39,13 @@ linear-layer GEMM kernel, which then dominates the step.
 runs only a plain 1 GiB device-to-device copy, three times, for scaling the
 FETCH_SIZE / WRITE_SIZE counters.
 
+    python bench.py --mfma-calibration
+
+runs the library's MFMA calibration loop (the head's MFMA with operands in
+registers, no memory traffic), with random bf16 operands and with small
+integers, on every CU for about 80 ms each, and prints the sustained TFLOP/s:
+what the head's MFMA reaches on this chip when nothing else limits it.
+
     python bench.py --head-sweep 8,16,56,128,256 [--steps K --warmup W]
 
 times the lm head alone (news head shape) at each scored-row count and prints
@@ -97,6 +104,7 @@ def parse():
                     help="contents in the oracle's sample (0: the workload's default, all of them for news, "
                          "tiny and extreme, 20 for moderation, 40 for fp8)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mfma-calibration", action="store_true")
     ap.add_argument("--head-batch", action="store_true",
                     help="one lm-head launch for all passes of the step (spb_score_options_batch) "
                          "instead of one per pass")
@@ -150,6 +158,29 @@ def copy_calibration():
           flush=True)
 
 
+def mfma_calibration():
+    import torch
+    import shared_prefix_branch_amd as spb
+    torch.cuda.set_device(0)
+    wg, iters = 256, 200000  # one work group of four waves per CU; about 80 ms at the nominal rate
+    out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = wg * 4 * iters * 16 * 32 * 32 * 16 * 2.0
+    for random in (True, False):
+        for rep in range(3):
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            spb.mfma_calibration(out, wg, iters, random, stream)
+            e.record(stream)
+            e.synchronize()
+            ms = b.elapsed_time(e)
+            tf = flops / (ms * 1e-3) / 1e12
+            print(json.dumps({"mfma_calibration": {"operands": "random bf16" if random else "small integers",
+                                                   "rep": rep, "ms": round(ms, 3), "tflops": round(tf, 1),
+                                                   "frac_of_nominal": round(tf / PEAK_BF16_TFLOPS, 4)}}),
+                  flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -158,6 +189,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_calibration:
+        mfma_calibration()
         return
     if args.head_sweep:
         head_sweep([int(x) for x in args.head_sweep.split(",")], args.steps, args.warmup)

@@ -270,6 +270,19 @@ typedef struct {
 spb_status spb_attention_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t in_dtype, int32_t hkv,
                                          int32_t head_dim, size_t *out);
 
+/* Roofline calibration, not part of the scoring path (the pages have no such
+ * step): the rate the head's MFMA (32x32x16 bf16, f32 accumulation) sustains
+ * alone.  Enqueues work_groups (1 .. 2^20) work groups of four waves, each wave
+ * running 16 independent accumulators through 16 x iters MFMAs on operands
+ * held in registers -- random bf16 values (random_operands != 0) or small
+ * integers -- with no memory traffic in the loop; flops = work_groups * 4 *
+ * iters * 16 * 32768.  The caller times it with events on `stream`.  d_out:
+ * device memory of work_groups * 256 floats, caller-owned (overwritten with
+ * sums that keep the loop from being eliminated).  SPB_ERR_ARG / SPB_ERR_LIMIT
+ * for bad sizes before any HIP call. */
+spb_status spb_mfma_calibration(float *d_out, int32_t work_groups, int32_t iters, int32_t random_operands,
+                                void *stream);
+
 spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *d_meta, const spb_attn_args *args,
                                 void *stream);
 

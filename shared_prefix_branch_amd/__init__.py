@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "SpbError", "lib", "library_path", "fingerprint", "Plan", "pack_pass", "branch_attention",
-    "score_options_noalloc", "attention_workspace_bytes",
+    "score_options_noalloc", "attention_workspace_bytes", "mfma_calibration",
     "PreparedAttention", "PreparedScore", "PreparedScoreBatch", "score_batch_workspace_bytes",
     "score_options_batch",
     "score_workspace_bytes", "score_options", "score_finalize", "F32", "BF16", "FP8_E4M3",
@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = [
     "spb_plan_num_passes", "spb_plan_info", "spb_plan_rows", "spb_plan_branches", "spb_plan_inputs",
     "spb_plan_visible",
     "spb_plan_upload", "spb_plan_meta_copy", "spb_branch_attention", "spb_score_workspace_bytes", "spb_score_options",
-    "spb_score_options_noalloc", "spb_attention_workspace_bytes",
+    "spb_score_options_noalloc", "spb_attention_workspace_bytes", "spb_mfma_calibration",
     "spb_score_batch_workspace_bytes", "spb_score_options_batch",
     "spb_score_finalize", "spb_plan_positions", "spb_rope_table", "spb_rmsnorm", "spb_linear",
     "spb_plan_slot", "spb_gather_rows", "spb_topk_workspace_bytes", "spb_topk_lse", "spb_decode_attention",
@@ -186,6 +186,8 @@ def lib() -> ctypes.CDLL:
         L.spb_plan_meta_copy.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]
         L.spb_branch_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.POINTER(_AttnArgs), ctypes.c_void_p]
+        L.spb_mfma_calibration.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_void_p]
         L.spb_attention_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.spb_score_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -395,6 +397,15 @@ def branch_attention(plan: Plan, pass_: int, d_meta, q, k, v, o, softmax_scale: 
     """q [rows, hq, d], k/v [rows, hkv, d], o [rows, hq, d]: contiguous device tensors.
     workspace: for e4m3 inputs, a uint8 device buffer of attention_workspace_bytes (or None)."""
     PreparedAttention(pass_, d_meta, q, k, v, o, softmax_scale, scales, workspace)(plan, stream)
+
+
+def mfma_calibration(out, work_groups: int, iters: int, random_operands: bool, stream=None):
+    """Enqueues the MFMA calibration loop (spb_mfma_calibration); out: a float32
+    device tensor of at least work_groups * 256 elements."""
+    if out.numel() < work_groups * 256:
+        raise SpbError(-4, "out holds fewer than work_groups * 256 floats")
+    _check(lib().spb_mfma_calibration(ctypes.c_void_p(out.data_ptr()), int(work_groups), int(iters),
+                                      1 if random_operands else 0, ctypes.c_void_p(_stream_handle(stream))))
 
 
 def attention_workspace_bytes(plan: Plan, pass_: int, in_dtype: int, hkv: int, head_dim: int) -> int:

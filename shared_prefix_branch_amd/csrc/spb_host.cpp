@@ -1260,6 +1260,16 @@ spb_status spb_branch_attention(const spb_plan *plan, int32_t pass, const void *
   return ok();
 }
 
+spb_status spb_mfma_calibration(float *d_out, int32_t work_groups, int32_t iters, int32_t random_operands,
+                                void *stream) {
+  if (!d_out) return fail(SPB_ERR_ARG, "d_out is NULL");
+  if (work_groups < 1 || iters < 1) return fail(SPB_ERR_ARG, "work_groups %d and iters %d must be >= 1", work_groups, iters);
+  if (work_groups > (1 << 20)) return fail(SPB_ERR_LIMIT, "work_groups %d above 2^20", work_groups);
+  int e = launch_mfma_calibration(d_out, work_groups, iters, random_operands ? 1 : 0, stream);
+  if (e) return fail(SPB_ERR_HIP, "calibration launch: %s", hip_error_string(e));
+  return ok();
+}
+
 spb_status spb_attention_workspace_bytes(const spb_plan *plan, int32_t pass, int32_t in_dtype, int32_t hkv,
                                          int32_t head_dim, size_t *out) {
   spb_status st = check_pass(plan, pass);

@@ -26,6 +26,7 @@ int launch_topk_lse(const TopkLaunch &, void *) { return kNoKernels; }
 int launch_decode_attention(const DecodeAttnLaunch &, void *) { return kNoKernels; }
 int launch_beam_step(const BeamLaunch &, void *) { return kNoKernels; }
 int score_scratch(void **) { return kNoKernels; }
+int launch_mfma_calibration(float *, int, int, int, void *) { return kNoKernels; }
 const char *hip_error_string(int err) {
   return err == kNoKernels ? "this host-only build holds no GPU kernels" : hipGetErrorString((hipError_t)err);
 }

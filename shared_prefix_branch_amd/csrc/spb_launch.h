@@ -188,6 +188,9 @@ int launch_score(const ScoreLaunch &a, void *stream);
 // device), or returns a hipError_t value.
 constexpr size_t kScoreScratchBytes = size_t(64) << 20;
 int score_scratch(void **out);
+// The MFMA calibration loop: work_groups x 256 threads, each wave 16 x iters
+// MFMA 32x32x16 bf16; writes work_groups * 256 floats to out.
+int launch_mfma_calibration(float *out, int work_groups, int iters, int random, void *stream);
 int launch_score_batch(const ScoreBatchLaunch &a, void *stream);
 const char *hip_error_string(int err);
 

@@ -543,6 +543,54 @@ int launch_score_batch(const ScoreBatchLaunch &a, void *stream) {
   return 0;
 }
 
+// ------------------------------------------------------ MFMA calibration
+// The rate the head's MFMA (32x32x16 bf16, f32 accumulation) sustains with
+// nothing else to do: each wave runs 16 independent accumulators through
+// `iters` rounds of 16 MFMAs, operands rotating through 16 registers each,
+// no memory traffic in the loop.  Operands are random bf16 values (random) or
+// small integers whose products leave most multiplier bits idle; with random
+// data the chip's power limit lowers the clock, so the two bound what the
+// head can reach.  One float per thread is written so nothing is eliminated.
+namespace {
+__global__ __launch_bounds__(256) void mfma_calibration_kernel(float *out, int iters, int random) {
+  f32x16 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x16{0.f};
+  u32x4 a[16], b[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t x = (threadIdx.x + 1u) * 2654435761u ^ (uint32_t)(i * 40503 + k * 0x9E3779B9u);
+      x ^= x >> 13; x *= 0x85EBCA6Bu; x ^= x >> 16;
+      uint32_t y = (threadIdx.x + 7u) * 2246822519u ^ (uint32_t)(i * 97 + k * 0x7F4A7C15u);
+      y ^= y >> 15; y *= 0xC2B2AE35u; y ^= y >> 13;
+      // random: bf16 pairs of either sign below 2 in magnitude; else the
+      // small integers 0..7 (exact bf16, few mantissa bits set)
+      a[k][i] = random ? (x & 0xBF7FBF7Fu) : (f2bf((float)(x & 7u)) | (f2bf((float)((x >> 8) & 7u)) << 16));
+      b[k][i] = random ? (y & 0xBF7FBF7Fu) : (f2bf((float)(y & 7u)) | (f2bf((float)((y >> 8) & 7u)) << 16));
+    }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(bf16x8_t *)&a[j], *(bf16x8_t *)&b[(j * 5 + 3) & 15], acc[j],
+                                                        0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[j][r];
+  out[blockIdx.x * 256 + threadIdx.x] = sum;
+}
+}  // namespace
+
+int launch_mfma_calibration(float *out, int work_groups, int iters, int random, void *stream) {
+  hipLaunchKernelGGL(mfma_calibration_kernel, dim3((unsigned)work_groups), dim3(256), 0, (hipStream_t)stream, out,
+                     iters, random);
+  return (int)hipGetLastError();
+}
+
 // ------------------------------------------------------ allocation-free head
 // The workspace of spb_score_options_noalloc: one file-scope device array per
 // GPU (each device that loads the library holds its own copy until the
