@@ -559,3 +559,12 @@ def test_noalloc_head_refuses_a_pass_beyond_its_scratch():
         spb.score_options_noalloc(plan, 0, meta, hid, W, *outs, stream=0, lm_head_kind=spb.HEAD_FP32)
     assert e.value.code == -4
     assert "allocation-free scratch" in spb.lib().spb_last_error().decode()
+
+
+def test_mfma_calibration_validates_before_any_hip_call():
+    # the roofline calibration entry refuses bad sizes on the host
+    L = spb.lib()
+    assert L.spb_mfma_calibration(None, 1, 1, 1, None) == -1
+    assert L.spb_mfma_calibration(ctypes.c_void_p(4096), 0, 1, 1, None) == -1
+    assert L.spb_mfma_calibration(ctypes.c_void_p(4096), 1, 0, 1, None) == -1
+    assert L.spb_mfma_calibration(ctypes.c_void_p(4096), (1 << 20) + 1, 1, 1, None) == -2
