@@ -25,6 +25,20 @@ __device__ inline void dma16(const void *base, uint32_t voff, uint32_t lds) {
       : "memory");
 }
 
+// The same for 4 bytes per lane: lane i writes lds + 4 i.
+__device__ inline void dma4(const void *base, uint32_t voff, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory");
+}
+
 template <int N>
 __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

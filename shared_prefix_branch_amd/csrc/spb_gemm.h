@@ -1,5 +1,6 @@
-// spb_gemm.h -- the MFMA K loop shared by the lm head and the decoder stack's
-// linear layers (gfx950).
+// spb_gemm.h -- the MFMA K steps shared by the lm head and the decoder
+// stack's linear layers, and the linears' K loop (gfx950).  The lm head runs
+// the same K steps in a stream over many tiles (head_lse_kernel).
 //
 // One work group (4 waves) computes a 256 x TM tile of Y^T = W . X^T: 256
 // rows of W (vocabulary rows, or output features) against TM = 32 * MB rows
@@ -103,7 +104,10 @@ __device__ __attribute__((always_inline)) inline void frag_piece(Frags<MB> &f, c
 // c1).  One MFMA, one read and a copy
 // per slot keep the MFMA pipe fed while the LDS and memory queues take the
 // rest; a burst of either would hold up MFMA issue.
-template <int MB, bool READ, int CPS, typename Copy>
+// With ZERO, the step starts the accumulators (acc = A.B, not acc + A.B).
+// With STRIDE > 1 the copies go out in groups of CPS after every STRIDE-th
+// MFMA only (group q after MFMA q * STRIDE).
+template <int MB, bool READ, int CPS, typename Copy, bool ZERO = false, int STRIDE = 1>
 __device__ __attribute__((always_inline)) inline void k_step(f32x16 (&acc)[2][MB], const Frags<MB> &fc,
                                                              Frags<MB> &fn, const u32x4 *Wb, const u32x4 *Hb,
                                                              int ks_next, int wave, int qi, int half, Copy copy,
@@ -113,11 +117,14 @@ __device__ __attribute__((always_inline)) inline void k_step(f32x16 (&acc)[2][MB
 #pragma unroll
     for (int vb = 0; vb < 2; ++vb) {
       const int j = mb * 2 + vb;
-      acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[vb], fc.b[mb], acc[vb][mb], 0, 0, 0);
+      acc[vb][mb] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[vb], fc.b[mb], ZERO ? f32x16{0.f} : acc[vb][mb], 0, 0, 0);
       if (READ && j < 2 + MB) frag_piece<MB>(fn, Wb, Hb, ks_next, j, wave, qi, half);
+      if (j % STRIDE == 0) {
 #pragma unroll
-      for (int c = c0 + j * CPS; c < c0 + (j + 1) * CPS; ++c)
-        if (c < c1) copy(c);
+        for (int c = c0 + (j / STRIDE) * CPS; c < c0 + (j / STRIDE + 1) * CPS; ++c)
+          if (c < c1) copy(c);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   // MB = 1: three pieces, two MFMAs
@@ -125,6 +132,16 @@ __device__ __attribute__((always_inline)) inline void k_step(f32x16 (&acc)[2][MB
   for (int j = 2 * MB; j < 2 + MB; ++j)
     if (READ) frag_piece<MB>(fn, Wb, Hb, ks_next, j, wave, qi, half);
 }
+
+// N copies spread evenly over the 2 MB MFMA slots of one K step: a group of
+// CPS copies after every STRIDE-th MFMA.
+template <int MB, int N>
+struct Spread {
+  static constexpr int SLOTS = 2 * MB;
+  static constexpr int STRIDE = (N > 0 && SLOTS / N > 0) ? SLOTS / N : 1;
+  static constexpr int GROUPS = SLOTS / STRIDE;
+  static constexpr int CPS = N > 0 ? (N + GROUPS - 1) / GROUPS : 0;
+};
 
 // Per-lane global byte offsets of the tile copies: one DMA instruction moves
 // 8 rows x 128 bytes, lane t filling LDS position t%8 of row r8 + t/8, which

@@ -12,13 +12,14 @@
 // Kernel 0 (gather_hidden_kernel): packs the scored rows' hidden states as
 //   bf16 rows, zero-padded to the GEMM's row tiling.
 // Kernel 1 (head_lse_kernel): Z^T[v, m] = W[v, :] . h[m, :] on MFMA 32x32x16
-//   bf16 with f32 accumulation, one work group per (256-row vocabulary slice,
+//   bf16 with f32 accumulation over tiles of (256-row vocabulary slice,
 //   32..256 scored rows), each wave a 64-row vocabulary strip against all the
-//   group's rows; W and h tiles of 64 hidden elements are copied global ->
-//   LDS asynchronously into XOR-swizzled rings.  Logits never leave
-//   registers: the epilogue writes, per (row, slice), the slice max and sum
-//   of exp(z - max), and stores the logits of the option tokens the row
-//   predicts.
+//   tile's rows.  One resident work group per compute unit walks its list of
+//   tiles as one stream of 64-element K stages, copied global -> LDS
+//   asynchronously into XOR-swizzled rings, so a tile's first stages load
+//   during the previous tile's epilogue.  Logits never leave registers: the
+//   epilogue writes, per (row, slice), the slice max and sum of exp(z - max),
+//   and stores the logits of the option tokens the row predicts.
 // Kernel 2 (finalize_kernel): one wave per branch merges a row's slices in
 //   slice order into LSE, sums each option's chain of log-probabilities in
 //   token order, and renormalises.
@@ -36,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
 #include <mutex>
 
 namespace spb {
@@ -147,150 +150,348 @@ struct HeadParams {
 template <int MB>
 using HeadTile = gemm::Tile<MB>;
 
-// Work group: 256 vocabulary rows x TM = 32*MB scored rows, on the shared K
-// loop (spb_gemm.h); the h tile is small and shared by every work group, so
-// L2-resident.
+// A work group stays resident and computes a list of 256 x TM tiles (256
+// vocabulary rows x TM = 32*MB scored rows) as one continuous stream of
+// 64-element K stages: stage g of the stream is stage g mod S of tile g / S
+// (S = Hrow / 64).  The W and h rings of the K loop (spb_gemm.h) rotate over
+// the whole stream, so the copies of a tile's first stages are issued during
+// the previous tile's last stages and land while its epilogue runs; a tile
+// never starts by waiting on memory, and no work group is launched per tile.
+//
+// XCD-aware order: work groups are dealt round-robin to the 8 XCDs, so block
+// b runs on XCD b mod 8 as its (b / 8)-th of P groups there.  The XCD's tile
+// slots are k = 0, 1, ... with slice (k / n_mchunks) * 8 + xcd and row chunk
+// k mod n_mchunks; group j takes slots j, j + P, j + 2P, ...  The P groups of
+// an XCD move through their lists at the same pace, so the row chunks of one
+// vocabulary slice run side by side there and share its W lines in that
+// XCD's L2.
 template <int MB>
 __global__ __launch_bounds__(kThreads, 1) void head_lse_kernel(HeadParams p) {
   using T = HeadTile<MB>;
   constexpr int TM = T::TM;
+  constexpr int NH = T::NH, NW = T::NW;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS];
-  static_assert(4 * TM * 2 * 4 <= T::LDS, "epilogue buffer must fit in the ring");
 
-  // XCD-aware order: work groups are dealt round-robin to the 8 XCDs, so the
-  // M chunks of one vocabulary slice get consecutive slots of one XCD and
-  // stream the same W rows through its L2 together.
   const int b = blockIdx.x;
-  const int xcd = b & 7, slot = b >> 3;
-  const int slice = (slot / p.n_mchunks) * 8 + xcd;
-  const int mchunk = slot % p.n_mchunks;
-  if (slice >= p.n_slices) return;
+  const int xcd = b & 7, j = b >> 3, P = (int)(gridDim.x >> 3);
+  const int slots = ((p.n_slices - xcd + 7) >> 3) * p.n_mchunks;
+  const int n_tiles = j < slots ? (slots - j + P - 1) / P : 0;
+  if (n_tiles == 0) return;
+  auto slice_of = [&](int t) { return ((j + t * P) / p.n_mchunks) * 8 + xcd; };
+  auto m0_of = [&](int t) { return ((j + t * P) % p.n_mchunks) * TM; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform within the wave
   const int qi = lane & 31, half = lane >> 5;
-  const int v0 = slice * kVocabTile;
-  const int m0 = mchunk * TM;
+  const int dr = lane >> 3;
 
-  uint32_t woff[8], hoff[MB];
-  gemm::tile_offsets<MB>(
-      woff, hoff, [&](int r) { return v0 + r < p.V ? v0 + r : p.V - 1; }, [&](int r) { return m0 + r; }, p.H,
-      p.Hrow, wave, lane);
+  // Copy offsets (bytes): one DMA instruction moves 8 rows x 128 bytes, lane
+  // t filling LDS position t%8 of row r8 + t/8, i.e. chunk (t%8) ^ ((r/2)%8)
+  // of that row (swz).  h rows are offsets from the tile's first row; W rows
+  // past the vocabulary (its last slice) are clamped onto its last row.
+  uint32_t hoff[MB], woff[8];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = (wave * MB + i) * 8 + dr;
+    hoff[i] = ((uint32_t)r * (uint32_t)p.Hrow + (uint32_t)((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
+  }
+  auto w_offsets = [&](int v0) {
+    const int rmax = p.V - 1 - v0;
+    int l = lane;
+    asm volatile("" : "+v"(l));  // recomputed from the lane here, not kept in registers across the loop
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave * 64 + i * 8 + (l >> 3);
+      woff[i] = ((uint32_t)min(r, rmax) * (uint32_t)p.H + (uint32_t)((l & 7) ^ ((r >> 1) & 7)) * 8) * 2;
+    }
+  };
+
+  char *const wring = lds;
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  const uint32_t hring0 = lds0 + T::RW * T::WBYTES;
+  // Copy i of a stage: the stage's base pointer and the wave's first LDS row
+  // in the slot are scalars, the lane's offset is fixed.
+  auto copy_h = [&](int i, const uint16_t *xs, uint32_t lbase) { dma16(xs, hoff[i], lbase + i * 8 * 128); };
+  auto copy_w = [&](int i, const uint16_t *ws, uint32_t lbase) { dma16(ws, woff[i], lbase + i * 8 * 128); };
+  auto h_stage = [&](const uint16_t *xb, int xk) { return xb + xk * kKT; };
+  auto w_stage = [&](const uint16_t *wb, int wk) {
+    int ws = wk;  // the fp32 kind sweeps W once per plane of h
+    if (ws >= p.SW) ws -= p.SW;
+    if (ws >= p.SW) ws -= p.SW;
+    return wb + ws * kKT;
+  };
+  auto h_lds = [&](int sl) {
+    return __builtin_amdgcn_readfirstlane(hring0 + (uint32_t)sl * T::HBYTES + wave * NH * 8 * 128);
+  };
+  auto w_lds = [&](int sl) { return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)sl * T::WBYTES + wave * 64 * 128); };
+
+  // The stream position of the next h copies (tile xt, stage xk) and of the
+  // next W copies (wt, wk).  Past the stream's last stage they stay on it:
+  // those copies reload it into a slot nothing reads again, so every trip
+  // has the same copies in flight.
+  const int S = p.Hrow / kKT;
+  int xt = 0, xk = 0, wt = 0, wk = 0;
+  const uint16_t *xb = p.hg + (size_t)m0_of(0) * p.Hrow;
+  int v0w = slice_of(0) * kVocabTile;
+  const uint16_t *wb = p.W + (size_t)v0w * p.H;
+  w_offsets(v0w);
+  auto next_x = [&]() {
+    if (xk + 1 < S) {
+      ++xk;
+    } else if (xt + 1 < n_tiles) {
+      ++xt;
+      xk = 0;
+      xb = p.hg + (size_t)m0_of(xt) * p.Hrow;
+    }
+  };
+  auto next_w = [&]() {
+    if (wk + 1 < S) {
+      ++wk;
+    } else if (wt + 1 < n_tiles) {
+      ++wt;
+      wk = 0;
+      v0w = slice_of(wt) * kVocabTile;
+      wb = p.W + (size_t)v0w * p.H;
+      w_offsets(v0w);
+    }
+  };
+
   f32x16 acc[2][MB];
-  gemm::k_loop<MB>(acc, lds, p.W, p.hg, woff, hoff, p.Hrow / kKT, p.SW, wave, qi, half);
 
-  // epilogue; the ring is free.  LDS: the four waves' (max, sum) per row,
-  // then the group's target CSR (offsets relative to its first target) and,
-  // when they fit, its target tokens, staged in one round trip so the
-  // capture below waits on LDS, not on a global load per target.
-  float (*red)[TM][2] = (float (*)[TM][2])lds;  // [4][TM][2]
-  int *s_off = (int *)(lds + 4 * TM * 2 * 4);   // [TM + 1]
-  int *s_tok = s_off + TM + 1;
-  constexpr int kTokCap = (T::LDS - 4 * TM * 2 * 4) / 4 - (TM + 1);
+  // Epilogue of tile t, in the 32 KB W slot R that the stream's stage just
+  // finished with (the next copy into it is issued on the next trip).  R
+  // holds the four waves' (max, sum) per row, then the tile's target CSR and,
+  // when they fit, its target tokens, copied in asynchronously while the
+  // slice statistics are computed, so no step waits on a global load.
+  constexpr int kOffN = (TM + 1 + 63) / 64 * 64;
+  constexpr int kTokCap = ((T::WBYTES - 4 * TM * 2 * 4 - 4 * kOffN) / 4) / 64 * 64;
   static_assert(kTokCap >= 4 * TM, "room for several targets per row");
-  const int tb = p.tgt_off[m0 < p.M ? m0 : p.M];
-  const int te = p.tgt_off[m0 + TM < p.M ? m0 + TM : p.M];
-  const bool staged = te - tb <= kTokCap;
-  for (int i = tid; i <= TM; i += kThreads) s_off[i] = p.tgt_off[m0 + i < p.M ? m0 + i : p.M] - tb;
-  if (staged)
-    for (int i = tid; i < te - tb; i += kThreads) s_tok[i] = p.tgt_tok[tb + i];
-  __syncthreads();
+  // A tile's first and end target positions (tb, te) are scalar loads (the
+  // CSR is constant while the kernel runs) issued one epilogue ahead, so no
+  // epilogue waits on them.
+  typedef const __attribute__((address_space(4))) int32_t *const_i32;
+  const const_i32 csr = (const_i32)p.tgt_off;
+  auto tile_targets = [&](int t, int &tb, int &te) {
+    const int m0 = m0_of(t);
+    tb = csr[min(m0, p.M)];
+    te = csr[min(m0 + TM, p.M)];
+  };
+  int tb_next = 0, te_next = 0;
+  tile_targets(0, tb_next, te_next);
+  auto epilogue = [&](int t, char *R) {
+    const int v0 = slice_of(t) * kVocabTile, m0 = m0_of(t);
+    float (*red)[TM][2] = (float (*)[TM][2])R;  // [4][TM][2]
+    int *s_off = (int *)(R + 4 * TM * 2 * 4);   // [kOffN]: the CSR entries of rows m0 .. m0 + TM, raw
+    int *s_tok = s_off + kOffN;                 // [kTokCap]
+    const int tb = tb_next, te = te_next;
+    if (t + 1 < n_tiles) tile_targets(t + 1, tb_next, te_next);
+    const int n_tok = te - tb;
+    const bool staged = n_tok <= kTokCap;
+    for (int i0 = wave * 64; i0 < kOffN; i0 += 256)
+      dma4(p.tgt_off, (uint32_t)min(m0 + i0 + lane, p.M) * 4, lds_addr(s_off + i0));
+    if (staged)
+      for (int i0 = wave * 64; i0 < n_tok; i0 += 256)
+        dma4(p.tgt_tok, (uint32_t)(tb + min(i0 + lane, n_tok - 1)) * 4, lds_addr(s_tok + i0));
 
-  // Lane holds column m = m0 + mb*32 + qi; register r of block vb holds
-  // vocabulary row v0 + wave*64 + vb*32 + (r/4)*8 + half*4 + r%4.
-  const int vw0 = v0 + wave * 64;
-  const int nvalid = p.V - vw0;      // rows past the vocabulary (last slice only) are excluded
-  const bool full = nvalid >= 64;    // uniform: every strip but the vocabulary's tail
-  constexpr float kL2e = 1.44269504088896340736f;
-  // one 32-row block at a time, so only its two accumulators leave the
-  // accumulation registers at once
+    // Lane holds column m = m0 + mb*32 + qi; register r of block vb holds
+    // vocabulary row v0 + wave*64 + vb*32 + (r/4)*8 + half*4 + r%4.
+    const int vw0 = v0 + wave * 64;
+    const int nvalid = p.V - vw0;    // rows past the vocabulary (last slice only) are excluded
+    const bool full = nvalid >= 64;  // uniform: every strip but the vocabulary's tail
+    constexpr float kL2e = 1.44269504088896340736f;
+    auto logits = [&](int mb, f32x16 (&z)[2]) {
+      z[0] = acc[0][mb];
+      z[1] = acc[1][mb];
+      asm volatile("" : "+v"(z[0]), "+v"(z[1]));  // the copy out of acc happens here
+      if (p.round_bf16) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    f32x16 z[2] = {acc[0][mb], acc[1][mb]};
-    asm volatile("" : "+v"(z[0]), "+v"(z[1]));  // the copy out of acc happens here, not at the loop exit
-    if (p.round_bf16) {
+        for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
+          for (int r = 0; r < 16; ++r) z[vb][r] = bf2f(f2bf(z[vb][r]));
+      }
+    };
+    // one 32-row block at a time, so only its two accumulators leave the
+    // accumulation registers at once
 #pragma unroll
-        for (int r = 0; r < 16; ++r) z[vb][r] = bf2f(f2bf(z[vb][r]));
-    }
-    float mx = kNegInf;
-    if (full) {
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, z[vb][r]);
-    } else {
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          mx = fmaxf(mx, vr < nvalid ? z[vb][r] : kNegInf);
-        }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float se = 0.f;
-    if (mx != kNegInf) {
-      // exp(z - mx) as 2^(z log2e - mx log2e): one fma and one v_exp_f32
-      const float nm = -mx * kL2e;
+    for (int mb = 0; mb < MB; ++mb) {
+      f32x16 z[2];
+      logits(mb, z);
+      float mx = kNegInf;
       if (full) {
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) se += __builtin_amdgcn_exp2f(__builtin_fmaf(z[vb][r], kL2e, nm));
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, z[vb][r]);
       } else {
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            se += vr < nvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[vb][r], kL2e, nm)) : 0.f;
+            mx = fmaxf(mx, vr < nvalid ? z[vb][r] : kNegInf);
           }
       }
-    }
-    se = se + __shfl_xor(se, 32);
-    const int ml = mb * 32 + qi;
-    if (half == 0) {
-      red[wave][ml][0] = mx;
-      red[wave][ml][1] = se;
-    }
-    // capture the logits of the tokens this row predicts
-    const int m = m0 + ml;
-    if (m < p.M) {
-      const int t0 = s_off[ml], t1 = s_off[ml + 1];
-      for (int t = t0; t < t1; ++t) {
-        const int rel = (staged ? s_tok[t] : p.tgt_tok[tb + t]) - vw0;
-        if (rel < 0 || rel >= 64) continue;
-        const int rr = rel & 31;
-        if (((rr >> 2) & 1) != half) continue;
-        const int vbt = rel >> 5, rt = (rr >> 3) * 4 + (rr & 3);
-        float val = 0.f;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float se = 0.f;
+      if (mx != kNegInf) {
+        // exp(z - mx) as 2^(z log2e - mx log2e): one fma and one v_exp_f32
+        const float nm = -mx * kL2e;
+        if (full) {
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
+          for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) val = (vb == vbt && r == rt) ? z[vb][r] : val;
-        p.tz[tb + t] = val;
+            for (int r = 0; r < 16; ++r) se += __builtin_amdgcn_exp2f(__builtin_fmaf(z[vb][r], kL2e, nm));
+        } else {
+#pragma unroll
+          for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int vr = vb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+              se += vr < nvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[vb][r], kL2e, nm)) : 0.f;
+            }
+        }
       }
+      se = se + __shfl_xor(se, 32);
+      if (half == 0) {
+        red[wave][mb * 32 + qi][0] = mx;
+        red[wave][mb * 32 + qi][1] = se;
+      }
+    }
+    wait_vmcnt<0>();  // the CSR and token copies (and the stream's W copies before them) landed
+    lds_barrier();
+
+    // capture the logits of the tokens each row predicts
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int ml = mb * 32 + qi;
+      if (m0 + ml < p.M) {
+        const int t0 = s_off[ml] - tb, t1 = s_off[ml + 1] - tb;
+        for (int t = t0; t < t1; ++t) {
+          const int rel = (staged ? s_tok[t] : p.tgt_tok[tb + t]) - vw0;
+          if (rel < 0 || rel >= 64) continue;
+          const int rr = rel & 31;
+          if (((rr >> 2) & 1) != half) continue;
+          const int vbt = rel >> 5, rt = (rr >> 3) * 4 + (rr & 3);
+          f32x16 z[2];
+          logits(mb, z);
+          float val = 0.f;
+#pragma unroll
+          for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) val = (vb == vbt && r == rt) ? z[vb][r] : val;
+          p.tz[tb + t] = val;
+        }
+      }
+    }
+    // merge the four waves' (max, sum) in wave order
+    for (int ml = tid; ml < TM; ml += kThreads) {
+      const int m = m0 + ml;
+      if (m < p.M) {
+        float M = red[0][ml][0], Ssum = red[0][ml][1];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          const float a = red[w][ml][0];
+          const float Mn = fmaxf(M, a);
+          Ssum = (M == kNegInf ? 0.f : Ssum * __expf(M - Mn)) + (a == kNegInf ? 0.f : red[w][ml][1] * __expf(a - Mn));
+          M = Mn;
+        }
+        float *dst = p.part + ((size_t)m * p.n_slices + v0 / kVocabTile) * 2;
+        dst[0] = M;
+        dst[1] = Ssum;
+      }
+    }
+    lds_barrier();  // R is free again for the stream's copies
+  };
+
+  // Trip g: K steps 0-2 of stage g, the hand-off, then K step 3, whose MFMAs
+  // carry the reads of stage g+1's first fragments.  The copies are spread
+  // evenly over the trip, a group after every few MFMAs, so the L2 -> LDS
+  // stream never comes in bursts: the first half of h(g+2) over K step 3
+  // (stage g's h slot is free once the barrier has passed), its second half
+  // over the next trip's K step 0, and W(g+2), two stages ahead, over K steps
+  // 1 and 2.  The barrier follows every read of stage g (its lgkmcnt(0)), so
+  // stage g's slots are free after it.  A result element sees the same MFMAs
+  // in the same order as in a loop over one tile: its W row and h row, K
+  // stage by stage, 16 elements per MFMA.
+  constexpr int NXA = (NH + 1) / 2, NXB = NH - NXA;  // h copies over K step 3, then the next K step 0
+  constexpr int NWA = NW / 2;                          // W copies over K step 1 (the rest over K step 2)
+  using SXA = gemm::Spread<MB, NXA>;
+  using SXB = gemm::Spread<MB, NXB>;
+  using SW1 = gemm::Spread<MB, NWA>;
+  using SW2 = gemm::Spread<MB, NW - NWA>;
+  const u32x4 *const wr = (const u32x4 *)wring;
+  const u32x4 *const hr = (const u32x4 *)(lds + T::RW * T::WBYTES);
+  constexpr int WQ = T::WBYTES / 16, HQ = T::HBYTES / 16;  // slot sizes in 16-byte units
+
+  // Prologue: h(0), W(0), W(1), then the first half of h(1).
+  {
+    const uint16_t *xs = h_stage(xb, xk);
+    const uint32_t xl = h_lds(0);
+#pragma unroll
+    for (int i = 0; i < NH; ++i) copy_h(i, xs, xl);
+    next_x();
+#pragma unroll
+    for (int s1 = 0; s1 < 2; ++s1) {
+      const uint16_t *ws = w_stage(wb, wk);
+      const uint32_t wl = w_lds(s1);
+#pragma unroll
+      for (int i = 0; i < NW; ++i) copy_w(i, ws, wl);
+      next_w();
     }
   }
-  __syncthreads();
-  // merge the four waves' (max, sum) in wave order
-  for (int ml = tid; ml < TM; ml += kThreads) {
-    const int m = m0 + ml;
-    if (m < p.M) {
-      float M = red[0][ml][0], S = red[0][ml][1];
+  wait_vmcnt<NW>();  // h(0), W(0) landed (this wave's copies)
+  lds_barrier();
+  const uint16_t *pxs = h_stage(xb, xk);  // the h stage whose copies are under way
+  uint32_t pxl = h_lds(1);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        const float a = red[w][ml][0];
-        const float Mn = fmaxf(M, a);
-        S = (M == kNegInf ? 0.f : S * __expf(M - Mn)) + (a == kNegInf ? 0.f : red[w][ml][1] * __expf(a - Mn));
-        M = Mn;
-      }
-      float *dst = p.part + ((size_t)m * p.n_slices + slice) * 2;
-      dst[0] = M;
-      dst[1] = S;
+  for (int i = 0; i < NXA; ++i) copy_h(i, pxs, pxl);
+
+  gemm::Frags<MB> f0, f1;
+  gemm::frags<MB>(f0, wr, hr, 0, wave, qi, half);
+  int sw = 0, sh = 0;  // ring slots of the stream's current stage
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    int sw_done = 0;
+    for (int kst = 0; kst < S; ++kst) {
+      const u32x4 *Wb = wr + sw * WQ;
+      const u32x4 *Hb = hr + sh * HQ;
+      const uint16_t *cws = w_stage(wb, wk);
+      const uint32_t cwl = w_lds(sw == 0 ? 2 : sw - 1);  // slot of the stage two ahead (= one behind, mod 3)
+      const uint16_t *cxs = pxs;
+      const uint32_t cxl = pxl;
+      auto copy_x = [&](int c) { copy_h(c, cxs, cxl); };
+      auto copy_wc = [&](int c) { copy_w(c, cws, cwl); };
+      __builtin_amdgcn_sched_barrier(0);
+      if (kst == 0)  // a tile's first K step starts its accumulators
+        gemm::k_step<MB, true, SXB::CPS, decltype(copy_x), true, SXB::STRIDE>(acc, f0, f1, Wb, Hb, 1, wave, qi,
+                                                                               half, copy_x, NXA, NH);
+      else
+        gemm::k_step<MB, true, SXB::CPS, decltype(copy_x), false, SXB::STRIDE>(acc, f0, f1, Wb, Hb, 1, wave, qi,
+                                                                                half, copy_x, NXA, NH);
+      next_x();
+      gemm::k_step<MB, true, SW1::CPS, decltype(copy_wc), false, SW1::STRIDE>(acc, f1, f0, Wb, Hb, 2, wave, qi, half,
+                                                                              copy_wc, 0, NWA);
+      gemm::k_step<MB, true, SW2::CPS, decltype(copy_wc), false, SW2::STRIDE>(acc, f0, f1, Wb, Hb, 3, wave, qi, half,
+                                                                              copy_wc, NWA, NW);
+      next_w();
+      wait_vmcnt<NW>();  // the next stage's h and W copies landed
+      lds_barrier();
+      sw_done = sw;
+      sw = sw == 2 ? 0 : sw + 1;
+      pxs = h_stage(xb, xk);  // h(g+2) goes into stage g's h slot
+      pxl = h_lds(sh);
+      sh ^= 1;
+      const uint16_t *nxs = pxs;
+      const uint32_t nxl = pxl;
+      auto copy_nx = [&](int c) { copy_h(c, nxs, nxl); };
+      gemm::k_step<MB, true, SXA::CPS, decltype(copy_nx), false, SXA::STRIDE>(acc, f1, f0, wr + sw * WQ,
+                                                                              hr + sh * HQ, 0, wave, qi, half,
+                                                                              copy_nx, 0, NXA);
     }
+    // The next stage's first fragments are read again after the epilogue
+    // (its slots are not the one the epilogue uses), so they hold no
+    // registers during it.
+    epilogue(tt, wring + sw_done * T::WBYTES);
+    gemm::frags<MB>(f0, wr + sw * WQ, hr + sh * HQ, 0, wave, qi, half);
   }
 }
 
@@ -386,10 +587,27 @@ int launch_gather(const GatherParams &g, int h_dtype, hipStream_t s) {
 
 // The GEMM + slice partials over M gathered rows, bracketed by the optional
 // timing events.
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cached[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 int launch_head(const HeadParams &p0, int mb, void *ev_begin, void *ev_end, hipStream_t s) {
   HeadParams p = p0;
-  long long groups = (long long)((p.n_slices + 7) / 8) * 8 * p.n_mchunks;
-  if (groups > 0x7FFFFFFFll) return (int)hipErrorInvalidValue;
+  // one resident work group per compute unit, P per XCD, each walking its
+  // list of tiles (never more groups than an XCD has tile slots)
+  const long long slots = (long long)((p.n_slices + 7) / 8) * p.n_mchunks;
+  if (slots > 0x7FFFFFFFll / 8) return (int)hipErrorInvalidValue;
+  const long long per_xcd = std::max(1, device_cus() / 8);
+  const long long groups = 8 * std::min(per_xcd, slots);
   dim3 grid((unsigned)groups), block(kThreads);
   int e;
   if (ev_begin) {
