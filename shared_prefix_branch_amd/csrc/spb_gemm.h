@@ -210,24 +210,32 @@ __device__ __attribute__((always_inline)) inline void k_loop(f32x16 (&acc)[2][MB
   const int last = S - 1;
   // Copies past the last stage reload it into a slot nothing reads again, so
   // the count of copies in flight is the same on every trip.
-  // Trip s issues X(s+1) then W(s+2); at its end only W(s+2) may be in flight.
+  // The copies are spread evenly over each trip, a group after every few
+  // MFMAs, so the L2 -> LDS stream never comes in bursts: the first half of
+  // X(s+2) over K step 3 of trip s (stage s's X slot is free once the barrier
+  // has passed), its second half over K step 0 of trip s+1, and W(s+2), two
+  // stages ahead, over K steps 1 and 2.  At a trip's end only W(s+2) may be
+  // in flight.
+  constexpr int NH = T::NH, NW = T::NW;
+  constexpr int NXA = (NH + 1) / 2;  // X copies over K step 3 (the rest over the next K step 0)
+  constexpr int NWA = NW / 2;        // W copies over K step 1 (the rest over K step 2)
+  using SXA = Spread<MB, NXA>;
+  using SXB = Spread<MB, NH - NXA>;
+  using SW1 = Spread<MB, NWA>;
+  using SW2 = Spread<MB, NW - NWA>;
   issue_h(0, 0);
   issue_w(0, 0);
   issue_w(min(1, last), 1);
-  wait_vmcnt<T::NW>();  // X(0), W(0) landed (this wave's copies)
+  wait_vmcnt<NW>();  // X(0), W(0) landed (this wave's copies)
   lds_barrier();
+  int xst = min(1, last), xsl = 1;  // the X stage whose copies are under way, and its slot
+#pragma unroll
+  for (int i = 0; i < NXA; ++i) copy_h(i, xst, xsl);
 
-  // The stage's copies: X(s+1), which every wave reads and which must land by
-  // this stage's barrier, alone over the slots of the first K step; then
-  // W(s+2), two stages ahead, over the second (the stage-end wait relies on X
-  // going first).
-  constexpr int NC = T::NH + T::NW;
-  constexpr int CPSX = (T::NH + 2 * MB - 1) / (2 * MB);
-  constexpr int CPSW = (T::NW + 2 * MB - 1) / (2 * MB);
   // The stage hand-off (copies landed, barrier) comes before the last K
   // step, whose MFMAs carry the reads of the next stage's first fragments, so
   // no stage starts by waiting on LDS.  The barrier follows every read of
-  // stage s (its lgkmcnt(0)), so trip s+1's copies may overwrite its slots.
+  // stage s (its lgkmcnt(0)), so the copies after it may overwrite its slots.
   // After the last stage those reads fetch landed copies of the last stage,
   // unused.
   Frags<MB> f0, f1;
@@ -237,23 +245,28 @@ __device__ __attribute__((always_inline)) inline void k_loop(f32x16 (&acc)[2][MB
     const u32x4 *Wb = (const u32x4 *)(wring + sw * T::WBYTES);
     const u32x4 *Hb = (const u32x4 *)(hring + sh * T::HBYTES);
     const int sw2 = sw == 0 ? 2 : sw - 1;  // slot of stage s + 2 (= s - 1 mod 3)
-    const int sx = min(s + 1, last), sx2 = min(s + 2, last);
-    auto copy = [&](int c) {
-      if (c < T::NH)
-        copy_h(c, sx, sh ^ 1);
-      else
-        copy_w(c - T::NH, sx2, sw2);
-    };
+    const int sx2 = min(s + 2, last);
+    const int cxst = xst, cxsl = xsl;
+    auto copy_x = [&](int c) { copy_h(c, cxst, cxsl); };
+    auto copy_wc = [&](int c) { copy_w(c, sx2, sw2); };
     __builtin_amdgcn_sched_barrier(0);
-    k_step<MB, true, CPSX>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy, 0, T::NH);
-    k_step<MB, true, CPSW>(acc, f1, f0, Wb, Hb, 2, wave, qi, half, copy, T::NH, NC);
-    k_step<MB, true, 0>(acc, f0, f1, Wb, Hb, 3, wave, qi, half, copy, 0, 0);
-    wait_vmcnt<T::NW>();  // X(s+1) and W(s+1) landed
+    k_step<MB, true, SXB::CPS, decltype(copy_x), false, SXB::STRIDE>(acc, f0, f1, Wb, Hb, 1, wave, qi, half, copy_x,
+                                                                     NXA, NH);
+    k_step<MB, true, SW1::CPS, decltype(copy_wc), false, SW1::STRIDE>(acc, f1, f0, Wb, Hb, 2, wave, qi, half,
+                                                                      copy_wc, 0, NWA);
+    k_step<MB, true, SW2::CPS, decltype(copy_wc), false, SW2::STRIDE>(acc, f0, f1, Wb, Hb, 3, wave, qi, half,
+                                                                      copy_wc, NWA, NW);
+    wait_vmcnt<NW>();  // X(s+1) and W(s+1) landed
     lds_barrier();
+    xst = sx2;  // X(s+2) goes into stage s's X slot
+    xsl = sh;
     sw = sw == 2 ? 0 : sw + 1;
     sh ^= 1;
-    k_step<MB, true, 0>(acc, f1, f0, (const u32x4 *)(wring + sw * T::WBYTES), (const u32x4 *)(hring + sh * T::HBYTES),
-                        0, wave, qi, half, copy, 0, 0);
+    const int nxst = xst, nxsl = xsl;
+    auto copy_nx = [&](int c) { copy_h(c, nxst, nxsl); };
+    k_step<MB, true, SXA::CPS, decltype(copy_nx), false, SXA::STRIDE>(
+        acc, f1, f0, (const u32x4 *)(wring + sw * T::WBYTES), (const u32x4 *)(hring + sh * T::HBYTES), 0, wave, qi,
+        half, copy_nx, 0, NXA);
   }
   wait_vmcnt<0>();  // no copy may land after the ring is reused or released
   lds_barrier();
