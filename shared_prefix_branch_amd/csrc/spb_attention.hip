@@ -26,7 +26,9 @@
 //    two-slot LDS ring (XOR-swizzled rows, no staging registers), one chunk
 //    ahead; every LDS fragment read is issued ahead of the MFMAs that use it.
 //    A wave owns 32 query rows of one query head (two heads for d = 64,
-//    sharing every K/V fragment read and visibility test).
+//    sharing every K/V fragment read and visibility test).  Q rows and bf16
+//    O rows also pass through LDS, so that their global accesses are whole
+//    16-byte pieces of consecutive rows rather than one row per lane pair.
 //  * f32 / fp8 inputs (staged kernel): K and V pass through registers, where
 //    f32 is rounded to bf16 and e4m3 V is widened to bf16, into a
 //    double-buffered padded LDS layout; one head per wave; the chunk list is
@@ -609,6 +611,15 @@ struct DmaCfg {
   static constexpr int ROWB = 2 * D;                // bytes per V row (and per K row for bf16)
   static constexpr int BUFK = 64 * ROWB_K;          // one chunk of K
   static constexpr int BUF = 64 * ROWB;             // one chunk of V
+  static constexpr int SLOT = BUFK + BUF;           // ring slot: K of a chunk, then its V
+  // Q rows of a wave (32 rows x HPW heads, QROWB bytes each) are copied
+  // into the 1 KB blocks of ring slot 1 that the wave itself later fills
+  // with chunk 1, when they fit there.
+  static constexpr int QROWB = FP8 ? D : 2 * D;
+  static constexpr int QBLK = 32 * HPW * QROWB / 1024;  // Q blocks per wave
+  static constexpr bool QLDS = QBLK * NW * 1024 <= SLOT;
+  // bf16 output rows of a wave (32 rows x HPW heads) staged in the ring
+  static constexpr int OROWB = 2 * HPW * D;
   // copies per wave per tensor for a 64-key and a 32-key chunk
   static constexpr int QK64 = 64 * ROWB_K / 1024 / NW;
   static constexpr int QK32 = 32 * ROWB_K / 1024 / NW;
@@ -621,6 +632,8 @@ struct DmaCfg {
   static_assert(Q32 >= 1 && Q32 * NW * 1024 == 32 * ROWB, "a 32-key chunk must give every wave whole copies");
   static_assert(QK32 >= 1 && QK32 * NW * 1024 == 32 * ROWB_K, "a 32-key chunk must give every wave whole copies");
   static_assert(!FP8 || D == 128, "e4m3 inputs need head_dim 128");
+  static_assert(NW * 32 * OROWB <= 2 * SLOT && (OROWB == 128 || OROWB == 256), "output staging must fit the ring");
+  static_assert(QROWB == 128 || QROWB == 256, "Q rows of 128 or 256 bytes");
 };
 
 // LDS row swizzles (16-byte chunk c of row r lives at chunk c ^ f(r)).  K: a
@@ -642,8 +655,8 @@ __global__ __launch_bounds__((DmaCfg<D, G, HPW_, RG_, IN>::NT), (DmaCfg<D, G, HP
 branch_attention_dma(AttnParams p) {
   using C = DmaCfg<D, G, HPW_, RG_, IN>;
   constexpr int HPW = C::HPW;
-  __shared__ __attribute__((aligned(1024))) char Ks[2][C::BUFK];
-  __shared__ __attribute__((aligned(1024))) char Vs[2][C::BUF];
+  // ring slot s: K of chunk s (mod 2) at ring + s * SLOT, its V BUFK bytes on
+  __shared__ __attribute__((aligned(1024))) char ring[2 * C::SLOT];
   __shared__ int4 chunks[kMaxChunks];
 
   const int w = blockIdx.x;
@@ -660,7 +673,7 @@ branch_attention_dma(AttnParams p) {
   const bool active = local < it.nrows;
   const int x = it.row0 + local;
 
-  const uint32_t k_lds = lds_addr(&Ks[0][0]), v_lds = lds_addr(&Vs[0][0]);
+  const uint32_t k_lds = lds_addr(&ring[0]), v_lds = k_lds + C::BUFK;
 
   // Copies chunk i (64 or 32 key rows; rows past the pass repeat its last
   // row, so every slot holds finite data) into ring slot i % 2.  Copy qq of
@@ -683,11 +696,11 @@ branch_attention_dma(AttnParams p) {
   const uint32_t ystridek = (uint32_t)(p.hkv * C::ROWB_K);
   auto copy_k = [&](int key0, int slot, int qq) {
     const int y = min(key0 + r0k + qq * RSTEPK, p.n_tokens - 1);
-    dma16(p.k, (uint32_t)y * ystridek + kofs, k_lds + (uint32_t)slot * C::BUFK + (uint32_t)(qq * C::NW + wave) * 1024);
+    dma16(p.k, (uint32_t)y * ystridek + kofs, k_lds + (uint32_t)slot * C::SLOT + (uint32_t)(qq * C::NW + wave) * 1024);
   };
   auto copy_v = [&](int key0, int slot, int qq) {
     const int y = min(key0 + r0 + qq * RSTEP, p.n_tokens - 1);
-    dma16(p.v, (uint32_t)y * ystride + vofs, v_lds + (uint32_t)slot * C::BUF + (uint32_t)(qq * C::NW + wave) * 1024);
+    dma16(p.v, (uint32_t)y * ystride + vofs, v_lds + (uint32_t)slot * C::SLOT + (uint32_t)(qq * C::NW + wave) * 1024);
   };
   auto copy_chunk = [&](int key0, int slot, bool content) {
     if (content) {
@@ -711,11 +724,32 @@ branch_attention_dma(AttnParams p) {
   const bool early = it.ncc > 0;
   if (early) copy_chunk(it.seg, 0, true);
 
+  // Q block b of this wave (rows 32 j + r of its heads, j = head, r = row of
+  // its 32, RPB rows per block) is ring block NW * b + wave of slot 1: the
+  // blocks this wave's own copies of chunk 1 overwrite, so no other wave
+  // reads or writes them in between.  Rows are swizzled like K rows; lanes
+  // past the item copy the pass's last row (finite; their rows see no key).
+  constexpr int RPB = 1024 / C::QROWB;
+  const uint32_t q_lds = k_lds + C::SLOT;
+  if constexpr (C::QLDS) {
+#pragma unroll
+    for (int b = 0; b < C::QBLK; ++b) {
+      const int rr = b * RPB + lane / (C::QROWB / 16);  // 32 j + r
+      const int pc = lane % (C::QROWB / 16);
+      const int xr = min(it.row0 + rg * 32 + (rr & 31), p.n_tokens - 1);
+      const int c = pc ^ swz_k<C::QROWB>(rr);
+      const uint32_t off = ((uint32_t)xr * (uint32_t)p.hq + (uint32_t)(h0 + (rr >> 5))) * C::QROWB + (uint32_t)c * 16;
+      dma16(p.q, off, q_lds + (uint32_t)(b * C::NW + wave) * 1024);
+    }
+  }
+
   load_chunk_list(p, it, chunks, tid, C::NT);
   const SpbRow row = load_row(p, x, active);
   QFrag<D, IN> qf[HPW];
+  if constexpr (!C::QLDS) {
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) load_q<D, IN>(qf[j], p, x, h0 + j, active, half);
+    for (int j = 0; j < HPW; ++j) load_q<D, IN>(qf[j], p, x, h0 + j, active, half);
+  }
 
   // fragment offsets in the swizzled layout
   FragOffsets<D, IN> fo;
@@ -748,13 +782,35 @@ branch_attention_dma(AttnParams p) {
   }
   __syncthreads();  // chunk list in LDS
   if (!early) issue(0);
-  wait_all_loads();  // chunk 0, the row and the Q fragments
+  wait_all_loads();  // chunk 0, the row and the Q rows
   lds_barrier();
+  if constexpr (C::QLDS) {
+    // Q fragments: the K fragment pieces of row 32 j + qi of the Q blocks
+    const char *qbase = ring + C::SLOT;
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int rr = j * 32 + qi;
+      const char *rowp = qbase + ((rr / RPB) * C::NW + wave) * 1024 + (rr % RPB) * C::QROWB;
+#pragma unroll
+      for (int t = 0; t < QFrag<D, IN>::STEPS; ++t) {
+        if constexpr (C::FP8) {
+          const u32x4 a0 = *(const u32x4 *)(rowp + (((4 * t + 2 * half) ^ swz_k<C::QROWB>(rr)) << 4));
+          const u32x4 a1 = *(const u32x4 *)(rowp + (((4 * t + 2 * half + 1) ^ swz_k<C::QROWB>(rr)) << 4));
+          qf[j].f[t] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        } else {
+          const u32x4 a = *(const u32x4 *)(rowp + (((2 * t + half) ^ swz_k<C::QROWB>(rr)) << 4));
+          qf[j].f[t] = *(const bf16x8_t *)&a;
+        }
+      }
+    }
+    // the reads are done before this wave's copies of chunk 1 reuse the blocks
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
   if (nch > 1) issue(1);
 
   auto block = [&](int slot, const Vis &vis, bool two, bool masked, bool anc) {
-    const char *Kb = Ks[slot];
-    const char *Vb = Vs[slot];
+    const char *Kb = ring + slot * C::SLOT;
+    const char *Vb = Kb + C::BUFK;
     f32x16 s0[HPW], s1[HPW];
     if constexpr (C::FP8)
       qk_chunk_fp8<D, HPW, C::ROWB_K>(Kb, fo, qf, s0, s1, two);
@@ -792,7 +848,38 @@ branch_attention_dma(AttnParams p) {
     if (i + 2 < nch) issue(i + 2);
   }
 
-  if (active) {
+  if constexpr (OUT == SPB_BF16) {
+    // bf16 O through LDS, so that each global store writes whole 16-byte
+    // pieces of 4 (or 8) consecutive rows: row r of the wave's 32 (heads
+    // h0 .. h0 + HPW - 1 side by side, OROWB bytes) at ring + wave * 32 *
+    // OROWB, 16-byte pieces swizzled by row.  The loop's last barrier has
+    // freed the ring; each wave reads back only what it wrote.
+    constexpr int NP = C::OROWB / 16;
+    char *tile = ring + wave * 32 * C::OROWB;
+    if (nch == 0) lds_barrier();  // no loop barrier: other waves may still read their Q blocks
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const float l = st[j].l + __shfl_xor(st[j].l, 32);
+      const float inv = p.s_v / l;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int piece = (j * D + db * 32 + gg * 8) / 8;  // d = db*32 + gg*8 + half*4 .. +4
+          const u32x2 v = {pack_bf16(o[j][db][4 * gg] * inv, o[j][db][4 * gg + 1] * inv),
+                           pack_bf16(o[j][db][4 * gg + 2] * inv, o[j][db][4 * gg + 3] * inv)};
+          *(u32x2 *)(tile + qi * C::OROWB + ((piece ^ swz_k<C::OROWB>(qi)) << 4) + half * 8) = v;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int b = 0; b < 32 * C::OROWB / 1024; ++b) {
+      const int r = b * (1024 / C::OROWB) + lane / NP, pc = lane % NP;
+      const u32x4 v = *(const u32x4 *)(tile + r * C::OROWB + ((pc ^ swz_k<C::OROWB>(r)) << 4));
+      if (rg * 32 + r < it.nrows)
+        *(u32x4 *)((char *)p.o + ((size_t)(it.row0 + rg * 32 + r) * p.hq + h0) * (2 * D) + pc * 16) = v;
+    }
+  } else if (active) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) store_o<D, OUT>(p, x, h0 + j, half, st[j], o[j]);
   }
