@@ -13,8 +13,8 @@ from tests.test_gpu_invariance import _same
 
 pytestmark = pytest.mark.gpu
 
-# Bounds, derived in the design doc from the rounding points: activations are
-# rounded to bf16 once per op (2^-9 relative each), the residual stream is f32.
+# Bounds from the rounding points: activations are rounded to bf16 once per
+# op (2^-9 relative each), the residual stream is f32.
 TOL_OP = 1e-2       # one linear layer or rmsnorm, per row, relative L2
 TOL_HIDDEN = 3e-2   # the final hidden rows after the stack, per row, relative L2
 
