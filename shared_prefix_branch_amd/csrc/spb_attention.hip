@@ -732,14 +732,17 @@ branch_attention_dma(AttnParams p) {
   constexpr int RPB = 1024 / C::QROWB;
   const uint32_t q_lds = k_lds + C::SLOT;
   if constexpr (C::QLDS) {
+    // offsets from the wave's first row (64-bit base), so Q may exceed 4 GiB
+    const int xb = min(it.row0 + rg * 32, p.n_tokens - 1);
+    const char *qb = (const char *)p.q + ((size_t)xb * p.hq + h0) * C::QROWB;
 #pragma unroll
     for (int b = 0; b < C::QBLK; ++b) {
       const int rr = b * RPB + lane / (C::QROWB / 16);  // 32 j + r
       const int pc = lane % (C::QROWB / 16);
       const int xr = min(it.row0 + rg * 32 + (rr & 31), p.n_tokens - 1);
       const int c = pc ^ swz_k<C::QROWB>(rr);
-      const uint32_t off = ((uint32_t)xr * (uint32_t)p.hq + (uint32_t)(h0 + (rr >> 5))) * C::QROWB + (uint32_t)c * 16;
-      dma16(p.q, off, q_lds + (uint32_t)(b * C::NW + wave) * 1024);
+      const uint32_t off = ((uint32_t)(xr - xb) * (uint32_t)p.hq + (uint32_t)(rr >> 5)) * C::QROWB + (uint32_t)c * 16;
+      dma16(qb, off, q_lds + (uint32_t)(b * C::NW + wave) * 1024);
     }
   }
 

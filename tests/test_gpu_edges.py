@@ -102,3 +102,33 @@ def test_plan_upload_device_path():
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(spb.SpbError):
         case.plan.upload(0, small, stream=stream)
+
+
+def test_attention_q_rows_past_4gib():
+    # one pass of 625,505 rows at 32 query heads x 128 (bf16): Q rows from
+    # 524,288 on start more than 2^32 bytes into Q, K and V stay under 4 GiB.
+    # Inputs at the start, across that row and at the end (the floors are
+    # packed last) against the oracle, sharp scores with the guard.
+    wl = synth.make_workload("news", hq=32, hkv=8, head_dim=128, hidden=128, vocab=1000)
+    wl.problem = synth.make_problem("random", 41, vocab=1000, n_inputs=1100, n_questions=6, min_content=420,
+                                    max_content=560, max_len=30, max_options=4, max_option_tokens=3)
+    wl.inputs = synth.logical_inputs(wl.problem, True)
+    say("case: one pass of 625,505 rows, Q over 4 GiB, bf16 hq=32 hkv=8, sharp")
+    case = Case(wl, 800000, peaked=True, sharp=True)
+    assert case.plan.n_passes == 1
+    n_tok = case.plan.info(0)["n_tokens"]
+    assert n_tok * 32 * 128 * 2 > 2 ** 32 + 2 ** 28
+    lr, _ = case.plan.rows(0)
+    off, _ = case.plan.inputs()
+
+    def pass_rows(n):
+        return np.nonzero((lr >= off[n]) & (lr < off[n + 1]))[0]
+
+    n_in = wl.problem.n_inputs
+    across = next(n for n in range(n_in) if pass_rows(n).min() <= 524288 <= pass_rows(n).max())
+    inputs = [0, across, n_in - 2, n_in - 1, n_in + 1]
+    assert all(pass_rows(n).min() > 524288 for n in inputs[2:])
+    W, _ = lm_head(wl)
+    case.run(W)
+    ea = check_attention(case, inputs=inputs, branches_per_input=2, rng=np.random.default_rng(41), guard=True)
+    say(f"  inputs {inputs}: attention rel err {ea:.2e}")
