@@ -145,6 +145,34 @@ def measured_traffic(kernel: str, workload: str, mode: str = "per_launch"):
     return float(m_val.group(1)), rel
 
 
+def head_roofline(M, head_ms, hidden: int, vocab: int) -> dict:
+    """The lm head's roofline from its launches: M scored rows and event time
+    (ms) per launch.  Each launch is placed against its own bound (HBM up to
+    HEAD_RIDGE_ROWS rows per W stream, MFMA above); the reported figure
+    aggregates the launches of the bound holding most of the head's time and
+    never mixes the two."""
+    M = np.asarray(M, dtype=np.float64)
+    head_ms = np.asarray(head_ms, dtype=np.float64)
+    flops = 2.0 * hidden * vocab * M
+    nbytes = 2.0 * hidden * vocab + M * hidden * 2.0
+    bounds = np.where(M > HEAD_RIDGE_ROWS, "mfma", "hbm")
+    fracs = np.where(bounds == "mfma", flops / (head_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     nbytes / (head_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+    t_mfma = float(head_ms[bounds == "mfma"].sum())
+    bound = "mfma" if t_mfma >= 0.5 * float(head_ms.sum()) else "hbm"
+    sel = bounds == bound
+    if bound == "mfma":
+        ach = float(flops[sel].sum() / (head_ms[sel].sum() * 1e-3) / 1e12)
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = float(nbytes[sel].sum() / (head_ms[sel].sum() * 1e-3) / 1e9)
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    return {"flops": flops, "bytes": nbytes, "bounds": bounds, "fracs": fracs, "bound": bound, "sel": sel,
+            "roof": roof, "time_weighted_frac": round(float((fracs * head_ms).sum() / head_ms.sum()), 4)}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -330,19 +358,11 @@ def main():
     att_ai = att_flops.sum() / att_bytes.sum()
     att_bound = "mfma" if att_ai > att_ridge else "hbm"
     M = np.array([sum(plan.info(k)["n_scored_rows"] for k in g) for g in groups], dtype=np.float64)
-    head_flops = 2.0 * d.hidden * d.vocab * M
-    w_bytes = 2.0 * d.hidden * d.vocab
-    head_bytes = w_bytes + M * d.hidden * 2.0
+    hr = head_roofline(M, head_ms, d.hidden, d.vocab)
+    head_flops, head_bytes, bounds, fracs = hr["flops"], hr["bytes"], hr["bounds"], hr["fracs"]
     head_tflops = head_flops.sum() / (head_ms.sum() * 1e-3) / 1e12
     head_gbs = head_bytes.sum() / (head_ms.sum() * 1e-3) / 1e9
-    # each launch against its own bound; the roofline aggregates the launches
-    # of the bound holding most of the head's time
-    bounds = np.where(M > HEAD_RIDGE_ROWS, "mfma", "hbm")
-    fracs = np.where(bounds == "mfma", head_flops / (head_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                     head_bytes / (head_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
-    t_mfma = float(head_ms[bounds == "mfma"].sum())
-    head_bound = "mfma" if t_mfma >= 0.5 * float(head_ms.sum()) else "hbm"
-    sel = bounds == head_bound
+    head_bound, sel = hr["bound"], hr["sel"]
     stack = None
     if n_lin:
         # linear launches: (n, k) per kind; m = the pass's tokens
@@ -376,14 +396,7 @@ def main():
         traffic, traffic_src = None, "counters taken with one lm-head launch per pass only"
     else:
         traffic, traffic_src = measured_traffic(kernel_name, args.workload)
-    if head_bound == "mfma":
-        ach = float(head_flops[sel].sum() / (head_ms[sel].sum() * 1e-3) / 1e12)
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    else:
-        ach = float(head_bytes[sel].sum() / (head_ms[sel].sum() * 1e-3) / 1e9)
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof = dict(hr["roof"])
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["traffic_source"] = traffic_src
     roof["algorithmic_bytes_per_launch"] = round(float(head_bytes.mean()))
@@ -392,7 +405,7 @@ def main():
                        f"achieved is over those"
     # the fp32 head runs three bf16 products per logit term (hi, mid, lo planes of h)
     roof["mfma_products_per_term"] = 3 if head_kind == 2 else 1
-    roof["time_weighted_frac"] = round(float((fracs * head_ms).sum() / head_ms.sum()), 4)
+    roof["time_weighted_frac"] = hr["time_weighted_frac"]
     roof["per_launch"] = {"ms": [round(x, 4) for x in head_ms], "scored_rows": M.astype(int).tolist(),
                           "bound": bounds.tolist(), "frac": [round(float(x), 4) for x in fracs],
                           "flops_per_scored_row": 2 * d.hidden * d.vocab,
