@@ -251,7 +251,8 @@ spb_status spb_plan_meta_copy(const spb_plan *plan, int32_t pass, void *host_dst
  * with a call in flight.  With it, V is first widened to bf16 there (exact:
  * every e4m3 value is a bf16 value) and K/V chunks reach LDS by asynchronous
  * copies; without it they pass through registers.  The two give the same
- * bits: same MFMAs in the same order.  SPB_ERR_SIZE if it is too small. */
+ * bits: same MFMAs in the same order.  SPB_ERR_SIZE if it is too small;
+ * SPB_ERR_LIMIT if the widened V (n_tokens * hkv * head_dim * 2) reaches 4 GiB. */
 typedef struct {
   const void *q, *k, *v;
   void *o;
